@@ -1,0 +1,24 @@
+"""MI355X-native linear-attention recurrent-state path.
+
+Kimi Delta Attention (per-channel decay) and Gated DeltaNet (per-head scalar
+gate) decode steps, the kernel-size-4 depthwise causal short conv, and the
+chunked prefill, all keyed by slot indices into slot-indexed state pools.
+The compute lives in hand-written HIP kernels for gfx950 behind the C ABI in
+``include/la.h`` (``libla.so``); :mod:`.binding` marshals torch tensors and
+streams into that ABI.  Importing a kernel entry point loads ``libla.so`` and
+raises if it has not been built -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+_BINDING_NAMES = {
+    "kda_decode_step", "gdn_decode_step", "shortconv_update", "shortconv_prefill",
+    "kda_prefill_chunked", "gdn_prefill_chunked", "prefill_workspace_bytes",
+    "pool_bytes", "version", "LAError", "load_library", "library_path",
+}
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

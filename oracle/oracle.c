@@ -1,0 +1,304 @@
+/*
+ * oracle.c -- plain, sequential, fp64 CPU oracle for the linear-attention
+ * recurrent-state path (Kimi Delta Attention and Gated DeltaNet decode and
+ * prefill, with the kernel-size-4 depthwise causal short conv).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file: only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, helper or constant
+ * with the HIP library; its inputs arrive as fp64 arrays (exact copies of the
+ * stored bf16/fp32 values) and it rounds to the storage dtype with its own
+ * codec below.
+ *
+ * Every function is the plain definition written out, token by token, with no
+ * blocking, fusion or reordering.  Sources (the pages):
+ *   [SGLang-pool]  "SGLang之KV Cache内存池机制" (yuyanqi.com), section 8.2
+ *                  (state shapes and pool layout) and section 8.5 (the decode
+ *                  kernel's steps: load state, decay by exp(g), delta
+ *                  correction, beta gating, rank-1 update, output, write-back;
+ *                  extend reads the initial state from the pool and writes the
+ *                  final state back in place).
+ *   [mamba-ish]    xxmr.cn/news/181459, the "Conv state" passage (depthwise
+ *                  causal short conv, kernel 4, keep the last 3 inputs), the
+ *                  "KDA recurrent update" passage (alpha is per key channel
+ *                  for KDA, a scalar per head for GDN) and the ReplaySSM
+ *                  exact-commit passage (k = rawk / sqrt(|rawk|^2 + eps),
+ *                  alpha = exp(g), S <- S Diag(alpha), d = beta (v - S k),
+ *                  S <- S + d k^T).
+ *   [deploy]       hotelren.com/news/5417338 section 2.1 (state [H, d_v, d_k]
+ *                  accumulating v k^T; conv state keeps the last 3 q/k/v
+ *                  projections).
+ * Readings where the pages are silent (all passed in or fixed here):
+ *   - state orientation [H, d_v, d_k], d_k contiguous;
+ *   - channel order of x / conv state: [Q heads | K heads | V heads],
+ *     head-major inside each block;
+ *   - conv is a cross-correlation: tap 3 multiplies the current token,
+ *     conv-state row 0 is the oldest token;
+ *   - SiLU after the conv on every channel; optional bias;
+ *   - q is L2-normalised like k, with the same eps form;
+ *   - the output uses the post-update state, times `scale`;
+ *   - GQA: value head h reads q/k head floor(h / (H_v / H_qk)).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Storage dtypes the oracle rounds to. */
+enum { ORC_FP32 = 0, ORC_BF16 = 1, ORC_FP64 = 2 };
+
+/* ------------------------------------------------------------------ */
+/* Rounding codec (independent of any GPU conversion).                */
+/* ------------------------------------------------------------------ */
+
+/* Round an fp64 value to the nearest bf16 value, ties to even.
+ * bf16 = 1 sign bit, 8 exponent bits (same range as fp32), 8 significant
+ * bits.  Works in the value domain: the quantum of a bf16 number with
+ * binade exponent e (|x| in [2^(e-1), 2^e)) is 2^(e-8); below the normal
+ * range the quantum stays at the subnormal spacing 2^-133. */
+static double round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);                       /* |x| = m * 2^e, m in [0.5, 1) */
+    if (e < -125) e = -125;             /* subnormal bf16 spacing */
+    double quantum = ldexp(1.0, e - 8);
+    double r = nearbyint(x / quantum) * quantum; /* current mode: ties-to-even */
+    const double bf16_max = ldexp(255.0, 120);   /* (2 - 2^-7) * 2^127 */
+    if (fabs(r) > bf16_max) return copysign(INFINITY, x);
+    return r;
+}
+
+double orc_round(double x, int dtype)
+{
+    switch (dtype) {
+    case ORC_FP32: return (double)(float)x; /* C conversion rounds to nearest-even */
+    case ORC_BF16: return round_bf16(x);
+    default: return x;
+    }
+}
+
+void orc_round_array(double *x, int64_t n, int dtype)
+{
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_round(x[i], dtype);
+}
+
+static double silu(double y) { return y / (1.0 + exp(-y)); }
+
+/* ------------------------------------------------------------------ */
+/* Short conv, one decode token ([mamba-ish] "Conv state" passage;    */
+/* [SGLang-pool] 8.5 step 1, in-place update of the indexed rows).    */
+/* ------------------------------------------------------------------ */
+
+/* One token per batch entry.  x [B, C]; w [C, 4]; bias [C] or NULL;
+ * conv_pool rows [3, C] at conv_pool + slot * conv_stride.
+ * y [B, C] receives SiLU(sum_i w[c,i] * window[i] + bias[c]) in fp64 (not
+ * rounded; callers round to their output dtype).  The conv state is rolled:
+ * rows 1, 2 move to 0, 1 and the current input becomes row 2, rounded to
+ * conv_dtype (a plain copy when x already has that dtype). */
+void orc_shortconv_step(int B, int C, const double *x, const double *w,
+                        const double *bias, double *conv_pool,
+                        int64_t conv_stride, int conv_dtype,
+                        const int32_t *slots, double *y)
+{
+    for (int b = 0; b < B; ++b) {
+        double *cs = conv_pool + (int64_t)slots[b] * conv_stride;
+        for (int c = 0; c < C; ++c) {
+            double win[4] = {cs[c], cs[C + c], cs[2 * C + c], x[(int64_t)b * C + c]};
+            double acc = bias ? bias[c] : 0.0;
+            for (int i = 0; i < 4; ++i) acc += w[4 * c + i] * win[i];
+            y[(int64_t)b * C + c] = silu(acc);
+            cs[c] = win[1];
+            cs[C + c] = win[2];
+            cs[2 * C + c] = orc_round(win[3], conv_dtype);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* The gated delta rule, one token for one (entry, value head).       */
+/* ------------------------------------------------------------------ */
+
+/* L2 normalisation x / sqrt(sum x^2 + eps) ([mamba-ish] ReplaySSM
+ * exact-commit passage, applied to k and, by the same form, to q). */
+static void l2norm(const double *in, double *out, int n, double eps)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) ss += in[i] * in[i];
+    double inv = 1.0 / sqrt(ss + eps);
+    for (int i = 0; i < n; ++i) out[i] = in[i] * inv;
+}
+
+/* S [dv, dk] (row i = value channel i) is updated in place:
+ *   S <- S Diag(alpha);  d = beta (v - S k);  S <- S + d k^T;  o = scale S q.
+ * q, k are already normalised; alpha has dk entries. */
+static void delta_rule_token(double *S, int dk, int dv, const double *q,
+                             const double *k, const double *v,
+                             const double *alpha, double beta, double scale,
+                             double *o)
+{
+    for (int i = 0; i < dv; ++i) {
+        double *row = S + (int64_t)i * dk;
+        for (int c = 0; c < dk; ++c) row[c] *= alpha[c];
+        double u = 0.0;
+        for (int c = 0; c < dk; ++c) u += row[c] * k[c];
+        double d = beta * (v[i] - u);
+        for (int c = 0; c < dk; ++c) row[c] += d * k[c];
+        double p = 0.0;
+        for (int c = 0; c < dk; ++c) p += row[c] * q[c];
+        o[i] = scale * p;
+    }
+}
+
+/* Decode recurrence for one token per entry.
+ * q, k [B, Hqk, dk] and v [B, Hv, dv] are the raw (pre-normalisation) vectors.
+ * KDA (kda=1): g [B, Hv, dk] log-decays, one per key channel.
+ * GDN (kda=0): g [B, Hv], one scalar per value head.
+ * beta [B, Hv].  ssm_pool rows [Hv, dv, dk] at ssm_pool + slot * ssm_stride;
+ * each row is read, advanced in fp64, and stored rounded to state_dtype.
+ * out [B, Hv, dv] is rounded to io_dtype. */
+int orc_recurrent_step(int kda, int B, int Hqk, int Hv, int dk, int dv,
+                       const double *q, const double *k, const double *v,
+                       const double *g, const double *beta,
+                       const int32_t *slots, double *ssm_pool,
+                       int64_t ssm_stride, int state_dtype, double *out,
+                       int io_dtype, double eps, double scale)
+{
+    if (Hqk <= 0 || Hv % Hqk != 0) return -1;
+    const int group = Hv / Hqk;
+    double *qn = malloc(sizeof(double) * dk), *kn = malloc(sizeof(double) * dk);
+    double *alpha = malloc(sizeof(double) * dk), *o = malloc(sizeof(double) * dv);
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hv; ++h) {
+            const int kh = h / group;
+            l2norm(q + ((int64_t)b * Hqk + kh) * dk, qn, dk, eps);
+            l2norm(k + ((int64_t)b * Hqk + kh) * dk, kn, dk, eps);
+            for (int c = 0; c < dk; ++c)
+                alpha[c] = exp(kda ? g[((int64_t)b * Hv + h) * dk + c] : g[(int64_t)b * Hv + h]);
+            double *S = ssm_pool + (int64_t)slots[b] * ssm_stride + (int64_t)h * dv * dk;
+            delta_rule_token(S, dk, dv, qn, kn, v + ((int64_t)b * Hv + h) * dv, alpha,
+                             beta[(int64_t)b * Hv + h], scale, o);
+            for (int i = 0; i < dv * dk; ++i) S[i] = orc_round(S[i], state_dtype);
+            for (int i = 0; i < dv; ++i)
+                out[((int64_t)b * Hv + h) * dv + i] = orc_round(o[i], io_dtype);
+        }
+    }
+    free(qn); free(kn); free(alpha); free(o);
+    return 0;
+}
+
+/* Full decode step: the short conv + SiLU over x [B, C] (skipped when
+ * w == NULL, then x already holds the post-conv q|k|v), the split into
+ * q [Hqk, dk] | k [Hqk, dk] | v [Hv, dv], then the recurrence.  The post-conv
+ * q/k/v stay in fp64 (never rounded to the I/O dtype). */
+int orc_decode(int kda, int B, int Hqk, int Hv, int dk, int dv,
+               const double *x, const double *w, const double *bias,
+               double *conv_pool, int64_t conv_stride, int conv_dtype,
+               const double *g, const double *beta, const int32_t *slots,
+               double *ssm_pool, int64_t ssm_stride, int state_dtype,
+               double *out, int io_dtype, double eps, double scale)
+{
+    const int C = 2 * Hqk * dk + Hv * dv;
+    double *y = malloc(sizeof(double) * (size_t)B * C);
+    if (w) orc_shortconv_step(B, C, x, w, bias, conv_pool, conv_stride, conv_dtype, slots, y);
+    else memcpy(y, x, sizeof(double) * (size_t)B * C);
+    double *q = malloc(sizeof(double) * (size_t)B * Hqk * dk);
+    double *k = malloc(sizeof(double) * (size_t)B * Hqk * dk);
+    double *v = malloc(sizeof(double) * (size_t)B * Hv * dv);
+    for (int b = 0; b < B; ++b) {
+        const double *yb = y + (int64_t)b * C;
+        memcpy(q + (int64_t)b * Hqk * dk, yb, sizeof(double) * Hqk * dk);
+        memcpy(k + (int64_t)b * Hqk * dk, yb + Hqk * dk, sizeof(double) * Hqk * dk);
+        memcpy(v + (int64_t)b * Hv * dv, yb + 2 * Hqk * dk, sizeof(double) * Hv * dv);
+    }
+    int rc = orc_recurrent_step(kda, B, Hqk, Hv, dk, dv, q, k, v, g, beta, slots, ssm_pool,
+                                ssm_stride, state_dtype, out, io_dtype, eps, scale);
+    free(y); free(q); free(k); free(v);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Prefill over packed variable-length sequences ([SGLang-pool] 8.5,  */
+/* extend: initial state read from the pool, final state written     */
+/* back; the method's result is the same recurrence token by token).  */
+/* ------------------------------------------------------------------ */
+
+/* Short conv over packed sequences.  Sequence n covers tokens
+ * [cu[n], cu[n+1]) of x [T, C].  Its history comes from conv_pool row
+ * slot_in[n] (zeros when slot_in[n] < 0); after the last token the three most
+ * recent pre-conv inputs (older history shifted in for sequences shorter than
+ * three tokens) are stored to row slot_out[n].  y [T, C] gets the SiLU output
+ * rounded to io_dtype. */
+void orc_shortconv_prefill(int N, int C, const double *x, const int32_t *cu,
+                           const int32_t *slot_in, const int32_t *slot_out,
+                           const double *w, const double *bias,
+                           double *conv_pool, int64_t conv_stride,
+                           int conv_dtype, double *y, int io_dtype)
+{
+    double *hist = malloc(sizeof(double) * 3 * (size_t)C);
+    for (int n = 0; n < N; ++n) {
+        if (slot_in[n] >= 0)
+            memcpy(hist, conv_pool + (int64_t)slot_in[n] * conv_stride, sizeof(double) * 3 * C);
+        else
+            memset(hist, 0, sizeof(double) * 3 * (size_t)C);
+        for (int t = cu[n]; t < cu[n + 1]; ++t) {
+            for (int c = 0; c < C; ++c) {
+                double win[4] = {hist[c], hist[C + c], hist[2 * C + c], x[(int64_t)t * C + c]};
+                double acc = bias ? bias[c] : 0.0;
+                for (int i = 0; i < 4; ++i) acc += w[4 * c + i] * win[i];
+                y[(int64_t)t * C + c] = orc_round(silu(acc), io_dtype);
+                hist[c] = win[1];
+                hist[C + c] = win[2];
+                hist[2 * C + c] = orc_round(win[3], conv_dtype);
+            }
+        }
+        memcpy(conv_pool + (int64_t)slot_out[n] * conv_stride, hist, sizeof(double) * 3 * C);
+    }
+    free(hist);
+}
+
+/* Recurrent-state prefill over packed sequences.  q, k [T, Hqk, dk] and
+ * v [T, Hv, dv] with token strides q_stride, k_stride, v_stride (elements);
+ * g [T, Hv, dk] (KDA) or [T, Hv] (GDN); beta [T, Hv]; out [T, Hv, dv].
+ * The state starts from pool row slot_in[n] (zero when slot_in[n] < 0), is
+ * carried in fp64 over the whole sequence, and is rounded to state_dtype only
+ * when written to row slot_out[n]. */
+int orc_prefill(int kda, int N, int Hqk, int Hv, int dk, int dv,
+                const double *q, int64_t q_stride, const double *k,
+                int64_t k_stride, const double *v, int64_t v_stride,
+                const double *g, const double *beta, const int32_t *cu,
+                const int32_t *slot_in, const int32_t *slot_out,
+                double *ssm_pool, int64_t ssm_stride, int state_dtype,
+                double *out, int io_dtype, double eps, double scale)
+{
+    if (Hqk <= 0 || Hv % Hqk != 0) return -1;
+    const int group = Hv / Hqk;
+    const size_t state_elems = (size_t)Hv * dv * dk;
+    double *S = malloc(sizeof(double) * state_elems);
+    double *qn = malloc(sizeof(double) * dk), *kn = malloc(sizeof(double) * dk);
+    double *alpha = malloc(sizeof(double) * dk), *o = malloc(sizeof(double) * dv);
+    for (int n = 0; n < N; ++n) {
+        if (slot_in[n] >= 0)
+            memcpy(S, ssm_pool + (int64_t)slot_in[n] * ssm_stride, sizeof(double) * state_elems);
+        else
+            memset(S, 0, sizeof(double) * state_elems);
+        for (int t = cu[n]; t < cu[n + 1]; ++t) {
+            for (int h = 0; h < Hv; ++h) {
+                const int kh = h / group;
+                l2norm(q + (int64_t)t * q_stride + (int64_t)kh * dk, qn, dk, eps);
+                l2norm(k + (int64_t)t * k_stride + (int64_t)kh * dk, kn, dk, eps);
+                for (int c = 0; c < dk; ++c)
+                    alpha[c] = exp(kda ? g[((int64_t)t * Hv + h) * dk + c] : g[(int64_t)t * Hv + h]);
+                delta_rule_token(S + (size_t)h * dv * dk, dk, dv, qn, kn,
+                                 v + (int64_t)t * v_stride + (int64_t)h * dv, alpha,
+                                 beta[(int64_t)t * Hv + h], scale, o);
+                for (int i = 0; i < dv; ++i)
+                    out[((int64_t)t * Hv + h) * dv + i] = orc_round(o[i], io_dtype);
+            }
+        }
+        double *dst = ssm_pool + (int64_t)slot_out[n] * ssm_stride;
+        for (size_t i = 0; i < state_elems; ++i) dst[i] = orc_round(S[i], state_dtype);
+    }
+    free(S); free(qn); free(kn); free(alpha); free(o);
+    return 0;
+}
