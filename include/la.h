@@ -1,0 +1,192 @@
+/*
+ * la.h -- C ABI of libla: the recurrent-state path of hybrid linear-attention
+ * layers (Kimi Delta Attention and Gated DeltaNet) on AMD MI355X (gfx950).
+ *
+ * The method.  Per request and value head, a fixed-size state S[d_v, d_k]
+ * (row i = value channel i, d_k contiguous) advances once per token:
+ *     S' = S Diag(alpha),  d = beta (v - S' k),  S = S' + d k^T,  o = scale S q
+ * with alpha = exp(g).  KDA has one log-decay g per key channel; GDN has one
+ * scalar per value head.  q and k are L2-normalised, x / sqrt(|x|^2 + eps).
+ * Sources: the decode kernel's steps and the in-place slot update in
+ * "SGLang之KV Cache内存池机制" (yuyanqi.com) section 8.5; the state and conv
+ * pool layouts in its section 8.2; the per-key-channel alpha of KDA and the
+ * exact replay (normalise k, decay, residual times beta, rank-1 update) in the
+ * ReplaySSM passages of xxmr.cn/news/181459; the short conv in that page's
+ * "Conv state" passage and in hotelren.com/news/5417338 section 2.1.
+ *
+ * Short conv.  A depthwise causal convolution of kernel 4 over the projected
+ * q|k|v channels x[C], C = 2 H_qk d_k + H_v d_v, channel blocks
+ * [Q heads | K heads | V heads], head-major inside each block.  With the
+ * 3-token history h[0..2] (row 0 oldest) kept per slot:
+ *     y[c] = SiLU( w[c,0] h[0][c] + w[c,1] h[1][c] + w[c,2] h[2][c]
+ *                  + w[c,3] x[c] + bias[c] )
+ * then the history rolls: h <- [h[1], h[2], x].
+ *
+ * Conventions shared by every call.
+ *   - Device pointers unless stated; every buffer is owned by the caller.
+ *     The library never allocates, frees or synchronises: each call only
+ *     launches kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns.
+ *   - Dtype codes: LA_F32 or LA_BF16.  Weights (w, bias), gates (g, beta)
+ *     are always fp32; slots and cu_seqlens are int32.
+ *   - Pools have `num_rows` = P + 1 rows; row 0 is the padding row (several
+ *     padded entries may name it; its contents are then undefined).  A pool
+ *     row is addressed as base + slot * slot_stride (elements), so per-layer
+ *     views of a [layers, P+1, ...] tensor work.  Inner dims are contiguous.
+ *   - Pools are read and written in place, only at the rows named by the
+ *     slots.  Non-zero slots within one call must be distinct (else the
+ *     result is undefined).  Slots outside [0, num_rows) are skipped by the
+ *     kernels (their outputs are written as zeros and no pool row is
+ *     touched); with the environment variable LA_CHECK=1 the call instead
+ *     copies the slots to the host, synchronously, and returns LA_ERR_SLOT
+ *     for an out-of-range or duplicate non-zero slot.
+ *   - Alignment: every pointer must be 16-byte aligned and every row stride
+ *     a multiple of 16 bytes (LA_ERR_ARG otherwise).
+ *   - Errors: no exception crosses the ABI.  Calls return an LA_* status;
+ *     la_last_error() gives a thread-local message for the last failure.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_VERSION 1
+
+/* Status codes. */
+#define LA_OK 0
+#define LA_ERR_ARG (-1)         /* null pointer, bad dimension, misalignment */
+#define LA_ERR_UNSUPPORTED (-2) /* dtype combination or head dim not built */
+#define LA_ERR_WORKSPACE (-3)   /* workspace missing or too small */
+#define LA_ERR_SLOT (-4)        /* LA_CHECK=1 only: bad or duplicate slot */
+#define LA_ERR_HIP (-5)         /* a HIP call or kernel launch failed */
+
+/* Dtype codes. */
+#define LA_F32 0
+#define LA_BF16 1
+
+/* Prefill precision modes (kda_prefill_chunked / gdn_prefill_chunked). */
+#define LA_PREFILL_FP32 0 /* every intra-block product in fp32 */
+#define LA_PREFILL_BF16 1 /* bf16 MFMA operands, fp32 accumulation */
+
+int la_version(void);
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char *la_last_error(void);
+
+/* Host call.  Bytes of the conv and SSM state pools for `layers` layers and
+ * `slots` usable slots (slots + 1 rows each, row 0 = padding):
+ *   ssm  = layers (slots+1) H_v d_v d_k  size(state_dtype)
+ *   conv = layers (slots+1) 3 C          size(conv_dtype)
+ * (section 8.2 of the pool page gives the [layers, pool_size+1, ...] shapes;
+ * the allocation logs of hotelren.com section 4.2 follow from it).
+ * Returns LA_OK, or LA_ERR_ARG for a negative size or unknown dtype. */
+int la_pool_bytes(int layers, int slots, int H_v, int d_v, int d_k, int conv_channels,
+                  int state_dtype, int conv_dtype, int64_t *ssm_bytes, int64_t *conv_bytes);
+
+/* One decode token of the short conv + SiLU, standalone.
+ *   x [B, C] (x_dtype) input projections of the current token;
+ *   w [C, 4], bias [C] or NULL;
+ *   conv_pool rows [3, C] (conv_dtype) at conv_pool + slot * conv_slot_stride;
+ *   slots [B]; y [B, C] (x_dtype) receives the activations.
+ * Rolls the history of each named row in place (the current input becomes
+ * row 2, converted to conv_dtype; a bit copy when the dtypes agree). */
+int shortconv_update(int B, int C, const void *x, int x_dtype, const float *w,
+                     const float *bias, void *conv_pool, int64_t conv_slot_stride,
+                     int conv_dtype, int num_rows, const int32_t *slots, void *y,
+                     void *stream);
+
+/* One KDA decode token per request, fused: short conv + SiLU over x, split
+ * into q [H_qk, d_k] | k [H_qk, d_k] | v [H_v, d_v], L2 norm of q and k, then
+ * the gated delta rule with a per-key-channel decay, in place on the state.
+ *   x [B, C] (io_dtype); C = 2 H_qk d_k + H_v d_v.
+ *   conv_w [C, 4] or NULL: NULL means x already holds the post-conv q|k|v;
+ *     the conv, the SiLU and the conv pool are then skipped (conv_pool may be
+ *     NULL).  conv_b [C] or NULL.
+ *   conv_pool rows [3, C] (conv_dtype), see shortconv_update.
+ *   g [B, H_v, d_k] fp32 log-decays (alpha = exp(g)); beta [B, H_v] fp32.
+ *   slots [B]; ssm_pool rows [H_v, d_v, d_k] (state_dtype) at
+ *     ssm_pool + slot * ssm_slot_stride.
+ *   out [B, H_v, d_v] (io_dtype) = scale * S_t q_t with the updated state.
+ *   eps: L2-norm epsilon (1e-6 in the reference workloads); scale: output
+ *   scale (1.0).
+ * Supported: d_k == d_v in {16, 32, 64, 128}; H_v a multiple of H_qk (value
+ * head h reads q/k head h / (H_v / H_qk)); every dtype pair of fp32/bf16.
+ * Arithmetic is fp32; bf16 stores round to nearest even. */
+int kda_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, int io_dtype,
+                    const float *conv_w, const float *conv_b, void *conv_pool,
+                    int64_t conv_slot_stride, int conv_dtype, const float *g,
+                    const float *beta, const int32_t *slots, int num_rows, void *ssm_pool,
+                    int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                    float scale, void *stream);
+
+/* GDN decode: as kda_decode_step with one log-decay per value head,
+ * g [B, H_v] fp32 (the decay Diag(alpha) is alpha I). */
+int gdn_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, int io_dtype,
+                    const float *conv_w, const float *conv_b, void *conv_pool,
+                    int64_t conv_slot_stride, int conv_dtype, const float *g,
+                    const float *beta, const int32_t *slots, int num_rows, void *ssm_pool,
+                    int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                    float scale, void *stream);
+
+/* Short conv + SiLU over N packed sequences (prefill).  Sequence n covers
+ * tokens [cu_seqlens[n], cu_seqlens[n+1]) of x [T, C] (io_dtype); its history
+ * comes from conv-pool row slot_in[n] (zeros when slot_in[n] < 0) and the last
+ * three pre-conv inputs (older history shifted in when the sequence is
+ * shorter than three tokens) are written to row slot_out[n] (slot_in[n] ==
+ * slot_out[n] is allowed).  y [T, C] (io_dtype) receives the activations.
+ * cu_seqlens [N+1] must be non-decreasing from 0 to T. */
+int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype,
+                      const int32_t *cu_seqlens, const int32_t *slot_in,
+                      const int32_t *slot_out, const float *w, const float *bias,
+                      void *conv_pool, int64_t conv_slot_stride, int conv_dtype,
+                      int num_rows, void *y, void *stream);
+
+/* Chunked KDA prefill over N packed sequences (extend: the initial state is
+ * read from the pool, the final state written back; the result is that of
+ * the token-by-token recurrence, computed by blocks of 64 tokens).
+ *   q [T, H_qk, d_k], k [T, H_qk, d_k], v [T, H_v, d_v] (io_dtype; raw,
+ *     post-conv: q and k are L2-normalised inside) with token strides
+ *     q_stride, k_stride, v_stride in elements (>= the row size; lets q|k|v be
+ *     views into one [T, C] conv output).
+ *   g [T, H_v, d_k] fp32; beta [T, H_v] fp32; cu_seqlens [N+1].
+ *   slot_in [N] (< 0: zero initial state), slot_out [N] rows of
+ *     ssm_pool [H_v, d_v, d_k] (state_dtype).
+ *   out [T, H_v, d_v] (io_dtype).
+ *   mode: LA_PREFILL_FP32 or LA_PREFILL_BF16.
+ *   workspace: device scratch of at least prefill_workspace_bytes(...)
+ *     bytes, 256-byte aligned; contents need no initialisation.
+ * Supported: d_k == d_v == 128; H_v a multiple of H_qk. */
+int kda_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
+                        int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                        int64_t v_stride, int io_dtype, const float *g, const float *beta,
+                        const int32_t *cu_seqlens, const int32_t *slot_in,
+                        const int32_t *slot_out, int num_rows, void *ssm_pool,
+                        int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                        float scale, int mode, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* GDN prefill: as kda_prefill_chunked with g [T, H_v] (one log-decay per
+ * value head). */
+int gdn_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
+                        int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                        int64_t v_stride, int io_dtype, const float *g, const float *beta,
+                        const int32_t *cu_seqlens, const int32_t *slot_in,
+                        const int32_t *slot_out, int num_rows, void *ssm_pool,
+                        int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                        float scale, int mode, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Host call: workspace bytes the prefill needs for N sequences and T tokens
+ * (0 for invalid arguments). */
+size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

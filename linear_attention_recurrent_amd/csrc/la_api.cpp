@@ -1,0 +1,348 @@
+// la_api.cpp -- the extern "C" entry points declared in include/la.h.
+//
+// Host side only: argument validation, the optional checked mode (LA_CHECK=1:
+// slots and sequence offsets copied to the host and verified), dtype / head
+// dim dispatch and error reporting.  Every computation happens in the HIP
+// kernels; nothing here allocates, frees or synchronises outside checked mode.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "la.h"
+#include "la_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return LA_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool checked_mode()
+{
+    const char *s = std::getenv("LA_CHECK");
+    return s && s[0] == '1';
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == LA_F32 || d == LA_BF16; }
+
+int dsize(int d) { return d == LA_BF16 ? 2 : 4; }
+
+bool supported_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Copies n int32 values from device to host (checked mode only).
+int fetch_i32(const int32_t *dev, int n, std::vector<int32_t> &host, hipStream_t stream)
+{
+    host.resize(n);
+    if (n == 0) return LA_OK;
+    hipError_t e = hipMemcpyAsync(host.data(), dev, sizeof(int32_t) * n, hipMemcpyDeviceToHost,
+                                  stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return hip_status(e, "checked mode: copying indices to the host");
+}
+
+// Non-zero slots in [1, num_rows) must be distinct; `allow_negative` admits
+// negative entries (prefill slot_in: fresh sequence).
+int check_slots(const std::vector<int32_t> &s, int num_rows, bool allow_negative, const char *name)
+{
+    std::unordered_set<int32_t> seen;
+    for (size_t i = 0; i < s.size(); ++i) {
+        const int32_t v = s[i];
+        if (v < 0 && allow_negative) continue;
+        if (v < 0 || v >= num_rows)
+            return fail(LA_ERR_SLOT, "%s[%zu] = %d outside [0, %d)", name, i, v, num_rows);
+        if (v != 0 && !seen.insert(v).second)
+            return fail(LA_ERR_SLOT, "%s[%zu] = %d repeats a slot of this call", name, i, v);
+    }
+    return LA_OK;
+}
+
+int check_cu(const std::vector<int32_t> &cu, int T)
+{
+    if (cu.empty() || cu[0] != 0 || cu.back() != T)
+        return fail(LA_ERR_ARG, "cu_seqlens must start at 0 and end at T = %d", T);
+    for (size_t i = 1; i < cu.size(); ++i)
+        if (cu[i] < cu[i - 1]) return fail(LA_ERR_ARG, "cu_seqlens decreases at %zu", i);
+    return LA_OK;
+}
+
+int decode_common(bool kda, int B, int Hqk, int Hv, int dk, int dv, const void *x, int io_dtype,
+                  const float *conv_w, const float *conv_b, void *conv_pool,
+                  int64_t conv_slot_stride, int conv_dtype, const float *g, const float *beta,
+                  const int32_t *slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                  int state_dtype, void *out, float eps, float scale, void *stream)
+{
+    const char *fn = kda ? "kda_decode_step" : "gdn_decode_step";
+    if (B < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be positive (B >= 0)", fn);
+    if (Hv % Hqk != 0)
+        return fail(LA_ERR_ARG, "%s: H_v = %d is not a multiple of H_qk = %d", fn, Hv, Hqk);
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype) || !valid_dtype(conv_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    if (dk != dv || !supported_head_dim(dk))
+        return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v in {16, 32, 64, 128} (got %d, %d)",
+                    fn, dk, dv);
+    if (B == 0) return ok();
+    if (!x || !g || !beta || !slots || !ssm_pool || !out || (conv_w && !conv_pool))
+        return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+    const void *ptrs[] = {x, g, beta, slots, ssm_pool, out, conv_w, conv_b, conv_pool};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    const int C = 2 * Hqk * dk + Hv * dv;
+    if (ssm_slot_stride < (int64_t)Hv * dv * dk || (ssm_slot_stride * dsize(state_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: ssm_slot_stride %lld must be >= H_v d_v d_k and a multiple "
+                    "of 16 bytes", fn, (long long)ssm_slot_stride);
+    if (conv_w && (conv_slot_stride < 3LL * C || (conv_slot_stride * dsize(conv_dtype)) % 16))
+        return fail(LA_ERR_ARG, "%s: conv_slot_stride %lld must be >= 3 C and a multiple of 16 "
+                    "bytes", fn, (long long)conv_slot_stride);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(slots, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "slots")) return rc;
+    }
+    la::DecodeArgs a{};
+    a.B = B; a.Hqk = Hqk; a.Hv = Hv; a.G = Hv / Hqk; a.C = C;
+    a.x = x; a.io_dtype = io_dtype;
+    a.w = conv_w; a.bias = conv_b;
+    a.conv_pool = conv_pool; a.conv_stride = conv_slot_stride; a.conv_dtype = conv_dtype;
+    a.g = g; a.beta = beta; a.slots = slots; a.num_rows = num_rows;
+    a.ssm_pool = ssm_pool; a.ssm_stride = ssm_slot_stride;
+    a.out = out; a.eps = eps; a.scale = scale;
+    return hip_status(la::launch_decode(a, dk, state_dtype, kda, st), fn);
+}
+
+int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, const void *q,
+                   int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                   int64_t v_stride, int io_dtype, const float *g, const float *beta,
+                   const int32_t *cu_seqlens, const int32_t *slot_in, const int32_t *slot_out,
+                   int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+                   void *out, float eps, float scale, int mode, void *workspace,
+                   size_t workspace_bytes, void *stream)
+{
+    const char *fn = kda ? "kda_prefill_chunked" : "gdn_prefill_chunked";
+    if (N < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be positive (N, T >= 0)", fn);
+    if (Hv % Hqk != 0)
+        return fail(LA_ERR_ARG, "%s: H_v = %d is not a multiple of H_qk = %d", fn, Hv, Hqk);
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    if (mode != LA_PREFILL_FP32 && mode != LA_PREFILL_BF16)
+        return fail(LA_ERR_UNSUPPORTED, "%s: unknown precision mode %d", fn, mode);
+    if (dk != 128 || dv != 128)
+        return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);
+    if (N == 0) return ok();
+    if (!q || !k || !v || !g || !beta || !cu_seqlens || !slot_in || !slot_out || !ssm_pool ||
+        (T > 0 && !out))
+        return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+    const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (q_stride < (int64_t)Hqk * dk || k_stride < (int64_t)Hqk * dk || v_stride < (int64_t)Hv * dv ||
+        (q_stride * dsize(io_dtype)) % 16 || (k_stride * dsize(io_dtype)) % 16 ||
+        (v_stride * dsize(io_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: token strides must cover a token's heads and be multiples "
+                    "of 16 bytes", fn);
+    if (ssm_slot_stride < (int64_t)Hv * dv * dk || (ssm_slot_stride * dsize(state_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: ssm_slot_stride %lld too small or misaligned", fn,
+                    (long long)ssm_slot_stride);
+    const size_t need = la::prefill_ws_bytes(N, T, Hqk, Hv, dk, mode);
+    if (need && (!workspace || workspace_bytes < need ||
+                 (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return fail(LA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                    fn, need, workspace_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> cu, si, so;
+        if (int rc = fetch_i32(cu_seqlens, N + 1, cu, st)) return rc;
+        if (int rc = check_cu(cu, T)) return rc;
+        if (int rc = fetch_i32(slot_in, N, si, st)) return rc;
+        if (int rc = fetch_i32(slot_out, N, so, st)) return rc;
+        if (int rc = check_slots(si, num_rows, true, "slot_in")) return rc;
+        if (int rc = check_slots(so, num_rows, false, "slot_out")) return rc;
+    }
+    la::PrefillArgs a{};
+    a.N = N; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.G = Hv / Hqk; a.D = dk;
+    a.q = q; a.k = k; a.v = v;
+    a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
+    a.io_dtype = io_dtype; a.g = g; a.beta = beta;
+    a.cu = cu_seqlens; a.slot_in = slot_in; a.slot_out = slot_out; a.num_rows = num_rows;
+    a.ssm_pool = ssm_pool; a.ssm_stride = ssm_slot_stride; a.state_dtype = state_dtype;
+    a.out = out; a.eps = eps; a.scale = scale; a.mode = mode; a.kda = kda;
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
+    return hip_status(la::launch_prefill(a, st), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_version(void) { return LA_VERSION; }
+
+const char *la_last_error(void) { return g_err.c_str(); }
+
+int la_pool_bytes(int layers, int slots, int H_v, int d_v, int d_k, int conv_channels,
+                  int state_dtype, int conv_dtype, int64_t *ssm_bytes, int64_t *conv_bytes)
+{
+    if (layers < 0 || slots < 0 || H_v < 0 || d_v < 0 || d_k < 0 || conv_channels < 0)
+        return fail(LA_ERR_ARG, "la_pool_bytes: negative size");
+    if (!valid_dtype(state_dtype) || !valid_dtype(conv_dtype))
+        return fail(LA_ERR_ARG, "la_pool_bytes: dtype codes must be LA_F32 or LA_BF16");
+    const int64_t rows = (int64_t)layers * (slots + 1);
+    if (ssm_bytes) *ssm_bytes = rows * H_v * d_v * d_k * dsize(state_dtype);
+    if (conv_bytes) *conv_bytes = rows * 3 * conv_channels * dsize(conv_dtype);
+    return ok();
+}
+
+int shortconv_update(int B, int C, const void *x, int x_dtype, const float *w, const float *bias,
+                     void *conv_pool, int64_t conv_slot_stride, int conv_dtype, int num_rows,
+                     const int32_t *slots, void *y, void *stream)
+{
+    if (B < 0 || C <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "shortconv_update: B >= 0, C > 0 and num_rows > 0 required");
+    if (!valid_dtype(x_dtype) || !valid_dtype(conv_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "shortconv_update: dtype codes must be LA_F32 or LA_BF16");
+    if (B == 0) return ok();
+    if (!x || !w || !conv_pool || !slots || !y)
+        return fail(LA_ERR_ARG, "shortconv_update: null pointer argument");
+    const void *ptrs[] = {x, w, bias, conv_pool, slots, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(LA_ERR_ARG, "shortconv_update: pointers must be 16-byte aligned");
+    if (conv_slot_stride < 3LL * C)
+        return fail(LA_ERR_ARG, "shortconv_update: conv_slot_stride must be >= 3 C");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(slots, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "slots")) return rc;
+    }
+    la::ConvStepArgs a{};
+    a.B = B; a.C = C; a.x = x; a.x_dtype = x_dtype; a.w = w; a.bias = bias;
+    a.conv_pool = conv_pool; a.conv_stride = conv_slot_stride; a.conv_dtype = conv_dtype;
+    a.num_rows = num_rows; a.slots = slots; a.y = y;
+    return hip_status(la::launch_shortconv_update(a, st), "shortconv_update");
+}
+
+int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype, const int32_t *cu_seqlens,
+                      const int32_t *slot_in, const int32_t *slot_out, const float *w,
+                      const float *bias, void *conv_pool, int64_t conv_slot_stride,
+                      int conv_dtype, int num_rows, void *y, void *stream)
+{
+    if (N < 0 || T < 0 || C <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "shortconv_prefill: N, T >= 0, C > 0, num_rows > 0 required");
+    if (!valid_dtype(io_dtype) || !valid_dtype(conv_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "shortconv_prefill: dtype codes must be LA_F32 or LA_BF16");
+    if (N == 0) return ok();
+    if (!x || !cu_seqlens || !slot_in || !slot_out || !w || !conv_pool || (T > 0 && !y))
+        return fail(LA_ERR_ARG, "shortconv_prefill: null pointer argument");
+    const void *ptrs[] = {x, cu_seqlens, slot_in, slot_out, w, bias, conv_pool, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return fail(LA_ERR_ARG, "shortconv_prefill: pointers must be 16-byte aligned");
+    if (conv_slot_stride < 3LL * C)
+        return fail(LA_ERR_ARG, "shortconv_prefill: conv_slot_stride must be >= 3 C");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> cu, si, so;
+        if (int rc = fetch_i32(cu_seqlens, N + 1, cu, st)) return rc;
+        if (int rc = check_cu(cu, T)) return rc;
+        if (int rc = fetch_i32(slot_in, N, si, st)) return rc;
+        if (int rc = fetch_i32(slot_out, N, so, st)) return rc;
+        if (int rc = check_slots(si, num_rows, true, "slot_in")) return rc;
+        if (int rc = check_slots(so, num_rows, false, "slot_out")) return rc;
+    }
+    la::ConvPrefillArgs a{};
+    a.N = N; a.T = T; a.C = C; a.x = x; a.io_dtype = io_dtype;
+    a.cu = cu_seqlens; a.slot_in = slot_in; a.slot_out = slot_out; a.w = w; a.bias = bias;
+    a.conv_pool = conv_pool; a.conv_stride = conv_slot_stride; a.conv_dtype = conv_dtype;
+    a.num_rows = num_rows; a.y = y;
+    return hip_status(la::launch_shortconv_prefill(a, st), "shortconv_prefill");
+}
+
+int kda_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, int io_dtype,
+                    const float *conv_w, const float *conv_b, void *conv_pool,
+                    int64_t conv_slot_stride, int conv_dtype, const float *g, const float *beta,
+                    const int32_t *slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                    int state_dtype, void *out, float eps, float scale, void *stream)
+{
+    return decode_common(true, B, H_qk, H_v, d_k, d_v, x, io_dtype, conv_w, conv_b, conv_pool,
+                         conv_slot_stride, conv_dtype, g, beta, slots, num_rows, ssm_pool,
+                         ssm_slot_stride, state_dtype, out, eps, scale, stream);
+}
+
+int gdn_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, int io_dtype,
+                    const float *conv_w, const float *conv_b, void *conv_pool,
+                    int64_t conv_slot_stride, int conv_dtype, const float *g, const float *beta,
+                    const int32_t *slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                    int state_dtype, void *out, float eps, float scale, void *stream)
+{
+    return decode_common(false, B, H_qk, H_v, d_k, d_v, x, io_dtype, conv_w, conv_b, conv_pool,
+                         conv_slot_stride, conv_dtype, g, beta, slots, num_rows, ssm_pool,
+                         ssm_slot_stride, state_dtype, out, eps, scale, stream);
+}
+
+int kda_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
+                        int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                        int64_t v_stride, int io_dtype, const float *g, const float *beta,
+                        const int32_t *cu_seqlens, const int32_t *slot_in,
+                        const int32_t *slot_out, int num_rows, void *ssm_pool,
+                        int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                        float scale, int mode, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    return prefill_common(true, N, T, H_qk, H_v, d_k, d_v, q, q_stride, k, k_stride, v, v_stride,
+                          io_dtype, g, beta, cu_seqlens, slot_in, slot_out, num_rows, ssm_pool,
+                          ssm_slot_stride, state_dtype, out, eps, scale, mode, workspace,
+                          workspace_bytes, stream);
+}
+
+int gdn_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
+                        int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                        int64_t v_stride, int io_dtype, const float *g, const float *beta,
+                        const int32_t *cu_seqlens, const int32_t *slot_in,
+                        const int32_t *slot_out, int num_rows, void *ssm_pool,
+                        int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                        float scale, int mode, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    return prefill_common(false, N, T, H_qk, H_v, d_k, d_v, q, q_stride, k, k_stride, v, v_stride,
+                          io_dtype, g, beta, cu_seqlens, slot_in, slot_out, num_rows, ssm_pool,
+                          ssm_slot_stride, state_dtype, out, eps, scale, mode, workspace,
+                          workspace_bytes, stream);
+}
+
+size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)
+{
+    if (N < 0 || T < 0 || H_qk <= 0 || H_v <= 0 || H_v % H_qk || d_k != d_v) return 0;
+    return la::prefill_ws_bytes(N, T, H_qk, H_v, d_k, mode);
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// la_device.h -- device helpers shared by the libla kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// bf16 values are stored as raw 16-bit patterns.
+using bf16_t = uint16_t;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Scalar load/store of an element given a runtime dtype (0 = fp32, 1 = bf16).
+__device__ __forceinline__ float load_elem(const void *base, int64_t i, int dtype)
+{
+    return dtype ? bf16_to_f32(static_cast<const uint16_t *>(base)[i])
+                 : static_cast<const float *>(base)[i];
+}
+__device__ __forceinline__ void store_elem(void *base, int64_t i, int dtype, float v)
+{
+    if (dtype) static_cast<uint16_t *>(base)[i] = f32_to_bf16(v);
+    else static_cast<float *>(base)[i] = v;
+}
+
+// Element storage traits for the templated state dtype.
+template <typename T> struct Stor;
+template <> struct Stor<float> {
+    static constexpr int kPer16B = 4;
+    __device__ static __forceinline__ void unpack(const uint4 &r, float *f)
+    {
+        f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+    }
+    __device__ static __forceinline__ uint4 pack(const float *f)
+    {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                          __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+};
+template <> struct Stor<bf16_t> {
+    static constexpr int kPer16B = 8;
+    __device__ static __forceinline__ void unpack(const uint4 &r, float *f)
+    {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+        f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z); f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+    }
+    __device__ static __forceinline__ uint4 pack(const float *f)
+    {
+        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+};
+
+// Cross-lane moves.  DPP controls: quad_perm [1,0,3,2] = 0xB1,
+// quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Exchange with lane ^ 16 inside each 32-lane half (ds_swizzle bitmask mode:
+// and 0x1F, or 0, xor 0x10).
+__device__ __forceinline__ float swz_xor16(float x)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32);
+// every lane of a group receives the bitwise-identical total (each step adds
+// a commuted pair, so all lanes see the same operands).
+template <int N> __device__ __forceinline__ float group_sum(float x)
+{
+    if constexpr (N >= 2) x += dpp_mov<0xB1>(x);
+    if constexpr (N >= 4) x += dpp_mov<0x4E>(x);
+    if constexpr (N >= 8) x += dpp_mov<0x141>(x);
+    if constexpr (N >= 16) x += dpp_mov<0x140>(x);
+    if constexpr (N >= 32) x += swz_xor16(x);
+    return x;
+}
+
+// Sum over the whole wave; the result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x = group_sum<32>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+}
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + expf(-y)); }
+
+}  // namespace la

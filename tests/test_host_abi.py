@@ -1,0 +1,128 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every entry point the header declares, computes pool sizes that reproduce
+the pages' printed figures, and rejects bad arguments before any launch."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrent_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden", "pool_bytes.json")
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kda_decode_step", "gdn_decode_step", "shortconv_update", "shortconv_prefill",
+            "kda_prefill_chunked", "la_pool_bytes", "la_last_error", "la_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    hdr = open(HEADER).read()
+    assert lib.la_version() == int(re.search(r"#define LA_VERSION (\d+)", hdr).group(1))
+
+
+def test_pool_bytes_reproduce_printed_figures(lib):
+    gold = json.load(open(GOLDEN))
+    L, H, d, C = gold["layers"], gold["H_v"], gold["d"], gold["conv_channels"]
+    # one row = one request's state across all layers
+    ssm, conv = binding.pool_bytes(L, 0, H, d, d, C, "bf16", "bf16")
+    pr = gold["per_request"]
+    assert ssm == eval(pr["ssm_bytes_product"]) == 27131904
+    assert conv == eval(pr["conv_bytes_product"]) == 1907712
+    assert round(ssm / 2**20, 1) == pr["ssm_mib"]
+    assert round(conv / 2**20, 2) == pr["conv_mib"]
+    # the page sums its rounded per-GPU figures over 8 GPUs
+    assert round((round(ssm / 2**20, 1) + round(conv / 2**20, 2)) * 8, 1) == pr["tp8_total_mb"]
+    for case in gold["allocation_logs"]:
+        ssm, conv = binding.pool_bytes(L, case["slots"], H, d, d, C, case["state"], case["conv"])
+        assert round(ssm / 2**30, 2) == case["ssm_gib"], case
+        assert round(conv / 2**30, 2) == case["conv_gib"], case
+
+
+def test_pool_bytes_rejects_bad_args(lib):
+    out = ctypes.c_int64()
+    assert lib.la_pool_bytes(-1, 1, 1, 1, 1, 1, 0, 0, ctypes.byref(out), None) == -1
+    assert b"negative" in lib.la_last_error()
+    assert lib.la_pool_bytes(1, 1, 1, 1, 1, 1, 7, 0, ctypes.byref(out), None) == -1
+
+
+def _decode_args(**over):
+    # all-null pointers with B = 4: validation fails before any launch
+    a = dict(B=4, Hqk=2, Hv=4, dk=128, dv=128, x=None, io=1, w=None, b=None, cp=None,
+             cstride=0, cdt=1, g=None, beta=None, slots=None, rows=9, sp=None,
+             sstride=4 * 128 * 128, sdt=1, out=None, eps=1e-6, scale=1.0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("fn", ["kda_decode_step", "gdn_decode_step"])
+def test_decode_validation(lib, fn):
+    f = getattr(lib, fn)
+    assert f(*_decode_args()) == -1                       # null pointers
+    assert b"null pointer" in lib.la_last_error()
+    assert f(*_decode_args(Hv=3)) == -1                   # H_v not a multiple of H_qk
+    assert f(*_decode_args(dk=96, dv=96)) == -2           # head dim not built
+    assert f(*_decode_args(dk=128, dv=64)) == -2
+    assert f(*_decode_args(io=5)) == -2                   # unknown dtype
+    assert f(*_decode_args(B=-1)) == -1
+    assert f(*_decode_args(B=0)) == 0                     # empty batch: no-op
+    assert lib.la_last_error() == b""
+    fake = ctypes.c_void_p(0x1000)
+    mis = ctypes.c_void_p(0x1004)
+    good = dict(x=fake, g=fake, beta=fake, slots=fake, sp=fake, out=fake)
+    assert f(*_decode_args(**{**good, "x": mis})) == -1   # misaligned
+    assert b"aligned" in lib.la_last_error()
+    assert f(*_decode_args(**{**good, "sstride": 100})) == -1  # stride too small
+    assert f(*_decode_args(**{**good, "w": fake})) == -1  # conv weights without a conv pool
+
+
+def test_prefill_validation(lib):
+    fake = ctypes.c_void_p(0x1000)
+    T, H, d = 100, 12, 128
+    args = [1, T, H, H, d, d, fake, H * d, fake, H * d, fake, H * d, 1, fake, fake, fake, fake,
+            fake, 5, fake, H * d * d, 0, fake, 1e-6, 1.0, 0, None, 0, None]
+    need = lib.prefill_workspace_bytes(1, T, H, H, d, d, 0)
+    if need:
+        assert lib.kda_prefill_chunked(*args) == -3       # workspace missing
+        assert b"workspace" in lib.la_last_error()
+    bad = list(args)
+    bad[4] = bad[5] = 64
+    assert lib.kda_prefill_chunked(*bad) == -2            # only d = 128 built
+    bad = list(args)
+    bad[7] = 10                                           # q stride shorter than a token
+    assert lib.kda_prefill_chunked(*bad) == -1
+    bad = list(args)
+    bad[25] = 9                                           # unknown mode
+    assert lib.kda_prefill_chunked(*bad) == -2
+    bad = list(args)
+    bad[0] = 0                                            # no sequences: no-op
+    assert lib.kda_prefill_chunked(*bad) == 0
+
+
+def test_shortconv_validation(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.shortconv_update(4, 64, None, 1, fake, None, fake, 192, 1, 5, fake, fake, None) == -1
+    assert lib.shortconv_update(4, 64, fake, 1, fake, None, fake, 100, 1, 5, fake, fake, None) == -1
+    assert lib.shortconv_update(0, 64, None, 1, None, None, None, 0, 1, 5, None, None, None) == 0
+    assert lib.shortconv_prefill(1, 8, 64, fake, 3, fake, fake, fake, fake, None, fake, 192, 1, 5,
+                                 fake, None) == -2
+
+
+def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        binding.load_library()
