@@ -96,24 +96,62 @@ def run_decode(sh, inp, out):
 
 
 def time_decode(sh, copies, steps, warmup):
-    """Times `steps` launches rotating over the copies; returns ms per launch
-    (hipEvents on the launch stream)."""
-    outs = [torch.empty((sh.B, sh.Hv, sh.dv), dtype=synth.TORCH_DTYPE[sh.io],
-                        device=copies[0]["x"].device) for _ in copies]
+    """Times `steps` decode launches rotating over the copies.  The rotation
+    (one launch per copy) is captured once as a HIP graph and replayed, as a
+    serving loop replays its decode graph; `steps` is rounded up to a whole
+    number of rotations.  Returns (ms per launch from hipEvents on the replay
+    stream, steps timed, eager ms per launch from direct calls)."""
+    dev = copies[0]["x"].device
+    outs = [torch.empty((sh.B, sh.Hv, sh.dv), dtype=synth.TORCH_DTYPE[sh.io], device=dev)
+            for _ in copies]
     n = len(copies)
-    for i in range(warmup):
+    for i in range(max(warmup, n)):
         run_decode(sh, copies[i % n], outs[i % n])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
+    # eager (one ctypes call per launch; includes host launch overhead)
     e0.record(stream)
-    for i in range(steps):
+    for i in range(4 * n):
         run_decode(sh, copies[i % n], outs[i % n])
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    eager_ms = e0.elapsed_time(e1) / (4 * n)
+    # graph replay
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            run_decode(sh, copies[i], outs[i])
+    torch.cuda.synchronize()
+    reps = -(-steps // n)
+    for _ in range(max(1, warmup // n)):
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * n), reps * n, eager_ms
+
+
+def copy_calibration(dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, run under rocprofv3 --pmc to scale
+    the FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes
+    `nbytes`)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "ms": ms,
+                      "gbs_rw": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def cpu_oracle_decode_rate(sh, seed, budget_s=12.0):
@@ -144,7 +182,7 @@ def headline(args, dev):
     per_copy = ((sh.P + 1) * (sh.Hv * sh.dv * sh.dk + 3 * sh.C) * 2)
     n_copies = max(16, -(-(1 << 30) // per_copy))
     copies = make_copies(sh, 1001, dev, n_copies)
-    ms, wall = time_decode(sh, copies, args.steps, args.warmup)
+    ms, steps, eager_ms = time_decode(sh, copies, args.steps, args.warmup)
     nbytes = decode_bytes(sh)
     gbs = nbytes / (ms * 1e-3) / 1e9
     src = source_hash("decode.hip", "la_device.h")
@@ -154,7 +192,7 @@ def headline(args, dev):
         "value": sh.B / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -171,7 +209,8 @@ def headline(args, dev):
                      "traffic": traffic,
                      "kernel": "decode_kernel<128, bf16, KDA>",
                      "algorithmic_bytes_per_launch": nbytes},
-        "wall_s_timed": wall,
+        "eager_ms_per_step": eager_ms,
+        "launch": "HIP graph of one decode launch per pool copy, replayed",
     }
     del copies
     torch.cuda.empty_cache()
@@ -185,6 +224,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (PMC counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -193,6 +234,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
     la.load_library()
     print(f"# bench: headline KDA decode, {args.steps} steps after {args.warmup} warmup",
           file=sys.stderr, flush=True)

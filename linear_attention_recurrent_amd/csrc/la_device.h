@@ -18,9 +18,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> one dword of two bf16 (one v_cvt_pk_bf16_f32, nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Scalar load/store of an element given a runtime dtype (0 = fp32, 1 = bf16).
@@ -33,6 +37,26 @@ __device__ __forceinline__ void store_elem(void *base, int64_t i, int dtype, flo
 {
     if (dtype) static_cast<uint16_t *>(base)[i] = f32_to_bf16(v);
     else static_cast<float *>(base)[i] = v;
+}
+
+// Scalar load/store with the dtype as a template parameter (float or bf16_t).
+template <typename T> __device__ __forceinline__ float ld(const void *base, int64_t i);
+template <> __device__ __forceinline__ float ld<float>(const void *base, int64_t i)
+{
+    return static_cast<const float *>(base)[i];
+}
+template <> __device__ __forceinline__ float ld<bf16_t>(const void *base, int64_t i)
+{
+    return bf16_to_f32(static_cast<const uint16_t *>(base)[i]);
+}
+template <typename T> __device__ __forceinline__ void st(void *base, int64_t i, float v);
+template <> __device__ __forceinline__ void st<float>(void *base, int64_t i, float v)
+{
+    static_cast<float *>(base)[i] = v;
+}
+template <> __device__ __forceinline__ void st<bf16_t>(void *base, int64_t i, float v)
+{
+    static_cast<uint16_t *>(base)[i] = f32_to_bf16(v);
 }
 
 // Element storage traits for the templated state dtype.
@@ -66,9 +90,11 @@ template <> struct Stor<bf16_t> {
 
 // Cross-lane moves.  DPP controls: quad_perm [1,0,3,2] = 0xB1,
 // quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+// bound_ctrl is set so the move folds into the consuming add (v_add_f32_dpp);
+// every pattern used here reads in-range lanes only.
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float x)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // Exchange with lane ^ 16 inside each 32-lane half (ds_swizzle bitmask mode:
 // and 0x1F, or 0, xor 0x10).
@@ -98,6 +124,12 @@ __device__ __forceinline__ float wave_sum(float x)
            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
 }
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + expf(-y)); }
+// exp via the hardware exp2 (v_exp_f32): relative error a few ulp over the
+// ranges used here (log-decays and conv activations of modest magnitude).
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+__device__ __forceinline__ float silu(float y)
+{
+    return y * __builtin_amdgcn_rcpf(1.0f + fast_exp(-y));
+}
 
 }  // namespace la
