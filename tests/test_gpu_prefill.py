@@ -1,0 +1,273 @@
+"""GPU parity of the prefill path against the fp64 oracle, through the C ABI:
+the varlen short conv (history hand-off through conv-pool slots) and the
+chunked KDA / GDN prefill (blocks of 64 tokens, initial state from slot_in,
+final state to slot_out).
+
+Bars: conv-state contents bit-exact; outputs and states within the relative
+L2 tolerance of their storage dtype per (sequence or token, head); packing
+sequences that start on 64-token boundaries is bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrent_amd import binding as la
+from linear_attention_recurrent_amd import synth
+from parity_util import assert_close_units, f64
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def prefill_case(lens, Hqk, Hv, seed, dev, *, kda=True, io="bf16", state="fp32",
+                 slot_in=None, slot_out=None, P=None):
+    sh = synth.PrefillShape(seqlens=tuple(lens), Hqk=Hqk, Hv=Hv, dk=D, dv=D, kda=kda, io=io,
+                            state=state)
+    inp = synth.prefill_inputs(sh, seed, dev)
+    N = len(lens)
+    P = P or (2 * N + 2)
+    pool = synth.normal_torch(seed, synth.S_SSM, (P + 1) * Hv * D * D, dev,
+                              synth.TORCH_DTYPE[state]).view(P + 1, Hv, D, D)
+    si = np.array(slot_in if slot_in is not None else [-1] * N, dtype=np.int32)
+    so = np.array(slot_out if slot_out is not None else list(range(1, N + 1)), dtype=np.int32)
+    return sh, inp, pool, si, so
+
+
+def run_gpu(sh, inp, pool, si, so, **kw):
+    fn = la.kda_prefill_chunked if sh.kda else la.gdn_prefill_chunked
+    dev = pool.device
+    return fn(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+              torch.from_numpy(si).to(dev), torch.from_numpy(so).to(dev), pool, **kw)
+
+
+def run_oracle(sh, inp, pool, si, so, heads=None):
+    """Oracle on all heads, or on a subset of value heads (and their q/k heads)."""
+    q, k, v, g, beta = (f64(inp[x]) for x in ("q", "k", "v", "g", "beta"))
+    p = f64(pool)
+    if heads is not None:
+        assert sh.Hv == sh.Hqk, "head sampling keeps one q/k head per value head"
+        q, k = q[:, heads], k[:, heads]
+        v, g, beta = v[:, heads], g[:, heads], beta[:, heads]
+        p = p[:, heads]
+    return oracle.prefill(q, k, v, g, beta, inp["cu_seqlens"].cpu().numpy(), si, so, p,
+                          kda=sh.kda, state_dtype=sh.state, io_dtype=sh.io)
+
+
+def check(sh, inp, pool, si, so, heads=None, what=""):
+    before = pool.clone()
+    o_ref, p_ref = run_oracle(sh, inp, before, si, so, heads)
+    out = run_gpu(sh, inp, pool, si, so)
+    torch.cuda.synchronize()
+    o = f64(out)
+    p = f64(pool)
+    if heads is not None:
+        o, p = o[:, heads], p[:, heads]
+    # outputs per (token, head); states per (slot, head)
+    assert_close_units(o, o_ref, 2, sh.io, f"{what} outputs")
+    assert_close_units(p[so], p_ref[so], 2, sh.state, f"{what} final states")
+    untouched = np.setdiff1d(np.arange(pool.shape[0]), so)
+    assert np.array_equal(f64(pool)[untouched], f64(before)[untouched])
+    return out
+
+
+@pytest.mark.parametrize("io,state", [("bf16", "fp32"), ("fp32", "fp32"), ("bf16", "bf16")])
+def test_kda_prefill_varlen_matches_oracle(io, state, dev):
+    lens = [5, 64, 70, 1, 130, 3]
+    N = len(lens)
+    si = [-1, 7, -1, 8, 9, -1]             # fresh and resumed sequences
+    so = [1, 7, 2, 3, 4, 5]                # slot_in == slot_out for one of them
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3000, dev, io=io, state=state, slot_in=si,
+                                         slot_out=so, P=10)
+    print(f"[prefill parity] kda io={io} state={state} lens={lens}", flush=True)
+    check(sh, inp, pool, si, so, what=f"kda {io}/{state}")
+
+
+def test_gdn_prefill_gqa_matches_oracle(dev):
+    lens = [100, 17, 64]
+    sh, inp, pool, si, so = prefill_case(lens, 1, 2, 3001, dev, kda=False, io="fp32",
+                                         state="fp32", slot_in=[2, -1, 3], slot_out=[4, 5, 6],
+                                         P=7)
+    check(sh, inp, pool, si, so, what="gdn gqa")
+
+
+def test_kda_prefill_gqa_matches_oracle(dev):
+    lens = [65, 40]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 4, 3002, dev, slot_in=[1, -1], slot_out=[2, 3],
+                                         P=4)
+    check(sh, inp, pool, si, so, what="kda gqa")
+
+
+def test_empty_and_single_token_sequences(dev):
+    lens = [0, 1, 0, 2, 63]
+    sh, inp, pool, si, so = prefill_case(lens, 1, 1, 3003, dev, slot_in=[3, -1, 4, -1, -1],
+                                         slot_out=[5, 6, 7, 8, 9], P=9)
+    before = pool.clone()
+    check(sh, inp, pool, si, so, what="empty/short")
+    # an empty sequence hands its initial state over unchanged
+    assert torch.equal(pool[5], before[3])
+    assert torch.equal(pool[7], before[4])
+
+
+def test_strong_decay_diagonal_factorisation(dev):
+    """Log decays near -4 per token (16-token spread ~64, inside the
+    exponent clamp) still match the oracle."""
+    lens = [96]
+    sh, inp, pool, si, so = prefill_case(lens, 1, 1, 3004, dev, io="fp32", state="fp32",
+                                         slot_in=[1], slot_out=[2], P=2)
+    inp["g"] = (inp["g"] * 5.0).clamp(min=-4.5).contiguous()
+    check(sh, inp, pool, si, so, what="strong decay")
+
+
+def test_split_through_slots_equals_one_call(dev):
+    """One sequence processed in three scheduler chunks (128 + 100 + 72
+    tokens), each chunk's end state handed to the next through a pool slot,
+    matches the single call and the oracle."""
+    lens = [300]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3005, dev, slot_in=[-1], slot_out=[1], P=3)
+    pool2 = pool.clone()
+    one = check(sh, inp, pool, si, so, what="one call")
+    cuts = [0, 128, 228, 300]
+    outs = []
+    for c in range(3):
+        a, b = cuts[c], cuts[c + 1]
+        sub = {x: inp[x][a:b].contiguous() for x in ("q", "k", "v", "g", "beta")}
+        sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32, device=dev)
+        csh = synth.PrefillShape(seqlens=(b - a,), Hqk=2, Hv=2, dk=D, dv=D)
+        outs.append(run_gpu(csh, sub, pool2, np.array([-1 if c == 0 else 2], np.int32),
+                            np.array([2], np.int32)))
+    torch.cuda.synchronize()
+    split = torch.cat(outs)
+    assert_close_units(f64(split), f64(one), 2, "bf16", "split vs one call outputs")
+    assert_close_units(f64(pool2[2]), f64(pool[1]), 1, "fp32", "split vs one call state")
+
+
+def test_packing_aligned_sequences_is_bit_exact(dev):
+    lens = [128, 64, 192]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3006, dev, slot_in=[1, 2, -1],
+                                         slot_out=[4, 5, 6], P=9)
+    pool_sep = pool.clone()
+    packed = run_gpu(sh, inp, pool, si, so)
+    cu = synth.cu_seqlens(lens)
+    for n in range(3):
+        a, b = cu[n], cu[n + 1]
+        sub = {x: inp[x][a:b].contiguous() for x in ("q", "k", "v", "g", "beta")}
+        sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32, device=dev)
+        o = run_gpu(sh, sub, pool_sep, si[n:n + 1], so[n:n + 1])
+        torch.cuda.synchronize()
+        assert torch.equal(o, packed[a:b]), n
+    assert torch.equal(pool, pool_sep)
+
+
+def test_strided_qkv_views_of_conv_output(dev):
+    """q, k, v given as token-strided views into one [T, C] tensor."""
+    lens = [70, 30]
+    Hqk = Hv = 2
+    sh, inp, pool, si, so = prefill_case(lens, Hqk, Hv, 3007, dev, slot_in=[-1, 1],
+                                         slot_out=[2, 3], P=3)
+    T = sum(lens)
+    y = torch.cat([inp["q"].reshape(T, -1), inp["k"].reshape(T, -1), inp["v"].reshape(T, -1)], 1)
+    views = dict(inp, q=y[:, :Hqk * D].unflatten(1, (Hqk, D)),
+                 k=y[:, Hqk * D:2 * Hqk * D].unflatten(1, (Hqk, D)),
+                 v=y[:, 2 * Hqk * D:].unflatten(1, (Hv, D)))
+    pool2 = pool.clone()
+    o1 = run_gpu(sh, inp, pool, si, so)
+    o2 = run_gpu(sh, views, pool2, si, so)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(pool, pool2)
+
+
+def test_workspace_too_small_is_rejected(dev):
+    sh, inp, pool, si, so = prefill_case([64], 1, 1, 3008, dev, P=2)
+    with pytest.raises(la.LAError, match="workspace"):
+        run_gpu(sh, inp, pool, si, so, workspace=torch.empty(1024, dtype=torch.uint8, device=dev))
+
+
+# ---------------------------------------------------------------- sampled --
+
+def test_sampled_kda_prefill_long_sequence_in_scheduler_chunks(dev):
+    """KDA prefill at the serving shape: H=12, d=128, bf16 I/O, fp32 state; one
+    13,600-token sequence in 6,144 / 6,144 / 1,312-token scheduler chunks, the
+    end-of-chunk state written to a pool slot each chunk.  Heads 0 and 7 are
+    checked against the oracle."""
+    H = 12
+    sh = synth.PrefillShape(seqlens=(13600,), Hqk=H, Hv=H, dk=D, dv=D)
+    inp = synth.prefill_inputs(sh, 1005, dev)
+    pool = torch.zeros((4, H, D, D), dtype=torch.float32, device=dev)
+    heads = [0, 7]
+    o_ref, p_ref = run_oracle(sh, inp, pool, np.array([-1], np.int32), np.array([1], np.int32),
+                              heads)
+    cuts = [0, 6144, 12288, 13600]
+    outs = []
+    for c in range(3):
+        a, b = cuts[c], cuts[c + 1]
+        sub = {x: inp[x][a:b].contiguous() for x in ("q", "k", "v", "g", "beta")}
+        sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32, device=dev)
+        csh = synth.PrefillShape(seqlens=(b - a,), Hqk=H, Hv=H, dk=D, dv=D)
+        # chunk c resumes from the slot chunk c - 1 wrote (slot c) and writes slot c + 1
+        slot_in = np.array([-1 if c == 0 else c], np.int32)
+        outs.append(run_gpu(csh, sub, pool, slot_in, np.array([c + 1], np.int32)))
+    torch.cuda.synchronize()
+    out = f64(torch.cat(outs))[:, heads]
+    assert_close_units(out, o_ref, 2, "bf16", "13600-token outputs (sampled heads)")
+    assert_close_units(f64(pool[3])[heads], p_ref[1], 1, "fp32", "end state (sampled heads)")
+
+
+def test_sampled_kda_prefill_eight_packed_sequences(dev):
+    """Eight 4,096-token sequences packed into one varlen call (H=12), fresh
+    states to eight distinct slots; heads 3 and 11 checked."""
+    H = 12
+    sh = synth.PrefillShape(seqlens=(4096,) * 8, Hqk=H, Hv=H, dk=D, dv=D)
+    inp = synth.prefill_inputs(sh, 1006, dev)
+    pool = torch.zeros((9, H, D, D), dtype=torch.float32, device=dev)
+    si = np.full(8, -1, np.int32)
+    so = np.arange(1, 9, dtype=np.int32)
+    heads = [3, 11]
+    o_ref, p_ref = run_oracle(sh, inp, pool, si, so, heads)
+    out = run_gpu(sh, inp, pool, si, so)
+    torch.cuda.synchronize()
+    assert_close_units(f64(out)[:, heads], o_ref, 2, "bf16", "packed outputs (sampled heads)")
+    assert_close_units(f64(pool)[1:, heads], p_ref[1:], 2, "fp32", "packed end states")
+
+
+# ------------------------------------------------------------ short conv ---
+
+@pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("fp32", "fp32")])
+def test_shortconv_prefill_matches_oracle(io, cdt, dev):
+    lens = [1, 2, 3, 40, 0, 9]
+    C = 4608
+    N = len(lens)
+    T = sum(lens)
+    seed = 3100
+    x = synth.to_torch(synth.normal(seed, 0, (T, C)), io, dev)
+    w = synth.to_torch(0.5 * synth.normal(seed, 1, (C, 4)), "fp32", dev)
+    P = 10
+    pool = synth.to_torch(synth.normal(seed, 2, (P + 1, 3, C)), cdt, dev)
+    si = np.array([4, -1, 5, 6, 7, -1], np.int32)
+    so = np.array([4, 1, 2, 6, 8, 9], np.int32)   # two in place
+    cu = synth.cu_seqlens(lens)
+    y_ref, pool_ref = oracle.shortconv_prefill(f64(x), cu, si, so, f64(w), None, f64(pool),
+                                               conv_dtype=cdt, io_dtype=io)
+    y = la.shortconv_prefill(x, torch.from_numpy(cu).to(dev), torch.from_numpy(si).to(dev),
+                             torch.from_numpy(so).to(dev), w, pool)
+    torch.cuda.synchronize()
+    assert_close_units(f64(y), y_ref, 1, io, "conv outputs")
+    assert np.array_equal(f64(pool), pool_ref), "conv history must match bit for bit"
+
+
+def test_shortconv_prefill_then_decode_continues_history(dev):
+    """Prefill conv of a 50-token sequence, then one decode token through the
+    standalone conv, equals the conv of the 51-token sequence."""
+    C, L = 4608, 50
+    x = synth.to_torch(synth.normal(3101, 0, (L + 1, C)), "bf16", dev)
+    w = synth.to_torch(0.5 * synth.normal(3101, 1, (C, 4)), "fp32", dev)
+    pool = torch.zeros((3, 3, C), dtype=torch.bfloat16, device=dev)
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)  # noqa: E731
+    y_all = la.shortconv_prefill(x, i32([0, L + 1]), i32([-1]), i32([2]), w, pool)
+    la.shortconv_prefill(x[:L].contiguous(), i32([0, L]), i32([-1]), i32([1]), w, pool)
+    y_last = la.shortconv_update(x[L:].contiguous(), w, pool, i32([1]))
+    torch.cuda.synchronize()
+    assert torch.equal(y_last[0], y_all[L])
+    assert torch.equal(pool[1], pool[2])
