@@ -2,21 +2,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
 
-Headline: KDA decode at the single-layer serving shape (64 requests, 12 heads,
-d_k = d_v = 128, bf16 state in an 80-slot pool, bf16 conv state, per-channel
-decay): one step = one fused decode launch (conv + SiLU + L2 norm + gated
-delta rule) for the 64-request batch.  To keep the 34 MB working set out of
-the 256 MB on-die cache, the K timed steps rotate over R independent copies of
-the pools and inputs (R * 34 MB >= 1 GB), as consecutive layers of a model do.
-`value` is tokens/s = 64 * K / elapsed.  Inputs are resident in HBM before the
+Headline (`value`): KDA decode at the single-layer serving shape -- 64
+requests, 12 heads, d_k = d_v = 128, bf16 state in an 80-slot pool, bf16 conv
+state, per-channel decay.  One step = one fused decode launch (short conv +
+SiLU + L2 norm + gated delta rule) for the 64-request batch.  The 34 MB working
+set would sit in the 256 MB on-die cache, so the K timed steps rotate over R
+independent copies of pools and inputs (>= 1 GB in all), as consecutive layers
+of a model do; the rotation is captured once as a HIP graph and replayed.
+`value` = 64 K / elapsed (tokens/s).  Inputs are resident in HBM before the
 timed region starts.
 
-The JSON line also carries the decode kernel's roofline (algorithmic bytes per
-launch / average launch time, against 8 TB/s), the HBM traffic measured with
-rocprofv3 counters when it was taken for the current kernel source, and the
-fp64 CPU oracle's rate on a bounded sample of the same workload.  `extra`
-holds the other configurations (69-layer KDA decode, 48-layer GDN fp32 decode,
-chunked prefill).
+`roofline` is the decode kernel's: algorithmic bytes per launch (every state
+row read and written once, the conv history read and written, x, gates,
+output and weights moved once) over the average launch time from hipEvents on
+the launch stream, against 8 TB/s; `traffic` is the HBM bytes per launch
+measured with rocprofv3 counters (FETCH_SIZE x the copy-calibrated factor,
+plus WRITE_SIZE) when they were taken for the current kernel source.
+`cpu_baseline` is the fp64 C oracle on the same workload, single-threaded.
+
+`extra` holds the other workloads: the 69-layer KDA decode (H=96, 128
+requests), the 48-layer GDN fp32 decode (16 q/k heads shared by 32 value
+heads, 256 requests) and the chunked prefill (one 13,600-token sequence in
+6,144 / 6,144 / 1,312-token scheduler chunks plus eight packed 4,096-token
+sequences, H=12), each with its own roofline line.
 """
 from __future__ import annotations
 
@@ -38,7 +46,12 @@ from linear_attention_recurrent_amd import binding as la  # noqa: E402
 from linear_attention_recurrent_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP32_PEAK_TFS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"# bench: {msg}", file=sys.stderr, flush=True)
 
 
 def esize(dt: str) -> int:
@@ -46,9 +59,7 @@ def esize(dt: str) -> int:
 
 
 def decode_bytes(sh: synth.DecodeShape) -> int:
-    """Algorithmic HBM bytes of one fused decode launch: every state row read
-    and written once, the 3-row conv history read and written, and x, g, beta,
-    the output, the conv weights and the slots moved once."""
+    """Algorithmic HBM bytes of one fused decode launch."""
     B, C = sh.B, sh.C
     state = 2 * B * sh.Hv * sh.dv * sh.dk * esize(sh.state)
     conv = 2 * B * 3 * C * esize(sh.conv)
@@ -68,10 +79,12 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
+DECODE_SOURCES = ("decode_kernel.h", "la_device.h")
+
+
 def measured_traffic(tag: str, src_hash: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (profiles/<tag>.traffic.txt), or None when it is absent or was taken for
-    a different kernel source."""
+    """HBM bytes per launch from profiles/<tag>.traffic.txt, or None when that
+    summary is absent or was taken for a different kernel source."""
     path = os.path.join(PROFILES, f"{tag}.traffic.txt")
     if not os.path.exists(path):
         return None
@@ -85,84 +98,284 @@ def measured_traffic(tag: str, src_hash: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
-def make_copies(sh, seed, dev, n):
-    return [synth.decode_inputs(sh, seed + 7919 * i, dev) for i in range(n)]
+def events():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def run_decode(sh, inp, out):
+# ---------------------------------------------------------------- decode ----
+
+def run_decode(sh, inp, out, layer=None):
     fn = la.kda_decode_step if sh.kda else la.gdn_decode_step
-    fn(inp["x"], inp["g"], inp["beta"], inp["slots"], inp["ssm_pool"], Hqk=sh.Hqk,
-       conv_w=inp["w"], conv_pool=inp["conv_pool"], out=out)
+    pick = (lambda t: t[layer]) if layer is not None else (lambda t: t)
+    fn(pick(inp["x"]), pick(inp["g"]), pick(inp["beta"]), inp["slots"], pick(inp["ssm_pool"]),
+       Hqk=sh.Hqk, conv_w=pick(inp["w"]), conv_pool=pick(inp["conv_pool"]), out=out)
 
 
-def time_decode(sh, copies, steps, warmup):
-    """Times `steps` decode launches rotating over the copies.  The rotation
-    (one launch per copy) is captured once as a HIP graph and replayed, as a
-    serving loop replays its decode graph; `steps` is rounded up to a whole
-    number of rotations.  Returns (ms per launch from hipEvents on the replay
-    stream, steps timed, eager ms per launch from direct calls)."""
-    dev = copies[0]["x"].device
-    outs = [torch.empty((sh.B, sh.Hv, sh.dv), dtype=synth.TORCH_DTYPE[sh.io], device=dev)
-            for _ in copies]
-    n = len(copies)
-    for i in range(max(warmup, n)):
-        run_decode(sh, copies[i % n], outs[i % n])
+def time_graph(launch_all, n_launch, steps, warmup):
+    """Captures `launch_all` (n_launch kernel launches) as a HIP graph and
+    replays it until >= `steps` launches; returns (ms per launch, launches)."""
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # eager (one ctypes call per launch; includes host launch overhead)
-    e0.record(stream)
-    for i in range(4 * n):
-        run_decode(sh, copies[i % n], outs[i % n])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / (4 * n)
-    # graph replay
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for i in range(n):
-            run_decode(sh, copies[i], outs[i])
+        launch_all()
     torch.cuda.synchronize()
-    reps = -(-steps // n)
-    for _ in range(max(1, warmup // n)):
+    reps = max(1, -(-steps // n_launch))
+    for _ in range(max(1, -(-warmup // n_launch))):
         graph.replay()
     torch.cuda.synchronize()
+    e0, e1 = events()
     stream = torch.cuda.current_stream()
     e0.record(stream)
     for _ in range(reps):
         graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * n), reps * n, eager_ms
+    return e0.elapsed_time(e1) / (reps * n_launch), reps * n_launch
 
 
-def copy_calibration(dev, nbytes=1 << 30, reps=5):
-    """A plain device copy of known size, run under rocprofv3 --pmc to scale
-    the FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes
-    `nbytes`)."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
+def headline(args, dev):
+    sh = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
+    per_copy = (sh.P + 1) * (sh.Hv * sh.dv * sh.dk + 3 * sh.C) * 2
+    n = max(16, -(-(1 << 30) // per_copy))
+    copies = [synth.decode_inputs(sh, 1001 + 7919 * i, dev) for i in range(n)]
+    outs = [torch.empty((sh.B, sh.Hv, sh.dv), dtype=torch.bfloat16, device=dev) for _ in copies]
+    for i in range(n):  # eager warm-up (and eager timing for reference)
+        run_decode(sh, copies[i], outs[i])
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = events()
     e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
+    for i in range(4 * n):
+        run_decode(sh, copies[i % n], outs[i % n])
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    print(json.dumps({"copy_calibration_bytes": nbytes, "ms": ms,
-                      "gbs_rw": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
+    eager_ms = e0.elapsed_time(e1) / (4 * n)
+
+    def launch_all():
+        for i in range(n):
+            run_decode(sh, copies[i], outs[i])
+
+    ms, steps = time_graph(launch_all, n, args.steps, args.warmup)
+    nbytes = decode_bytes(sh)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("decode_kda_b64_h12_bf16", source_hash(*DECODE_SOURCES))
+    res = {
+        "metric": "KDA decode tokens/s (single layer, 64 requests, H=12, d=128, bf16 state)",
+        "value": sh.B / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded SplitMix64/Box-Muller; random pools rotated over {n} copies)",
+        "config": {"workload": "kda_decode_single_layer", "batch": sh.B, "H": sh.Hv,
+                   "d_k": sh.dk, "d_v": sh.dv, "state_dtype": sh.state, "pool_slots": sh.P,
+                   "conv_kernel": 4, "pool_copies_rotated": n},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "decode_kernel<128, bf16 state, bf16 io, bf16 conv, KDA, G=1>",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "eager_ms_per_step": eager_ms,
+        "launch": "HIP graph of one decode launch per pool copy, replayed",
+    }
+    del copies, outs
+    torch.cuda.empty_cache()
+    return sh, res
+
+
+def decode_stack(sh, layers, steps, seed, dev):
+    """`layers` stacked layers, each with its own pools and inputs; one step =
+    one decode launch per layer (captured as one graph).  Returns a dict."""
+    L, B, C = layers, sh.B, sh.C
+    log(f"decode stack: {L} layers, B={B}, H_qk={sh.Hqk}, H_v={sh.Hv}, {sh.state} state")
+    n_ssm = (sh.P + 1) * sh.Hv * sh.dv * sh.dk
+    n_conv = (sh.P + 1) * 3 * C
+    ssm = torch.empty((L, sh.P + 1, sh.Hv, sh.dv, sh.dk), dtype=synth.TORCH_DTYPE[sh.state],
+                      device=dev)
+    conv = torch.empty((L, sh.P + 1, 3, C), dtype=synth.TORCH_DTYPE[sh.conv], device=dev)
+    for l in range(L):
+        ssm[l].view(-1).copy_(synth.normal_torch(seed + l, synth.S_SSM, n_ssm, dev,
+                                                 synth.TORCH_DTYPE[sh.state]))
+        conv[l].view(-1).copy_(synth.normal_torch(seed + l, synth.S_CONV, n_conv, dev,
+                                                  synth.TORCH_DTYPE[sh.conv]))
+    gsz = B * sh.Hv * (sh.dk if sh.kda else 1)
+    inp = dict(
+        x=synth.normal_torch(seed, synth.S_X, L * B * C, dev, synth.TORCH_DTYPE[sh.io]).view(L, B, C),
+        w=(0.5 * synth.normal_torch(seed, synth.S_W, L * C * 4, dev, torch.float64)).to(
+            torch.float32).view(L, C, 4),
+        g=synth.log_decay_torch(seed, synth.S_G, L * gsz, dev).view(
+            (L, B, sh.Hv, sh.dk) if sh.kda else (L, B, sh.Hv)),
+        beta=synth.beta_gate_torch(seed, synth.S_BETA, L * B * sh.Hv, dev).view(L, B, sh.Hv),
+        slots=torch.from_numpy(synth.slot_permutation(seed, synth.S_SLOTS, sh.P)[:B].copy()).to(dev),
+        ssm_pool=ssm, conv_pool=conv)
+    outs = [torch.empty((B, sh.Hv, sh.dv), dtype=synth.TORCH_DTYPE[sh.io], device=dev)
+            for _ in range(L)]
+    for l in range(L):
+        run_decode(sh, inp, outs[l], layer=l)
+    torch.cuda.synchronize()
+
+    def launch_all():
+        for l in range(L):
+            run_decode(sh, inp, outs[l], layer=l)
+
+    ms_launch, launches = time_graph(launch_all, L, steps * L, 2 * L)
+    step_ms = ms_launch * L
+    nbytes = decode_bytes(sh) * L
+    gbs = nbytes / (step_ms * 1e-3) / 1e9
+    del inp, ssm, conv, outs
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": B / (step_ms * 1e-3), "ms_per_step": step_ms,
+            "steps": launches // L, "layers": L, "batch": B,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_step": nbytes}}
+
+
+# --------------------------------------------------------------- prefill ----
+
+def prefill_mfma_flops(seqlens, Hv) -> float:
+    """fp32 MFMA flops the two prefill kernels issue for a packed call (each
+    v_mfma_f32_16x16x4f32 = 2048 flops), following their loop structure."""
+    T = int(sum(seqlens))
+    tiles = -(-T // 64)
+    intra = tiles * Hv * 1344            # A, P: 640; T blocks: 64; U, W: 640
+    chain = 0
+    cu = np.concatenate([[0], np.cumsum(seqlens)])
+    for n in range(len(seqlens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b <= a:
+            continue
+        for tile in range(a // 64, (b - 1) // 64 + 1):
+            L = min(b, 64 * tile + 64) - max(a, 64 * tile)
+            waves = -(-L // 16)
+            chain += waves * 32 + sum(32 + 4 * (i + 1) for i in range(waves)) + 8 * (-(-L // 4))
+    chain *= 8 * Hv                      # eight 16-row slices of the state per head
+    return 2048.0 * (intra + chain)
+
+
+def prefill_bench(dev, reps=5):
+    """Chunked KDA prefill, H=12, d=128, bf16 I/O, fp32 state: W1 = one
+    13,600-token sequence in 6,144 / 6,144 / 1,312-token calls chained through
+    a pool slot; W2 = eight 4,096-token sequences packed in one call.  Each call
+    is the varlen short conv over the projections (C = 12 * 384) followed by
+    the chunked prefill on q|k|v views of its output."""
+    H, D = 12, 128
+    C = 3 * H * D
+    seed = 1005
+    log("prefill: generating inputs")
+
+    def make(T):
+        x = synth.normal_torch(seed + T, synth.S_X, T * C, dev, torch.bfloat16).view(T, C)
+        g = synth.log_decay_torch(seed + T, synth.S_G, T * H * D, dev).view(T, H, D)
+        beta = synth.beta_gate_torch(seed + T, synth.S_BETA, T * H, dev).view(T, H)
+        return x, g, beta
+
+    w = (0.5 * synth.normal_torch(seed, synth.S_W, C * 4, dev, torch.float64)).to(
+        torch.float32).view(C, 4)
+    conv_pool = torch.zeros((10, 3, C), dtype=torch.bfloat16, device=dev)
+    ssm_pool = torch.zeros((10, H, D, D), dtype=torch.float32, device=dev)
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)  # noqa: E731
+    x1, g1, b1 = make(13600)
+    x2, g2, b2 = make(8 * 4096)
+    cuts = [0, 6144, 12288, 13600]
+    calls = []  # (x, g, beta, cu, slot_in, slot_out, seqlens)
+    for c in range(3):
+        a, b = cuts[c], cuts[c + 1]
+        calls.append((x1[a:b], g1[a:b], b1[a:b], i32([0, b - a]), i32([-1 if c == 0 else c]),
+                      i32([c + 1]), (b - a,)))
+    calls.append((x2, g2, b2, i32(list(range(0, 8 * 4096 + 1, 4096))), i32([-1] * 8),
+                  i32(list(range(2, 10))), (4096,) * 8))
+    ws = torch.empty(la.prefill_workspace_bytes(8, 8 * 4096, H, H, D, D), dtype=torch.uint8,
+                     device=dev)
+    ys = [torch.empty((cl[0].shape[0], C), dtype=torch.bfloat16, device=dev) for cl in calls]
+    outs = [torch.empty((cl[0].shape[0], H, D), dtype=torch.bfloat16, device=dev) for cl in calls]
+
+    def conv(i):
+        x, g, beta, cu, si, so, _ = calls[i]
+        la.shortconv_prefill(x, cu, si, so, w, conv_pool, y=ys[i])
+
+    def chunk(i):
+        x, g, beta, cu, si, so, _ = calls[i]
+        y = ys[i]
+        q = y[:, :H * D].unflatten(1, (H, D))
+        k = y[:, H * D:2 * H * D].unflatten(1, (H, D))
+        v = y[:, 2 * H * D:].unflatten(1, (H, D))
+        la.kda_prefill_chunked(q, k, v, g, beta, cu, si, so, ssm_pool, out=outs[i], workspace=ws)
+
+    for i in range(4):
+        conv(i)
+        chunk(i)
+    torch.cuda.synchronize()
+    t_conv = [0.0] * 4
+    t_chunk = [0.0] * 4
+    for _ in range(reps):
+        for i in range(4):
+            e0, e1 = events()
+            e2, e3 = events()
+            e0.record()
+            conv(i)
+            e1.record()
+            e2.record()
+            chunk(i)
+            e3.record()
+            torch.cuda.synchronize()
+            t_conv[i] += e0.elapsed_time(e1) / reps
+            t_chunk[i] += e2.elapsed_time(e3) / reps
+    w1_ms = sum(t_conv[:3]) + sum(t_chunk[:3])
+    w2_ms = t_conv[3] + t_chunk[3]
+    flops = sum(prefill_mfma_flops(cl[6], H) for cl in calls)
+    chunk_ms = sum(t_chunk)
+    tf = flops / (chunk_ms * 1e-3) / 1e12
+    conv_bytes = sum(2 * cl[0].numel() * 2 for cl in calls)  # x read + y written, bf16
+    conv_gbs = conv_bytes / (sum(t_conv) * 1e-3) / 1e9
+    T_all = 13600 + 8 * 4096
+    res = {
+        "tokens_per_s": T_all / ((w1_ms + w2_ms) * 1e-3),
+        "w1_13600_tokens_per_s": 13600 / (w1_ms * 1e-3),
+        "w2_8x4096_tokens_per_s": 8 * 4096 / (w2_ms * 1e-3),
+        "ms": {"w1_total": w1_ms, "w2_total": w2_ms, "conv_calls": t_conv,
+               "chunked_calls": t_chunk},
+        "mode": "fp32 (every intra-block product in fp32 on v_mfma_f32_16x16x4f32)",
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_FP32_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": tf / MFMA_FP32_PEAK_TFS,
+                     "issued_mfma_flops": flops,
+                     "algorithmic_flops": 164e3 * T_all * H,
+                     "note": "prefill kernels only; the chain over 213 dependent blocks of "
+                             "the 13,600-token sequence bounds W1"},
+        "conv_roofline": {"bound": "hbm", "achieved": conv_gbs, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS},
+    }
+    del x1, x2, g1, g2, b1, b2, ws, ys, outs, calls
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_prefill_rate(budget_tokens=1536):
+    """The fp64 oracle's prefill on one head of `budget_tokens` tokens,
+    scaled to tokens/s for all 12 heads (single thread)."""
+    import oracle
+    H, D = 1, 128
+    sh = synth.PrefillShape(seqlens=(budget_tokens,), Hqk=H, Hv=H, dk=D, dv=D)
+    inp = synth.prefill_inputs(sh, 77, "cpu")
+    f = {k: v.to(torch.float64).numpy() for k, v in inp.items() if k != "cu_seqlens"}
+    pool = np.zeros((2, H, D, D))
+    t0 = time.perf_counter()
+    oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], [0, budget_tokens], [-1], [1], pool)
+    el = time.perf_counter() - t0
+    return budget_tokens / el / 12.0, el
 
 
 def cpu_oracle_decode_rate(sh, seed, budget_s=12.0):
-    """The fp64 oracle on the same workload's first-layer inputs, repeated
-    until `budget_s` seconds; single-threaded."""
+    """The fp64 oracle on the headline workload, repeated for `budget_s`
+    seconds; single-threaded."""
     import oracle
     inp = synth.decode_inputs(sh, seed, "cpu")
     f = {k: v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()
          for k, v in inp.items()}
-    # compact pools holding only the batch's rows (row 0 = padding)
-    rows = np.concatenate([[0], f["slots"]])
+    rows = np.concatenate([[0], f["slots"]])  # compact pools: the batch's rows only
     f["conv_pool"], f["ssm_pool"] = f["conv_pool"][rows], f["ssm_pool"][rows]
     f["slots"] = np.arange(1, sh.B + 1, dtype=np.int32)
     reps, t0 = 0, time.perf_counter()
@@ -177,53 +390,31 @@ def cpu_oracle_decode_rate(sh, seed, budget_s=12.0):
     return sh.B * reps / el, reps, el
 
 
-def headline(args, dev):
-    sh = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
-    per_copy = ((sh.P + 1) * (sh.Hv * sh.dv * sh.dk + 3 * sh.C) * 2)
-    n_copies = max(16, -(-(1 << 30) // per_copy))
-    copies = make_copies(sh, 1001, dev, n_copies)
-    ms, steps, eager_ms = time_decode(sh, copies, args.steps, args.warmup)
-    nbytes = decode_bytes(sh)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    src = source_hash("decode.hip", "la_device.h")
-    traffic = measured_traffic("decode_kda_b64_h12_bf16", src)
-    res = {
-        "metric": "KDA decode tokens/s (single layer, 64 requests, H=12, d=128, bf16 state)",
-        "value": sh.B / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded SplitMix64/Box-Muller; random state, pools rotated over "
-                f"{n_copies} copies)",
-        "config": {"workload": "kda_decode_single_layer", "batch": sh.B, "H": sh.Hv,
-                   "d_k": sh.dk, "d_v": sh.dv, "state_dtype": sh.state, "pool_slots": sh.P,
-                   "conv_kernel": 4, "pool_copies_rotated": n_copies},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": traffic,
-                     "kernel": "decode_kernel<128, bf16, KDA>",
-                     "algorithmic_bytes_per_launch": nbytes},
-        "eager_ms_per_step": eager_ms,
-        "launch": "HIP graph of one decode launch per pool copy, replayed",
-    }
-    del copies
-    torch.cuda.empty_cache()
-    return sh, res
+def copy_calibration(dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, run under rocprofv3 --pmc to scale
+    the FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes
+    `nbytes`)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = events()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "ms": ms,
+                      "gbs_rw": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--steps", type=int, default=3200)
+    ap.add_argument("--warmup", type=int, default=320)
+    ap.add_argument("--no-extra", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (PMC counter scaling)")
     args = ap.parse_args()
@@ -238,19 +429,32 @@ def main():
         copy_calibration(dev)
         return
     la.load_library()
-    print(f"# bench: headline KDA decode, {args.steps} steps after {args.warmup} warmup",
-          file=sys.stderr, flush=True)
+    log(f"headline KDA decode, {args.steps} launches after {args.warmup} warm-up")
     sh, res = headline(args, dev)
     extra = {}
-    res["extra"] = extra
+    if not args.no_extra:
+        extra["kda_decode_69_layers_h96_b128"] = decode_stack(
+            synth.DecodeShape(B=128, Hqk=96, Hv=96, dk=128, dv=128, P=128), 69, 16, 1002, dev)
+        extra["gdn_decode_48_layers_fp32_b256"] = decode_stack(
+            synth.DecodeShape(B=256, Hqk=16, Hv=32, dk=128, dv=128, P=256, kda=False, io="fp32",
+                              state="fp32", conv="fp32"), 48, 16, 1003, dev)
+        log("prefill")
+        extra["kda_prefill_chunked_h12"] = prefill_bench(dev)
     if not args.no_cpu:
-        print("# bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        log("CPU oracle baselines")
         rate, reps, el = cpu_oracle_decode_rate(sh, 1001)
         res["cpu_baseline"] = {
             "value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 C oracle, {reps} full decode steps of the 64-request batch "
-                      f"(all 12 heads) in {el:.1f} s, single thread, host "
-                      f"{platform.processor() or platform.machine()} x{os.cpu_count()}"}
+            "sample": f"fp64 C oracle, {reps} full decode steps of the 64-request, 12-head "
+                      f"batch in {el:.1f} s, one thread on {platform.machine()} "
+                      f"(host has {os.cpu_count()} logical CPUs)"}
+        if "kda_prefill_chunked_h12" in extra:
+            prate, pel = cpu_prefill_rate()
+            extra["kda_prefill_chunked_h12"]["cpu_baseline"] = {
+                "value": prate, "unit": "tokens/s (12 heads)", "cores": 1, "kind": "oracle",
+                "sample": f"fp64 C oracle prefill of one 1,536-token sequence on one head in "
+                          f"{pel:.1f} s, scaled by 1/12 for 12 heads"}
+    res["extra"] = extra
     print(json.dumps(res), flush=True)
 
 

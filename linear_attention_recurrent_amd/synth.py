@@ -111,7 +111,8 @@ def raw_u64_torch(seed: int, stream: int, n: int, offset: int = 0, device="cpu")
 def normal_torch(seed: int, stream: int, numel: int, device="cpu", dtype=torch.float32,
                  chunk: int = 1 << 26) -> torch.Tensor:
     """Flat tensor of ``numel`` normal draws (same definition as :func:`normal`),
-    rounded to ``dtype`` (fp64 -> fp32 -> bf16), generated chunk by chunk."""
+    rounded to ``dtype`` (fp64 kept; else fp64 -> fp32 -> bf16), generated
+    chunk by chunk."""
     out = torch.empty(numel, dtype=dtype, device=device)
     m_total = (numel + 1) // 2
     for p0 in range(0, m_total, chunk):
@@ -124,7 +125,8 @@ def normal_torch(seed: int, stream: int, numel: int, device="cpu", dtype=torch.f
         z = torch.stack((r * torch.cos(th), r * torch.sin(th)), dim=1).reshape(-1)
         lo = 2 * p0
         hi = min(numel, lo + 2 * m)
-        out[lo:hi] = z[: hi - lo].to(torch.float32).to(dtype)
+        zc = z[: hi - lo]
+        out[lo:hi] = zc if dtype == torch.float64 else zc.to(torch.float32).to(dtype)
     return out
 
 
@@ -148,6 +150,17 @@ def log_decay(seed: int, stream: int, shape) -> np.ndarray:
 def beta_gate(seed: int, stream: int, shape) -> np.ndarray:
     """beta = sigmoid(randn), stored as fp32."""
     return sigmoid(normal(seed, stream, shape)).astype(np.float32)
+
+
+def log_decay_torch(seed: int, stream: int, numel: int, device="cpu") -> torch.Tensor:
+    """Flat fp32 tensor of g = -softplus(randn) (torch path, same definition)."""
+    z = normal_torch(seed, stream, numel, device, torch.float64)
+    return (-torch.nn.functional.softplus(z)).to(torch.float32)
+
+
+def beta_gate_torch(seed: int, stream: int, numel: int, device="cpu") -> torch.Tensor:
+    """Flat fp32 tensor of beta = sigmoid(randn) (torch path)."""
+    return torch.sigmoid(normal_torch(seed, stream, numel, device, torch.float64)).to(torch.float32)
 
 
 def slot_permutation(seed: int, stream: int, P: int) -> np.ndarray:
