@@ -69,9 +69,13 @@ extern "C" {
 #define LA_F32 0
 #define LA_BF16 1
 
-/* Prefill precision modes (kda_prefill_chunked / gdn_prefill_chunked). */
-#define LA_PREFILL_FP32 0 /* every intra-block product in fp32 */
-#define LA_PREFILL_BF16 1 /* bf16 MFMA operands, fp32 accumulation */
+/* Prefill precision modes (kda_prefill_chunked / gdn_prefill_chunked): the
+ * operand precision of the matrix-core products.  Accumulation is fp32 in
+ * both, and the state carried between blocks is fp32; both meet a 1e-4
+ * relative error on fp32 states. */
+#define LA_PREFILL_FP32 0   /* fp32 operands (v_mfma_f32_16x16x4f32) */
+#define LA_PREFILL_BF16X3 1 /* two-term bf16 split of each operand, three bf16
+                               products (about 2^-16 relative per product) */
 
 int la_version(void);
 
@@ -157,7 +161,7 @@ int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype,
  *   slot_in [N] (< 0: zero initial state), slot_out [N] rows of
  *     ssm_pool [H_v, d_v, d_k] (state_dtype).
  *   out [T, H_v, d_v] (io_dtype).
- *   mode: LA_PREFILL_FP32 or LA_PREFILL_BF16.
+ *   mode: LA_PREFILL_FP32 or LA_PREFILL_BF16X3.
  *   workspace: device scratch of at least prefill_workspace_bytes(...)
  *     bytes, 256-byte aligned; contents need no initialisation.
  * Supported: d_k == d_v == 128; H_v a multiple of H_qk. */

@@ -18,7 +18,7 @@ _LIB_PATH = os.path.join(_PKG, "libla.so")
 _lib = None
 
 LA_F32, LA_BF16 = 0, 1
-LA_PREFILL_FP32, LA_PREFILL_BF16 = 0, 1
+LA_PREFILL_FP32, LA_PREFILL_BF16X3 = 0, 1
 _DT = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
 _DT_NAME = {"fp32": LA_F32, "bf16": LA_BF16}
 

@@ -154,7 +154,7 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
         return fail(LA_ERR_ARG, "%s: H_v = %d is not a multiple of H_qk = %d", fn, Hv, Hqk);
     if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
         return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
-    if (mode != LA_PREFILL_FP32 && mode != LA_PREFILL_BF16)
+    if (mode != LA_PREFILL_FP32 && mode != LA_PREFILL_BF16X3)
         return fail(LA_ERR_UNSUPPORTED, "%s: unknown precision mode %d", fn, mode);
     if (dk != 128 || dv != 128)
         return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);

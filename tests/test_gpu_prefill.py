@@ -55,41 +55,51 @@ def run_oracle(sh, inp, pool, si, so, heads=None):
                           kda=sh.kda, state_dtype=sh.state, io_dtype=sh.io)
 
 
-def check(sh, inp, pool, si, so, heads=None, what=""):
+MODES = {"fp32": la.LA_PREFILL_FP32, "bf16x3": la.LA_PREFILL_BF16X3}
+
+
+def tol_class(dtype, mode):
+    """Both precision modes are held to the bar of the tensor's storage dtype."""
+    return dtype
+
+
+def check(sh, inp, pool, si, so, heads=None, what="", mode=la.LA_PREFILL_FP32):
     before = pool.clone()
     o_ref, p_ref = run_oracle(sh, inp, before, si, so, heads)
-    out = run_gpu(sh, inp, pool, si, so)
+    out = run_gpu(sh, inp, pool, si, so, mode=mode)
     torch.cuda.synchronize()
     o = f64(out)
     p = f64(pool)
     if heads is not None:
         o, p = o[:, heads], p[:, heads]
     # outputs per (token, head); states per (slot, head)
-    assert_close_units(o, o_ref, 2, sh.io, f"{what} outputs")
-    assert_close_units(p[so], p_ref[so], 2, sh.state, f"{what} final states")
+    assert_close_units(o, o_ref, 2, tol_class(sh.io, mode), f"{what} outputs")
+    assert_close_units(p[so], p_ref[so], 2, tol_class(sh.state, mode), f"{what} final states")
     untouched = np.setdiff1d(np.arange(pool.shape[0]), so)
     assert np.array_equal(f64(pool)[untouched], f64(before)[untouched])
     return out
 
 
+@pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("io,state", [("bf16", "fp32"), ("fp32", "fp32"), ("bf16", "bf16")])
-def test_kda_prefill_varlen_matches_oracle(io, state, dev):
+def test_kda_prefill_varlen_matches_oracle(io, state, mode, dev):
     lens = [5, 64, 70, 1, 130, 3]
     N = len(lens)
     si = [-1, 7, -1, 8, 9, -1]             # fresh and resumed sequences
     so = [1, 7, 2, 3, 4, 5]                # slot_in == slot_out for one of them
     sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3000, dev, io=io, state=state, slot_in=si,
                                          slot_out=so, P=10)
-    print(f"[prefill parity] kda io={io} state={state} lens={lens}", flush=True)
-    check(sh, inp, pool, si, so, what=f"kda {io}/{state}")
+    print(f"[prefill parity] kda io={io} state={state} mode={mode} lens={lens}", flush=True)
+    check(sh, inp, pool, si, so, what=f"kda {io}/{state}/{mode}", mode=MODES[mode])
 
 
-def test_gdn_prefill_gqa_matches_oracle(dev):
+@pytest.mark.parametrize("mode", list(MODES))
+def test_gdn_prefill_gqa_matches_oracle(mode, dev):
     lens = [100, 17, 64]
     sh, inp, pool, si, so = prefill_case(lens, 1, 2, 3001, dev, kda=False, io="fp32",
                                          state="fp32", slot_in=[2, -1, 3], slot_out=[4, 5, 6],
                                          P=7)
-    check(sh, inp, pool, si, so, what="gdn gqa")
+    check(sh, inp, pool, si, so, what=f"gdn gqa {mode}", mode=MODES[mode])
 
 
 def test_kda_prefill_gqa_matches_oracle(dev):
@@ -110,14 +120,15 @@ def test_empty_and_single_token_sequences(dev):
     assert torch.equal(pool[7], before[4])
 
 
-def test_strong_decay_diagonal_factorisation(dev):
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+def test_strong_decay_diagonal_factorisation(mode, dev):
     """Log decays near -4 per token (16-token spread ~64, inside the
     exponent clamp) still match the oracle."""
     lens = [96]
     sh, inp, pool, si, so = prefill_case(lens, 1, 1, 3004, dev, io="fp32", state="fp32",
                                          slot_in=[1], slot_out=[2], P=2)
     inp["g"] = (inp["g"] * 5.0).clamp(min=-4.5).contiguous()
-    check(sh, inp, pool, si, so, what="strong decay")
+    check(sh, inp, pool, si, so, what="strong decay", mode=MODES[mode])
 
 
 def test_split_through_slots_equals_one_call(dev):
@@ -187,7 +198,8 @@ def test_workspace_too_small_is_rejected(dev):
 
 # ---------------------------------------------------------------- sampled --
 
-def test_sampled_kda_prefill_long_sequence_in_scheduler_chunks(dev):
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+def test_sampled_kda_prefill_long_sequence_in_scheduler_chunks(mode, dev):
     """KDA prefill at the serving shape: H=12, d=128, bf16 I/O, fp32 state; one
     13,600-token sequence in 6,144 / 6,144 / 1,312-token scheduler chunks, the
     end-of-chunk state written to a pool slot each chunk.  Heads 0 and 7 are
@@ -208,14 +220,16 @@ def test_sampled_kda_prefill_long_sequence_in_scheduler_chunks(dev):
         csh = synth.PrefillShape(seqlens=(b - a,), Hqk=H, Hv=H, dk=D, dv=D)
         # chunk c resumes from the slot chunk c - 1 wrote (slot c) and writes slot c + 1
         slot_in = np.array([-1 if c == 0 else c], np.int32)
-        outs.append(run_gpu(csh, sub, pool, slot_in, np.array([c + 1], np.int32)))
+        outs.append(run_gpu(csh, sub, pool, slot_in, np.array([c + 1], np.int32),
+                            mode=MODES[mode]))
     torch.cuda.synchronize()
     out = f64(torch.cat(outs))[:, heads]
     assert_close_units(out, o_ref, 2, "bf16", "13600-token outputs (sampled heads)")
     assert_close_units(f64(pool[3])[heads], p_ref[1], 1, "fp32", "end state (sampled heads)")
 
 
-def test_sampled_kda_prefill_eight_packed_sequences(dev):
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+def test_sampled_kda_prefill_eight_packed_sequences(mode, dev):
     """Eight 4,096-token sequences packed into one varlen call (H=12), fresh
     states to eight distinct slots; heads 3 and 11 checked."""
     H = 12
@@ -226,7 +240,7 @@ def test_sampled_kda_prefill_eight_packed_sequences(dev):
     so = np.arange(1, 9, dtype=np.int32)
     heads = [3, 11]
     o_ref, p_ref = run_oracle(sh, inp, pool, si, so, heads)
-    out = run_gpu(sh, inp, pool, si, so)
+    out = run_gpu(sh, inp, pool, si, so, mode=MODES[mode])
     torch.cuda.synchronize()
     assert_close_units(f64(out)[:, heads], o_ref, 2, "bf16", "packed outputs (sampled heads)")
     assert_close_units(f64(pool)[1:, heads], p_ref[1:], 2, "fp32", "packed end states")

@@ -105,7 +105,7 @@ def test_prefill_validation(lib):
     bad[7] = 10                                           # q stride shorter than a token
     assert lib.kda_prefill_chunked(*bad) == -1
     bad = list(args)
-    bad[25] = 9                                           # unknown mode
+    bad[25] = 2                                           # unknown mode
     assert lib.kda_prefill_chunked(*bad) == -2
     bad = list(args)
     bad[0] = 0                                            # no sequences: no-op
