@@ -64,8 +64,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int CB = 64;         // tokens per tile
 constexpr int DK = 128;        // head dim (d_k = d_v)
-constexpr int LDK = DK + 8;    // LDS row stride (floats) of [64 x 128] arrays (16-byte rows)
-constexpr int LDJ = CB + 4;    // LDS row stride of [* x 64] arrays
+// LDS row strides are 4 (mod 32) floats: rows stay 16-byte aligned and the
+// 16-byte fragment reads of 8 consecutive lanes (8 rows) cover all 32 banks.
+constexpr int LDK = DK + 4;    // [* x 128] arrays
+constexpr int LDJ = CB + 4;    // [* x 64] arrays
+constexpr int kRegion = 128 * LDJ > CB * LDK ? 128 * LDJ : CB * LDK;  // one [64 x 128] or [128 x 64] array
 constexpr float kExpClamp = 80.f;
 enum { PM_F32 = 0, PM_BF16X3 = 1 };
 
@@ -94,12 +97,14 @@ template <int MODE, int K> __device__ __forceinline__ int frag_off4(int q, int g
     if constexpr (MODE == PM_F32) return q * (K / 4) + 4 * g;
     else return 32 * (g >> 1) + 8 * q + 4 * (g & 1);
 }
-template <int MODE, int K>
-__device__ __forceinline__ void load_frag(float *fr, const float *row, int q)
+// Loads n consecutive runs of 64 float4 (fragment-major storage): this lane's
+// float4 of each run, into fr[4 g .. 4 g + 3].
+__device__ __forceinline__ void load_run(float *fr, const float *base, int n, int lane)
 {
 #pragma unroll
-    for (int g = 0; g < K / 16; ++g) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + frag_off4<MODE, K>(q, g));
+    for (int g = 0; g < 8; ++g) {
+        if (g >= n) break;
+        const float4 v = *reinterpret_cast<const float4 *>(base + (g * 64 + lane) * 4);
         fr[4 * g] = v.x; fr[4 * g + 1] = v.y; fr[4 * g + 2] = v.z; fr[4 * g + 3] = v.w;
     }
 }
@@ -167,33 +172,44 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
 }
 
 // ---- workspace -------------------------------------------------------------
-// fp32 arrays indexed by (token, value head): U, W, Q Gamma [.., 128],
-// P [.., 64] (tile-local columns), the piece's total log decay [.., 128] (at
-// piece-end tokens); and K Gamma_L / Gamma transposed per (tile, head):
-// [128 channels][64 tokens].
+// Everything the block chain reads per (tile, value head), bh = tile * H_v + h,
+// stored in fragment-major order: each run of 64 float4 is exactly what one
+// wave-wide 16-byte load of the chain kernel reads, lane after lane, so every
+// such load covers 1 KiB of contiguous memory.  With lane = 16 lq + li:
+//   U  [bh][I 4][rs 8][lane][4]  U[16I + 4lq + r][16rs + li] (matrix-core result order)
+//   W  [bh][I 4][g 8][lane][4]   W[16I + li][frag_off4<DK>(lq, g) + e]
+//   Qt [bh][I 4][g 8][lane][4]   (Q Gamma)[16I + li][frag_off4<DK>(lq, g) + e]
+//   P  [bh][I 4][g 4][lane][4]   P[16I + li][frag_off4<CB>(lq, g) + e]
+//   KhT[bh][cg 8][g 4][lane][4]  (K Gamma_L / Gamma)^T[16cg + li][frag_off4<CB>(lq, g) + e]
+// and, indexed by token, Ge [T][H_v][128]: the piece's total log decay, at
+// piece-end tokens.  The fragment order depends on the precision mode.
+constexpr int kBlkDK = CB * DK;  // floats of one [64 x 128] array per (tile, head)
+constexpr int kBlkCB = CB * CB;  // floats of P per (tile, head)
 struct Ws {
-    float *U, *W, *Qt, *P, *Ge, *KhT;
+    float *U, *W, *Qt, *P, *KhT, *Ge;
 };
 __host__ __device__ inline Ws ws_layout(void *base, int T, int Hv)
 {
-    const size_t n = (size_t)T * Hv;
+    const size_t nb = (size_t)((T + CB - 1) / CB) * Hv;
     float *p = static_cast<float *>(base);
     Ws w;
     w.U = p;
-    w.W = w.U + n * DK;
-    w.Qt = w.W + n * DK;
-    w.Ge = w.Qt + n * DK;
-    w.P = w.Ge + n * DK;
-    w.KhT = w.P + n * CB;
+    w.W = w.U + nb * kBlkDK;
+    w.Qt = w.W + nb * kBlkDK;
+    w.P = w.Qt + nb * kBlkDK;
+    w.KhT = w.P + nb * kBlkCB;
+    w.Ge = w.KhT + nb * kBlkDK;
     return w;
 }
+// Float offset of (group g, lane) inside a fragment-major run.
+__device__ __forceinline__ int fidx(int g, int lane) { return (g * 64 + lane) * 4; }
 
 size_t prefill_ws_bytes(int N, int T, int Hqk, int Hv, int D, int mode)
 {
     (void)N; (void)Hqk; (void)mode;
     if (D != DK || T <= 0) return 0;
-    const size_t tiles = (size_t)(T + CB - 1) / CB;
-    const size_t floats = (size_t)T * Hv * (4 * DK + CB) + tiles * Hv * DK * CB;
+    const size_t nb = (size_t)((T + CB - 1) / CB) * Hv;
+    const size_t floats = nb * (4 * kBlkDK + kBlkCB) + (size_t)T * Hv * DK;
     return (floats * sizeof(float) + 255) & ~size_t(255);
 }
 
@@ -234,7 +250,7 @@ template <> __device__ __forceinline__ void load16<bf16_t>(float *f, const void 
 // Kernel 1: intra-block quantities, one workgroup (8 waves) per (tile, head).
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 512;
-constexpr size_t kIntraLdsFloats = 3 * CB * LDK + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
+constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
 constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + 2 * CB * sizeof(int);
 
 template <typename IOT, bool KDA, int MODE>
@@ -242,9 +258,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 {
     extern __shared__ float sm[];
     float *Qn = sm;                  // q_hat [64][LDK]; later (beta K Gamma)^T [128][LDJ]
-    float *Kn = Qn + CB * LDK;       // k_hat [64][LDK]; later (beta V)^T [128][LDJ]
-    float *Gc = Kn + CB * LDK;       // cumulative log decay over the tile
-    float *Nm = Gc + CB * LDK;       // N = Diag(beta) A (strictly lower, masked); earlier K^ T
+    float *Kn = Qn + kRegion;        // k_hat [64][LDK]; later (beta V)^T [128][LDJ]
+    float *Gc = Kn + kRegion;        // cumulative log decay over the tile
+    float *Nm = Gc + kRegion;        // N = Diag(beta) A (strictly lower, masked); earlier K^ T
     float *Tm = Nm + CB * LDJ;       // T = (I + N)^-1
     float *bet = Tm + CB * LDJ;      // beta
     float *qsum = bet + CB;          // [4][128] partial sums of the tile scan
@@ -328,41 +344,54 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     }
     __syncthreads();
 
-    // ---- 3. Q Gamma (global), the piece's total decay (global, at piece ends),
-    //         K Gamma_L / Gamma transposed through LDS
+    // ---- 3. K Gamma_L / Gamma transposed through LDS and the piece's total
+    //         decay (global, at piece ends): thread (channel c, 16 tokens);
+    //         Q Gamma straight to global in fragment order
+    const int64_t bh = (int64_t)tile * a.Hv + h;
     {
-        float qt[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = c0 + e;
-            const float G = Gc[t * LDK + c];
-            const float Gs = ps > 0 ? Gc[(ps - 1) * LDK + c] : 0.f;
-            const float Ge = Gc[pe * LDK + c];
-            qt[e] = Qn[t * LDK + c] * exp_acc(G - Gs);
-            KhTl[c * LDJ + t] = Kn[t * LDK + c] * exp_acc(Ge - G);
-            if (valid && t == pe) ws.Ge[row(t) * DK + c] = Ge - Gs;
-        }
-        if (valid) {
-#pragma unroll
-            for (int e = 0; e < 16; e += 4)
-                *reinterpret_cast<float4 *>(ws.Qt + row(t) * DK + c0 + e) =
-                    make_float4(qt[e], qt[e + 1], qt[e + 2], qt[e + 3]);
+        const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const int tt = tq + i;
+            const int pst_t = pst[tt], pen_t = pen[tt];
+            const float G = Gc[tt * LDK + c];
+            const float Ge = Gc[pen_t * LDK + c];
+            KhTl[c * LDJ + tt] = Kn[tt * LDK + c] * exp_acc(Ge - G);
+            if (tt < nt && tt == pen_t) {
+                const float Gs = pst_t > 0 ? Gc[(pst_t - 1) * LDK + c] : 0.f;
+                ws.Ge[row(tt) * DK + c] = Ge - Gs;
+            }
         }
     }
+    for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
+        const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
+        const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
+        const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
+        const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
+        float4 Gs = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (pst[tt] > 0) Gs = *reinterpret_cast<const float4 *>(Gc + (pst[tt] - 1) * LDK + k0);
+        *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
+            make_float4(qn.x * exp_acc(G.x - Gs.x), qn.y * exp_acc(G.y - Gs.y),
+                        qn.z * exp_acc(G.z - Gs.z), qn.w * exp_acc(G.w - Gs.w));
+    }
     __syncthreads();
-    {   // KhT: [128][64] per (tile, head); thread (channel c, 16 tokens)
-        const int c = tid >> 2, tq = 16 * (tid & 3);
-        float *dst = ws.KhT + (((int64_t)tile * a.Hv + h) * DK + c) * CB + tq;
-#pragma unroll
-        for (int e = 0; e < 16; e += 4)
-            *reinterpret_cast<float4 *>(dst + e) = *reinterpret_cast<const float4 *>(KhTl + c * LDJ + tq + e);
+    for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {  // KhT in fragment order
+        const int cg = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
+        const int c = 16 * cg + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
+        *reinterpret_cast<float4 *>(ws.KhT + bh * kBlkDK + 4 * idx) =
+            *reinterpret_cast<const float4 *>(KhTl + c * LDJ + j0);
     }
     __syncthreads();
     for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
     __syncthreads();
 
-    // ---- 4. A and P, one 16x16 tile pair (I, J <= I) per wave job
-    for (int job = wave; job < 10; job += 8) {
+    // ---- 4. A and P, one 16x16 tile pair (I, J <= I) per wave job; P is
+    //         kept in registers and staged through LDS once Q is dead
+    f32x4 pkeep[2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int job = wave + 8 * jj;
+        if (job >= 10) break;
         // jobs in order of cost: (3,0..3), (2,0..2), (1,0..1), (0,0)
         const int I = job < 4 ? 3 : job < 7 ? 2 : job < 9 ? 1 : 0;
         const int J = job < 4 ? job : job < 7 ? job - 4 : job < 9 ? job - 7 : 0;
@@ -389,14 +418,24 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             const int tt = 16 * I + 4 * lq + r, j = 16 * J + li;
             const bool same = j >= pst[tt] && tt < nt;
             Nm[tt * LDJ + j] = (same && j < tt) ? bet[tt] * accA[r] : 0.f;
-            if (tt < nt) ws.P[row(tt) * CB + j] = (same && j <= tt) ? accP[r] : 0.f;
+            pkeep[jj][r] = (same && j <= tt) ? accP[r] : 0.f;
         }
     }
-    for (int idx = tid; idx < nt * CB; idx += kIntraThreads) {  // upper tiles of P are zero
-        const int tt = idx / CB, j = idx % CB;
-        if ((j >> 4) > (tt >> 4)) ws.P[row(tt) * CB + j] = 0.f;
-    }
     __syncthreads();
+    float *Ps = Qn;  // P [64][LDJ]; q_hat is no longer read
+    for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {  // upper tiles of P are zero
+        const int tt = idx / CB, j = idx % CB;
+        if ((j >> 4) > (tt >> 4)) Ps[tt * LDJ + j] = 0.f;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int job = wave + 8 * jj;
+        if (job >= 10) break;
+        const int I = job < 4 ? 3 : job < 7 ? 2 : job < 9 ? 1 : 0;
+        const int J = job < 4 ? job : job < 7 ? job - 4 : job < 9 ? job - 7 : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ps[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = pkeep[jj][r];
+    }
 
     // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
     //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
@@ -415,6 +454,14 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
     }
     __syncthreads();
+    if (wave >= 4) {  // P to global in fragment order while waves 0..3 run the levels
+        for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
+            const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
+            const int tt = 16 * I + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
+            *reinterpret_cast<float4 *>(ws.P + bh * kBlkCB + 4 * idx) =
+                *reinterpret_cast<const float4 *>(Ps + tt * LDJ + j0);
+        }
+    }
     float *ws16 = scr + wave * 16 * 17;
     for (int lev = 1; lev <= 3; ++lev) {
         const int I = wave, J = wave - lev;
@@ -454,23 +501,33 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + i) =
                 make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
     }
-    {
-        float vv[16];
-        load16<IOT>(vv, static_cast<const IOT *>(a.v) + tok * a.v_stride + h * DK + c0);
+    {   // thread (channel c, 16 tokens): rows of (beta V)^T, loads coalesced over c
+        const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
+        float xv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int tt = tq + i;
+            const int64_t tk = t0 + min(tt, nt - 1);
+            xv[i] = bet[tt] * ld<IOT>(a.v, tk * a.v_stride + h * DK + c);  // bet = 0 past nt
+        }
         __syncthreads();  // Kn is free
 #pragma unroll
-        for (int e = 0; e < 16; ++e) XtV[(c0 + e) * LDJ + t] = valid ? bet[t] * vv[e] : 0.f;
+        for (int i = 0; i < 16; i += 4)
+            *reinterpret_cast<float4 *>(XtV + c * LDJ + tq + i) =
+                make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
     }
     __syncthreads();
 
     // ---- 7. U = T (beta V) and W = T (beta K Gamma): wave w owns output
-    //         columns 16w .. 16w + 15 of both, for the four token blocks
+    //         columns 16w .. 16w + 15 of both, for the four token blocks.
+    //         U leaves in the result layout; W is staged in LDS (the decay
+    //         cumsum is dead) and leaves in fragment order.
+    float *Wst = Gc;  // [64][LDK]
     {
         const int C = wave;
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const float *Xt = which ? XtK : XtV;
-            float *dst = which ? ws.W : ws.U;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -479,13 +536,21 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 auto fb = [&](int, int j) { return Xrow[j]; };
                 if (I < 2) mma_gen<MODE, 32>(acc, lq, fa, fb);  // T rows < 32: columns < 32
                 else mma_gen<MODE, 64>(acc, lq, fa, fb);
+                if (which == 0) {
+                    *reinterpret_cast<f32x4 *>(ws.U + bh * kBlkDK + fidx(I * 8 + C, lane)) = acc;
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tt = 16 * I + 4 * lq + r;
-                    if (tt < nt) dst[row(tt) * DK + 16 * C + li] = acc[r];
+                    for (int r = 0; r < 4; ++r) Wst[(16 * I + 4 * lq + r) * LDK + 16 * C + li] = acc[r];
                 }
             }
         }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
+        const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
+        const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
+        *reinterpret_cast<float4 *>(ws.W + bh * kBlkDK + 4 * idx) =
+            *reinterpret_cast<const float4 *>(Wst + tt * LDK + k0);
     }
 }
 
@@ -493,29 +558,31 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 // Kernel 2: the block chain, one workgroup per (sequence, head, 16 state rows).
 // Waves 0..3 ("row waves") own token rows 16I.. of D and O; waves 4..7
 // ("column waves") own state columns 32(w-4) .. 32(w-4) + 31 of the update.
-// The next tile's W, U (row waves) and K^T, Gamma (column waves) are loaded
-// into registers while the current tile computes.
+// All of a tile's operands are loaded into registers while the previous tile
+// computes, and the state slice is double-buffered in LDS, so a tile costs
+// two barriers: D, then the output and the new state side by side.
 // ---------------------------------------------------------------------------
 constexpr int kChainThreads = 512;
-constexpr size_t kChainLds = (16 * LDK + 16 * LDJ) * sizeof(float);
+constexpr size_t kChainLds = (2 * 16 * LDK + 16 * LDJ) * sizeof(float);
 
-// Per-lane prefetch buffer, shared by the two wave roles:
-//   row waves:    [0, 32) W row fragment (K = 128 channels), [32, 36) U values;
-//   column waves: [0, 32) K^T row fragments of two column tiles (K = 64
-//                 tokens, 16 each), [32, 34) Gamma_L of the lane's columns.
-constexpr int kOps = 36;
+// Per-lane operands of one tile.  Row waves: [0, 32) W row fragment (K = 128
+// channels), [32, 36) U in the result layout, [36, 68) Q Gamma row fragment,
+// [68, 84) P row fragment (K = 64 tile-local tokens).  Column waves: [0, 32)
+// K^T row fragments of two column tiles (K = 64 tokens), [32, 34) Gamma_L of
+// the lane's two columns.  The two roles run separate loops with the same
+// barrier sequence, so each keeps its own arrays in registers.
+constexpr int kRowOps = 84, kColOps = 34;
 
 template <typename IOT, typename ST, int MODE>
 __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArgs a)
 {
     extern __shared__ float sm[];
-    float *St = sm;               // state slice [16 rows][LDK]
-    float *Dt = St + 16 * LDK;    // D^T of the tile [16 rows][LDJ] (tile-local tokens)
+    float *Sbuf = sm;                 // two state slices [16 rows][LDK]
+    float *Dt = sm + 2 * 16 * LDK;    // D^T of the tile [16 rows][LDJ] (tile-local tokens)
 
     const int n = blockIdx.x, h = blockIdx.y, rs = blockIdx.z;  // rows 16 rs .. 16 rs + 15
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
-    const bool rowwave = wave < 4;
     const int I = wave & 3;       // token block (row waves) / column pair (column waves)
     const Ws ws = ws_layout(a.ws, a.T, a.Hv);
     const int start = a.cu[n], end = a.cu[n + 1];
@@ -534,45 +601,28 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
         if (si >= 0)
             v = ld<ST>(a.ssm_pool,
                        (int64_t)si * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c);
-        St[i * LDK + c] = v;
+        Sbuf[i * LDK + c] = v;
     }
 
     const int tb0 = start / CB, tb1 = end > start ? (end - 1) / CB : tb0 - 1;
-    // Operand prefetch for tile tb (clamped: loads stay inside the arrays).
-    auto load_ops = [&](int tb, float *ops) {
-        const int base = tb * CB;
-        if (rowwave) {
-            const int tt = min(base + 16 * I + li, a.T - 1);
-            load_frag<MODE, DK>(ops, ws.W + ((int64_t)tt * a.Hv + h) * DK, lq);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tr = min(base + 16 * I + 4 * lq + r, a.T - 1);
-                ops[32 + r] = ws.U[((int64_t)tr * a.Hv + h) * DK + 16 * rs + li];
-            }
-        } else {
-            const int pend = min(end, base + CB) - 1;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int c = 32 * I + 16 * q + li;
-                load_frag<MODE, CB>(ops + 16 * q, ws.KhT + (((int64_t)tb * a.Hv + h) * DK + c) * CB, lq);
-                ops[32 + q] = ws.Ge[((int64_t)max(pend, 0) * a.Hv + h) * DK + c];
-            }
-        }
-    };
-
-    float cur[kOps], nxt[kOps];
-    if (tb1 >= tb0) load_ops(tb0, cur);
-    for (int tb = tb0; tb <= tb1; ++tb) {
-        const int base = tb * CB;
-        const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
-        load_ops(min(tb + 1, tb1), nxt);  // next tile (the last one reloads itself)
-        __syncthreads();                   // state of the previous tile in place
-
-        float fq[DK / 4], fp[CB / 4];
-        const float *Srow = St + li * LDK, *Drow = Dt + li * LDJ;
-        auto lds_s = [&](int, int c) { return Srow[c]; };
-        auto lds_d = [&](int, int j) { return Drow[j]; };
-        if (rowwave) {
+    const int ntiles = tb1 - tb0 + 1;  // 0 for an empty sequence
+    if (wave < 4) {
+        auto load_ops = [&](int tb, float *ops) {
+            const int64_t bh = (int64_t)tb * a.Hv + h;
+            load_run(ops, ws.W + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            load_run(ops + 32, ws.U + bh * kBlkDK + fidx(8 * I + rs, 0), 1, lane);
+            load_run(ops + 36, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            load_run(ops + 68, ws.P + bh * kBlkCB + fidx(4 * I, 0), 4, lane);
+        };
+        float cur[kRowOps], nxt[kRowOps];
+        if (ntiles > 0) load_ops(tb0, cur);
+        for (int it = 0; it < ntiles; ++it) {
+            const int tb = tb0 + it, base = tb * CB;
+            const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
+            load_ops(min(tb + 1, tb1), nxt);  // next tile (the last one reloads itself)
+            __syncthreads();                   // state slice in place, last D^T consumed
+            const float *Srow = Sbuf + (it & 1) * 16 * LDK + li * LDK, *Drow = Dt + li * LDJ;
+            auto lds_s = [&](int, int c) { return Srow[c]; };
             // D = U - W S^T, rows outside the piece masked
             const int ti = 16 * I + li;
             const bool in_i = ti >= p0 && ti < p1;
@@ -584,19 +634,12 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
                 const bool in_r = tr >= p0 && tr < p1;
                 Dt[li * LDJ + tr] = in_r ? cur[32 + r] - acc[r] : 0.f;
             }
-            // Q Gamma and P rows for the output (off the chain's critical path)
-            const int tt = min(base + ti, a.T - 1);
-            load_frag<MODE, DK>(fq, ws.Qt + ((int64_t)tt * a.Hv + h) * DK, lq);
-            load_frag<MODE, CB>(fp, ws.P + ((int64_t)tt * a.Hv + h) * CB, lq);
-        }
-        __syncthreads();  // D^T complete
-
-        f32x4 snew[2];
-        if (rowwave) {
+            __syncthreads();  // D^T complete
             // O = scale (Q Gamma S^T + P D)
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma_gen<MODE, DK>(acc, lq, [&](int idx, int) { return fq[idx]; }, lds_s);
-            mma_gen<MODE, CB>(acc, lq, [&](int idx, int) { return fp[idx]; }, lds_d);
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma_gen<MODE, DK>(acc, lq, [&](int idx, int) { return cur[36 + idx]; }, lds_s);
+            mma_gen<MODE, CB>(acc, lq, [&](int idx, int) { return cur[68 + idx]; },
+                              [&](int, int j) { return Drow[j]; });
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tr = 16 * I + 4 * lq + r;
@@ -604,36 +647,57 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
                     st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + 16 * rs + li,
                             a.scale * acc[r]);
             }
-        } else {
+#pragma unroll
+            for (int i = 0; i < kRowOps; ++i) cur[i] = nxt[i];
+        }
+    } else {
+        auto load_ops = [&](int tb, float *ops) {
+            const int pend = min(end, tb * CB + CB) - 1;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = 32 * I + 16 * q + li;
+                load_run(ops + 16 * q,
+                         ws.KhT + ((int64_t)tb * a.Hv + h) * kBlkDK + fidx(4 * (2 * I + q), 0), 4,
+                         lane);
+                ops[32 + q] = ws.Ge[((int64_t)pend * a.Hv + h) * DK + c];
+            }
+        };
+        float cur[kColOps], nxt[kColOps];
+        if (ntiles > 0) load_ops(tb0, cur);
+        for (int it = 0; it < ntiles; ++it) {
+            const int tb = tb0 + it, base = tb * CB;
+            const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
+            load_ops(min(tb + 1, tb1), nxt);
+            __syncthreads();
+            __syncthreads();  // D^T complete
             // new state columns: S Gamma_L + D^T K^  (K^ columns outside the piece masked)
+            const float *Scur = Sbuf + (it & 1) * 16 * LDK;
+            float *Snext = Sbuf + ((it & 1) ^ 1) * 16 * LDK;
+            const float *Drow = Dt + li * LDJ;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                mma_gen<MODE, CB>(acc, lq, lds_d, [&](int idx, int j) {
-                    return (j >= p0 && j < p1) ? cur[16 * q + idx] : 0.f;
-                });
+                mma_gen<MODE, CB>(acc, lq, [&](int, int j) { return Drow[j]; },
+                                  [&](int idx, int j) {
+                                      return (j >= p0 && j < p1) ? cur[16 * q + idx] : 0.f;
+                                  });
                 const int c = 32 * I + 16 * q + li;
                 const float gm = exp_acc(cur[32 + q]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf(St[(4 * lq + r) * LDK + c], gm, acc[r]);
-                snew[q] = acc;
+                for (int r = 0; r < 4; ++r)
+                    Snext[(4 * lq + r) * LDK + c] =
+                        fmaf(Scur[(4 * lq + r) * LDK + c], gm, acc[r]);
             }
+#pragma unroll
+            for (int i = 0; i < kColOps; ++i) cur[i] = nxt[i];
         }
-        __syncthreads();  // every wave done reading the old state
-        if (!rowwave) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) St[(4 * lq + r) * LDK + 32 * I + 16 * q + li] = snew[q][r];
-        }
-#pragma unroll
-        for (int i = 0; i < kOps; ++i) cur[i] = nxt[i];
     }
     __syncthreads();
+    const float *Sfin = Sbuf + (ntiles & 1) * 16 * LDK;
     for (int idx = tid; idx < 16 * DK; idx += kChainThreads) {
         const int i = idx / DK, c = idx % DK;
         st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c,
-               St[i * LDK + c]);
+               Sfin[i * LDK + c]);
     }
 }
 
