@@ -227,8 +227,10 @@ int orc_decode(int kda, int B, int Hqk, int Hv, int dk, int dv,
  * [cu[n], cu[n+1]) of x [T, C].  Its history comes from conv_pool row
  * slot_in[n] (zeros when slot_in[n] < 0); after the last token the three most
  * recent pre-conv inputs (older history shifted in for sequences shorter than
- * three tokens) are stored to row slot_out[n].  y [T, C] gets the SiLU output
- * rounded to io_dtype. */
+ * three tokens) are stored to row slot_out[n], rounded to conv_dtype.  Inside
+ * the call the window holds the sequence's own inputs; the stored history only
+ * supplies the positions before the sequence's first token.  y [T, C] gets the
+ * SiLU output rounded to io_dtype. */
 void orc_shortconv_prefill(int N, int C, const double *x, const int32_t *cu,
                            const int32_t *slot_in, const int32_t *slot_out,
                            const double *w, const double *bias,
@@ -249,10 +251,12 @@ void orc_shortconv_prefill(int N, int C, const double *x, const int32_t *cu,
                 y[(int64_t)t * C + c] = orc_round(silu(acc), io_dtype);
                 hist[c] = win[1];
                 hist[C + c] = win[2];
-                hist[2 * C + c] = orc_round(win[3], conv_dtype);
+                hist[2 * C + c] = win[3];  /* inside the call the window holds the inputs */
             }
         }
-        memcpy(conv_pool + (int64_t)slot_out[n] * conv_stride, hist, sizeof(double) * 3 * C);
+        /* only the hand-off to the next call is stored in the conv dtype */
+        for (int64_t i = 0; i < 3 * (int64_t)C; ++i)
+            conv_pool[(int64_t)slot_out[n] * conv_stride + i] = orc_round(hist[i], conv_dtype);
     }
     free(hist);
 }

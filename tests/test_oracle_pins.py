@@ -117,6 +117,31 @@ def test_conv_short_sequence_shifts_in_old_history():
     np.testing.assert_array_equal(newpool[2], np.stack([pool[1][2], x[0], x[1]]))
 
 
+def test_conv_dtype_only_rounds_the_handoff():
+    """Inside one call the window holds the sequence's own inputs: with no
+    prior history the conv-state dtype cannot change the outputs, and only the
+    three inputs handed to slot_out are rounded to it.  Splitting a sequence
+    over two calls through an fp64 history reproduces the single call."""
+    C, T = 6, 9
+    x = synth.normal(7, 0, (T, C)) * 1.37  # not representable in bf16
+    w = synth.normal(7, 1, (C, 4))
+    pool = np.zeros((3, 3, C))
+    y64, p64 = oracle.shortconv_prefill(x, [0, T], [-1], [1], w, None, pool, conv_dtype="fp64",
+                                        io_dtype="fp64")
+    ybf, pbf = oracle.shortconv_prefill(x, [0, T], [-1], [1], w, None, pool, conv_dtype="bf16",
+                                        io_dtype="fp64")
+    np.testing.assert_array_equal(ybf, y64)
+    np.testing.assert_array_equal(pbf[1], oracle.round_to(x[-3:], "bf16"))
+    assert not np.array_equal(pbf[1], p64[1])
+    for cut in (1, 2, 5):
+        ya, pa = oracle.shortconv_prefill(x[:cut], [0, cut], [-1], [1], w, None, pool,
+                                          conv_dtype="fp64", io_dtype="fp64")
+        yb, pb = oracle.shortconv_prefill(x[cut:], [0, T - cut], [1], [2], w, None, pa,
+                                          conv_dtype="fp64", io_dtype="fp64")
+        np.testing.assert_array_equal(np.concatenate([ya, yb]), y64)
+        np.testing.assert_array_equal(pb[2], p64[1])
+
+
 def test_conv_decode_step_matches_direct_sum():
     B, C, P = 4, 9, 6
     x = synth.normal(6, 0, (B, C))
