@@ -17,7 +17,8 @@
 // State streaming.  Row i of a head's state (d_k contiguous) is split over
 // LPR lanes holding 16 bytes each (8 bf16 or 4 fp32), so one wave instruction
 // moves RPW = 64 / LPR consecutive rows = 1 KB contiguous: fully coalesced.
-// Each wave owns a contiguous band of RW rows per head.  Both row reductions
+// Each wave owns a contiguous band of RW rows per head; the row loads and
+// stores carry the non-temporal hint.  Both row reductions
 // (S'k and S'q) come out of one pass over the registers (DPP adds inside the
 // LPR-lane group, bit-identical in every lane), the update is applied in
 // registers and the row is stored back: the state crosses HBM once each way.
@@ -131,7 +132,7 @@ __device__ __forceinline__ void load_rows(uint4 *buf, const ST *S, int wave, int
     for (int j = 0; j < Cfg::NJ; ++j) {
         const int r = (wave * Cfg::NJ + j) * Cfg::RPW + lane / Cfg::LPR;
         if (D >= Cfg::RPW || r < D)
-            buf[j] = *reinterpret_cast<const uint4 *>(S + (int64_t)r * D + col0);
+            buf[j] = ld_stream(S + (int64_t)r * D + col0);
         else
             buf[j] = make_uint4(0, 0, 0, 0);
     }
@@ -288,7 +289,7 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
 #pragma unroll
             for (int e = 0; e < EPL; ++e) s[e] = fmaf(s[e], al[e], d * kk[e]);
             if (D >= RPW || r < D)
-                *reinterpret_cast<uint4 *>(S + (int64_t)r * D + col0) = Stor<ST>::pack(s);
+                st_stream(S + (int64_t)r * D + col0, Stor<ST>::pack(s));
         }
         // one output store per lane: lane (l % LPR == j) holds row instruction j
         const int j = lane % LPR;

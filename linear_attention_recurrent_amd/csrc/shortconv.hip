@@ -6,8 +6,10 @@
 // section 2.1).  Tap 3 multiplies the current token and history row 0 is the
 // oldest token:  y = SiLU(w0 h0 + w1 h1 + w2 h2 + w3 x + bias).
 //
-// Both kernels are streaming elementwise passes: one lane per channel, the
-// channel index contiguous across lanes so every access is coalesced.
+// All kernels are streaming passes with the channel index contiguous across
+// lanes, so every access is coalesced.  The prefill output kernel moves
+// 16 bytes of channels per lane and slides the 4-token window along a run of
+// tokens, so each input row is read once (plus three rows at a run's start).
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -78,9 +80,10 @@ __device__ __forceinline__ bool seq_slots_ok(const ConvPrefillArgs &a, int n)
     return si < a.num_rows && so >= 0 && so < a.num_rows;
 }
 
-// Outputs.  grid (ceil(C / 256), ceil(T / kTokPerBlock)), block 256.  The
-// pool is only read here; the history is written by the next kernel, so a
-// sequence whose slot_in equals its slot_out reads its old history safely.
+// Outputs, scalar path (any C).  grid (ceil(C / 256), ceil(T / kTokPerBlock)),
+// block 256.  The pool is only read here (as in the vector path); the history
+// is written by the next kernel, so a sequence whose slot_in equals its
+// slot_out reads its old history safely.
 constexpr int kTokPerBlock = 8;
 __global__ void __launch_bounds__(256) shortconv_prefill_out_kernel(ConvPrefillArgs a)
 {
@@ -112,6 +115,80 @@ __global__ void __launch_bounds__(256) shortconv_prefill_out_kernel(ConvPrefillA
                              : 0.f;
         }
         store_elem(a.y, yi, a.io_dtype, conv4(wc, bias, win[0], win[1], win[2], win[3]));
+    }
+}
+
+// Vector path (C a multiple of 8): lane = 16 bytes of channels, thread = a
+// run of kConvTok tokens.  grid (ceil(C / (256 V)), ceil(T / kConvTok)),
+// block 256.  Same arithmetic, in the same order, as the scalar kernel.
+constexpr int kConvTok = 16;
+template <typename IOT, typename CT>
+__global__ void __launch_bounds__(256) shortconv_prefill_vec_kernel(ConvPrefillArgs a)
+{
+    constexpr int V = Stor<IOT>::kPer16B;  // channels per lane
+    const int c0 = (blockIdx.x * 256 + threadIdx.x) * V;
+    if (c0 >= a.C) return;
+    const int t0 = blockIdx.y * kConvTok;
+    const int nt = min(kConvTok, a.T - t0);
+    const IOT *x = static_cast<const IOT *>(a.x);
+    IOT *y = static_cast<IOT *>(a.y);
+
+    uint4 raw[kConvTok];  // the run's inputs, issued back to back (clamped rows)
+#pragma unroll
+    for (int i = 0; i < kConvTok; ++i)
+        raw[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)min(t0 + i, a.T - 1) * a.C + c0);
+    float4 wc[V];
+    float bs[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        wc[e] = reinterpret_cast<const float4 *>(a.w)[c0 + e];
+        bs[e] = a.bias ? a.bias[c0 + e] : 0.f;
+    }
+
+    int n = find_seq(a.cu, a.N, t0);
+    bool ok = seq_slots_ok(a, n);
+    float h[3][V];
+    // The three inputs before token t of sequence n: earlier tokens of the
+    // sequence, else the slot_in history (zeros for slot_in < 0).
+    auto window = [&](int t) {
+        const int start = a.cu[n], si = a.slot_in[n];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int pos = t - 3 + r;
+            if (pos >= start) {
+                Stor<IOT>::unpack(*reinterpret_cast<const uint4 *>(x + (int64_t)pos * a.C + c0), h[r]);
+            } else if (ok && si >= 0) {
+                const int64_t hrow = (int64_t)si * a.conv_stride + (int64_t)(pos - start + 3) * a.C;
+#pragma unroll
+                for (int e = 0; e < V; ++e) h[r][e] = ld<CT>(a.conv_pool, hrow + c0 + e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) h[r][e] = 0.f;
+            }
+        }
+    };
+    window(t0);
+    int next = a.cu[n + 1];
+#pragma unroll
+    for (int i = 0; i < kConvTok; ++i) {
+        if (i >= nt) break;
+        const int t = t0 + i;
+        if (t == next) {  // token t starts a later (non-empty) sequence
+            while (n + 1 < a.N && a.cu[n + 1] <= t) ++n;
+            next = a.cu[n + 1];
+            ok = seq_slots_ok(a, n);
+            window(t);
+        }
+        float xv[V], yv[V];
+        Stor<IOT>::unpack(raw[i], xv);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            yv[e] = ok ? conv4(wc[e], bs[e], h[0][e], h[1][e], h[2][e], xv[e]) : 0.f;
+            h[0][e] = h[1][e];
+            h[1][e] = h[2][e];
+            h[2][e] = xv[e];
+        }
+        *reinterpret_cast<uint4 *>(y + (int64_t)t * a.C + c0) = Stor<IOT>::pack(yv);
     }
 }
 
@@ -148,7 +225,18 @@ __global__ void __launch_bounds__(256) shortconv_prefill_state_kernel(ConvPrefil
 hipError_t launch_shortconv_prefill(const ConvPrefillArgs &a, hipStream_t stream)
 {
     const unsigned cb = (unsigned)((a.C + 255) / 256);
-    if (a.T > 0) {
+    if (a.T > 0 && a.C % 8 == 0) {
+        const int V = a.io_dtype ? 8 : 4;
+        dim3 g1((unsigned)((a.C / V + 255) / 256), (unsigned)((a.T + kConvTok - 1) / kConvTok));
+        switch ((a.io_dtype ? 2 : 0) | (a.conv_dtype ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<float, float>), g1, dim3(256), 0, stream, a); break;
+        case 1: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<float, bf16_t>), g1, dim3(256), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<bf16_t, float>), g1, dim3(256), 0, stream, a); break;
+        default: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<bf16_t, bf16_t>), g1, dim3(256), 0, stream, a); break;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else if (a.T > 0) {
         dim3 g1(cb, (unsigned)((a.T + kTokPerBlock - 1) / kTokPerBlock));
         hipLaunchKernelGGL(shortconv_prefill_out_kernel, g1, dim3(256), 0, stream, a);
         hipError_t e = hipGetLastError();

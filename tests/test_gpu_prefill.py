@@ -248,10 +248,13 @@ def test_sampled_kda_prefill_eight_packed_sequences(mode, dev):
 
 # ------------------------------------------------------------ short conv ---
 
-@pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("fp32", "fp32")])
-def test_shortconv_prefill_matches_oracle(io, cdt, dev):
-    lens = [1, 2, 3, 40, 0, 9]
-    C = 4608
+@pytest.mark.parametrize("C", [8, 36, 4608])  # 36: the scalar path (C not a multiple of 8)
+@pytest.mark.parametrize("io,cdt", [("bf16", "bf16"), ("fp32", "fp32"), ("fp32", "bf16"),
+                                    ("bf16", "fp32")])
+def test_shortconv_prefill_matches_oracle(io, cdt, C, dev):
+    # sequences shorter than the window, an empty one, and sequences that
+    # start inside and run across the 16-token runs of the vector path
+    lens = [1, 2, 3, 40, 0, 9, 17, 33]
     N = len(lens)
     T = sum(lens)
     seed = 3100
@@ -259,8 +262,8 @@ def test_shortconv_prefill_matches_oracle(io, cdt, dev):
     w = synth.to_torch(0.5 * synth.normal(seed, 1, (C, 4)), "fp32", dev)
     P = 10
     pool = synth.to_torch(synth.normal(seed, 2, (P + 1, 3, C)), cdt, dev)
-    si = np.array([4, -1, 5, 6, 7, -1], np.int32)
-    so = np.array([4, 1, 2, 6, 8, 9], np.int32)   # two in place
+    si = np.array([4, -1, 5, 6, 7, -1, 3, 10], np.int32)
+    so = np.array([4, 1, 2, 6, 8, 9, 3, 10], np.int32)   # four in place
     cu = synth.cu_seqlens(lens)
     y_ref, pool_ref = oracle.shortconv_prefill(f64(x), cu, si, so, f64(w), None, f64(pool),
                                                conv_dtype=cdt, io_dtype=io)
@@ -269,6 +272,30 @@ def test_shortconv_prefill_matches_oracle(io, cdt, dev):
     torch.cuda.synchronize()
     assert_close_units(f64(y), y_ref, 1, io, "conv outputs")
     assert np.array_equal(f64(pool), pool_ref), "conv history must match bit for bit"
+
+
+@pytest.mark.parametrize("C", [36, 4608])
+def test_shortconv_prefill_skips_out_of_range_slots(C, dev):
+    """A sequence whose slot is out of range gets zero outputs and touches no
+    pool row; the other sequences are unaffected."""
+    lens = [5, 20, 7]
+    T = sum(lens)
+    x = synth.to_torch(synth.normal(3102, 0, (T, C)), "bf16", dev)
+    w = synth.to_torch(0.5 * synth.normal(3102, 1, (C, 4)), "fp32", dev)
+    P = 4
+    pool = synth.to_torch(synth.normal(3102, 2, (P + 1, 3, C)), "bf16", dev)
+    before = pool.clone()
+    cu = synth.cu_seqlens(lens)
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)  # noqa: E731
+    y = la.shortconv_prefill(x, torch.from_numpy(cu).to(dev), i32([1, 2, P + 1]),
+                             i32([1, P + 7, 3]), w, pool)
+    torch.cuda.synchronize()
+    y_ref, pool_ref = oracle.shortconv_prefill(f64(x)[:5], [0, 5], [1], [1], f64(w), None,
+                                               f64(before), conv_dtype="bf16", io_dtype="bf16")
+    assert_close_units(f64(y)[:5], y_ref, 1, "bf16", "valid sequence")
+    assert torch.count_nonzero(y[5:]) == 0
+    assert np.array_equal(f64(pool)[1], pool_ref[1])
+    assert torch.equal(pool[2:], before[2:]) and torch.equal(pool[0], before[0])
 
 
 def test_shortconv_prefill_then_decode_continues_history(dev):
