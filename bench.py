@@ -47,6 +47,7 @@ from linear_attention_recurrent_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFS = 157.3
+MFMA_BF16_PEAK_TFS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -236,27 +237,31 @@ def decode_stack(sh, layers, steps, seed, dev):
 
 # --------------------------------------------------------------- prefill ----
 
-def prefill_mfma_flops(seqlens, Hv) -> float:
-    """fp32 MFMA flops the two prefill kernels issue for a packed call (each
-    v_mfma_f32_16x16x4f32 = 2048 flops), following their loop structure."""
+def prefill_mfma_flops(seqlens, Hv, mode=0) -> float:
+    """Matrix-core flops the two prefill kernels issue for one packed call,
+    following their loop structure.  mode 0 (fp32): v_mfma_f32_16x16x4f32,
+    2,048 flops each; mode 1 (bf16x3): three v_mfma_f32_16x16x32_bf16 per
+    32-deep step, 16,384 flops each (the T-inverse level products stay fp32
+    in both modes)."""
     T = int(sum(seqlens))
     tiles = -(-T // 64)
-    intra = tiles * Hv * 1344            # A, P: 640; T blocks: 64; U, W: 640
-    chain = 0
+    if mode == 0:
+        # per (tile, head): A and P 10 jobs x 2 x 32; T levels 64; U, W 8 waves x 2 x 48
+        intra = tiles * Hv * (640 + 64 + 768) * 2048.0
+        per_chain_tile = (4 * 80 + 4 * 32) * 2048.0       # row waves D + O; column waves
+    else:
+        intra = tiles * Hv * ((240 + 288) * 16384.0 + 64 * 2048.0)
+        per_chain_tile = (4 * 30 + 4 * 12) * 16384.0
+    chain_tiles = 0
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     for n in range(len(seqlens)):
         a, b = int(cu[n]), int(cu[n + 1])
-        if b <= a:
-            continue
-        for tile in range(a // 64, (b - 1) // 64 + 1):
-            L = min(b, 64 * tile + 64) - max(a, 64 * tile)
-            waves = -(-L // 16)
-            chain += waves * 32 + sum(32 + 4 * (i + 1) for i in range(waves)) + 8 * (-(-L // 4))
-    chain *= 8 * Hv                      # eight 16-row slices of the state per head
-    return 2048.0 * (intra + chain)
+        if b > a:
+            chain_tiles += (b - 1) // 64 - a // 64 + 1
+    return intra + chain_tiles * 8 * Hv * per_chain_tile   # eight 16-row state slices per head
 
 
-def prefill_bench(dev, reps=5):
+def prefill_bench(dev, reps=10):
     """Chunked KDA prefill, H=12, d=128, bf16 I/O, fp32 state: W1 = one
     13,600-token sequence in 6,144 / 6,144 / 1,312-token calls chained through
     a pool slot; W2 = eight 4,096-token sequences packed in one call.  Each call
@@ -297,40 +302,42 @@ def prefill_bench(dev, reps=5):
         x, g, beta, cu, si, so, _ = calls[i]
         la.shortconv_prefill(x, cu, si, so, w, conv_pool, y=ys[i])
 
-    def chunk(i):
+    def chunk(i, mode=0):
         x, g, beta, cu, si, so, _ = calls[i]
         y = ys[i]
         q = y[:, :H * D].unflatten(1, (H, D))
         k = y[:, H * D:2 * H * D].unflatten(1, (H, D))
         v = y[:, 2 * H * D:].unflatten(1, (H, D))
-        la.kda_prefill_chunked(q, k, v, g, beta, cu, si, so, ssm_pool, out=outs[i], workspace=ws)
+        la.kda_prefill_chunked(q, k, v, g, beta, cu, si, so, ssm_pool, out=outs[i], workspace=ws,
+                               mode=mode)
 
-    for i in range(4):
-        conv(i)
-        chunk(i)
-    torch.cuda.synchronize()
-    t_conv = [0.0] * 4
-    t_chunk = [0.0] * 4
-    for _ in range(reps):
+    def run_all(mode):
         for i in range(4):
-            e0, e1 = events()
-            e2, e3 = events()
-            e0.record()
             conv(i)
-            e1.record()
-            e2.record()
-            chunk(i)
-            e3.record()
-            torch.cuda.synchronize()
-            t_conv[i] += e0.elapsed_time(e1) / reps
-            t_chunk[i] += e2.elapsed_time(e3) / reps
+            chunk(i, mode)
+
+    res_modes = {}
+    for mode in (0, 1):
+        run_all(mode)  # every slot a call reads now holds its predecessor's hand-off
+        torch.cuda.synchronize()
+        t_conv = [time_graph(lambda i=i: [conv(i) for _ in range(reps)], reps, 4 * reps, reps)[0]
+                  for i in range(4)]
+        t_chunk = [time_graph(lambda i=i: [chunk(i, mode) for _ in range(reps)], reps, 4 * reps,
+                              reps)[0] for i in range(4)]
+        res_modes[mode] = (t_conv, t_chunk)
+    t_conv, t_chunk = res_modes[0]
     w1_ms = sum(t_conv[:3]) + sum(t_chunk[:3])
     w2_ms = t_conv[3] + t_chunk[3]
-    flops = sum(prefill_mfma_flops(cl[6], H) for cl in calls)
+    flops = sum(prefill_mfma_flops(cl[6], H, 0) for cl in calls)
     chunk_ms = sum(t_chunk)
     tf = flops / (chunk_ms * 1e-3) / 1e12
     conv_bytes = sum(2 * cl[0].numel() * 2 for cl in calls)  # x read + y written, bf16
     conv_gbs = conv_bytes / (sum(t_conv) * 1e-3) / 1e9
+    x3_conv, x3_chunk = res_modes[1]
+    x3_w1 = sum(x3_conv[:3]) + sum(x3_chunk[:3])
+    x3_w2 = x3_conv[3] + x3_chunk[3]
+    x3_flops = sum(prefill_mfma_flops(cl[6], H, 1) for cl in calls)
+    x3_tf = x3_flops / (sum(x3_chunk) * 1e-3) / 1e12
     T_all = 13600 + 8 * 4096
     res = {
         "tokens_per_s": T_all / ((w1_ms + w2_ms) * 1e-3),
@@ -347,6 +354,17 @@ def prefill_bench(dev, reps=5):
                              "the 13,600-token sequence bounds W1"},
         "conv_roofline": {"bound": "hbm", "achieved": conv_gbs, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS},
+        "bf16x3_mode": {
+            "tokens_per_s": T_all / ((x3_w1 + x3_w2) * 1e-3),
+            "w1_13600_tokens_per_s": 13600 / (x3_w1 * 1e-3),
+            "w2_8x4096_tokens_per_s": 8 * 4096 / (x3_w2 * 1e-3),
+            "chunked_calls_ms": x3_chunk,
+            "roofline": {"bound": "mfma", "achieved": x3_tf, "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": x3_tf / MFMA_BF16_PEAK_TFS,
+                         "issued_mfma_flops": x3_flops},
+        },
+        "timing": "each call replayed from a captured HIP graph; W1 = its three conv and "
+                  "three chunked calls",
     }
     del x1, x2, g1, g2, b1, b2, ws, ys, outs, calls
     torch.cuda.empty_cache()

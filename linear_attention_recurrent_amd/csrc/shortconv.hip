@@ -9,7 +9,8 @@
 // All kernels are streaming passes with the channel index contiguous across
 // lanes, so every access is coalesced.  The prefill output kernel moves
 // 16 bytes of channels per lane and slides the 4-token window along a run of
-// tokens, so each input row is read once (plus three rows at a run's start).
+// tokens, so each input row is read once (plus three rows at a run's start);
+// the hand-off kernel writes each sequence's first three outputs.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -120,9 +121,14 @@ __global__ void __launch_bounds__(256) shortconv_prefill_out_kernel(ConvPrefillA
 
 // Vector path (C a multiple of 8): lane = 16 bytes of channels, thread = a
 // run of kConvTok tokens.  grid (ceil(C / (256 V)), ceil(T / kConvTok)),
-// block 256.  Same arithmetic, in the same order, as the scalar kernel.
+// block 256.  Only tokens whose whole window lies inside their own sequence
+// (t - 3 >= the sequence's first token) are computed here, from input rows
+// loaded up front; the first three tokens of every sequence need the slot
+// history and are written by the hand-off kernel.  No load is issued inside
+// the token loop, so stores never wait on loads.  Same arithmetic, in the
+// same order, as the scalar kernel.
 constexpr int kConvTok = 16;
-template <typename IOT, typename CT>
+template <typename IOT>
 __global__ void __launch_bounds__(256) shortconv_prefill_vec_kernel(ConvPrefillArgs a)
 {
     constexpr int V = Stor<IOT>::kPer16B;  // channels per lane
@@ -133,70 +139,79 @@ __global__ void __launch_bounds__(256) shortconv_prefill_vec_kernel(ConvPrefillA
     const IOT *x = static_cast<const IOT *>(a.x);
     IOT *y = static_cast<IOT *>(a.y);
 
-    uint4 raw[kConvTok];  // the run's inputs, issued back to back (clamped rows)
-#pragma unroll
-    for (int i = 0; i < kConvTok; ++i)
-        raw[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)min(t0 + i, a.T - 1) * a.C + c0);
+    // The run's first sequence and its bounds, and the weights, before the
+    // row loads (so waiting for them does not wait for the rows).  A missing
+    // bias reads the weights instead and is scaled by 0: no branch around a load.
+    int n = find_seq(a.cu, a.N, t0);
+    int s0 = a.cu[n], e0 = a.cu[n + 1];
+    bool ok0 = seq_slots_ok(a, n);
+    const float bias_on = a.bias ? 1.f : 0.f;
+    const float *bsrc = a.bias ? a.bias : a.w;
     float4 wc[V];
     float bs[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         wc[e] = reinterpret_cast<const float4 *>(a.w)[c0 + e];
-        bs[e] = a.bias ? a.bias[c0 + e] : 0.f;
+        bs[e] = bsrc[c0 + e];
     }
-
-    int n = find_seq(a.cu, a.N, t0);
-    bool ok = seq_slots_ok(a, n);
-    float h[3][V];
-    // The three inputs before token t of sequence n: earlier tokens of the
-    // sequence, else the slot_in history (zeros for slot_in < 0).
-    auto window = [&](int t) {
-        const int start = a.cu[n], si = a.slot_in[n];
+    // rows t0 - 3 .. t0 + kConvTok - 1 (clamped into [0, T)), issued back to back
+    uint4 raw[kConvTok + 3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            const int pos = t - 3 + r;
-            if (pos >= start) {
-                Stor<IOT>::unpack(*reinterpret_cast<const uint4 *>(x + (int64_t)pos * a.C + c0), h[r]);
-            } else if (ok && si >= 0) {
-                const int64_t hrow = (int64_t)si * a.conv_stride + (int64_t)(pos - start + 3) * a.C;
-#pragma unroll
-                for (int e = 0; e < V; ++e) h[r][e] = ld<CT>(a.conv_pool, hrow + c0 + e);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) h[r][e] = 0.f;
-            }
+    for (int i = 0; i < kConvTok + 3; ++i) {
+        const int t = min(max(t0 - 3 + i, 0), a.T - 1);
+        raw[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)t * a.C + c0);
+    }
+    // Token masks of the run: bit i set in `comp` = compute token t0 + i here
+    // (its window lies inside its sequence), in `zero` = its sequence is
+    // skipped (out-of-range slot), so its output is zero.
+    uint32_t comp = 0, zero = 0;
+    const int tend = t0 + nt;
+    auto mark = [&](int st, int en, bool ok) {
+        const int lo = max(st + (ok ? 3 : 0), t0), hi = min(en, tend);
+        if (lo < hi) {
+            const uint32_t bits = ((1u << (hi - lo)) - 1u) << (lo - t0);
+            if (ok) comp |= bits;
+            else zero |= bits;
         }
     };
-    window(t0);
-    int next = a.cu[n + 1];
+    mark(s0, e0, ok0);
+    while (e0 < tend) {  // further sequences starting inside the run (rare)
+        ++n;
+        s0 = a.cu[n];
+        e0 = a.cu[n + 1];
+        mark(s0, e0, seq_slots_ok(a, n));
+    }
+    float win[4][V];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) Stor<IOT>::unpack(raw[r], win[r + 1]);
 #pragma unroll
     for (int i = 0; i < kConvTok; ++i) {
-        if (i >= nt) break;
-        const int t = t0 + i;
-        if (t == next) {  // token t starts a later (non-empty) sequence
-            while (n + 1 < a.N && a.cu[n + 1] <= t) ++n;
-            next = a.cu[n + 1];
-            ok = seq_slots_ok(a, n);
-            window(t);
-        }
-        float xv[V], yv[V];
-        Stor<IOT>::unpack(raw[i], xv);
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int e = 0; e < V; ++e) win[r][e] = win[r + 1][e];
+        Stor<IOT>::unpack(raw[i + 3], win[3]);
+        // computed unconditionally (branch-free); the masks only gate the store
+        const bool c = (comp >> i) & 1u;
+        float yv[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            yv[e] = ok ? conv4(wc[e], bs[e], h[0][e], h[1][e], h[2][e], xv[e]) : 0.f;
-            h[0][e] = h[1][e];
-            h[1][e] = h[2][e];
-            h[2][e] = xv[e];
+            const float v = conv4(wc[e], bs[e] * bias_on, win[0][e], win[1][e], win[2][e], win[3][e]);
+            yv[e] = c ? v : 0.f;
         }
-        *reinterpret_cast<uint4 *>(y + (int64_t)t * a.C + c0) = Stor<IOT>::pack(yv);
+        if (c || ((zero >> i) & 1u))
+            *reinterpret_cast<uint4 *>(y + (int64_t)(t0 + i) * a.C + c0) = Stor<IOT>::pack(yv);
     }
 }
 
 // History hand-off.  grid (ceil(C / 256), N), block 256.  The last three
 // pre-conv inputs of sequence n (older history shifted in for sequences
 // shorter than three tokens) go to row slot_out[n]; each lane reads all it
-// needs before writing, so slot_in == slot_out is safe.
-__global__ void __launch_bounds__(256) shortconv_prefill_state_kernel(ConvPrefillArgs a)
+// needs before writing, so slot_in == slot_out is safe.  With `head_outputs`
+// (the vector path) it also writes the outputs of the sequence's first
+// min(3, len) tokens, whose windows reach into the slot_in history.
+__global__ void __launch_bounds__(256) shortconv_prefill_state_kernel(ConvPrefillArgs a,
+                                                                      int head_outputs)
 {
     const int c = blockIdx.x * 256 + threadIdx.x;
     const int n = blockIdx.y;
@@ -209,6 +224,26 @@ __global__ void __launch_bounds__(256) shortconv_prefill_state_kernel(ConvPrefil
         const char *cs = static_cast<const char *>(a.conv_pool) + (int64_t)si * a.conv_stride * csz;
 #pragma unroll
         for (int r = 0; r < 3; ++r) h[r] = load_elem(cs, (int64_t)r * a.C + c, a.conv_dtype);
+    }
+    if (head_outputs) {
+        const float4 wc = reinterpret_cast<const float4 *>(a.w)[c];
+        const float bias = a.bias ? a.bias[c] : 0.f;
+        float xin[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            xin[j] = j < len ? load_elem(a.x, (int64_t)(start + j) * a.C + c, a.io_dtype) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            if (j >= len) break;
+            float win[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int pos = j - 3 + r;  // position relative to the sequence start
+                win[r] = pos >= 0 ? xin[pos] : h[pos + 3];
+            }
+            store_elem(a.y, (int64_t)(start + j) * a.C + c, a.io_dtype,
+                       conv4(wc, bias, win[0], win[1], win[2], win[3]));
+        }
     }
     float nh[3];
 #pragma unroll
@@ -225,15 +260,14 @@ __global__ void __launch_bounds__(256) shortconv_prefill_state_kernel(ConvPrefil
 hipError_t launch_shortconv_prefill(const ConvPrefillArgs &a, hipStream_t stream)
 {
     const unsigned cb = (unsigned)((a.C + 255) / 256);
-    if (a.T > 0 && a.C % 8 == 0) {
+    const bool vec = a.C % 8 == 0;
+    if (a.T > 0 && vec) {
         const int V = a.io_dtype ? 8 : 4;
         dim3 g1((unsigned)((a.C / V + 255) / 256), (unsigned)((a.T + kConvTok - 1) / kConvTok));
-        switch ((a.io_dtype ? 2 : 0) | (a.conv_dtype ? 1 : 0)) {
-        case 0: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<float, float>), g1, dim3(256), 0, stream, a); break;
-        case 1: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<float, bf16_t>), g1, dim3(256), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<bf16_t, float>), g1, dim3(256), 0, stream, a); break;
-        default: hipLaunchKernelGGL((shortconv_prefill_vec_kernel<bf16_t, bf16_t>), g1, dim3(256), 0, stream, a); break;
-        }
+        if (a.io_dtype)
+            hipLaunchKernelGGL(shortconv_prefill_vec_kernel<bf16_t>, g1, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(shortconv_prefill_vec_kernel<float>, g1, dim3(256), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else if (a.T > 0) {
@@ -243,7 +277,7 @@ hipError_t launch_shortconv_prefill(const ConvPrefillArgs &a, hipStream_t stream
         if (e != hipSuccess) return e;
     }
     dim3 g2(cb, (unsigned)a.N);
-    hipLaunchKernelGGL(shortconv_prefill_state_kernel, g2, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(shortconv_prefill_state_kernel, g2, dim3(256), 0, stream, a, (int)vec);
     return hipGetLastError();
 }
 
