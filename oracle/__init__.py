@@ -56,6 +56,11 @@ def _load():
     lib.orc_shortconv_prefill.restype = None
     lib.orc_prefill.argtypes = [I, I, I, I, I, I, P, L, P, L, P, L, P, P, P, P, P, P, L, I, P, I, D, D]
     lib.orc_prefill.restype = I
+    lib.orc_verify.argtypes = [I, I, I, P, I, I, I, I, P, P, P, P, L, I, P, P, P, P, L, P, I, P,
+                               I, P, P, P, P, P, P, P, D, D]
+    lib.orc_verify.restype = I
+    lib.orc_commit.argtypes = [I, I, P, I, I, I, P, P, L, I, I, P, P, P, P, P, D]
+    lib.orc_commit.restype = I
     _lib = lib
     return lib
 
@@ -176,3 +181,82 @@ def prefill(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, *, kda=Tr
     if rc != 0:
         raise ValueError("oracle: H_v must be a positive multiple of H_qk")
     return out, pool
+
+
+# ------------------------------------------------------ speculative decode --
+
+def new_ring(num_rows, Hv, L, dk, dv, kda=True):
+    """An empty ReplaySSM ring (zeros): per pool row, per value head, L steps
+    of d [dv], k [dk], g [dk] (KDA) or [1] (GDN), rawv [dv], rawk [dk], and
+    beta [] (scalar)."""
+    return {"d": np.zeros((num_rows, Hv, L, dv)), "k": np.zeros((num_rows, Hv, L, dk)),
+            "g": np.zeros((num_rows, Hv, L, dk if kda else 1)),
+            "rawv": np.zeros((num_rows, Hv, L, dv)), "rawk": np.zeros((num_rows, Hv, L, dk)),
+            "beta": np.zeros((num_rows, Hv, L))}
+
+
+def verify(x, w, bias, conv_pool, g, beta, slots, n_tok, ssm_pool, ring, ring_base, *, Hqk,
+           Hv, dk, dv, kda=True, conv_dtype="fp32", io_dtype="fp32", eps=1e-6, scale=1.0):
+    """Speculative verify of up to D draft tokens per request (x [B, D, C];
+    n_tok[b] of them used) from the pool checkpoint; the pools are not
+    modified.  Returns (out [B, D, Hv, dv], windows [B, D, 3, C], new ring):
+    each step's output, the conv history after each step, and the ring with
+    every step's record written at (ring_base[b] + t) mod L."""
+    x, w, bias, g, beta = _f64(x), _f64(w), _f64(bias), _f64(g), _f64(beta)
+    conv = _f64(conv_pool) if conv_pool is not None else np.zeros((1, 3, 1))
+    pool = _f64(ssm_pool)
+    slots, n_tok, ring_base = _i32(slots), _i32(n_tok), _i32(ring_base)
+    B, D, C = x.shape
+    L = ring["d"].shape[2]
+    r = {k: _f64(v).copy() for k, v in ring.items()}
+    out = np.empty((B, D, Hv, dv))
+    windows = np.zeros((B, D, 3, C))
+    rc = _load().orc_verify(int(kda), B, D, _ptr(n_tok), Hqk, Hv, dk, dv, _ptr(x), _ptr(w),
+                            _ptr(bias), _ptr(conv), conv.shape[1] * conv.shape[2],
+                            _DTYPES[conv_dtype], _ptr(g), _ptr(beta), _ptr(slots), _ptr(pool),
+                            Hv * dv * dk, _ptr(out), _DTYPES[io_dtype], _ptr(windows), L,
+                            _ptr(ring_base), _ptr(r["d"]), _ptr(r["k"]), _ptr(r["g"]),
+                            _ptr(r["rawv"]), _ptr(r["rawk"]), _ptr(r["beta"]), eps, scale)
+    if rc != 0:
+        raise ValueError("oracle: H_v must be a positive multiple of H_qk")
+    return out, windows, r
+
+
+def commit(accepted, slots, ssm_pool, ring, ring_base, *, kda=True, state_dtype="fp32",
+           eps=1e-6):
+    """Exact commit: replay the first accepted[b] ring steps of each request
+    from its pool row and store the result back.  Returns the new pool."""
+    pool = _f64(ssm_pool).copy()
+    _, Hv, dv, dk = pool.shape
+    L = ring["rawv"].shape[2]
+    r = {k: _f64(v) for k, v in ring.items()}
+    accepted, slots, ring_base = _i32(accepted), _i32(slots), _i32(ring_base)
+    _load().orc_commit(int(kda), len(slots), _ptr(accepted), Hv, dk, dv, _ptr(slots), _ptr(pool),
+                       Hv * dv * dk, _DTYPES[state_dtype], L, _ptr(ring_base), _ptr(r["g"]),
+                       _ptr(r["rawv"]), _ptr(r["rawk"]), _ptr(r["beta"]), eps)
+    return pool
+
+
+def track_copy(conv_pool, ssm_pool, mask, src, dst):
+    """State tracking ([SGLang-pool] / [mamba-ish] track passage): for every
+    entry i with mask[i] (all when mask is None), pool rows dst[i] of both
+    pools become copies of rows src[i].  Returns the new (conv, ssm) pools."""
+    conv, ssm = np.array(conv_pool, copy=True), np.array(ssm_pool, copy=True)
+    for i in range(len(src)):
+        if mask is None or mask[i]:
+            conv[dst[i]] = conv_pool[src[i]]
+            ssm[dst[i]] = ssm_pool[src[i]]
+    return conv, ssm
+
+
+def conv_window_scatter(conv_pool, windows, mask, slots, step):
+    """Commit of the conv history after speculative verify ([mamba-ish]
+    "intermediate_conv_window" passage): for every entry b with mask[b] (all
+    when mask is None) and 0 <= step[b] < D, pool row slots[b] becomes
+    windows[b, step[b]].  Returns the new conv pool."""
+    conv = np.array(conv_pool, copy=True)
+    D = windows.shape[1]
+    for b in range(len(slots)):
+        if (mask is None or mask[b]) and 0 <= step[b] < D:
+            conv[slots[b]] = windows[b, step[b]]
+    return conv

@@ -24,7 +24,10 @@
  *                  for KDA, a scalar per head for GDN) and the ReplaySSM
  *                  exact-commit passage (k = rawk / sqrt(|rawk|^2 + eps),
  *                  alpha = exp(g), S <- S Diag(alpha), d = beta (v - S k),
- *                  S <- S + d k^T).
+ *                  S <- S + d k^T); the ReplaySSM verify/commit passages
+ *                  (per-step outputs from the checkpoint, a per-slot ring of
+ *                  step records, replay of the accepted prefix) and the
+ *                  "intermediate_conv_window" passage (per-step conv history).
  *   [deploy]       hotelren.com/news/5417338 section 2.1 (state [H, d_v, d_k]
  *                  accumulating v k^T; conv state keeps the last 3 q/k/v
  *                  projections).
@@ -132,10 +135,10 @@ static void l2norm(const double *in, double *out, int n, double eps)
 /* S [dv, dk] (row i = value channel i) is updated in place:
  *   S <- S Diag(alpha);  d = beta (v - S k);  S <- S + d k^T;  o = scale S q.
  * q, k are already normalised; alpha has dk entries. */
-static void delta_rule_token(double *S, int dk, int dv, const double *q,
-                             const double *k, const double *v,
-                             const double *alpha, double beta, double scale,
-                             double *o)
+static void delta_rule_token_d(double *S, int dk, int dv, const double *q,
+                               const double *k, const double *v,
+                               const double *alpha, double beta, double scale,
+                               double *o, double *dvec)
 {
     for (int i = 0; i < dv; ++i) {
         double *row = S + (int64_t)i * dk;
@@ -144,10 +147,20 @@ static void delta_rule_token(double *S, int dk, int dv, const double *q,
         for (int c = 0; c < dk; ++c) u += row[c] * k[c];
         double d = beta * (v[i] - u);
         for (int c = 0; c < dk; ++c) row[c] += d * k[c];
+        if (dvec) dvec[i] = d;
+        if (!o) continue;
         double p = 0.0;
         for (int c = 0; c < dk; ++c) p += row[c] * q[c];
         o[i] = scale * p;
     }
+}
+
+static void delta_rule_token(double *S, int dk, int dv, const double *q,
+                             const double *k, const double *v,
+                             const double *alpha, double beta, double scale,
+                             double *o)
+{
+    delta_rule_token_d(S, dk, dv, q, k, v, alpha, beta, scale, o, NULL);
 }
 
 /* Decode recurrence for one token per entry.
@@ -304,5 +317,146 @@ int orc_prefill(int kda, int N, int Hqk, int Hv, int dk, int dv,
         for (size_t i = 0; i < state_elems; ++i) dst[i] = orc_round(S[i], state_dtype);
     }
     free(S); free(qn); free(kn); free(alpha); free(o);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Speculative verify and exact commit ([mamba-ish] ReplaySSM         */
+/* passages: verify computes every draft step's output from the       */
+/* checkpoint without writing the state back and appends the step's   */
+/* record to a per-slot ring of depth L; the commit replays the       */
+/* accepted prefix from the checkpoint with k = rawk/sqrt(|rawk|^2 +  */
+/* eps), alpha = exp(g), S <- S Diag(alpha), d = beta (rawv - S k),   */
+/* S <- S + d k^T, and writes the result back).                       */
+/* ------------------------------------------------------------------ */
+
+/* Ring layout, per pool row (slot): [num_rows, Hv, L, n] for the vectors
+ * (d and rawv: n = dv; k and rawk: n = dk; g: n = dk for KDA, 1 for GDN) and
+ * [num_rows, Hv, L] for beta.  Draft step t of request b lives at position
+ * (ring_base[b] + t) mod L.  d, k, rawv, rawk are stored rounded to io_dtype;
+ * g and beta keep their fp32 input values. */
+static int64_t ring_at(int slot, int Hv, int L, int h, int pos, int n)
+{
+    return (((int64_t)slot * Hv + h) * L + pos) * n;
+}
+
+/* x [B, D, C] pre-conv inputs of up to D draft tokens per request (n_tok[b]
+ * of them used); g [B, D, Hv, dk] (KDA) or [B, D, Hv]; beta [B, D, Hv].
+ * For each request, from the conv history and state of pool row slots[b]
+ * (neither is modified): token by token, the short conv + SiLU (the output
+ * rounded to io_dtype, as a separate conv kernel would store it), the split
+ * into q | k | v, the L2 norms, and the gated delta rule with the state
+ * carried in fp64 across the tokens.  out [B, D, Hv, dv] gets each step's
+ * output (zeros past n_tok[b]); windows [B, D, 3, C] the conv history after
+ * each step (what the conv pool would hold had that step been the last
+ * accepted one).  w == NULL: x already holds the post-conv q|k|v and windows
+ * is not written. */
+int orc_verify(int kda, int B, int D, const int32_t *n_tok, int Hqk, int Hv, int dk, int dv,
+               const double *x, const double *w, const double *bias,
+               const double *conv_pool, int64_t conv_stride, int conv_dtype,
+               const double *g, const double *beta, const int32_t *slots,
+               const double *ssm_pool, int64_t ssm_stride,
+               double *out, int io_dtype, double *windows,
+               int L, const int32_t *ring_base, double *ring_d, double *ring_k,
+               double *ring_g, double *ring_rawv, double *ring_rawk, double *ring_beta,
+               double eps, double scale)
+{
+    if (Hqk <= 0 || Hv % Hqk != 0) return -1;
+    const int group = Hv / Hqk;
+    const int C = 2 * Hqk * dk + Hv * dv;
+    const size_t state_elems = (size_t)Hv * dv * dk;
+    double *S = malloc(sizeof(double) * state_elems);
+    double *hist = malloc(sizeof(double) * 3 * (size_t)C);
+    double *y = malloc(sizeof(double) * (size_t)C);
+    double *qn = malloc(sizeof(double) * dk), *kn = malloc(sizeof(double) * dk);
+    double *alpha = malloc(sizeof(double) * dk), *o = malloc(sizeof(double) * dv);
+    double *dd = malloc(sizeof(double) * dv);
+    for (int b = 0; b < B; ++b) {
+        const int slot = slots[b];
+        memcpy(S, ssm_pool + (int64_t)slot * ssm_stride, sizeof(double) * state_elems);
+        if (w) memcpy(hist, conv_pool + (int64_t)slot * conv_stride, sizeof(double) * 3 * C);
+        for (int t = 0; t < D; ++t) {
+            double *ob = out + ((int64_t)b * D + t) * Hv * dv;
+            if (t >= n_tok[b]) {
+                memset(ob, 0, sizeof(double) * (size_t)Hv * dv);
+                continue;
+            }
+            const double *xt = x + ((int64_t)b * D + t) * C;
+            if (w) {
+                for (int c = 0; c < C; ++c) {
+                    double win[4] = {hist[c], hist[C + c], hist[2 * C + c], xt[c]};
+                    double acc = bias ? bias[c] : 0.0;
+                    for (int i = 0; i < 4; ++i) acc += w[4 * c + i] * win[i];
+                    y[c] = orc_round(silu(acc), io_dtype);
+                    hist[c] = win[1];
+                    hist[C + c] = win[2];
+                    hist[2 * C + c] = orc_round(win[3], conv_dtype);
+                }
+                memcpy(windows + ((int64_t)b * D + t) * 3 * C, hist, sizeof(double) * 3 * C);
+            } else {
+                memcpy(y, xt, sizeof(double) * C);
+            }
+            const int pos = (ring_base[b] + t) & (L - 1);
+            for (int h = 0; h < Hv; ++h) {
+                const int kh = h / group;
+                const double *qr = y + kh * dk, *kr = y + Hqk * dk + kh * dk;
+                const double *vr = y + 2 * Hqk * dk + h * dv;
+                l2norm(qr, qn, dk, eps);
+                l2norm(kr, kn, dk, eps);
+                const double *gt = kda ? g + (((int64_t)b * D + t) * Hv + h) * dk
+                                       : g + ((int64_t)b * D + t) * Hv + h;
+                for (int c = 0; c < dk; ++c) alpha[c] = exp(kda ? gt[c] : gt[0]);
+                const double bt = beta[((int64_t)b * D + t) * Hv + h];
+                delta_rule_token_d(S + (int64_t)h * dv * dk, dk, dv, qn, kn, vr, alpha, bt, scale,
+                                   o, dd);
+                for (int i = 0; i < dv; ++i) ob[(int64_t)h * dv + i] = orc_round(o[i], io_dtype);
+                for (int i = 0; i < dv; ++i) {
+                    ring_d[ring_at(slot, Hv, L, h, pos, dv) + i] = orc_round(dd[i], io_dtype);
+                    ring_rawv[ring_at(slot, Hv, L, h, pos, dv) + i] = vr[i];
+                }
+                for (int c = 0; c < dk; ++c) {
+                    ring_k[ring_at(slot, Hv, L, h, pos, dk) + c] = orc_round(kn[c], io_dtype);
+                    ring_rawk[ring_at(slot, Hv, L, h, pos, dk) + c] = kr[c];
+                }
+                if (kda)
+                    for (int c = 0; c < dk; ++c) ring_g[ring_at(slot, Hv, L, h, pos, dk) + c] = gt[c];
+                else
+                    ring_g[ring_at(slot, Hv, L, h, pos, 1)] = gt[0];
+                ring_beta[ring_at(slot, Hv, L, h, pos, 1)] = bt;
+            }
+        }
+    }
+    free(S); free(hist); free(y); free(qn); free(kn); free(alpha); free(o); free(dd);
+    return 0;
+}
+
+/* Exact commit: for each request, the first accepted[b] ring steps (from
+ * position ring_base[b]) are replayed in fp64 from the state of pool row
+ * slots[b], which is then stored back rounded to state_dtype. */
+int orc_commit(int kda, int B, const int32_t *accepted, int Hv, int dk, int dv,
+               const int32_t *slots, double *ssm_pool, int64_t ssm_stride, int state_dtype,
+               int L, const int32_t *ring_base, const double *ring_g, const double *ring_rawv,
+               const double *ring_rawk, const double *ring_beta, double eps)
+{
+    const size_t state_elems = (size_t)Hv * dv * dk;
+    double *kn = malloc(sizeof(double) * dk), *alpha = malloc(sizeof(double) * dk);
+    for (int b = 0; b < B; ++b) {
+        const int slot = slots[b];
+        double *S = ssm_pool + (int64_t)slot * ssm_stride;
+        for (int t = 0; t < accepted[b]; ++t) {
+            const int pos = (ring_base[b] + t) & (L - 1);
+            for (int h = 0; h < Hv; ++h) {
+                l2norm(ring_rawk + ring_at(slot, Hv, L, h, pos, dk), kn, dk, eps);
+                for (int c = 0; c < dk; ++c)
+                    alpha[c] = exp(kda ? ring_g[ring_at(slot, Hv, L, h, pos, dk) + c]
+                                       : ring_g[ring_at(slot, Hv, L, h, pos, 1)]);
+                delta_rule_token_d(S + (int64_t)h * dv * dk, dk, dv, NULL, kn,
+                                   ring_rawv + ring_at(slot, Hv, L, h, pos, dv), alpha,
+                                   ring_beta[ring_at(slot, Hv, L, h, pos, 1)], 0.0, NULL, NULL);
+            }
+        }
+        for (size_t i = 0; i < state_elems; ++i) S[i] = orc_round(S[i], state_dtype);
+    }
+    free(kn); free(alpha);
     return 0;
 }
