@@ -189,6 +189,101 @@ int gdn_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const
  * (0 for invalid arguments). */
 size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode);
 
+/* ---- Speculative decode (multi-token verify with an exact commit) --------
+ * Sources: the ReplaySSM passages of xxmr.cn/news/181459 (verify computes
+ * every draft step's output from the checkpoint without writing the state
+ * back; a per-slot ring records each step; the commit replays the accepted
+ * prefix from the checkpoint), its "intermediate_conv_window" passage (the
+ * per-step conv history, scattered at the last accepted step) and its
+ * state-tracking passage (masked copy of conv + SSM rows to a tracking slot).
+ *
+ * The ring of step records, one per pool row (slot), value head and step
+ * position (L positions, L a power of two; the pages size it as the next
+ * power of two >= 2 x the draft tokens of a call).  Step t of request b of a
+ * verify call is stored at position (ring_base[b] + t) mod L.  Vectors are in
+ * the call's I/O dtype; gates are fp32.  All pointers are device pointers,
+ * owned by the caller; the struct itself is read on the host.
+ *   d     [num_rows, H_v, L, d_v]  beta (rawv - S' k): the step's corrected value
+ *   k     [num_rows, H_v, L, d_k]  the normalised key
+ *   rawv  [num_rows, H_v, L, d_v]  the value entering the delta rule
+ *   rawk  [num_rows, H_v, L, d_k]  the key before normalisation
+ *   g     [num_rows, H_v, L, d_k] (KDA) or [num_rows, H_v, L] (GDN), fp32
+ *   beta  [num_rows, H_v, L] fp32 */
+typedef struct la_ring {
+    int L;
+    void *d, *k, *rawv, *rawk;
+    float *g, *beta;
+} la_ring;
+
+/* KDA verify: for each request b, the first n_tok[b] (<= D) of its D draft
+ * tokens run from the conv history and state of pool row slots[b] -- neither
+ * pool is modified -- through the short conv + SiLU (output rounded to
+ * io_dtype, the dtype a separate conv kernel would store), the L2 norms and the
+ * gated delta rule, the state carried in fp32 across the tokens.
+ *   x [B, D, C] (io_dtype); conv_w [C, 4] or NULL (x is then post-conv and
+ *     conv_windows is not written); conv_b [C] or NULL.
+ *   g [B, D, H_v, d_k] fp32; beta [B, D, H_v] fp32; slots, n_tok [B] int32.
+ *   out [B, D, H_v, d_v] (io_dtype): each step's o = scale S_t q_t; zeros for
+ *     steps past n_tok[b] and for skipped entries (slot out of range).
+ *   conv_windows [B, D, 3, C] (conv_dtype): the conv history after each step
+ *     (what the conv pool would hold had that step been the last accepted).
+ *   ring / ring_base [B]: each step's record is written to the ring rows of
+ *     slots[b] (see la_ring); L >= D is required.
+ * Supported: d_k == d_v == 128; H_v a multiple of H_qk; fp32/bf16 dtypes. */
+int kda_verify(int B, int D, const int32_t *n_tok, int H_qk, int H_v, int d_k, int d_v,
+               const void *x, int io_dtype, const float *conv_w, const float *conv_b,
+               const void *conv_pool, int64_t conv_slot_stride, int conv_dtype, const float *g,
+               const float *beta, const int32_t *slots, int num_rows, const void *ssm_pool,
+               int64_t ssm_slot_stride, int state_dtype, void *out, void *conv_windows,
+               const la_ring *ring, const int32_t *ring_base, float eps, float scale,
+               void *stream);
+
+/* GDN verify: as kda_verify with g [B, D, H_v] (one log-decay per head). */
+int gdn_verify(int B, int D, const int32_t *n_tok, int H_qk, int H_v, int d_k, int d_v,
+               const void *x, int io_dtype, const float *conv_w, const float *conv_b,
+               const void *conv_pool, int64_t conv_slot_stride, int conv_dtype, const float *g,
+               const float *beta, const int32_t *slots, int num_rows, const void *ssm_pool,
+               int64_t ssm_slot_stride, int state_dtype, void *out, void *conv_windows,
+               const la_ring *ring, const int32_t *ring_base, float eps, float scale,
+               void *stream);
+
+/* Exact commit (KDA): for each request, the first accepted[b] (<= L) ring
+ * steps from position ring_base[b] are replayed from the state of pool row
+ * slots[b] with k = rawk / sqrt(|rawk|^2 + eps), alpha = exp(g),
+ * S <- S Diag(alpha), d = beta (rawv - S k), S <- S + d k^T (fp32), and the
+ * result is stored back (state_dtype).  accepted[b] = 0 leaves the row
+ * untouched.  io_dtype is the dtype of the ring's vectors.  The replay runs
+ * the same per-row arithmetic as verify, so committing a verify's first a
+ * steps gives the state verify held after step a. */
+int kda_commit(int B, const int32_t *accepted, int H_v, int d_k, int d_v, const int32_t *slots,
+               int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+               int io_dtype, const la_ring *ring, const int32_t *ring_base, float eps,
+               void *stream);
+
+/* Exact commit (GDN): as kda_commit with the ring's per-head g. */
+int gdn_commit(int B, const int32_t *accepted, int H_v, int d_k, int d_v, const int32_t *slots,
+               int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+               int io_dtype, const la_ring *ring, const int32_t *ring_base, float eps,
+               void *stream);
+
+/* Conv-state commit after verify: for every b with mask[b] != 0 (mask NULL =
+ * all) and 0 <= step[b] < D, conv pool row slots[b] becomes
+ * windows[b, step[b]] (windows [B, D, 3, C] in conv_dtype, as written by
+ * *_verify).  3 C elements must be a multiple of 16 bytes. */
+int conv_window_scatter(int B, int D, int C, const uint8_t *mask, const int32_t *slots,
+                        const int32_t *step, const void *windows, void *conv_pool,
+                        int64_t conv_slot_stride, int conv_dtype, int num_rows, void *stream);
+
+/* State tracking: for every b with mask[b] != 0 (mask NULL = all), pool rows
+ * dst[b] of the conv pool (conv_row_elems elements of conv_dtype) and of the
+ * SSM pool (ssm_row_elems elements of state_dtype) become bit copies of rows
+ * src[b].  Rows must be multiples of 16 bytes.  src == dst is a no-op; a dst
+ * that is another entry's src gives an undefined result. */
+int state_track_copy(int B, const uint8_t *mask, const int32_t *src, const int32_t *dst,
+                     void *conv_pool, int64_t conv_slot_stride, int64_t conv_row_elems,
+                     int conv_dtype, void *ssm_pool, int64_t ssm_slot_stride,
+                     int64_t ssm_row_elems, int state_dtype, int num_rows, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

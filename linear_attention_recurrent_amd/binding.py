@@ -33,6 +33,13 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+class LaRing(ctypes.Structure):
+    """``la_ring`` of include/la.h (device pointers of the ring arrays)."""
+    _fields_ = [("L", ctypes.c_int), ("d", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("rawv", ctypes.c_void_p), ("rawk", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p)]
+
+
 def load_library():
     """Load ``libla.so`` (built by ``linear_attention_recurrent_amd.build``)."""
     global _lib
@@ -56,6 +63,14 @@ def load_library():
         "gdn_prefill_chunked": ([I, I, I, I, I, I, P, L, P, L, P, L, I, P, P, P, P, P, I, P, L, I,
                                  P, F, F, I, P, Z, P], I),
         "prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "kda_verify": ([I, I, P, I, I, I, I, P, I, P, P, P, L, I, P, P, P, I, P, L, I, P, P,
+                        ctypes.POINTER(LaRing), P, F, F, P], I),
+        "gdn_verify": ([I, I, P, I, I, I, I, P, I, P, P, P, L, I, P, P, P, I, P, L, I, P, P,
+                        ctypes.POINTER(LaRing), P, F, F, P], I),
+        "kda_commit": ([I, P, I, I, I, P, I, P, L, I, I, ctypes.POINTER(LaRing), P, F, P], I),
+        "gdn_commit": ([I, P, I, I, I, P, I, P, L, I, I, ctypes.POINTER(LaRing), P, F, P], I),
+        "conv_window_scatter": ([I, I, I, P, P, P, P, P, L, I, I, P], I),
+        "state_track_copy": ([I, P, P, P, P, L, L, I, P, L, L, I, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -227,3 +242,114 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_poo
 def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw):
     """Chunked GDN prefill; as :func:`kda_prefill_chunked` with g [T, Hv]."""
     return _prefill(False, q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw)
+
+
+# ------------------------------------------------------ speculative decode --
+
+def new_ring(num_rows, Hv, L, dk, dv, *, kda=True, dtype=torch.bfloat16, device="cuda"):
+    """Allocates a zeroed ReplaySSM ring (dict of tensors) for a pool of
+    num_rows rows: d, rawv [rows, Hv, L, dv] and k, rawk [rows, Hv, L, dk] in
+    `dtype` (the I/O dtype of the verify calls), g [rows, Hv, L, dk] (KDA) or
+    [rows, Hv, L] (GDN) and beta [rows, Hv, L] in fp32."""
+    z = lambda *sh, dt=dtype: torch.zeros(sh, dtype=dt, device=device)  # noqa: E731
+    return {"d": z(num_rows, Hv, L, dv), "k": z(num_rows, Hv, L, dk),
+            "rawv": z(num_rows, Hv, L, dv), "rawk": z(num_rows, Hv, L, dk),
+            "g": z(*((num_rows, Hv, L, dk) if kda else (num_rows, Hv, L)), dt=torch.float32),
+            "beta": z(num_rows, Hv, L, dt=torch.float32)}
+
+
+def _ring_struct(ring):
+    for k in ("d", "k", "rawv", "rawk", "g", "beta"):
+        _contig(ring[k], f"ring[{k!r}]")
+    return LaRing(ring["d"].shape[2], ring["d"].data_ptr(), ring["k"].data_ptr(),
+                  ring["rawv"].data_ptr(), ring["rawk"].data_ptr(), ring["g"].data_ptr(),
+                  ring["beta"].data_ptr())
+
+
+def _verify(kda, x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, *, Hqk, conv_w=None,
+            conv_b=None, conv_pool=None, out=None, windows=None, eps=1e-6, scale=1.0):
+    B, D, C = x.shape
+    _contig(x, "x")
+    rows, Hv, dv, dk = ssm_pool.shape
+    if C != 2 * Hqk * dk + Hv * dv:
+        raise ValueError(f"x has {C} channels, expected 2*Hqk*dk + Hv*dv")
+    sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    cstride, cdt = 0, LA_F32
+    if conv_w is not None:
+        cstride = _row_view(conv_pool, (3, C), "conv_pool")
+        cdt = _dtype(conv_pool)
+        if windows is None:
+            windows = torch.empty((B, D, 3, C), dtype=conv_pool.dtype, device=x.device)
+    out = torch.empty((B, D, Hv, dv), dtype=x.dtype, device=x.device) if out is None else out
+    r = _ring_struct(ring)
+    fn = load_library().kda_verify if kda else load_library().gdn_verify
+    _check(fn(B, D, _ptr(_contig(n_tok, "n_tok")), Hqk, Hv, dk, dv, _ptr(x), _dtype(x),
+              _ptr(conv_w), _ptr(conv_b), _ptr(conv_pool), cstride, cdt, _ptr(_contig(g, "g")),
+              _ptr(_contig(beta, "beta")), _ptr(_contig(slots, "slots")), rows, _ptr(ssm_pool),
+              sstride, _dtype(ssm_pool), _ptr(_contig(out, "out")), _ptr(windows),
+              ctypes.byref(r), _ptr(_contig(ring_base, "ring_base")), eps, scale,
+              _stream(x.device)))
+    return out, windows
+
+
+def kda_verify(x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, **kw):
+    """KDA speculative verify of D draft tokens per request.  x [B, D, C];
+    g [B, D, Hv, dk]; beta [B, D, Hv]; slots, n_tok, ring_base [B] int32;
+    ring from :func:`new_ring`.  The pools are not modified.  Returns
+    (out [B, D, Hv, dv], conv windows [B, D, 3, C] or None)."""
+    return _verify(True, x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, **kw)
+
+
+def gdn_verify(x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, **kw):
+    """GDN verify; as :func:`kda_verify` with g [B, D, Hv]."""
+    return _verify(False, x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, **kw)
+
+
+def _commit(kda, accepted, slots, ssm_pool, ring, ring_base, eps=1e-6):
+    rows, Hv, dv, dk = ssm_pool.shape
+    sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    r = _ring_struct(ring)
+    fn = load_library().kda_commit if kda else load_library().gdn_commit
+    _check(fn(slots.shape[0], _ptr(_contig(accepted, "accepted")), Hv, dk, dv,
+              _ptr(_contig(slots, "slots")), rows, _ptr(ssm_pool), sstride, _dtype(ssm_pool),
+              _dtype(ring["d"]), ctypes.byref(r), _ptr(_contig(ring_base, "ring_base")), eps,
+              _stream(ssm_pool.device)))
+
+
+def kda_commit(accepted, slots, ssm_pool, ring, ring_base, eps=1e-6):
+    """Exact commit: replays the first accepted[b] ring steps of each request
+    from its pool row, in place."""
+    _commit(True, accepted, slots, ssm_pool, ring, ring_base, eps)
+
+
+def gdn_commit(accepted, slots, ssm_pool, ring, ring_base, eps=1e-6):
+    """GDN exact commit; as :func:`kda_commit`."""
+    _commit(False, accepted, slots, ssm_pool, ring, ring_base, eps)
+
+
+def conv_window_scatter(windows, slots, step, conv_pool, mask=None):
+    """conv_pool[slots[b]] = windows[b, step[b]] where mask[b] (uint8 or bool;
+    None = all) and 0 <= step[b] < D."""
+    B, D, three, C = windows.shape
+    stride = _row_view(conv_pool, (3, C), "conv_pool")
+    if mask is not None:
+        mask = _contig(mask.to(torch.uint8), "mask")
+    _check(load_library().conv_window_scatter(
+        B, D, C, _ptr(mask), _ptr(_contig(slots, "slots")), _ptr(_contig(step, "step")),
+        _ptr(_contig(windows, "windows")), _ptr(conv_pool), stride, _dtype(conv_pool),
+        conv_pool.shape[0], _stream(conv_pool.device)))
+
+
+def state_track_copy(src, dst, conv_pool, ssm_pool, mask=None):
+    """Rows dst[b] of both pools become copies of rows src[b] where mask[b]."""
+    crow = conv_pool[0].numel()
+    srow = ssm_pool[0].numel()
+    if not conv_pool[0].is_contiguous() or not ssm_pool[0].is_contiguous():
+        raise ValueError("pool rows must be contiguous")
+    if mask is not None:
+        mask = _contig(mask.to(torch.uint8), "mask")
+    _check(load_library().state_track_copy(
+        src.shape[0], _ptr(mask), _ptr(_contig(src, "src")), _ptr(_contig(dst, "dst")),
+        _ptr(conv_pool), conv_pool.stride(0), crow, _dtype(conv_pool), _ptr(ssm_pool),
+        ssm_pool.stride(0), srow, _dtype(ssm_pool), ssm_pool.shape[0],
+        _stream(ssm_pool.device)))

@@ -200,6 +200,113 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
     return hip_status(la::launch_prefill(a, st), fn);
 }
 
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_ring(const la_ring *r, int D, const char *fn)
+{
+    if (!r || !r->d || !r->k || !r->rawv || !r->rawk || !r->g || !r->beta)
+        return fail(LA_ERR_ARG, "%s: ring and all of its arrays must be given", fn);
+    if (!pow2(r->L) || r->L < D)
+        return fail(LA_ERR_ARG, "%s: ring depth L = %d must be a power of two >= %d", fn, r->L, D);
+    const void *ptrs[] = {r->d, r->k, r->rawv, r->rawk, r->g, r->beta};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(LA_ERR_ARG, "%s: ring arrays must be 16-byte aligned", fn);
+    return LA_OK;
+}
+
+la::RingArgs ring_args(const la_ring *r)
+{
+    la::RingArgs g{};
+    g.L = r->L; g.d = r->d; g.k = r->k; g.rawv = r->rawv; g.rawk = r->rawk;
+    g.g = r->g; g.beta = r->beta;
+    return g;
+}
+
+int verify_common(bool kda, int B, int D, const int32_t *n_tok, int Hqk, int Hv, int dk, int dv,
+                  const void *x, int io_dtype, const float *conv_w, const float *conv_b,
+                  const void *conv_pool, int64_t conv_slot_stride, int conv_dtype,
+                  const float *g, const float *beta, const int32_t *slots, int num_rows,
+                  const void *ssm_pool, int64_t ssm_slot_stride, int state_dtype, void *out,
+                  void *conv_windows, const la_ring *ring, const int32_t *ring_base, float eps,
+                  float scale, void *stream)
+{
+    const char *fn = kda ? "kda_verify" : "gdn_verify";
+    if (B < 0 || D <= 0 || Hqk <= 0 || Hv <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be positive (B >= 0)", fn);
+    if (Hv % Hqk != 0)
+        return fail(LA_ERR_ARG, "%s: H_v = %d is not a multiple of H_qk = %d", fn, Hv, Hqk);
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype) || !valid_dtype(conv_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    if (dk != 128 || dv != 128)
+        return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);
+    if (B == 0) return ok();
+    if (int rc = check_ring(ring, D, fn)) return rc;
+    if (!x || !g || !beta || !slots || !n_tok || !ssm_pool || !out || !ring_base ||
+        (conv_w && (!conv_pool || !conv_windows)))
+        return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+    const void *ptrs[] = {x, g, beta, slots, n_tok, ssm_pool, out, ring_base, conv_w, conv_b,
+                          conv_pool, conv_windows};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    const int C = 2 * Hqk * dk + Hv * dv;
+    if (ssm_slot_stride < (int64_t)Hv * dv * dk || (ssm_slot_stride * dsize(state_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: ssm_slot_stride %lld too small or misaligned", fn,
+                    (long long)ssm_slot_stride);
+    if (conv_w && (conv_slot_stride < 3LL * C || (conv_slot_stride * dsize(conv_dtype)) % 16))
+        return fail(LA_ERR_ARG, "%s: conv_slot_stride %lld too small or misaligned", fn,
+                    (long long)conv_slot_stride);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(slots, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "slots")) return rc;
+    }
+    la::VerifyArgs a{};
+    a.B = B; a.D = D; a.Hqk = Hqk; a.Hv = Hv; a.G = Hv / Hqk; a.C = C; a.n_tok = n_tok;
+    a.x = x; a.io_dtype = io_dtype; a.w = conv_w; a.bias = conv_b;
+    a.conv_pool = conv_pool; a.conv_stride = conv_slot_stride; a.conv_dtype = conv_dtype;
+    a.g = g; a.beta = beta; a.slots = slots; a.num_rows = num_rows;
+    a.ssm_pool = ssm_pool; a.ssm_stride = ssm_slot_stride; a.out = out; a.windows = conv_windows;
+    a.ring = ring_args(ring); a.ring_base = ring_base; a.eps = eps; a.scale = scale;
+    return hip_status(la::launch_verify(a, state_dtype, kda, st), fn);
+}
+
+int commit_common(bool kda, int B, const int32_t *accepted, int Hv, int dk, int dv,
+                  const int32_t *slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                  int state_dtype, int io_dtype, const la_ring *ring, const int32_t *ring_base,
+                  float eps, void *stream)
+{
+    const char *fn = kda ? "kda_commit" : "gdn_commit";
+    if (B < 0 || Hv <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be positive (B >= 0)", fn);
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    if (dk != 128 || dv != 128)
+        return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);
+    if (B == 0) return ok();
+    if (int rc = check_ring(ring, 1, fn)) return rc;
+    if (!accepted || !slots || !ssm_pool || !ring_base)
+        return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+    const void *ptrs[] = {accepted, slots, ssm_pool, ring_base};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (ssm_slot_stride < (int64_t)Hv * dv * dk || (ssm_slot_stride * dsize(state_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: ssm_slot_stride %lld too small or misaligned", fn,
+                    (long long)ssm_slot_stride);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(slots, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "slots")) return rc;
+    }
+    la::CommitArgs a{};
+    a.B = B; a.Hv = Hv; a.accepted = accepted; a.slots = slots; a.num_rows = num_rows;
+    a.ssm_pool = ssm_pool; a.ssm_stride = ssm_slot_stride; a.io_dtype = io_dtype;
+    a.ring = ring_args(ring); a.ring_base = ring_base; a.eps = eps;
+    return hip_status(la::launch_commit(a, state_dtype, kda, st), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,4 +452,121 @@ size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v
     return la::prefill_ws_bytes(N, T, H_qk, H_v, d_k, mode);
 }
 
+
+int kda_verify(int B, int D, const int32_t *n_tok, int H_qk, int H_v, int d_k, int d_v,
+               const void *x, int io_dtype, const float *conv_w, const float *conv_b,
+               const void *conv_pool, int64_t conv_slot_stride, int conv_dtype, const float *g,
+               const float *beta, const int32_t *slots, int num_rows, const void *ssm_pool,
+               int64_t ssm_slot_stride, int state_dtype, void *out, void *conv_windows,
+               const la_ring *ring, const int32_t *ring_base, float eps, float scale,
+               void *stream)
+{
+    return verify_common(true, B, D, n_tok, H_qk, H_v, d_k, d_v, x, io_dtype, conv_w, conv_b,
+                         conv_pool, conv_slot_stride, conv_dtype, g, beta, slots, num_rows,
+                         ssm_pool, ssm_slot_stride, state_dtype, out, conv_windows, ring,
+                         ring_base, eps, scale, stream);
+}
+
+int gdn_verify(int B, int D, const int32_t *n_tok, int H_qk, int H_v, int d_k, int d_v,
+               const void *x, int io_dtype, const float *conv_w, const float *conv_b,
+               const void *conv_pool, int64_t conv_slot_stride, int conv_dtype, const float *g,
+               const float *beta, const int32_t *slots, int num_rows, const void *ssm_pool,
+               int64_t ssm_slot_stride, int state_dtype, void *out, void *conv_windows,
+               const la_ring *ring, const int32_t *ring_base, float eps, float scale,
+               void *stream)
+{
+    return verify_common(false, B, D, n_tok, H_qk, H_v, d_k, d_v, x, io_dtype, conv_w, conv_b,
+                         conv_pool, conv_slot_stride, conv_dtype, g, beta, slots, num_rows,
+                         ssm_pool, ssm_slot_stride, state_dtype, out, conv_windows, ring,
+                         ring_base, eps, scale, stream);
+}
+
+int kda_commit(int B, const int32_t *accepted, int H_v, int d_k, int d_v, const int32_t *slots,
+               int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+               int io_dtype, const la_ring *ring, const int32_t *ring_base, float eps,
+               void *stream)
+{
+    return commit_common(true, B, accepted, H_v, d_k, d_v, slots, num_rows, ssm_pool,
+                         ssm_slot_stride, state_dtype, io_dtype, ring, ring_base, eps, stream);
+}
+
+int gdn_commit(int B, const int32_t *accepted, int H_v, int d_k, int d_v, const int32_t *slots,
+               int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+               int io_dtype, const la_ring *ring, const int32_t *ring_base, float eps,
+               void *stream)
+{
+    return commit_common(false, B, accepted, H_v, d_k, d_v, slots, num_rows, ssm_pool,
+                         ssm_slot_stride, state_dtype, io_dtype, ring, ring_base, eps, stream);
+}
+
+int conv_window_scatter(int B, int D, int C, const uint8_t *mask, const int32_t *slots,
+                        const int32_t *step, const void *windows, void *conv_pool,
+                        int64_t conv_slot_stride, int conv_dtype, int num_rows, void *stream)
+{
+    const char *fn = "conv_window_scatter";
+    if (B < 0 || D <= 0 || C <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be positive (B >= 0)", fn);
+    if (!valid_dtype(conv_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    if ((3LL * C * dsize(conv_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: a window (3 C elements) must be a multiple of 16 bytes", fn);
+    if (B == 0) return ok();
+    if (!slots || !step || !windows || !conv_pool)
+        return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+    const void *ptrs[] = {slots, step, windows, conv_pool};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (conv_slot_stride < 3LL * C || (conv_slot_stride * dsize(conv_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: conv_slot_stride %lld too small or misaligned", fn,
+                    (long long)conv_slot_stride);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(slots, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "slots")) return rc;
+    }
+    la::ScatterArgs a{};
+    a.B = B; a.D = D; a.C = C; a.mask = mask; a.slots = slots; a.step = step; a.windows = windows;
+    a.conv_pool = conv_pool; a.conv_stride = conv_slot_stride; a.conv_dtype = conv_dtype;
+    a.num_rows = num_rows;
+    return hip_status(la::launch_conv_scatter(a, st), fn);
+}
+
+int state_track_copy(int B, const uint8_t *mask, const int32_t *src, const int32_t *dst,
+                     void *conv_pool, int64_t conv_slot_stride, int64_t conv_row_elems,
+                     int conv_dtype, void *ssm_pool, int64_t ssm_slot_stride,
+                     int64_t ssm_row_elems, int state_dtype, int num_rows, void *stream)
+{
+    const char *fn = "state_track_copy";
+    if (B < 0 || num_rows <= 0 || conv_row_elems < 0 || ssm_row_elems < 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be non-negative", fn);
+    if (!valid_dtype(conv_dtype) || !valid_dtype(state_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    const int64_t crow = conv_row_elems * dsize(conv_dtype), srow = ssm_row_elems * dsize(state_dtype);
+    if (crow % 16 || srow % 16)
+        return fail(LA_ERR_ARG, "%s: rows must be multiples of 16 bytes", fn);
+    if (B == 0) return ok();
+    if (!src || !dst || (crow && !conv_pool) || (srow && !ssm_pool))
+        return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+    const void *ptrs[] = {src, dst, conv_pool, ssm_pool};  // mask: bytes, any alignment
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if ((crow && (conv_slot_stride < conv_row_elems || (conv_slot_stride * dsize(conv_dtype)) % 16)) ||
+        (srow && (ssm_slot_stride < ssm_row_elems || (ssm_slot_stride * dsize(state_dtype)) % 16)))
+        return fail(LA_ERR_ARG, "%s: slot strides must cover a row and be multiples of 16 bytes",
+                    fn);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(dst, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "dst")) return rc;
+    }
+    la::TrackArgs a{};
+    a.B = B; a.mask = mask; a.src = src; a.dst = dst;
+    a.conv_pool = static_cast<char *>(conv_pool); a.ssm_pool = static_cast<char *>(ssm_pool);
+    a.conv_stride_b = conv_slot_stride * dsize(conv_dtype); a.conv_row_b = crow;
+    a.ssm_stride_b = ssm_slot_stride * dsize(state_dtype); a.ssm_row_b = srow;
+    a.num_rows = num_rows;
+    return hip_status(la::launch_track_copy(a, st), fn);
+}
 }  // extern "C"

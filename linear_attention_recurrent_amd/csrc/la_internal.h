@@ -77,4 +77,70 @@ struct PrefillArgs {
 size_t prefill_ws_bytes(int N, int T, int Hqk, int Hv, int D, int mode);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+
+// ---- speculative decode: verify, exact commit, conv-window scatter, state
+//      tracking copy ----
+struct RingArgs {
+    int L;                          // ring depth, a power of two
+    void *d, *k, *rawv, *rawk;      // [num_rows, Hv, L, 128] io dtype
+    float *g, *beta;                // [num_rows, Hv, L, 128 (KDA) or 1], [num_rows, Hv, L]
+};
+
+struct VerifyArgs {
+    int B, D, Hqk, Hv, G, C;        // D = draft tokens per request (max)
+    const int32_t *n_tok;           // [B] tokens used per request
+    const void *x;                  // [B, D, C] io dtype
+    int io_dtype;
+    const float *w, *bias;          // conv weights or nullptr (x is post-conv)
+    const void *conv_pool;
+    int64_t conv_stride;
+    int conv_dtype;
+    const float *g, *beta;          // [B, D, Hv, 128] / [B, D, Hv]; [B, D, Hv]
+    const int32_t *slots;
+    int num_rows;
+    const void *ssm_pool;
+    int64_t ssm_stride;
+    void *out;                      // [B, D, Hv, 128] io dtype
+    void *windows;                  // [B, D, 3, C] conv dtype
+    RingArgs ring;
+    const int32_t *ring_base;       // [B]
+    float eps, scale;
+};
+hipError_t launch_verify(const VerifyArgs &a, int state_dtype, bool kda, hipStream_t stream);
+
+struct CommitArgs {
+    int B, Hv;
+    const int32_t *accepted, *slots;
+    int num_rows;
+    void *ssm_pool;
+    int64_t ssm_stride;
+    int io_dtype;                   // dtype of the ring's vectors
+    RingArgs ring;
+    const int32_t *ring_base;
+    float eps;
+};
+hipError_t launch_commit(const CommitArgs &a, int state_dtype, bool kda, hipStream_t stream);
+
+struct ScatterArgs {
+    int B, D, C;
+    const uint8_t *mask;            // [B] or nullptr
+    const int32_t *slots, *step;    // [B]
+    const void *windows;            // [B, D, 3, C] conv dtype
+    void *conv_pool;
+    int64_t conv_stride;
+    int conv_dtype;
+    int num_rows;
+};
+hipError_t launch_conv_scatter(const ScatterArgs &a, hipStream_t stream);
+
+struct TrackArgs {
+    int B;
+    const uint8_t *mask;            // [B] or nullptr
+    const int32_t *src, *dst;       // [B]
+    char *conv_pool, *ssm_pool;     // byte views
+    int64_t conv_stride_b, conv_row_b, ssm_stride_b, ssm_row_b;  // bytes
+    int num_rows;
+};
+hipError_t launch_track_copy(const TrackArgs &a, hipStream_t stream);
+
 }  // namespace la

@@ -1,0 +1,389 @@
+// spec.hip -- speculative decode on the recurrent state: multi-token verify,
+// exact commit, the conv-window scatter and the state-tracking copy.
+//
+// What they compute (the ReplaySSM passages of xxmr.cn/news/181459):
+//   verify  -- up to D draft tokens per request run through the short conv
+//              and the gated delta rule from the pool checkpoint; every step's
+//              output is produced, the state is carried across the tokens and
+//              never written back, and each step's record (d, k, g, rawv,
+//              rawk, beta) is appended to a per-slot ring of depth L, together
+//              with the conv history after each step (the per-step conv
+//              window of that page's "intermediate_conv_window" passage);
+//   commit  -- the accepted prefix is replayed from the checkpoint with
+//              k = rawk / sqrt(|rawk|^2 + eps), alpha = exp(g),
+//              S <- S Diag(alpha), d = beta (rawv - S k), S <- S + d k^T,
+//              and the result is stored back;
+//   scatter -- the conv history of the last accepted step is written to the
+//              persistent conv state, under a mask;
+//   track   -- the conv and SSM rows of an active slot are copied to a
+//              tracking slot, under a mask (that page's state-tracking
+//              passage).
+// The conv output is rounded to the I/O dtype before the recurrence, as a
+// separate conv kernel's output tensor would be, so the ring holds exactly the
+// values verify used and the commit reproduces verify's arithmetic: both
+// kernels run the same per-row update code.
+//
+// Work decomposition of verify and commit: one workgroup per (request, value
+// head), the head's state rows spread over the waves as in the decode kernel
+// (16-byte lane chunks, LPR lanes per row), held in fp32 registers across the
+// steps.  Verify computes the head's q|k|v conv outputs per step into a
+// double-buffered LDS area (one barrier per step); the commit needs no
+// barrier at all.
+#include "decode_kernel.h"
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+namespace {
+
+constexpr int HD = 128;  // head dim of the speculative kernels (d_k = d_v)
+
+template <typename T> __device__ __forceinline__ float round_to(float v);
+template <> __device__ __forceinline__ float round_to<float>(float v) { return v; }
+template <> __device__ __forceinline__ float round_to<bf16_t>(float v)
+{
+    return bf16_to_f32(f32_to_bf16(v));
+}
+
+__device__ __forceinline__ int64_t ring_at(int slot, int Hv, int L, int h, int pos, int n)
+{
+    return (((int64_t)slot * Hv + h) * L + pos) * n;
+}
+
+// The shared per-row step:  s <- s Diag(al);  u = s . kk;  d = beta (v - u);
+// s <- s + d kk.  Returns d (identical in every lane of the row's group).
+template <int EPL, int LPR>
+__device__ __forceinline__ float row_step(float (&s)[EPL], const float (&al)[EPL],
+                                          const float (&kk)[EPL], float v, float beta)
+{
+    float u = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        s[e] *= al[e];
+        u = fmaf(s[e], kk[e], u);
+    }
+    u = group_sum<LPR>(u);
+    const float d = beta * (v - u);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s[e] = fmaf(d, kk[e], s[e]);
+    return d;
+}
+
+// 1 / sqrt(|x|^2 + eps) of a 128-vector held as lane, lane + 64 (wave-wide).
+__device__ __forceinline__ float inv_norm128(float x0, float x1, float eps)
+{
+    return 1.0f / sqrtf(wave_sum(fmaf(x1, x1, x0 * x0)) + eps);
+}
+
+// ---------------------------------------------------------------------------
+// verify
+// ---------------------------------------------------------------------------
+template <typename ST, typename IOT, typename CT, bool KDA, bool CONV>
+__global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyArgs a)
+{
+    using Cfg = DecodeCfg<HD, ST>;
+    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
+    constexpr int NCH = 3 * HD;                // the head's q, k, v channels
+    constexpr int CPT = (NCH + NT - 1) / NT;   // channels per thread
+    __shared__ float ybuf[2][NCH];             // conv outputs per step parity (I/O-dtype values)
+
+    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv, kh = h / a.G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = a.slots[b];
+    const int n = min(max(a.n_tok[b], 0), a.D);
+    auto out_at = [&](int t, int i) { return (((int64_t)b * a.D + t) * a.Hv + h) * HD + i; };
+    const int first_zero = (slot < 0 || slot >= a.num_rows) ? 0 : n;
+    for (int i = tid + first_zero * HD; i < a.D * HD; i += NT)  // steps past n (or a skipped entry)
+        st<IOT>(a.out, out_at(i / HD, i % HD), 0.f);
+    if (first_zero == 0) return;
+
+    // The channels this thread owns (local index j = tid + NT m over [q | k | v]
+    // of this head) and their conv history, carried across the steps.
+    int gch[CPT];
+    bool own[CPT], win_out[CPT];
+    float h0[CPT], h1[CPT], h2[CPT], bias[CPT];
+    float4 wc[CPT];
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+        const int j = tid + NT * m, jj = min(j, NCH - 1);
+        own[m] = j < NCH;
+        gch[m] = jj < HD ? kh * HD + jj
+               : jj < 2 * HD ? a.Hqk * HD + kh * HD + (jj - HD)
+                             : 2 * a.Hqk * HD + h * HD + (jj - 2 * HD);
+        // q/k windows are written by the first value head of the group only
+        win_out[m] = own[m] && (jj >= 2 * HD || h % a.G == 0);
+        if constexpr (CONV) {
+            const int64_t row = (int64_t)slot * a.conv_stride;
+            h0[m] = ld<CT>(a.conv_pool, row + gch[m]);
+            h1[m] = ld<CT>(a.conv_pool, row + a.C + gch[m]);
+            h2[m] = ld<CT>(a.conv_pool, row + 2 * a.C + gch[m]);
+            wc[m] = reinterpret_cast<const float4 *>(a.w)[gch[m]];
+            bias[m] = a.bias ? a.bias[gch[m]] : 0.f;
+        }
+    }
+
+    // The head's state rows, unpacked to fp32 registers for the whole call.
+    const ST *S = static_cast<const ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride +
+                  (int64_t)h * HD * HD;
+    float s[NJ][EPL];
+    {
+        uint4 raw[NJ];
+        load_rows<HD, ST>(raw, S, wave, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
+    }
+    const int col0 = (lane % LPR) * EPL;
+    const RingArgs &R = a.ring;
+
+    for (int t = 0; t < n; ++t) {
+        const int pos = (a.ring_base[b] + t) & (R.L - 1);
+        const int64_t bt = (int64_t)b * a.D + t;
+        float *yb = ybuf[t & 1];
+        // ---- conv + SiLU of the owned channels, rounded to the I/O dtype
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) {
+            if (!own[m]) continue;
+            const float x = ld<IOT>(a.x, bt * a.C + gch[m]);
+            float y = x;
+            if constexpr (CONV) {
+                float acc = bias[m];
+                acc = fmaf(wc[m].x, h0[m], acc);
+                acc = fmaf(wc[m].y, h1[m], acc);
+                acc = fmaf(wc[m].z, h2[m], acc);
+                acc = fmaf(wc[m].w, x, acc);
+                y = silu(acc);
+                h0[m] = h1[m];
+                h1[m] = h2[m];
+                h2[m] = round_to<CT>(x);
+                if (win_out[m]) {
+                    const int64_t wrow = bt * 3 * a.C + gch[m];
+                    st<CT>(a.windows, wrow, h0[m]);
+                    st<CT>(a.windows, wrow + a.C, h1[m]);
+                    st<CT>(a.windows, wrow + 2 * a.C, h2[m]);
+                }
+            }
+            y = round_to<IOT>(y);
+            const int j = tid + NT * m;
+            yb[j] = y;
+            if (j >= 2 * HD) st<IOT>(R.rawv, ring_at(slot, a.Hv, R.L, h, pos, HD) + (j - 2 * HD), y);
+            else if (j >= HD) st<IOT>(R.rawk, ring_at(slot, a.Hv, R.L, h, pos, HD) + (j - HD), y);
+        }
+        __syncthreads();  // this step's q|k|v complete (the other buffer is still being read)
+
+        // ---- norms (every wave computes the same values), normalised k in the ring
+        const float q0 = yb[lane], q1 = yb[lane + 64];
+        const float k0 = yb[HD + lane], k1 = yb[HD + lane + 64];
+        const float inv_q = inv_norm128(q0, q1, a.eps);
+        const float inv_k = inv_norm128(k0, k1, a.eps);
+        if (wave == 0) {
+            const int64_t kr = ring_at(slot, a.Hv, R.L, h, pos, HD);
+            st<IOT>(R.k, kr + lane, k0 * inv_k);
+            st<IOT>(R.k, kr + lane + 64, k1 * inv_k);
+        }
+        float kk[EPL], qq[EPL], al[EPL];
+        float gv[EPL];
+        if constexpr (KDA) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) gv[e] = a.g[(bt * a.Hv + h) * HD + col0 + e];
+        } else {
+            const float g1 = a.g[bt * a.Hv + h];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) gv[e] = g1;
+        }
+        const float beta = a.beta[bt * a.Hv + h];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            kk[e] = yb[HD + col0 + e] * inv_k;
+            qq[e] = yb[col0 + e] * inv_q;
+            al[e] = fast_exp(gv[e]);
+        }
+        if (tid < LPR) {  // one row group records the gates
+            if constexpr (KDA) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + col0 + e] = gv[e];
+            } else if (tid == 0) {
+                R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = gv[0];
+            }
+            if (tid == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = beta;
+        }
+
+        // ---- rows: the shared step, then o = scale S_t q
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = (wave * NJ + j) * RPW + lane / LPR;
+            const float d = row_step<EPL, LPR>(s[j], al, kk, yb[2 * HD + r], beta);
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) p = fmaf(s[j][e], qq[e], p);
+            p = group_sum<LPR>(p);
+            if (lane % LPR == 0) {
+                st<IOT>(a.out, out_at(t, r), a.scale * p);
+                st<IOT>(R.d, ring_at(slot, a.Hv, R.L, h, pos, HD) + r, d);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// commit
+// ---------------------------------------------------------------------------
+template <typename ST, typename IOT, bool KDA>
+__global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitArgs a)
+{
+    using Cfg = DecodeCfg<HD, ST>;
+    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ;
+    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = a.slots[b];
+    const int na = min(a.accepted[b], a.ring.L);
+    if (slot < 0 || slot >= a.num_rows || na <= 0) return;  // nothing accepted: row unchanged
+
+    ST *S = static_cast<ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD;
+    float s[NJ][EPL];
+    {
+        uint4 raw[NJ];
+        load_rows<HD, ST>(raw, S, wave, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
+    }
+    const int col0 = (lane % LPR) * EPL;
+    const RingArgs &R = a.ring;
+    for (int t = 0; t < na; ++t) {
+        const int pos = (a.ring_base[b] + t) & (R.L - 1);
+        const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD);
+        const float inv_k = inv_norm128(ld<IOT>(R.rawk, vr + lane), ld<IOT>(R.rawk, vr + lane + 64),
+                                        a.eps);
+        float kk[EPL], al[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            kk[e] = ld<IOT>(R.rawk, vr + col0 + e) * inv_k;
+            al[e] = fast_exp(KDA ? R.g[vr + col0 + e] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)]);
+        }
+        const float beta = R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = (wave * NJ + j) * RPW + lane / LPR;
+            row_step<EPL, LPR>(s[j], al, kk, ld<IOT>(R.rawv, vr + r), beta);
+        }
+    }
+    const int c0 = col0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int r = (wave * NJ + j) * RPW + lane / LPR;
+        st_stream(S + (int64_t)r * HD + c0, Stor<ST>::pack(s[j]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// conv-window scatter and state-tracking copy: 16-byte copies
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) conv_scatter_kernel(ScatterArgs a)
+{
+    const int b = blockIdx.y;
+    if (a.mask && !a.mask[b]) return;
+    const int step = a.step[b], slot = a.slots[b];
+    if (step < 0 || step >= a.D || slot < 0 || slot >= a.num_rows) return;
+    const int es = a.conv_dtype ? 2 : 4;
+    const int64_t units = (int64_t)3 * a.C * es / 16;
+    const char *src = static_cast<const char *>(a.windows) + ((int64_t)b * a.D + step) * 3 * a.C * es;
+    char *dst = static_cast<char *>(a.conv_pool) + (int64_t)slot * a.conv_stride * es;
+    for (int64_t u = blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256)
+        reinterpret_cast<uint4 *>(dst)[u] = reinterpret_cast<const uint4 *>(src)[u];
+}
+
+__global__ void __launch_bounds__(256) track_copy_kernel(TrackArgs a)
+{
+    const int b = blockIdx.y;
+    if (a.mask && !a.mask[b]) return;
+    const int src = a.src[b], dst = a.dst[b];
+    if (src < 0 || src >= a.num_rows || dst < 0 || dst >= a.num_rows || src == dst) return;
+    const int64_t su = a.ssm_row_b / 16, cu = a.conv_row_b / 16;
+    for (int64_t u = blockIdx.x * 256 + threadIdx.x; u < su + cu; u += (int64_t)gridDim.x * 256) {
+        if (u < su) {
+            const uint4 v = ld_stream(a.ssm_pool + src * a.ssm_stride_b + 16 * u);
+            st_stream(a.ssm_pool + dst * a.ssm_stride_b + 16 * u, v);
+        } else {
+            const int64_t c = u - su;
+            const uint4 v = ld_stream(a.conv_pool + src * a.conv_stride_b + 16 * c);
+            st_stream(a.conv_pool + dst * a.conv_stride_b + 16 * c, v);
+        }
+    }
+}
+
+template <typename ST, typename IOT, typename CT, bool KDA>
+hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(a.B * a.Hv)), block(DecodeCfg<HD, ST>::NT);
+    if (a.w)
+        hipLaunchKernelGGL((verify_kernel<ST, IOT, CT, KDA, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((verify_kernel<ST, IOT, CT, KDA, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename ST, typename IOT, typename CT>
+hipError_t launch_verify_k(const VerifyArgs &a, bool kda, hipStream_t stream)
+{
+    return kda ? launch_verify_t<ST, IOT, CT, true>(a, stream)
+               : launch_verify_t<ST, IOT, CT, false>(a, stream);
+}
+
+template <typename ST, typename IOT, bool KDA>
+hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((commit_kernel<ST, IOT, KDA>), dim3((unsigned)(a.B * a.Hv)),
+                       dim3(DecodeCfg<HD, ST>::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify(const VerifyArgs &a, int state_dtype, bool kda, hipStream_t stream)
+{
+    const int code = (state_dtype ? 4 : 0) | (a.io_dtype ? 2 : 0) | (a.conv_dtype ? 1 : 0);
+    switch (code) {
+    case 0: return launch_verify_k<float, float, float>(a, kda, stream);
+    case 1: return launch_verify_k<float, float, bf16_t>(a, kda, stream);
+    case 2: return launch_verify_k<float, bf16_t, float>(a, kda, stream);
+    case 3: return launch_verify_k<float, bf16_t, bf16_t>(a, kda, stream);
+    case 4: return launch_verify_k<bf16_t, float, float>(a, kda, stream);
+    case 5: return launch_verify_k<bf16_t, float, bf16_t>(a, kda, stream);
+    case 6: return launch_verify_k<bf16_t, bf16_t, float>(a, kda, stream);
+    default: return launch_verify_k<bf16_t, bf16_t, bf16_t>(a, kda, stream);
+    }
+}
+
+hipError_t launch_commit(const CommitArgs &a, int state_dtype, bool kda, hipStream_t stream)
+{
+    const int code = (state_dtype ? 2 : 0) | (a.io_dtype ? 1 : 0);
+    switch (code) {
+    case 0: return kda ? launch_commit_t<float, float, true>(a, stream)
+                       : launch_commit_t<float, float, false>(a, stream);
+    case 1: return kda ? launch_commit_t<float, bf16_t, true>(a, stream)
+                       : launch_commit_t<float, bf16_t, false>(a, stream);
+    case 2: return kda ? launch_commit_t<bf16_t, float, true>(a, stream)
+                       : launch_commit_t<bf16_t, float, false>(a, stream);
+    default: return kda ? launch_commit_t<bf16_t, bf16_t, true>(a, stream)
+                        : launch_commit_t<bf16_t, bf16_t, false>(a, stream);
+    }
+}
+
+hipError_t launch_conv_scatter(const ScatterArgs &a, hipStream_t stream)
+{
+    const int64_t units = (int64_t)3 * a.C * (a.conv_dtype ? 2 : 4) / 16;
+    const unsigned gx = (unsigned)((units + 255) / 256);
+    hipLaunchKernelGGL(conv_scatter_kernel, dim3(gx, (unsigned)a.B), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_track_copy(const TrackArgs &a, hipStream_t stream)
+{
+    const int64_t units = (a.ssm_row_b + a.conv_row_b) / 16;
+    const int64_t blocks = (units + 255) / 256;
+    const unsigned gx = (unsigned)(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(track_copy_kernel, dim3(gx, (unsigned)a.B), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,167 @@
+"""GPU parity of the speculative-decode entry points (verify, exact commit,
+conv-window scatter, state-tracking copy) against the fp64 oracle, through the
+C ABI.
+
+Bars: every step's output, the ring's vectors and the committed state within
+the relative-L2 tolerance of their storage dtype (1e-4 fp32, 2e-2 bf16) per
+(request, step, head) or (request, head); conv windows, the ring's gates, the
+scattered conv rows, the tracking copies and every untouched pool row
+bit-exact.  With an fp32 state, committing a verify's first steps and
+verifying the rest from the committed state reproduces the first call's later
+outputs bit for bit (commit and verify run the same arithmetic).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrent_amd import binding as la
+from linear_attention_recurrent_amd import synth
+from parity_util import TOL, assert_close_units, f64
+
+pytestmark = pytest.mark.gpu
+
+D_HEAD = 128
+
+
+def make_case(seed, B, D, Hqk, Hv, kda, io, state, conv, P, dev, L=16):
+    d = D_HEAD
+    C = 2 * Hqk * d + Hv * d
+    x = synth.to_torch(synth.normal(seed, synth.S_X, (B, D, C)), io, dev)
+    w = synth.to_torch(0.5 * synth.normal(seed, synth.S_W, (C, 4)), "fp32", dev)
+    g = torch.from_numpy(synth.log_decay(seed, synth.S_G, (B, D, Hv, d) if kda else (B, D, Hv))).to(dev)
+    beta = torch.from_numpy(synth.beta_gate(seed, synth.S_BETA, (B, D, Hv))).to(dev)
+    conv_pool = synth.to_torch(synth.normal(seed, synth.S_CONV, (P + 1, 3, C)), conv, dev)
+    ssm_pool = synth.to_torch(synth.normal(seed, synth.S_SSM, (P + 1, Hv, d, d)), state, dev)
+    slots = torch.from_numpy(synth.slot_permutation(seed, synth.S_SLOTS, P)[:B].astype(np.int32)).to(dev)
+    ring = la.new_ring(P + 1, Hv, L, d, d, kda=kda, dtype=x.dtype, device=dev)
+    return dict(x=x, w=w, g=g, beta=beta, conv_pool=conv_pool, ssm_pool=ssm_pool, slots=slots,
+                ring=ring, C=C)
+
+
+def i32(v, dev):
+    return torch.tensor(v, dtype=torch.int32, device=dev)
+
+
+def run_verify(kda, c, n_tok, base, Hqk, dev):
+    fn = la.kda_verify if kda else la.gdn_verify
+    return fn(c["x"], c["g"], c["beta"], c["slots"], i32(n_tok, dev), c["ssm_pool"], c["ring"],
+              i32(base, dev), Hqk=Hqk, conv_w=c["w"], conv_pool=c["conv_pool"])
+
+
+def oracle_verify(kda, c, n_tok, base, Hqk, Hv, io, conv):
+    return oracle.verify(f64(c["x"]), f64(c["w"]), None, f64(c["conv_pool"]), f64(c["g"]),
+                         f64(c["beta"]), c["slots"].cpu().numpy(), n_tok, f64(c["ssm_pool"]),
+                         oracle.new_ring(c["ssm_pool"].shape[0], Hv, c["ring"]["d"].shape[2],
+                                         D_HEAD, D_HEAD, kda), base, Hqk=Hqk, Hv=Hv,
+                         dk=D_HEAD, dv=D_HEAD, kda=kda, conv_dtype=conv, io_dtype=io)
+
+
+CASES = [  # kda, Hqk, Hv, io, state, conv
+    (True, 2, 2, "bf16", "bf16", "bf16"),
+    (True, 2, 2, "fp32", "fp32", "fp32"),
+    (True, 1, 2, "bf16", "fp32", "bf16"),
+    (False, 2, 4, "fp32", "fp32", "fp32"),
+    (False, 2, 4, "bf16", "bf16", "fp32"),
+]
+
+
+@pytest.mark.parametrize("kda,Hqk,Hv,io,state,conv", CASES)
+def test_verify_and_commit_match_oracle(kda, Hqk, Hv, io, state, conv, dev):
+    B, D, P = 4, 8, 10
+    c = make_case(7100 + Hv + 10 * kda, B, D, Hqk, Hv, kda, io, state, conv, P, dev)
+    n_tok = [8, 5, 1, 0]
+    base = [0, 13, 7, 3]                      # wraps around the 16-deep ring
+    conv0, ssm0 = c["conv_pool"].clone(), c["ssm_pool"].clone()
+    out, win = run_verify(kda, c, n_tok, base, Hqk, dev)
+    torch.cuda.synchronize()
+    o_ref, w_ref, r_ref = oracle_verify(kda, c, n_tok, base, Hqk, Hv, io, conv)
+    assert torch.equal(c["conv_pool"], conv0) and torch.equal(c["ssm_pool"], ssm0)
+    assert_close_units(f64(out), o_ref, 3, io, "verify outputs")
+    assert np.all(f64(out)[1, 5:] == 0) and np.all(f64(out)[3] == 0)
+    slots = c["slots"].cpu().numpy()
+    ring = {k: f64(v) for k, v in c["ring"].items()}
+    for b in range(B):
+        s = slots[b]
+        pos = [(base[b] + t) % 16 for t in range(n_tok[b])]
+        if not pos:
+            continue
+        np.testing.assert_array_equal(f64(win)[b, :n_tok[b]], w_ref[b, :n_tok[b]])
+        for key in ("g", "beta"):  # (GDN's g is [rows, Hv, L] here, [rows, Hv, L, 1] there)
+            want = r_ref[key][s][:, pos]
+            np.testing.assert_array_equal(ring[key][s][:, pos].reshape(want.shape), want)
+        for key in ("d", "k", "rawv", "rawk"):
+            assert_close_units(ring[key][s][:, pos], r_ref[key][s][:, pos], 2, io, f"ring {key}")
+
+    accepted = [6, 3, 1, 0]
+    fn = la.kda_commit if kda else la.gdn_commit
+    fn(i32(accepted, dev), c["slots"], c["ssm_pool"], c["ring"], i32(base, dev))
+    torch.cuda.synchronize()
+    p_ref = oracle.commit(accepted, slots, f64(ssm0), ring, base, kda=kda, state_dtype=state)
+    got = f64(c["ssm_pool"])
+    assert_close_units(got[slots[:3]], p_ref[slots[:3]], 2, state, "committed state")
+    untouched = np.setdiff1d(np.arange(P + 1), slots[:3])
+    np.testing.assert_array_equal(got[untouched], f64(ssm0)[untouched])
+
+
+def test_commit_then_verify_continues_bit_exactly(dev):
+    """fp32 state: verify 5 tokens; commit 3 and scatter the conv window of
+    step 2; verify the remaining 2 tokens from the committed pools: their
+    outputs equal the first call's steps 3 and 4 bit for bit."""
+    B, D, Hqk, Hv, P = 3, 5, 2, 2, 8
+    c = make_case(7200, B, D, Hqk, Hv, True, "bf16", "fp32", "bf16", P, dev)
+    out1, win1 = run_verify(True, c, [5, 5, 5], [0, 0, 0], Hqk, dev)
+    a = 3
+    la.kda_commit(i32([a] * B, dev), c["slots"], c["ssm_pool"], c["ring"], i32([0] * B, dev))
+    la.conv_window_scatter(win1, c["slots"], i32([a - 1] * B, dev), c["conv_pool"])
+    c2 = dict(c, x=c["x"][:, a:].contiguous(), g=c["g"][:, a:].contiguous(),
+              beta=c["beta"][:, a:].contiguous())
+    out2, _ = run_verify(True, c2, [2, 2, 2], [a] * B, Hqk, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out1[:, a:])
+
+
+def test_conv_window_scatter_and_track_copy_are_bit_exact(dev):
+    B, D, C, P = 5, 4, 768, 12
+    conv = synth.to_torch(synth.normal(7300, 0, (P + 1, 3, C)), "bf16", dev)
+    ssm = synth.to_torch(synth.normal(7300, 1, (P + 1, 2, D_HEAD, D_HEAD)), "fp32", dev)
+    windows = synth.to_torch(synth.normal(7300, 2, (B, D, 3, C)), "bf16", dev)
+    slots = [3, 7, 1, 9, 4]
+    step = [0, 3, 2, -1, 1]                   # -1: nothing accepted
+    mask = torch.tensor([1, 1, 0, 1, 1], dtype=torch.uint8, device=dev)
+    ref = oracle.conv_window_scatter(f64(conv), f64(windows), mask.cpu().numpy(), slots, step)
+    la.conv_window_scatter(windows, i32(slots, dev), i32(step, dev), conv, mask=mask)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(conv), ref)
+
+    src, dst = [1, 2, 3, 5], [10, 11, 3, 12]  # one self-copy
+    tmask = torch.tensor([1, 1, 1, 0], dtype=torch.uint8, device=dev)
+    ref_c, ref_s = oracle.track_copy(f64(conv), f64(ssm), tmask.cpu().numpy(), src, dst)
+    la.state_track_copy(i32(src, dev), i32(dst, dev), conv, ssm, mask=tmask)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64(conv), ref_c)
+    np.testing.assert_array_equal(f64(ssm), ref_s)
+
+
+def test_verify_full_shape_kda_64x12_bf16(dev):
+    """The serving shape of one layer (64 requests, 12 heads, bf16) with 8
+    draft tokens, every request and step against the oracle, then the commit
+    of a per-request accepted count."""
+    B, D, H, P = 64, 8, 12, 80
+    c = make_case(7400, B, D, H, H, True, "bf16", "bf16", "bf16", P, dev)
+    rng = np.random.default_rng(7400)
+    n_tok = [D] * B
+    base = rng.integers(0, 16, B).tolist()
+    ssm0 = c["ssm_pool"].clone()
+    out, win = run_verify(True, c, n_tok, base, H, dev)
+    torch.cuda.synchronize()
+    o_ref, w_ref, _ = oracle_verify(True, c, n_tok, base, H, H, "bf16", "bf16")
+    assert_close_units(f64(out), o_ref, 3, "bf16", "verify outputs")
+    np.testing.assert_array_equal(f64(win), w_ref)
+    accepted = rng.integers(0, D + 1, B).tolist()
+    la.kda_commit(i32(accepted, dev), c["slots"], c["ssm_pool"], c["ring"], i32(base, dev))
+    torch.cuda.synchronize()
+    ring = {k: f64(v) for k, v in c["ring"].items()}
+    slots = c["slots"].cpu().numpy()
+    p_ref = oracle.commit(accepted, slots, f64(ssm0), ring, base, kda=True, state_dtype="bf16")
+    assert_close_units(f64(c["ssm_pool"])[slots], p_ref[slots], 2, "bf16", "committed state")

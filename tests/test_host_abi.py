@@ -126,3 +126,39 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError, match="no CPU fallback"):
         binding.load_library()
+
+
+def test_speculative_validation(lib):
+    fake = ctypes.c_void_p(0x1000)
+    ring = binding.LaRing(16, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    H, d = 2, 128
+    C = 3 * H * d
+
+    def verify(**over):
+        a = dict(B=4, D=8, n_tok=fake, Hqk=H, Hv=H, dk=d, dv=d, x=fake, io=1, w=None, b=None,
+                 cp=None, cstride=0, cdt=1, g=fake, beta=fake, slots=fake, rows=9, sp=fake,
+                 sstride=H * d * d, sdt=1, out=fake, win=None, ring=ctypes.byref(ring),
+                 base=fake, eps=1e-6, scale=1.0, stream=None)
+        a.update(over)
+        return lib.kda_verify(*a.values())
+
+    assert verify(x=None) == -1                              # null pointer
+    assert verify(dk=64, dv=64) == -2                        # only d = 128 built
+    assert verify(D=32) == -1                                # ring shallower than the drafts
+    assert b"power of two" in lib.la_last_error()
+    bad = binding.LaRing(12, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert verify(ring=ctypes.byref(bad)) == -1              # L not a power of two
+    assert verify(ring=None) == -1                           # no ring
+    assert verify(w=fake, cp=fake, cstride=3 * C) == -1      # conv without a windows buffer
+    assert verify(B=0) == 0
+    assert lib.kda_commit(4, fake, H, d, d, fake, 9, fake, H * d * d, 1, 1, None, fake, 1e-6,
+                          None) == -1                        # no ring
+    assert lib.kda_commit(0, None, H, d, d, None, 9, None, H * d * d, 1, 1, None, None, 1e-6,
+                          None) == 0
+    assert lib.conv_window_scatter(4, 8, 1, None, fake, fake, fake, fake, 16, 0, 9, None) == -1
+    assert b"16 bytes" in lib.la_last_error()                # a 12-byte window
+    assert lib.conv_window_scatter(0, 8, C, None, None, None, None, None, 3 * C, 1, 9, None) == 0
+    assert lib.state_track_copy(4, None, fake, fake, fake, 40, 36, 1, fake, 64, 64, 0, 9,
+                                None) == -1                  # 72-byte conv row
+    assert lib.state_track_copy(4, None, fake, None, fake, 48, 48, 1, fake, 64, 64, 0, 9,
+                                None) == -1                  # null dst
