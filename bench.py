@@ -235,6 +235,77 @@ def decode_stack(sh, layers, steps, seed, dev):
                          "algorithmic_bytes_per_step": nbytes}}
 
 
+# ----------------------------------------------------- speculative decode ----
+
+def spec_bench(dev, D=8, L=16, reps=200):
+    """Speculative verify of D draft tokens and the exact commit at the
+    single-layer serving shape (64 requests x 12 heads, d=128, bf16 I/O, state,
+    conv and ring), plus the tracking copy and the conv-window scatter of the
+    same batch.  Pools, rings and inputs are rotated over copies worth >= 1 GiB
+    so every call streams from HBM; each call type is replayed from a captured
+    HIP graph."""
+    sh = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
+    B, H, d, C, P = sh.B, sh.Hv, sh.dk, sh.C, sh.P
+    bf = torch.bfloat16
+    per_copy = (P + 1) * (H * d * d * 2 + 3 * C * 2 + H * L * (4 * d * 2 + d * 4 + 4))
+    n = max(16, -(-(1 << 30) // per_copy))
+    log(f"speculative decode: {n} rotated copies")
+    copies = []
+    for i in range(n):
+        seed = 2001 + 7919 * i
+        base = synth.decode_inputs(sh, seed, dev)
+        copies.append(dict(
+            base,
+            x=synth.normal_torch(seed, synth.S_X, B * D * C, dev, bf).view(B, D, C),
+            g=synth.log_decay_torch(seed, synth.S_G, B * D * H * d, dev).view(B, D, H, d),
+            beta=synth.beta_gate_torch(seed, synth.S_BETA, B * D * H, dev).view(B, D, H),
+            ring=la.new_ring(P + 1, H, L, d, d, kda=True, dtype=bf, device=dev),
+            n_tok=torch.full((B,), D, dtype=torch.int32, device=dev),
+            base=torch.zeros(B, dtype=torch.int32, device=dev),
+            acc=torch.full((B,), D, dtype=torch.int32, device=dev),
+            step=torch.full((B,), D - 1, dtype=torch.int32, device=dev),
+            out=torch.empty((B, D, H, d), dtype=bf, device=dev),
+            win=torch.empty((B, D, 3, C), dtype=bf, device=dev),
+            dst=(base["slots"] % P) + 1))  # another row of the same pool
+    def verify(c):
+        la.kda_verify(c["x"], c["g"], c["beta"], c["slots"], c["n_tok"], c["ssm_pool"], c["ring"],
+                      c["base"], Hqk=H, conv_w=c["w"], conv_pool=c["conv_pool"], out=c["out"],
+                      windows=c["win"])
+    def commit(c):
+        la.kda_commit(c["acc"], c["slots"], c["ssm_pool"], c["ring"], c["base"])
+    def scatter(c):
+        la.conv_window_scatter(c["win"], c["slots"], c["step"], c["conv_pool"])
+    def track(c):
+        la.state_track_copy(c["slots"], c["dst"], c["conv_pool"], c["ssm_pool"])
+    for c in copies:
+        verify(c)
+    torch.cuda.synchronize()
+    res = {"batch": B, "heads": H, "draft_tokens": D, "ring_depth": L, "dtype": "bf16",
+           "pool_copies_rotated": n}
+    state = B * H * d * d * 2
+    ring_step = H * (4 * d * 2 + d * 4 + 4)            # d, k, rawv, rawk, g, beta per request
+    nbytes = {
+        # state read; x, g, beta read; conv history read; outputs, windows, ring written
+        "verify": state + B * D * (C * 2 + H * d * 4 + H * 4) + B * 3 * C * 2 + C * 16
+                  + B * D * (H * d * 2 + 3 * C * 2 + ring_step),
+        # state read + written; rawk, rawv, g, beta of D steps read
+        "commit": 2 * state + B * D * H * (2 * d * 2 + d * 4 + 4),
+        "conv_window_scatter": 2 * B * 3 * C * 2,
+        "state_track_copy": 2 * B * (H * d * d * 2 + 3 * C * 2),
+    }
+    for name, fn in (("verify", verify), ("commit", commit), ("conv_window_scatter", scatter),
+                     ("state_track_copy", track)):
+        ms, _ = time_graph(lambda: [fn(c) for c in copies], n, reps, n)
+        gbs = nbytes[name] / (ms * 1e-3) / 1e9
+        res[name] = {"us": ms * 1e3, "roofline": {
+            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes[name]}}
+    res["verify"]["draft_tokens_per_s"] = B * D / (res["verify"]["us"] * 1e-6)
+    del copies
+    torch.cuda.empty_cache()
+    return res
+
+
 # --------------------------------------------------------------- prefill ----
 
 def prefill_mfma_flops(seqlens, Hv, mode=0) -> float:
@@ -458,6 +529,7 @@ def main():
                               state="fp32", conv="fp32"), 48, 16, 1003, dev)
         log("prefill")
         extra["kda_prefill_chunked_h12"] = prefill_bench(dev)
+        extra["kda_speculative_b64_h12_d8"] = spec_bench(dev)
     if not args.no_cpu:
         log("CPU oracle baselines")
         rate, reps, el = cpu_oracle_decode_rate(sh, 1001)

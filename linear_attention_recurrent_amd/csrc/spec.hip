@@ -27,8 +27,10 @@
 // head), the head's state rows spread over the waves as in the decode kernel
 // (16-byte lane chunks, LPR lanes per row), held in fp32 registers across the
 // steps.  Verify computes the head's q|k|v conv outputs per step into a
-// double-buffered LDS area (one barrier per step); the commit needs no
-// barrier at all.
+// double-buffered LDS area (one barrier per step).  Both kernels first stage
+// the inputs of up to eight steps in LDS (verify: the pre-conv inputs of the
+// head's channels and the gates; commit: the ring records), with every load
+// issued back to back, so a step waits for memory once per eight steps.
 #include "decode_kernel.h"
 #include "la_device.h"
 #include "la_internal.h"
@@ -37,7 +39,8 @@ namespace la {
 
 namespace {
 
-constexpr int HD = 128;  // head dim of the speculative kernels (d_k = d_v)
+constexpr int HD = 128;     // head dim of the speculative kernels (d_k = d_v)
+constexpr int kChunk = 8;   // steps whose inputs are staged in LDS at once
 
 template <typename T> __device__ __forceinline__ float round_to(float v);
 template <> __device__ __forceinline__ float round_to<float>(float v) { return v; }
@@ -86,7 +89,12 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
     constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
     constexpr int NCH = 3 * HD;                // the head's q, k, v channels
     constexpr int CPT = (NCH + NT - 1) / NT;   // channels per thread
+    constexpr int XPT = (kChunk * NCH + NT - 1) / NT;  // staged inputs per thread
+    constexpr int GPT = (kChunk * HD + NT - 1) / NT;   // staged gates per thread
     __shared__ float ybuf[2][NCH];             // conv outputs per step parity (I/O-dtype values)
+    __shared__ float xs[kChunk][NCH];          // the chunk's pre-conv inputs of the head's channels
+    __shared__ float gs[kChunk][HD];           // the chunk's log-decays (GDN: broadcast)
+    __shared__ float bs[kChunk];               // the chunk's betas
 
     const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv, kh = h / a.G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -136,7 +144,46 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
     const int col0 = (lane % LPR) * EPL;
     const RingArgs &R = a.ring;
 
-    for (int t = 0; t < n; ++t) {
+    // The local channel j (over [q | k | v] of this head) -> global channel.
+    auto glob = [&](int j) {
+        return j < HD ? kh * HD + j
+             : j < 2 * HD ? a.Hqk * HD + kh * HD + (j - HD) : 2 * a.Hqk * HD + h * HD + (j - 2 * HD);
+    };
+    for (int t0 = 0; t0 < n; t0 += kChunk) {
+    // ---- stage the chunk's inputs and gates in LDS: every load issued back to
+    //      back (indices clamped into the chunk, so no branch around a load)
+    const int nc = min(kChunk, n - t0);
+    {
+        float xv[XPT], gv2[GPT], bv = 0.f;
+#pragma unroll
+        for (int q = 0; q < XPT; ++q) {
+            const int i = min(tid + q * NT, kChunk * NCH - 1);
+            const int tt = min(i / NCH, nc - 1);
+            xv[q] = ld<IOT>(a.x, ((int64_t)b * a.D + t0 + tt) * a.C + glob(i % NCH));
+        }
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+            const int i = min(tid + q * NT, kChunk * HD - 1);
+            const int64_t bt = (int64_t)b * a.D + t0 + min(i / HD, nc - 1);
+            gv2[q] = KDA ? a.g[(bt * a.Hv + h) * HD + i % HD] : a.g[bt * a.Hv + h];
+        }
+        if (tid < kChunk) bv = a.beta[((int64_t)b * a.D + t0 + min(tid, nc - 1)) * a.Hv + h];
+        __syncthreads();  // the previous chunk's staged values are no longer read
+#pragma unroll
+        for (int q = 0; q < XPT; ++q) {
+            const int i = tid + q * NT;
+            if (i < kChunk * NCH) xs[i / NCH][i % NCH] = xv[q];
+        }
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+            const int i = tid + q * NT;
+            if (i < kChunk * HD) gs[i / HD][i % HD] = gv2[q];
+        }
+        if (tid < kChunk) bs[tid] = bv;
+        __syncthreads();
+    }
+    for (int tt = 0; tt < nc; ++tt) {
+        const int t = t0 + tt;
         const int pos = (a.ring_base[b] + t) & (R.L - 1);
         const int64_t bt = (int64_t)b * a.D + t;
         float *yb = ybuf[t & 1];
@@ -144,7 +191,7 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
 #pragma unroll
         for (int m = 0; m < CPT; ++m) {
             if (!own[m]) continue;
-            const float x = ld<IOT>(a.x, bt * a.C + gch[m]);
+            const float x = xs[tt][tid + NT * m];
             float y = x;
             if constexpr (CONV) {
                 float acc = bias[m];
@@ -183,15 +230,9 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
         }
         float kk[EPL], qq[EPL], al[EPL];
         float gv[EPL];
-        if constexpr (KDA) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) gv[e] = a.g[(bt * a.Hv + h) * HD + col0 + e];
-        } else {
-            const float g1 = a.g[bt * a.Hv + h];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) gv[e] = g1;
-        }
-        const float beta = a.beta[bt * a.Hv + h];
+        for (int e = 0; e < EPL; ++e) gv[e] = gs[tt][col0 + e];
+        const float beta = bs[tt];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             kk[e] = yb[HD + col0 + e] * inv_k;
@@ -223,6 +264,7 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
             }
         }
     }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -232,9 +274,11 @@ template <typename ST, typename IOT, bool KDA>
 __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitArgs a)
 {
     using Cfg = DecodeCfg<HD, ST>;
-    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ;
+    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
+    constexpr int VPT = (kChunk * HD + NT - 1) / NT;  // staged ring values per thread
+    __shared__ float ks[kChunk][HD], vs[kChunk][HD], gsh[kChunk][HD], bsh[kChunk];
     const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = a.slots[b];
     const int na = min(a.accepted[b], a.ring.L);
     if (slot < 0 || slot >= a.num_rows || na <= 0) return;  // nothing accepted: row unchanged
@@ -249,22 +293,49 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitA
     }
     const int col0 = (lane % LPR) * EPL;
     const RingArgs &R = a.ring;
-    for (int t = 0; t < na; ++t) {
-        const int pos = (a.ring_base[b] + t) & (R.L - 1);
-        const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD);
-        const float inv_k = inv_norm128(ld<IOT>(R.rawk, vr + lane), ld<IOT>(R.rawk, vr + lane + 64),
-                                        a.eps);
-        float kk[EPL], al[EPL];
+    for (int t0 = 0; t0 < na; t0 += kChunk) {
+        // stage the chunk's ring records in LDS, all loads back to back
+        const int nc = min(kChunk, na - t0);
+        float kv[VPT], vv[VPT], gv[VPT], bv = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            kk[e] = ld<IOT>(R.rawk, vr + col0 + e) * inv_k;
-            al[e] = fast_exp(KDA ? R.g[vr + col0 + e] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)]);
+        for (int q = 0; q < VPT; ++q) {
+            const int i = min(tid + q * NT, kChunk * HD - 1);
+            const int pos = (a.ring_base[b] + t0 + min(i / HD, nc - 1)) & (R.L - 1);
+            const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD) + i % HD;
+            kv[q] = ld<IOT>(R.rawk, vr);
+            vv[q] = ld<IOT>(R.rawv, vr);
+            gv[q] = KDA ? R.g[vr] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
         }
-        const float beta = R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)];
+        if (tid < kChunk) {
+            const int pos = (a.ring_base[b] + t0 + min(tid, nc - 1)) & (R.L - 1);
+            bv = R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)];
+        }
+        __syncthreads();  // the previous chunk's records are no longer read
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int r = (wave * NJ + j) * RPW + lane / LPR;
-            row_step<EPL, LPR>(s[j], al, kk, ld<IOT>(R.rawv, vr + r), beta);
+        for (int q = 0; q < VPT; ++q) {
+            const int i = tid + q * NT;
+            if (i < kChunk * HD) {
+                ks[i / HD][i % HD] = kv[q];
+                vs[i / HD][i % HD] = vv[q];
+                gsh[i / HD][i % HD] = gv[q];
+            }
+        }
+        if (tid < kChunk) bsh[tid] = bv;
+        __syncthreads();
+        for (int tt = 0; tt < nc; ++tt) {
+            const float inv_k = inv_norm128(ks[tt][lane], ks[tt][lane + 64], a.eps);
+            float kk[EPL], al[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                kk[e] = ks[tt][col0 + e] * inv_k;
+                al[e] = fast_exp(gsh[tt][col0 + e]);
+            }
+            const float beta = bsh[tt];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int r = (wave * NJ + j) * RPW + lane / LPR;
+                row_step<EPL, LPR>(s[j], al, kk, vs[tt][r], beta);
+            }
         }
     }
     const int c0 = col0;
