@@ -61,6 +61,8 @@ def _load():
     lib.orc_verify.restype = I
     lib.orc_commit.argtypes = [I, I, P, I, I, I, P, P, L, I, I, P, P, P, P, P, D]
     lib.orc_commit.restype = I
+    lib.orc_ring_fold.argtypes = [I, I, P, I, I, I, P, P, P, L, I, I, P, P, P, P, P, P, I, D, D]
+    lib.orc_ring_fold.restype = I
     _lib = lib
     return lib
 
@@ -260,3 +262,22 @@ def conv_window_scatter(conv_pool, windows, mask, slots, step):
         if (mask is None or mask[b]) and 0 <= step[b] < D:
             conv[slots[b]] = windows[b, step[b]]
     return conv
+
+
+def ring_fold(m, slots, dst, ssm_pool, ring, ring_base, q=None, *, kda=True,
+              state_dtype="fp32", io_dtype="fp32", eps=1e-6, scale=1.0):
+    """ReplaySSM fast rebuild: S_m from the checkpoint rows slots[b] and the
+    ring's (d, k, g) of m[b] steps by the unrolled sum, stored to rows dst[b].
+    Returns (new pool, out [B, Hv, dv] = scale S_m q_hat or None)."""
+    pool = _f64(ssm_pool).copy()
+    _, Hv, dv, dk = pool.shape
+    L = ring["d"].shape[2]
+    r = {k: _f64(v) for k, v in ring.items()}
+    m, slots, dst, ring_base = _i32(m), _i32(slots), _i32(dst), _i32(ring_base)
+    q = _f64(q)
+    out = np.empty((len(slots), Hv, dv)) if q is not None else None
+    _load().orc_ring_fold(int(kda), len(slots), _ptr(m), Hv, dk, dv, _ptr(slots), _ptr(dst),
+                          _ptr(pool), Hv * dv * dk, _DTYPES[state_dtype], L, _ptr(ring_base),
+                          _ptr(r["d"]), _ptr(r["k"]), _ptr(r["g"]), _ptr(q), _ptr(out),
+                          _DTYPES[io_dtype], eps, scale)
+    return pool, out

@@ -460,3 +460,68 @@ int orc_commit(int kda, int B, const int32_t *accepted, int Hv, int dk, int dv,
     free(kn); free(alpha);
     return 0;
 }
+
+/* ReplaySSM fast rebuild ([mamba-ish] ReplaySSM "d / k / g" passage): the
+ * state after m ring steps is the checkpoint decayed by the product of the
+ * steps' alphas plus every step's rank-1 term d_j k_j^T decayed by the alphas
+ * of the steps after it,
+ *     S_m = S_0 Diag(prod_{i<=m} alpha_i)
+ *           + sum_{j<=m} d_j (k_j . prod_{j<i<=m} alpha_i)^T,   alpha = exp(g),
+ * with no per-step state and no replay of the delta rule (d is read from the
+ * ring).  For each request the checkpoint is pool row slots[b]; the m[b] steps
+ * start at ring position ring_base[b]; S_m is stored to row dst[b] (rounded to
+ * state_dtype).  With q [B, Hv, dk] (raw; L2-normalised here, as in decode),
+ * out [B, Hv, dv] = scale S_m q_hat, rounded to io_dtype. */
+int orc_ring_fold(int kda, int B, const int32_t *m, int Hv, int dk, int dv,
+                  const int32_t *slots, const int32_t *dst, double *ssm_pool,
+                  int64_t ssm_stride, int state_dtype, int L, const int32_t *ring_base,
+                  const double *ring_d, const double *ring_k, const double *ring_g,
+                  const double *q, double *out, int io_dtype, double eps, double scale)
+{
+    const size_t head = (size_t)dv * dk;
+    double *S = malloc(sizeof(double) * head);
+    double *decay = malloc(sizeof(double) * dk), *qn = malloc(sizeof(double) * dk);
+    for (int b = 0; b < B; ++b) {
+        const int slot = slots[b];
+        for (int h = 0; h < Hv; ++h) {
+            const double *S0 = ssm_pool + (int64_t)slot * ssm_stride + (int64_t)h * head;
+            /* checkpoint term: S_0 Diag(prod of all m alphas) */
+            for (int c = 0; c < dk; ++c) decay[c] = 1.0;
+            for (int i = 0; i < m[b]; ++i) {
+                const int pos = (ring_base[b] + i) & (L - 1);
+                for (int c = 0; c < dk; ++c)
+                    decay[c] *= exp(kda ? ring_g[ring_at(slot, Hv, L, h, pos, dk) + c]
+                                        : ring_g[ring_at(slot, Hv, L, h, pos, 1)]);
+            }
+            for (int r = 0; r < dv; ++r)
+                for (int c = 0; c < dk; ++c) S[(int64_t)r * dk + c] = S0[(int64_t)r * dk + c] * decay[c];
+            /* rank-1 terms, each decayed by the steps after it */
+            for (int j = 0; j < m[b]; ++j) {
+                const int pj = (ring_base[b] + j) & (L - 1);
+                for (int c = 0; c < dk; ++c) decay[c] = 1.0;
+                for (int i = j + 1; i < m[b]; ++i) {
+                    const int pos = (ring_base[b] + i) & (L - 1);
+                    for (int c = 0; c < dk; ++c)
+                        decay[c] *= exp(kda ? ring_g[ring_at(slot, Hv, L, h, pos, dk) + c]
+                                            : ring_g[ring_at(slot, Hv, L, h, pos, 1)]);
+                }
+                const double *dj = ring_d + ring_at(slot, Hv, L, h, pj, dv);
+                const double *kj = ring_k + ring_at(slot, Hv, L, h, pj, dk);
+                for (int r = 0; r < dv; ++r)
+                    for (int c = 0; c < dk; ++c) S[(int64_t)r * dk + c] += dj[r] * kj[c] * decay[c];
+            }
+            if (q && out) {
+                l2norm(q + ((int64_t)b * Hv + h) * dk, qn, dk, eps);
+                for (int r = 0; r < dv; ++r) {
+                    double p = 0.0;
+                    for (int c = 0; c < dk; ++c) p += S[(int64_t)r * dk + c] * qn[c];
+                    out[((int64_t)b * Hv + h) * dv + r] = orc_round(scale * p, io_dtype);
+                }
+            }
+            double *Sd = ssm_pool + (int64_t)dst[b] * ssm_stride + (int64_t)h * head;
+            for (size_t i = 0; i < head; ++i) Sd[i] = orc_round(S[i], state_dtype);
+        }
+    }
+    free(S); free(decay); free(qn);
+    return 0;
+}

@@ -143,3 +143,31 @@ def test_track_copy_copies_masked_rows_only():
     np.testing.assert_array_equal(new_ssm[4], ssm[1])
     np.testing.assert_array_equal(new_conv[5], conv[5])   # masked off
     np.testing.assert_array_equal(new_ssm[[0, 1, 2, 3, 5]], ssm[[0, 1, 2, 3, 5]])
+
+
+@pytest.mark.parametrize("kda", [True, False])
+def test_ring_fold_equals_the_exact_commit_on_exact_records(kda):
+    """With fp64 records the fast rebuild's unrolled sum and the exact replay
+    of the same steps give the same state; m = 0 copies the checkpoint; the
+    projection is scale S_m q_hat."""
+    B, D, Hqk, Hv, d, L = 3, 6, 1, 2, 16, 8
+    C, x, w, g, beta, conv, ssm, slots = _case(46 + kda, B, D, Hqk, Hv, d, kda)
+    base = np.array([5, 0, 3], np.int32)
+    ring = oracle.new_ring(ssm.shape[0], Hv, L, d, d, kda)
+    _, _, ring = oracle.verify(x, w, None, conv, g, beta, slots, [D] * B, ssm, ring, base,
+                               Hqk=Hqk, Hv=Hv, dk=d, dv=d, kda=kda, conv_dtype="fp64",
+                               io_dtype="fp64")
+    m = np.array([6, 2, 0], np.int32)
+    exact = oracle.commit(m, slots, ssm, ring, base, kda=kda, state_dtype="fp64")
+    dst = np.array([slots[0], 0, slots[2]], np.int32)   # one to another row
+    q = synth.normal(48, 0, (B, Hv, d))
+    fold, out = oracle.ring_fold(m, slots, dst, ssm, ring, base, q, kda=kda, state_dtype="fp64",
+                                 io_dtype="fp64", scale=0.5)
+    np.testing.assert_allclose(fold[slots[0]], exact[slots[0]], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(fold[0], exact[slots[1]], rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(fold[slots[2]], ssm[slots[2]])
+    qh = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + EPS)
+    for b, s in enumerate(dst):
+        for h in range(Hv):
+            np.testing.assert_allclose(out[b, h], 0.5 * fold[s, h] @ qh[b, h], rtol=1e-12,
+                                       atol=1e-13)
