@@ -266,7 +266,9 @@ def spec_bench(dev, D=8, L=16, reps=200):
             step=torch.full((B,), D - 1, dtype=torch.int32, device=dev),
             out=torch.empty((B, D, H, d), dtype=bf, device=dev),
             win=torch.empty((B, D, 3, C), dtype=bf, device=dev),
-            dst=(base["slots"] % P) + 1))  # another row of the same pool
+            dst=(base["slots"] % P) + 1,  # another row of the same pool
+            q=synth.normal_torch(seed, synth.S_Q, B * H * d, dev, bf).view(B, H, d),
+            o1=torch.empty((B, H, d), dtype=bf, device=dev)))
     def verify(c):
         la.kda_verify(c["x"], c["g"], c["beta"], c["slots"], c["n_tok"], c["ssm_pool"], c["ring"],
                       c["base"], Hqk=H, conv_w=c["w"], conv_pool=c["conv_pool"], out=c["out"],
@@ -277,6 +279,9 @@ def spec_bench(dev, D=8, L=16, reps=200):
         la.conv_window_scatter(c["win"], c["slots"], c["step"], c["conv_pool"])
     def track(c):
         la.state_track_copy(c["slots"], c["dst"], c["conv_pool"], c["ssm_pool"])
+    def fold(c):
+        la.kda_ring_fold(c["acc"], c["slots"], c["ssm_pool"], c["ring"], c["base"], q=c["q"],
+                         out=c["o1"])
     for c in copies:
         verify(c)
     torch.cuda.synchronize()
@@ -291,10 +296,12 @@ def spec_bench(dev, D=8, L=16, reps=200):
         # state read + written; rawk, rawv, g, beta of D steps read
         "commit": 2 * state + B * D * H * (2 * d * 2 + d * 4 + 4),
         "conv_window_scatter": 2 * B * 3 * C * 2,
+        # state read + written; d, k, g of D steps read; q read, out written
+        "ring_fold": 2 * state + B * D * H * (2 * d * 2 + d * 4) + 2 * B * H * d * 2,
         "state_track_copy": 2 * B * (H * d * d * 2 + 3 * C * 2),
     }
-    for name, fn in (("verify", verify), ("commit", commit), ("conv_window_scatter", scatter),
-                     ("state_track_copy", track)):
+    for name, fn in (("verify", verify), ("commit", commit), ("ring_fold", fold),
+                     ("conv_window_scatter", scatter), ("state_track_copy", track)):
         ms, _ = time_graph(lambda: [fn(c) for c in copies], n, reps, n)
         gbs = nbytes[name] / (ms * 1e-3) / 1e9
         res[name] = {"us": ms * 1e3, "roofline": {

@@ -284,6 +284,26 @@ int state_track_copy(int B, const uint8_t *mask, const int32_t *src, const int32
                      int conv_dtype, void *ssm_pool, int64_t ssm_slot_stride,
                      int64_t ssm_row_elems, int state_dtype, int num_rows, void *stream);
 
+/* ReplaySSM fast rebuild (KDA): for each request, the state after the m[b]
+ * (<= L) ring steps from position ring_base[b], from the checkpoint in pool
+ * row slots[b] and the steps' (d, k, g) alone (no replay of the delta rule):
+ *     S_m = S_0 Diag(prod alpha) + sum_j d_j (k_j . prod_{i>j} alpha_i)^T,
+ * the unrolled sum of the ReplaySSM d/k/g passage of xxmr.cn/news/181459.
+ * S_m is stored to row dst_slots[b] (dst_slots NULL: in place); destination
+ * rows must not be another entry's source.  With q [B, H_v, d_k] (raw, L2-
+ * normalised inside) and out [B, H_v, d_v], out = scale S_m q_hat.  io_dtype
+ * is the dtype of the ring's vectors, q and out.  Supported: d_k == d_v == 128. */
+int kda_ring_fold(int B, const int32_t *m, int H_v, int d_k, int d_v, const int32_t *slots,
+                  const int32_t *dst_slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                  int state_dtype, int io_dtype, const la_ring *ring, const int32_t *ring_base,
+                  const void *q, void *out, float eps, float scale, void *stream);
+
+/* Fast rebuild (GDN): as kda_ring_fold with the ring's per-head g. */
+int gdn_ring_fold(int B, const int32_t *m, int H_v, int d_k, int d_v, const int32_t *slots,
+                  const int32_t *dst_slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                  int state_dtype, int io_dtype, const la_ring *ring, const int32_t *ring_base,
+                  const void *q, void *out, float eps, float scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,7 +15,7 @@ _BINDING_NAMES = {
     "kda_prefill_chunked", "gdn_prefill_chunked", "prefill_workspace_bytes",
     "pool_bytes", "version", "LAError", "load_library", "library_path",
     "kda_verify", "gdn_verify", "kda_commit", "gdn_commit", "conv_window_scatter",
-    "state_track_copy", "new_ring",
+    "state_track_copy", "new_ring", "kda_ring_fold", "gdn_ring_fold",
 }
 
 

@@ -70,6 +70,10 @@ def load_library():
         "kda_commit": ([I, P, I, I, I, P, I, P, L, I, I, ctypes.POINTER(LaRing), P, F, P], I),
         "gdn_commit": ([I, P, I, I, I, P, I, P, L, I, I, ctypes.POINTER(LaRing), P, F, P], I),
         "conv_window_scatter": ([I, I, I, P, P, P, P, P, L, I, I, P], I),
+        "kda_ring_fold": ([I, P, I, I, I, P, P, I, P, L, I, I, ctypes.POINTER(LaRing), P, P, P, F,
+                           F, P], I),
+        "gdn_ring_fold": ([I, P, I, I, I, P, P, I, P, L, I, I, ctypes.POINTER(LaRing), P, P, P, F,
+                           F, P], I),
         "state_track_copy": ([I, P, P, P, P, L, L, I, P, L, L, I, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -353,3 +357,34 @@ def state_track_copy(src, dst, conv_pool, ssm_pool, mask=None):
         _ptr(conv_pool), conv_pool.stride(0), crow, _dtype(conv_pool), _ptr(ssm_pool),
         ssm_pool.stride(0), srow, _dtype(ssm_pool), ssm_pool.shape[0],
         _stream(ssm_pool.device)))
+
+
+def _fold(kda, m, slots, ssm_pool, ring, ring_base, dst=None, q=None, out=None, eps=1e-6,
+          scale=1.0):
+    rows, Hv, dv, dk = ssm_pool.shape
+    sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    B = slots.shape[0]
+    if q is not None and out is None:
+        out = torch.empty((B, Hv, dv), dtype=q.dtype, device=q.device)
+    r = _ring_struct(ring)
+    fn = load_library().kda_ring_fold if kda else load_library().gdn_ring_fold
+    _check(fn(B, _ptr(_contig(m, "m")), Hv, dk, dv, _ptr(_contig(slots, "slots")),
+              _ptr(dst if dst is None else _contig(dst, "dst")), rows, _ptr(ssm_pool), sstride,
+              _dtype(ssm_pool), _dtype(ring["d"]), ctypes.byref(r),
+              _ptr(_contig(ring_base, "ring_base")), _ptr(q if q is None else _contig(q, "q")),
+              _ptr(out), eps, scale, _stream(ssm_pool.device)))
+    return out
+
+
+def kda_ring_fold(m, slots, ssm_pool, ring, ring_base, dst=None, q=None, out=None, eps=1e-6,
+                  scale=1.0):
+    """ReplaySSM fast rebuild: folds m[b] ring steps (d, k, g) into the
+    checkpoint rows slots[b], storing the state to rows dst[b] (None: in
+    place); with q [B, Hv, dk] returns out = scale S_m q_hat."""
+    return _fold(True, m, slots, ssm_pool, ring, ring_base, dst, q, out, eps, scale)
+
+
+def gdn_ring_fold(m, slots, ssm_pool, ring, ring_base, dst=None, q=None, out=None, eps=1e-6,
+                  scale=1.0):
+    """GDN fast rebuild; as :func:`kda_ring_fold`."""
+    return _fold(False, m, slots, ssm_pool, ring, ring_base, dst, q, out, eps, scale)

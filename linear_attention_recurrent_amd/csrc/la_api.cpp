@@ -307,6 +307,43 @@ int commit_common(bool kda, int B, const int32_t *accepted, int Hv, int dk, int 
     return hip_status(la::launch_commit(a, state_dtype, kda, st), fn);
 }
 
+
+int fold_common(bool kda, int B, const int32_t *m, int Hv, int dk, int dv, const int32_t *slots,
+                const int32_t *dst_slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                int state_dtype, int io_dtype, const la_ring *ring, const int32_t *ring_base,
+                const void *q, void *out, float eps, float scale, void *stream)
+{
+    const char *fn = kda ? "kda_ring_fold" : "gdn_ring_fold";
+    if (B < 0 || Hv <= 0 || num_rows <= 0)
+        return fail(LA_ERR_ARG, "%s: dimensions must be positive (B >= 0)", fn);
+    if (!valid_dtype(io_dtype) || !valid_dtype(state_dtype))
+        return fail(LA_ERR_UNSUPPORTED, "%s: dtype codes must be LA_F32 or LA_BF16", fn);
+    if (dk != 128 || dv != 128)
+        return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);
+    if (B == 0) return ok();
+    if (int rc = check_ring(ring, 1, fn)) return rc;
+    if (!m || !slots || !ssm_pool || !ring_base || (!q) != (!out))
+        return fail(LA_ERR_ARG, "%s: null pointer argument (q and out go together)", fn);
+    const void *ptrs[] = {m, slots, dst_slots, ssm_pool, ring_base, q, out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (ssm_slot_stride < (int64_t)Hv * dv * dk || (ssm_slot_stride * dsize(state_dtype)) % 16)
+        return fail(LA_ERR_ARG, "%s: ssm_slot_stride %lld too small or misaligned", fn,
+                    (long long)ssm_slot_stride);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (checked_mode()) {
+        std::vector<int32_t> hs;
+        if (int rc = fetch_i32(dst_slots ? dst_slots : slots, B, hs, st)) return rc;
+        if (int rc = check_slots(hs, num_rows, false, "dst_slots")) return rc;
+    }
+    la::FoldArgs a{};
+    a.B = B; a.Hv = Hv; a.m = m; a.slots = slots; a.dst = dst_slots; a.num_rows = num_rows;
+    a.ssm_pool = ssm_pool; a.ssm_stride = ssm_slot_stride; a.io_dtype = io_dtype;
+    a.ring = ring_args(ring); a.ring_base = ring_base; a.q = q; a.out = out; a.eps = eps;
+    a.scale = scale;
+    return hip_status(la::launch_fold(a, state_dtype, kda, st), fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -568,5 +605,25 @@ int state_track_copy(int B, const uint8_t *mask, const int32_t *src, const int32
     a.ssm_stride_b = ssm_slot_stride * dsize(state_dtype); a.ssm_row_b = srow;
     a.num_rows = num_rows;
     return hip_status(la::launch_track_copy(a, st), fn);
+}
+
+int kda_ring_fold(int B, const int32_t *m, int H_v, int d_k, int d_v, const int32_t *slots,
+                  const int32_t *dst_slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                  int state_dtype, int io_dtype, const la_ring *ring, const int32_t *ring_base,
+                  const void *q, void *out, float eps, float scale, void *stream)
+{
+    return fold_common(true, B, m, H_v, d_k, d_v, slots, dst_slots, num_rows, ssm_pool,
+                       ssm_slot_stride, state_dtype, io_dtype, ring, ring_base, q, out, eps, scale,
+                       stream);
+}
+
+int gdn_ring_fold(int B, const int32_t *m, int H_v, int d_k, int d_v, const int32_t *slots,
+                  const int32_t *dst_slots, int num_rows, void *ssm_pool, int64_t ssm_slot_stride,
+                  int state_dtype, int io_dtype, const la_ring *ring, const int32_t *ring_base,
+                  const void *q, void *out, float eps, float scale, void *stream)
+{
+    return fold_common(false, B, m, H_v, d_k, d_v, slots, dst_slots, num_rows, ssm_pool,
+                       ssm_slot_stride, state_dtype, io_dtype, ring, ring_base, q, out, eps, scale,
+                       stream);
 }
 }  // extern "C"

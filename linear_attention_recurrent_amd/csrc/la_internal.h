@@ -143,4 +143,20 @@ struct TrackArgs {
 };
 hipError_t launch_track_copy(const TrackArgs &a, hipStream_t stream);
 
+
+struct FoldArgs {
+    int B, Hv;
+    const int32_t *m, *slots, *dst;  // [B]; dst == nullptr: in place
+    int num_rows;
+    void *ssm_pool;
+    int64_t ssm_stride;
+    int io_dtype;                    // dtype of the ring's vectors, q and out
+    RingArgs ring;
+    const int32_t *ring_base;
+    const void *q;                   // [B, Hv, 128] raw queries or nullptr
+    void *out;                       // [B, Hv, 128] or nullptr
+    float eps, scale;
+};
+hipError_t launch_fold(const FoldArgs &a, int state_dtype, bool kda, hipStream_t stream);
+
 }  // namespace la

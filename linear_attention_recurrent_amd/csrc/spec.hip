@@ -17,7 +17,10 @@
 //              persistent conv state, under a mask;
 //   track   -- the conv and SSM rows of an active slot are copied to a
 //              tracking slot, under a mask (that page's state-tracking
-//              passage).
+//              passage);
+//   fold    -- the fast rebuild: the state after m ring steps from the
+//              checkpoint and the steps' (d, k, g) by the unrolled sum, with
+//              no replay of the delta rule (that page's d/k/g passage).
 // The conv output is rounded to the I/O dtype before the recurrence, as a
 // separate conv kernel's output tensor would be, so the ring holds exactly the
 // values verify used and the commit reproduces verify's arithmetic: both
@@ -347,6 +350,118 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitA
 }
 
 // ---------------------------------------------------------------------------
+// fast rebuild (ring fold)
+// ---------------------------------------------------------------------------
+// S_m = S_0 Diag(exp(G_m)) + sum_j d_j (k_j . exp(G_m - G_j))^T with G_j the
+// cumulative log decay of the first j folded steps: the unrolled sum of the
+// ReplaySSM d/k/g passage, 16 steps per LDS pass (passes compose).
+constexpr int kFold = 16;
+template <typename ST, typename IOT, bool KDA, bool PROJ>
+__global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) fold_kernel(FoldArgs a)
+{
+    using Cfg = DecodeCfg<HD, ST>;
+    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
+    constexpr int VPT = (kFold * HD + NT - 1) / NT;
+    __shared__ float dsh[kFold][HD];  // d_j
+    __shared__ float esh[kFold][HD];  // k_j, then k_j exp(G_end - G_j)
+    __shared__ float gsh[kFold][HD];  // g_j, then G_j
+    __shared__ float eend[HD];        // exp(G_end)
+    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = a.slots[b], dst = a.dst ? a.dst[b] : slot;
+    if (slot < 0 || slot >= a.num_rows || dst < 0 || dst >= a.num_rows) {
+        if constexpr (PROJ)
+            for (int i = tid; i < HD; i += NT) st<IOT>(a.out, ((int64_t)b * a.Hv + h) * HD + i, 0.f);
+        return;
+    }
+    const int m = min(max(a.m[b], 0), a.ring.L);
+    const ST *S0 = static_cast<const ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride +
+                   (int64_t)h * HD * HD;
+    float s[NJ][EPL];
+    {
+        uint4 raw[NJ];
+        load_rows<HD, ST>(raw, S0, wave, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
+    }
+    const int col0 = (lane % LPR) * EPL;
+    const RingArgs &R = a.ring;
+    for (int t0 = 0; t0 < m; t0 += kFold) {
+        const int nc = min(kFold, m - t0);
+        float dv_[VPT], kv[VPT], gv[VPT];
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {  // clamped indices: every load issued, no branch
+            const int i = min(tid + q * NT, kFold * HD - 1);
+            const int pos = (a.ring_base[b] + t0 + min(i / HD, nc - 1)) & (R.L - 1);
+            const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD) + i % HD;
+            dv_[q] = ld<IOT>(R.d, vr);
+            kv[q] = ld<IOT>(R.k, vr);
+            gv[q] = KDA ? R.g[vr] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
+        }
+        __syncthreads();  // the previous pass's tables are no longer read
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            const int i = tid + q * NT;
+            if (i < kFold * HD) {
+                dsh[i / HD][i % HD] = dv_[q];
+                esh[i / HD][i % HD] = kv[q];
+                gsh[i / HD][i % HD] = gv[q];
+            }
+        }
+        __syncthreads();
+        if (tid < HD) {  // per channel: cumulative decay, then the decayed keys
+            float G = 0.f;
+            for (int t = 0; t < nc; ++t) {
+                G += gsh[t][tid];
+                gsh[t][tid] = G;
+            }
+            eend[tid] = fast_exp(G);
+            for (int t = 0; t < nc; ++t) esh[t][tid] *= fast_exp(G - gsh[t][tid]);
+        }
+        __syncthreads();
+        float ee[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ee[e] = eend[col0 + e];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s[j][e] *= ee[e];
+        for (int t = 0; t < nc; ++t) {
+            float kt[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) kt[e] = esh[t][col0 + e];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const float dt = dsh[t][(wave * NJ + j) * RPW + lane / LPR];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s[j][e] = fmaf(dt, kt[e], s[j][e]);
+            }
+        }
+    }
+    ST *Sd = static_cast<ST *>(a.ssm_pool) + (int64_t)dst * a.ssm_stride + (int64_t)h * HD * HD;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int r = (wave * NJ + j) * RPW + lane / LPR;
+        st_stream(Sd + (int64_t)r * HD + col0, Stor<ST>::pack(s[j]));
+    }
+    if constexpr (PROJ) {
+        const int64_t qb = ((int64_t)b * a.Hv + h) * HD;
+        const float inv_q = inv_norm128(ld<IOT>(a.q, qb + lane), ld<IOT>(a.q, qb + lane + 64), a.eps);
+        float qq[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qq[e] = ld<IOT>(a.q, qb + col0 + e) * inv_q;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) p = fmaf(s[j][e], qq[e], p);
+            p = group_sum<LPR>(p);
+            if (lane % LPR == 0) st<IOT>(a.out, qb + (wave * NJ + j) * RPW + lane / LPR, a.scale * p);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // conv-window scatter and state-tracking copy: 16-byte copies
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) conv_scatter_kernel(ScatterArgs a)
@@ -408,7 +523,33 @@ hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <typename ST, typename IOT, bool KDA>
+hipError_t launch_fold_t(const FoldArgs &a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(a.B * a.Hv)), block(DecodeCfg<HD, ST>::NT);
+    if (a.q)
+        hipLaunchKernelGGL((fold_kernel<ST, IOT, KDA, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((fold_kernel<ST, IOT, KDA, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_fold(const FoldArgs &a, int state_dtype, bool kda, hipStream_t stream)
+{
+    const int code = (state_dtype ? 2 : 0) | (a.io_dtype ? 1 : 0);
+    switch (code) {
+    case 0: return kda ? launch_fold_t<float, float, true>(a, stream)
+                       : launch_fold_t<float, float, false>(a, stream);
+    case 1: return kda ? launch_fold_t<float, bf16_t, true>(a, stream)
+                       : launch_fold_t<float, bf16_t, false>(a, stream);
+    case 2: return kda ? launch_fold_t<bf16_t, float, true>(a, stream)
+                       : launch_fold_t<bf16_t, float, false>(a, stream);
+    default: return kda ? launch_fold_t<bf16_t, bf16_t, true>(a, stream)
+                        : launch_fold_t<bf16_t, bf16_t, false>(a, stream);
+    }
+}
 
 hipError_t launch_verify(const VerifyArgs &a, int state_dtype, bool kda, hipStream_t stream)
 {

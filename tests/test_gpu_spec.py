@@ -165,3 +165,42 @@ def test_verify_full_shape_kda_64x12_bf16(dev):
     slots = c["slots"].cpu().numpy()
     p_ref = oracle.commit(accepted, slots, f64(ssm0), ring, base, kda=True, state_dtype="bf16")
     assert_close_units(f64(c["ssm_pool"])[slots], p_ref[slots], 2, "bf16", "committed state")
+
+
+FOLD_CASES = [  # kda, Hqk, Hv, io, state, L, D
+    (True, 2, 2, "bf16", "bf16", 16, 8),
+    (True, 1, 2, "fp32", "fp32", 32, 20),     # two LDS passes (16 + 4 steps)
+    (False, 2, 4, "bf16", "fp32", 16, 8),
+]
+
+
+@pytest.mark.parametrize("kda,Hqk,Hv,io,state,L,D", FOLD_CASES)
+def test_ring_fold_matches_oracle(kda, Hqk, Hv, io, state, L, D, dev):
+    """The fast rebuild of the ring a verify wrote, against the oracle's
+    unrolled sum on the same records: state (in place and to another row)
+    and the projection scale S_m q_hat."""
+    B, P = 4, 10
+    c = make_case(7500 + Hv + L, B, D, Hqk, Hv, kda, io, state, "bf16", P, dev, L=L)
+    base = [0, L - 3, 5, 1]
+    run_verify(kda, c, [D] * B, base, Hqk, dev)
+    ssm0 = c["ssm_pool"].clone()
+    slots = c["slots"].cpu().numpy()
+    m = [D, 3, 0, 5]
+    dst = [int(slots[0]), 0, int(slots[2]), int(slots[3])]   # entry 1 folds into row 0
+    q = synth.to_torch(synth.normal(7501, 0, (B, Hv, D_HEAD)), io, dev)
+    fn = la.kda_ring_fold if kda else la.gdn_ring_fold
+    out = fn(i32(m, dev), c["slots"], c["ssm_pool"], c["ring"], i32(base, dev), dst=i32(dst, dev),
+             q=q, scale=0.75)
+    torch.cuda.synchronize()
+    ring = {k: f64(v) for k, v in c["ring"].items()}
+    p_ref, o_ref = oracle.ring_fold(m, slots, dst, f64(ssm0), ring, base, f64(q), kda=kda,
+                                    state_dtype=state, io_dtype=io, scale=0.75)
+    got = f64(c["ssm_pool"])
+    assert_close_units(got[dst], p_ref[dst], 2, state, "folded state")
+    assert_close_units(f64(out), o_ref, 2, io, "projection")
+    untouched = np.setdiff1d(np.arange(P + 1), dst)
+    np.testing.assert_array_equal(got[untouched], f64(ssm0)[untouched])
+    if io == "fp32":  # exact fp32 records: the fold agrees with the exact replay
+        exact = oracle.commit(m, slots, f64(ssm0), ring, base, kda=kda, state_dtype="fp64")
+        for b in (0, 3):
+            assert_close_units(got[dst[b]], exact[slots[b]], 1, "fp32", "fold vs exact commit")
