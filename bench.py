@@ -403,19 +403,21 @@ def prefill_bench(dev, reps=10):
         t_chunk = [time_graph(lambda i=i: [chunk(i, mode) for _ in range(reps)], reps, 4 * reps,
                               reps)[0] for i in range(4)]
         res_modes[mode] = (t_conv, t_chunk)
-    t_conv, t_chunk = res_modes[0]
+    # primary: the bf16x3 mode (pre-split bf16 operands, fp32 accumulation;
+    # meets 1e-4 on the fp32 end state like the fp32 mode)
+    t_conv, t_chunk = res_modes[1]
     w1_ms = sum(t_conv[:3]) + sum(t_chunk[:3])
     w2_ms = t_conv[3] + t_chunk[3]
-    flops = sum(prefill_mfma_flops(cl[6], H, 0) for cl in calls)
+    flops = sum(prefill_mfma_flops(cl[6], H, 1) for cl in calls)
     chunk_ms = sum(t_chunk)
     tf = flops / (chunk_ms * 1e-3) / 1e12
     conv_bytes = sum(2 * cl[0].numel() * 2 for cl in calls)  # x read + y written, bf16
     conv_gbs = conv_bytes / (sum(t_conv) * 1e-3) / 1e9
-    x3_conv, x3_chunk = res_modes[1]
-    x3_w1 = sum(x3_conv[:3]) + sum(x3_chunk[:3])
-    x3_w2 = x3_conv[3] + x3_chunk[3]
-    x3_flops = sum(prefill_mfma_flops(cl[6], H, 1) for cl in calls)
-    x3_tf = x3_flops / (sum(x3_chunk) * 1e-3) / 1e12
+    f_conv, f_chunk = res_modes[0]
+    f_w1 = sum(f_conv[:3]) + sum(f_chunk[:3])
+    f_w2 = f_conv[3] + f_chunk[3]
+    f_flops = sum(prefill_mfma_flops(cl[6], H, 0) for cl in calls)
+    f_tf = f_flops / (sum(f_chunk) * 1e-3) / 1e12
     T_all = 13600 + 8 * 4096
     res = {
         "tokens_per_s": T_all / ((w1_ms + w2_ms) * 1e-3),
@@ -423,23 +425,25 @@ def prefill_bench(dev, reps=10):
         "w2_8x4096_tokens_per_s": 8 * 4096 / (w2_ms * 1e-3),
         "ms": {"w1_total": w1_ms, "w2_total": w2_ms, "conv_calls": t_conv,
                "chunked_calls": t_chunk},
-        "mode": "fp32 (every intra-block product in fp32 on v_mfma_f32_16x16x4f32)",
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_FP32_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": tf / MFMA_FP32_PEAK_TFS,
+        "mode": "bf16x3 (operands split into bf16 hi + lo, three v_mfma_f32_16x16x32_bf16 "
+                "per 32-deep step, fp32 accumulation)",
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFS,
                      "issued_mfma_flops": flops,
                      "algorithmic_flops": 164e3 * T_all * H,
-                     "note": "prefill kernels only; the chain over 213 dependent blocks of "
-                             "the 13,600-token sequence bounds W1"},
+                     "note": "prefill kernels only; issued flops count the three bf16 products "
+                             "of every split step; the chain over 213 dependent blocks of the "
+                             "13,600-token sequence bounds W1"},
         "conv_roofline": {"bound": "hbm", "achieved": conv_gbs, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS},
-        "bf16x3_mode": {
-            "tokens_per_s": T_all / ((x3_w1 + x3_w2) * 1e-3),
-            "w1_13600_tokens_per_s": 13600 / (x3_w1 * 1e-3),
-            "w2_8x4096_tokens_per_s": 8 * 4096 / (x3_w2 * 1e-3),
-            "chunked_calls_ms": x3_chunk,
-            "roofline": {"bound": "mfma", "achieved": x3_tf, "peak": MFMA_BF16_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": x3_tf / MFMA_BF16_PEAK_TFS,
-                         "issued_mfma_flops": x3_flops},
+        "fp32_mode": {
+            "tokens_per_s": T_all / ((f_w1 + f_w2) * 1e-3),
+            "w1_13600_tokens_per_s": 13600 / (f_w1 * 1e-3),
+            "w2_8x4096_tokens_per_s": 8 * 4096 / (f_w2 * 1e-3),
+            "chunked_calls_ms": f_chunk,
+            "roofline": {"bound": "mfma", "achieved": f_tf, "peak": MFMA_FP32_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": f_tf / MFMA_FP32_PEAK_TFS,
+                         "issued_mfma_flops": f_flops},
         },
         "timing": "each call replayed from a captured HIP graph; W1 = its three conv and "
                   "three chunked calls",

@@ -125,6 +125,24 @@ __device__ __forceinline__ bf16x8_t lo_bf16x8(const float *f, bf16x8_t hi)
     return __builtin_convertvector(v, bf16x8_t);
 }
 
+// bf16x3 operands pre-split in memory: 8 fp32 values as a bf16 "hi" word
+// quad and a bf16 "lo" word quad (hi + lo equals the value to about 2^-16).
+__device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo)
+{
+    const bf16x8_t h = to_bf16x8(f), l = lo_bf16x8(f, h);
+    hi = __builtin_bit_cast(uint4, h);
+    lo = __builtin_bit_cast(uint4, l);
+}
+// Writes the split 8-value group of step m of a lane into a fragment-major
+// block: the hi quad to run 2m, the lo quad to run 2m + 1 (bf16x3 layout).
+__device__ __forceinline__ void store_split(float *blk, int m, int lane, const float *v)
+{
+    uint4 hi, lo;
+    split8(v, hi, lo);
+    *reinterpret_cast<uint4 *>(blk + (2 * m * 64 + lane) * 4) = hi;
+    *reinterpret_cast<uint4 *>(blk + ((2 * m + 1) * 64 + lane) * 4) = lo;
+}
+
 // Elements a lane supplies per instruction, and the k consumed per instruction.
 template <int MODE> struct Step {
     static constexpr int W = MODE == PM_F32 ? 1 : 8;
@@ -363,23 +381,44 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             }
         }
     }
-    for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
-        const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
-        const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
-        const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
-        const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
-        float4 Gs = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (pst[tt] > 0) Gs = *reinterpret_cast<const float4 *>(Gc + (pst[tt] - 1) * LDK + k0);
-        *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
-            make_float4(qn.x * exp_acc(G.x - Gs.x), qn.y * exp_acc(G.y - Gs.y),
-                        qn.z * exp_acc(G.z - Gs.z), qn.w * exp_acc(G.w - Gs.w));
+    if constexpr (MODE == PM_F32) {
+        for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
+            const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
+            const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
+            const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
+            const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
+            float4 Gs = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (pst[tt] > 0) Gs = *reinterpret_cast<const float4 *>(Gc + (pst[tt] - 1) * LDK + k0);
+            *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
+                make_float4(qn.x * exp_acc(G.x - Gs.x), qn.y * exp_acc(G.y - Gs.y),
+                            qn.z * exp_acc(G.z - Gs.z), qn.w * exp_acc(G.w - Gs.w));
+        }
+    } else {  // split layout: thread = (row block I, step m, lane), 8 channels
+        for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+            const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
+            const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
+            const float *gs = pst[tt] > 0 ? Gc + (pst[tt] - 1) * LDK + k0 : nullptr;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e] = Qn[tt * LDK + k0 + e] * exp_acc(Gc[tt * LDK + k0 + e] - (gs ? gs[e] : 0.f));
+            store_split(ws.Qt + bh * kBlkDK + I * 2048, m, ln, v);
+        }
     }
     __syncthreads();
-    for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {  // KhT in fragment order
-        const int cg = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
-        const int c = 16 * cg + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
-        *reinterpret_cast<float4 *>(ws.KhT + bh * kBlkDK + 4 * idx) =
-            *reinterpret_cast<const float4 *>(KhTl + c * LDJ + j0);
+    if constexpr (MODE == PM_F32) {
+        for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {  // KhT in fragment order
+            const int cg = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
+            const int c = 16 * cg + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
+            *reinterpret_cast<float4 *>(ws.KhT + bh * kBlkDK + 4 * idx) =
+                *reinterpret_cast<const float4 *>(KhTl + c * LDJ + j0);
+        }
+    } else {
+        for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+            const int cg = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
+            const int c = 16 * cg + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
+            store_split(ws.KhT + bh * kBlkDK + cg * 1024, m, ln, KhTl + c * LDJ + j0);
+        }
     }
     __syncthreads();
     for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
@@ -455,11 +494,19 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     }
     __syncthreads();
     if (wave >= 4) {  // P to global in fragment order while waves 0..3 run the levels
-        for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
-            const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
-            const int tt = 16 * I + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
-            *reinterpret_cast<float4 *>(ws.P + bh * kBlkCB + 4 * idx) =
-                *reinterpret_cast<const float4 *>(Ps + tt * LDJ + j0);
+        if constexpr (MODE == PM_F32) {
+            for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
+                const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
+                const int tt = 16 * I + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
+                *reinterpret_cast<float4 *>(ws.P + bh * kBlkCB + 4 * idx) =
+                    *reinterpret_cast<const float4 *>(Ps + tt * LDJ + j0);
+            }
+        } else {
+            for (int idx = tid - 256; idx < kBlkCB / 8; idx += 256) {
+                const int I = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
+                const int tt = 16 * I + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
+                store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
+            }
         }
     }
     float *ws16 = scr + wave * 16 * 17;
@@ -546,11 +593,19 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
-        const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
-        const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
-        *reinterpret_cast<float4 *>(ws.W + bh * kBlkDK + 4 * idx) =
-            *reinterpret_cast<const float4 *>(Wst + tt * LDK + k0);
+    if constexpr (MODE == PM_F32) {
+        for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
+            const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
+            const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
+            *reinterpret_cast<float4 *>(ws.W + bh * kBlkDK + 4 * idx) =
+                *reinterpret_cast<const float4 *>(Wst + tt * LDK + k0);
+        }
+    } else {
+        for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+            const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
+            const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
+            store_split(ws.W + bh * kBlkDK + I * 2048, m, ln, Wst + tt * LDK + k0);
+        }
     }
 }
 
@@ -559,8 +614,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 // Waves 0..3 ("row waves") own token rows 16I.. of D and O; waves 4..7
 // ("column waves") own state columns 32(w-4) .. 32(w-4) + 31 of the update.
 // All of a tile's operands are loaded into registers while the previous tile
-// computes, and the state slice is double-buffered in LDS, so a tile costs
-// two barriers: D, then the output and the new state side by side.
+// computes (ping-pong buffers), and the state slice is double-buffered in LDS,
+// so a tile costs two barriers: D, then the output and the new state side by
+// side.
 // ---------------------------------------------------------------------------
 constexpr int kChainThreads = 512;
 constexpr size_t kChainLds = (2 * 16 * LDK + 16 * LDJ) * sizeof(float);
@@ -606,6 +662,11 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
 
     const int tb0 = start / CB, tb1 = end > start ? (end - 1) / CB : tb0 - 1;
     const int ntiles = tb1 - tb0 + 1;  // 0 for an empty sequence
+    // Both roles run the same barrier sequence: two per block.  The block loop
+    // is unrolled by two over a pair of operand buffers (ping-pong), so the
+    // loads for block it + 1, issued as block it starts, are first waited for
+    // when block it + 1 computes.  Full 64-token blocks (the common case) skip
+    // the piece masks.
     if (wave < 4) {
         auto load_ops = [&](int tb, float *ops) {
             const int64_t bh = (int64_t)tb * a.Hv + h;
@@ -614,20 +675,23 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
             load_run(ops + 36, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
             load_run(ops + 68, ws.P + bh * kBlkCB + fidx(4 * I, 0), 4, lane);
         };
-        float cur[kRowOps], nxt[kRowOps];
-        if (ntiles > 0) load_ops(tb0, cur);
-        for (int it = 0; it < ntiles; ++it) {
+        auto block = [&](int it, const float *cur) {
             const int tb = tb0 + it, base = tb * CB;
             const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
-            load_ops(min(tb + 1, tb1), nxt);  // next tile (the last one reloads itself)
-            __syncthreads();                   // state slice in place, last D^T consumed
+            const bool full = p0 == 0 && p1 == CB;
+            __syncthreads();  // state slice in place, last D^T consumed
             const float *Srow = Sbuf + (it & 1) * 16 * LDK + li * LDK, *Drow = Dt + li * LDJ;
             auto lds_s = [&](int, int c) { return Srow[c]; };
             // D = U - W S^T, rows outside the piece masked
-            const int ti = 16 * I + li;
-            const bool in_i = ti >= p0 && ti < p1;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            mma_gen<MODE, DK>(acc, lq, [&](int idx, int) { return in_i ? cur[idx] : 0.f; }, lds_s);
+            if (full) {
+                mma_gen<MODE, DK>(acc, lq, [&](int idx, int) { return cur[idx]; }, lds_s);
+            } else {
+                const int ti = 16 * I + li;
+                const bool in_i = ti >= p0 && ti < p1;
+                mma_gen<MODE, DK>(acc, lq, [&](int idx, int) { return in_i ? cur[idx] : 0.f; },
+                                  lds_s);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tr = 16 * I + 4 * lq + r;
@@ -647,8 +711,15 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
                     st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + 16 * rs + li,
                             a.scale * acc[r]);
             }
-#pragma unroll
-            for (int i = 0; i < kRowOps; ++i) cur[i] = nxt[i];
+        };
+        float bufA[kRowOps], bufB[kRowOps];
+        if (ntiles > 0) load_ops(tb0, bufA);
+        for (int it = 0; it < ntiles; it += 2) {
+            load_ops(min(tb0 + it + 1, tb1), bufB);
+            block(it, bufA);
+            if (it + 1 >= ntiles) break;
+            load_ops(min(tb0 + it + 2, tb1), bufA);
+            block(it + 1, bufB);
         }
     } else {
         auto load_ops = [&](int tb, float *ops) {
@@ -662,34 +733,49 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
                 ops[32 + q] = ws.Ge[((int64_t)pend * a.Hv + h) * DK + c];
             }
         };
-        float cur[kColOps], nxt[kColOps];
-        if (ntiles > 0) load_ops(tb0, cur);
-        for (int it = 0; it < ntiles; ++it) {
+        auto block = [&](int it, const float *cur) {
             const int tb = tb0 + it, base = tb * CB;
             const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
-            load_ops(min(tb + 1, tb1), nxt);
-            __syncthreads();
-            __syncthreads();  // D^T complete
-            // new state columns: S Gamma_L + D^T K^  (K^ columns outside the piece masked)
+            const bool full = p0 == 0 && p1 == CB;
             const float *Scur = Sbuf + (it & 1) * 16 * LDK;
             float *Snext = Sbuf + ((it & 1) ^ 1) * 16 * LDK;
             const float *Drow = Dt + li * LDJ;
+            __syncthreads();
+            float sc[2][4];  // this lane's old state entries, read while D is formed
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sc[q][r] = Scur[(4 * lq + r) * LDK + 32 * I + 16 * q + li];
+            __syncthreads();  // D^T complete
+            // new state columns: S Gamma_L + D^T K^  (K^ columns outside the piece masked)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                mma_gen<MODE, CB>(acc, lq, [&](int, int j) { return Drow[j]; },
-                                  [&](int idx, int j) {
-                                      return (j >= p0 && j < p1) ? cur[16 * q + idx] : 0.f;
-                                  });
+                if (full) {
+                    mma_gen<MODE, CB>(acc, lq, [&](int, int j) { return Drow[j]; },
+                                      [&](int idx, int) { return cur[16 * q + idx]; });
+                } else {
+                    mma_gen<MODE, CB>(acc, lq, [&](int, int j) { return Drow[j]; },
+                                      [&](int idx, int j) {
+                                          return (j >= p0 && j < p1) ? cur[16 * q + idx] : 0.f;
+                                      });
+                }
                 const int c = 32 * I + 16 * q + li;
                 const float gm = exp_acc(cur[32 + q]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Snext[(4 * lq + r) * LDK + c] =
-                        fmaf(Scur[(4 * lq + r) * LDK + c], gm, acc[r]);
+                    Snext[(4 * lq + r) * LDK + c] = fmaf(sc[q][r], gm, acc[r]);
             }
-#pragma unroll
-            for (int i = 0; i < kColOps; ++i) cur[i] = nxt[i];
+        };
+        float bufA[kColOps], bufB[kColOps];
+        if (ntiles > 0) load_ops(tb0, bufA);
+        for (int it = 0; it < ntiles; it += 2) {
+            load_ops(min(tb0 + it + 1, tb1), bufB);
+            block(it, bufA);
+            if (it + 1 >= ntiles) break;
+            load_ops(min(tb0 + it + 2, tb1), bufA);
+            block(it + 1, bufB);
         }
     }
     __syncthreads();
@@ -698,6 +784,194 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
         const int i = idx / DK, c = idx % DK;
         st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c,
                Sfin[i * LDK + c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2, bf16x3 mode: the same chain with every matrix-core operand already
+// split into bf16 hi / lo.  The workspace holds W, Q Gamma, P and the
+// transposed decayed keys split (hi quad in run 2m, lo quad in run 2m + 1 for
+// step m); the state slice is kept in LDS both in fp32 (for the update) and
+// split, and D^T only split.  A 32-deep step is then two 16-byte reads or
+// register quads per operand and three v_mfma_f32_16x16x32_bf16.  Tokens
+// outside the piece need no operand masks: their D rows are stored as zeros
+// and every other operand there is finite.
+// ---------------------------------------------------------------------------
+constexpr int LDKH = DK + 8;   // bf16 row stride of the split state (272 B = 4 mod 32 words)
+constexpr int LDJH = CB + 8;   // bf16 row stride of the split D^T (144 B)
+
+__device__ __forceinline__ bf16x8_t quad8(const float *w)
+{
+    return __builtin_bit_cast(bf16x8_t, make_uint4(__float_as_uint(w[0]), __float_as_uint(w[1]),
+                                                   __float_as_uint(w[2]), __float_as_uint(w[3])));
+}
+__device__ __forceinline__ bf16x8_t lds8(const bf16_t *p)
+{
+    return *reinterpret_cast<const bf16x8_t *>(p);
+}
+__device__ __forceinline__ void mma3(f32x4 &acc, bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void split1(float v, bf16_t &hi, bf16_t &lo)
+{
+    hi = f32_to_bf16(v);
+    lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+template <typename IOT, typename ST>
+__global__ void __launch_bounds__(kChainThreads) prefill_chain_x3_kernel(PrefillArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float Sf[2][16][LDK];          // fp32 state slice
+    __shared__ __attribute__((aligned(16))) bf16_t SH[2][16][LDKH], SL[2][16][LDKH];
+    __shared__ __attribute__((aligned(16))) bf16_t DH[16][LDJH], DL[16][LDJH];
+
+    const int n = blockIdx.x, h = blockIdx.y, rs = blockIdx.z;  // rows 16 rs .. 16 rs + 15
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int I = wave & 3;
+    const Ws ws = ws_layout(a.ws, a.T, a.Hv);
+    const int start = a.cu[n], end = a.cu[n + 1];
+    const int si = a.slot_in[n], so = a.slot_out[n];
+
+    if (si >= a.num_rows || so < 0 || so >= a.num_rows) {  // skipped sequence
+        for (int idx = tid; idx < (end - start) * 16; idx += kChainThreads) {
+            const int t = start + idx / 16, c = 16 * rs + idx % 16;
+            st<IOT>(a.out, ((int64_t)t * a.Hv + h) * DK + c, 0.f);
+        }
+        return;
+    }
+    for (int idx = tid; idx < 16 * DK; idx += kChainThreads) {  // initial state slice
+        const int i = idx / DK, c = idx % DK;
+        float v = 0.f;
+        if (si >= 0)
+            v = ld<ST>(a.ssm_pool,
+                       (int64_t)si * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c);
+        Sf[0][i][c] = v;
+        split1(v, SH[0][i][c], SL[0][i][c]);
+    }
+
+    const int tb0 = start / CB, tb1 = end > start ? (end - 1) / CB : tb0 - 1;
+    const int ntiles = tb1 - tb0 + 1;
+    if (wave < 4) {
+        auto load_ops = [&](int tb, float *ops) {
+            const int64_t bh = (int64_t)tb * a.Hv + h;
+            load_run(ops, ws.W + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            load_run(ops + 32, ws.U + bh * kBlkDK + fidx(8 * I + rs, 0), 1, lane);
+            load_run(ops + 36, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            load_run(ops + 68, ws.P + bh * kBlkCB + fidx(4 * I, 0), 4, lane);
+        };
+        auto block = [&](int it, const float *cur) {
+            const int tb = tb0 + it, base = tb * CB;
+            const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
+            const int b = it & 1;
+            __syncthreads();  // state slice in place, last D^T consumed
+            // D = U - W S^T  (ops words [8m, 8m+4) hi, [8m+4, 8m+8) lo)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                mma3(acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4),
+                     lds8(&SH[b][li][32 * m + 8 * lq]), lds8(&SL[b][li][32 * m + 8 * lq]));
+            {
+                float d[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = 16 * I + 4 * lq + r;
+                    d[r] = (tr >= p0 && tr < p1) ? cur[32 + r] - acc[r] : 0.f;
+                }
+                bf16_t hi[4], lo[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) split1(d[r], hi[r], lo[r]);
+                const int c0 = 16 * I + 4 * lq;
+                *reinterpret_cast<uint2 *>(&DH[li][c0]) =
+                    make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
+                *reinterpret_cast<uint2 *>(&DL[li][c0]) =
+                    make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+            }
+            __syncthreads();  // D^T complete
+            // O = scale (Q Gamma S^T + P D)
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                mma3(acc, quad8(cur + 36 + 8 * m), quad8(cur + 36 + 8 * m + 4),
+                     lds8(&SH[b][li][32 * m + 8 * lq]), lds8(&SL[b][li][32 * m + 8 * lq]));
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                mma3(acc, quad8(cur + 68 + 8 * m), quad8(cur + 68 + 8 * m + 4),
+                     lds8(&DH[li][32 * m + 8 * lq]), lds8(&DL[li][32 * m + 8 * lq]));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tr = 16 * I + 4 * lq + r;
+                if (tr >= p0 && tr < p1)
+                    st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + 16 * rs + li,
+                            a.scale * acc[r]);
+            }
+        };
+        float bufA[kRowOps], bufB[kRowOps];
+        if (ntiles > 0) load_ops(tb0, bufA);
+        for (int it = 0; it < ntiles; it += 2) {
+            load_ops(min(tb0 + it + 1, tb1), bufB);
+            block(it, bufA);
+            if (it + 1 >= ntiles) break;
+            load_ops(min(tb0 + it + 2, tb1), bufA);
+            block(it + 1, bufB);
+        }
+    } else {
+        auto load_ops = [&](int tb, float *ops) {
+            const int pend = min(end, tb * CB + CB) - 1;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = 32 * I + 16 * q + li;
+                load_run(ops + 16 * q,
+                         ws.KhT + ((int64_t)tb * a.Hv + h) * kBlkDK + fidx(4 * (2 * I + q), 0), 4,
+                         lane);
+                ops[32 + q] = ws.Ge[((int64_t)pend * a.Hv + h) * DK + c];
+            }
+        };
+        auto block = [&](int it, const float *cur) {
+            const int b = it & 1;
+            __syncthreads();
+            float sc[2][4];  // this lane's old state entries, read while D is formed
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[q][r] = Sf[b][4 * lq + r][32 * I + 16 * q + li];
+            __syncthreads();  // D^T complete
+            // new state columns: S Gamma_L + D^T K^
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    mma3(acc, lds8(&DH[li][32 * m + 8 * lq]), lds8(&DL[li][32 * m + 8 * lq]),
+                         quad8(cur + 16 * q + 8 * m), quad8(cur + 16 * q + 8 * m + 4));
+                const int c = 32 * I + 16 * q + li;
+                const float gm = exp_acc(cur[32 + q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = fmaf(sc[q][r], gm, acc[r]);
+                    Sf[b ^ 1][4 * lq + r][c] = v;
+                    split1(v, SH[b ^ 1][4 * lq + r][c], SL[b ^ 1][4 * lq + r][c]);
+                }
+            }
+        };
+        float bufA[kColOps], bufB[kColOps];
+        if (ntiles > 0) load_ops(tb0, bufA);
+        for (int it = 0; it < ntiles; it += 2) {
+            load_ops(min(tb0 + it + 1, tb1), bufB);
+            block(it, bufA);
+            if (it + 1 >= ntiles) break;
+            load_ops(min(tb0 + it + 2, tb1), bufA);
+            block(it + 1, bufB);
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 16 * DK; idx += kChainThreads) {
+        const int i = idx / DK, c = idx % DK;
+        st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c,
+               Sf[ntiles & 1][i][c]);
     }
 }
 
@@ -724,8 +998,12 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
         if (e != hipSuccess) return e;
     }
     const dim3 g2((unsigned)a.N, (unsigned)a.Hv, (unsigned)(DK / 16));
-    hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), g2, dim3(kChainThreads), kChainLds,
-                       stream, a);
+    if constexpr (MODE == PM_F32)
+        hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), g2, dim3(kChainThreads),
+                           kChainLds, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST>), g2, dim3(kChainThreads), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
