@@ -821,8 +821,12 @@ __device__ __forceinline__ void split1(float v, bf16_t &hi, bf16_t &lo)
     lo = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
-template <typename IOT, typename ST>
-__global__ void __launch_bounds__(kChainThreads) prefill_chain_x3_kernel(PrefillArgs a)
+// PF: operands of the next block prefetched into a second register buffer
+// (for launches with few workgroups); without it the kernel fits two
+// workgroups per CU, which then hide each other's operand loads (for launches
+// with many sequences).
+template <typename IOT, typename ST, bool PF>
+__global__ void __launch_bounds__(kChainThreads, PF ? 2 : 4) prefill_chain_x3_kernel(PrefillArgs a)
 {
     __shared__ __attribute__((aligned(16))) float Sf[2][16][LDK];          // fp32 state slice
     __shared__ __attribute__((aligned(16))) bf16_t SH[2][16][LDKH], SL[2][16][LDKH];
@@ -909,14 +913,22 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_x3_kernel(Prefill
                             a.scale * acc[r]);
             }
         };
-        float bufA[kRowOps], bufB[kRowOps];
-        if (ntiles > 0) load_ops(tb0, bufA);
-        for (int it = 0; it < ntiles; it += 2) {
-            load_ops(min(tb0 + it + 1, tb1), bufB);
-            block(it, bufA);
-            if (it + 1 >= ntiles) break;
-            load_ops(min(tb0 + it + 2, tb1), bufA);
-            block(it + 1, bufB);
+        if constexpr (PF) {
+            float bufA[kRowOps], bufB[kRowOps];
+            if (ntiles > 0) load_ops(tb0, bufA);
+            for (int it = 0; it < ntiles; it += 2) {
+                load_ops(min(tb0 + it + 1, tb1), bufB);
+                block(it, bufA);
+                if (it + 1 >= ntiles) break;
+                load_ops(min(tb0 + it + 2, tb1), bufA);
+                block(it + 1, bufB);
+            }
+        } else {
+            float buf[kRowOps];
+            for (int it = 0; it < ntiles; ++it) {
+                load_ops(tb0 + it, buf);
+                block(it, buf);
+            }
         }
     } else {
         auto load_ops = [&](int tb, float *ops) {
@@ -957,14 +969,22 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_x3_kernel(Prefill
                 }
             }
         };
-        float bufA[kColOps], bufB[kColOps];
-        if (ntiles > 0) load_ops(tb0, bufA);
-        for (int it = 0; it < ntiles; it += 2) {
-            load_ops(min(tb0 + it + 1, tb1), bufB);
-            block(it, bufA);
-            if (it + 1 >= ntiles) break;
-            load_ops(min(tb0 + it + 2, tb1), bufA);
-            block(it + 1, bufB);
+        if constexpr (PF) {
+            float bufA[kColOps], bufB[kColOps];
+            if (ntiles > 0) load_ops(tb0, bufA);
+            for (int it = 0; it < ntiles; it += 2) {
+                load_ops(min(tb0 + it + 1, tb1), bufB);
+                block(it, bufA);
+                if (it + 1 >= ntiles) break;
+                load_ops(min(tb0 + it + 2, tb1), bufA);
+                block(it + 1, bufB);
+            }
+        } else {
+            float buf[kColOps];
+            for (int it = 0; it < ntiles; ++it) {
+                load_ops(tb0 + it, buf);
+                block(it, buf);
+            }
         }
     }
     __syncthreads();
@@ -1001,9 +1021,12 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     if constexpr (MODE == PM_F32)
         hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), g2, dim3(kChainThreads),
                            kChainLds, stream, a);
-    else
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST>), g2, dim3(kChainThreads), 0, stream,
-                           a);
+    else if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: prefetch
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, true>), g2, dim3(kChainThreads), 0,
+                           stream, a);
+    else  // many: two workgroups per CU
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, false>), g2, dim3(kChainThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
