@@ -822,37 +822,40 @@ __device__ __forceinline__ void split1(float v, bf16_t &hi, bf16_t &lo)
 }
 
 // PF: operands of the next block prefetched into a second register buffer
-// (for launches with few workgroups); without it the kernel fits two
-// workgroups per CU, which then hide each other's operand loads (for launches
-// with many sequences).
-template <typename IOT, typename ST, bool PF>
-__global__ void __launch_bounds__(kChainThreads, PF ? 2 : 4) prefill_chain_x3_kernel(PrefillArgs a)
+// (for launches with few workgroups).  NSL: 16-row state slices per
+// workgroup; with NSL = 2 every operand fragment loaded serves twice the
+// matrix work, halving the operand traffic per unit of work (for launches with
+// many sequences, where that traffic between L2 and the CUs is the limit).
+template <typename IOT, typename ST, bool PF, int NSL>
+__global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_kernel(PrefillArgs a)
 {
-    __shared__ __attribute__((aligned(16))) float Sf[2][16][LDK];          // fp32 state slice
-    __shared__ __attribute__((aligned(16))) bf16_t SH[2][16][LDKH], SL[2][16][LDKH];
-    __shared__ __attribute__((aligned(16))) bf16_t DH[16][LDJH], DL[16][LDJH];
+    constexpr int NR = 16 * NSL;  // state rows of the workgroup
+    constexpr int kRowOpsN = 80 + 4 * NSL;  // W 32, Q Gamma 32, P 16, U 4 per slice
+    __shared__ __attribute__((aligned(16))) float Sf[2][NR][LDK];          // fp32 state rows
+    __shared__ __attribute__((aligned(16))) bf16_t SH[2][NR][LDKH], SL[2][NR][LDKH];
+    __shared__ __attribute__((aligned(16))) bf16_t DH[NR][LDJH], DL[NR][LDJH];
 
-    const int n = blockIdx.x, h = blockIdx.y, rs = blockIdx.z;  // rows 16 rs .. 16 rs + 15
+    const int n = blockIdx.x, h = blockIdx.y, rs = blockIdx.z;  // rows NR rs .. NR rs + NR - 1
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int I = wave & 3;
     const Ws ws = ws_layout(a.ws, a.T, a.Hv);
     const int start = a.cu[n], end = a.cu[n + 1];
     const int si = a.slot_in[n], so = a.slot_out[n];
+    const int row0 = NR * rs;
 
     if (si >= a.num_rows || so < 0 || so >= a.num_rows) {  // skipped sequence
-        for (int idx = tid; idx < (end - start) * 16; idx += kChainThreads) {
-            const int t = start + idx / 16, c = 16 * rs + idx % 16;
+        for (int idx = tid; idx < (end - start) * NR; idx += kChainThreads) {
+            const int t = start + idx / NR, c = row0 + idx % NR;
             st<IOT>(a.out, ((int64_t)t * a.Hv + h) * DK + c, 0.f);
         }
         return;
     }
-    for (int idx = tid; idx < 16 * DK; idx += kChainThreads) {  // initial state slice
+    for (int idx = tid; idx < NR * DK; idx += kChainThreads) {  // initial state rows
         const int i = idx / DK, c = idx % DK;
         float v = 0.f;
         if (si >= 0)
-            v = ld<ST>(a.ssm_pool,
-                       (int64_t)si * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c);
+            v = ld<ST>(a.ssm_pool, (int64_t)si * a.ssm_stride + ((int64_t)h * DK + row0 + i) * DK + c);
         Sf[0][i][c] = v;
         split1(v, SH[0][i][c], SL[0][i][c]);
     }
@@ -863,58 +866,67 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 4) prefill_chain_x3_ke
         auto load_ops = [&](int tb, float *ops) {
             const int64_t bh = (int64_t)tb * a.Hv + h;
             load_run(ops, ws.W + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
-            load_run(ops + 32, ws.U + bh * kBlkDK + fidx(8 * I + rs, 0), 1, lane);
-            load_run(ops + 36, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
-            load_run(ops + 68, ws.P + bh * kBlkCB + fidx(4 * I, 0), 4, lane);
+            load_run(ops + 32, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            load_run(ops + 64, ws.P + bh * kBlkCB + fidx(4 * I, 0), 4, lane);
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl)
+                load_run(ops + 80 + 4 * sl, ws.U + bh * kBlkDK + fidx(8 * I + NSL * rs + sl, 0), 1,
+                         lane);
         };
         auto block = [&](int it, const float *cur) {
             const int tb = tb0 + it, base = tb * CB;
             const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
             const int b = it & 1;
-            __syncthreads();  // state slice in place, last D^T consumed
-            // D = U - W S^T  (ops words [8m, 8m+4) hi, [8m+4, 8m+8) lo)
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            __syncthreads();  // state rows in place, last D^T consumed
+            // D = U - W S^T for each slice (ops words [8m, 8m+4) hi, [8m+4, 8m+8) lo)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                mma3(acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4),
-                     lds8(&SH[b][li][32 * m + 8 * lq]), lds8(&SL[b][li][32 * m + 8 * lq]));
-            {
+            for (int sl = 0; sl < NSL; ++sl) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const int sr = 16 * sl + li;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    mma3(acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4),
+                         lds8(&SH[b][sr][32 * m + 8 * lq]), lds8(&SL[b][sr][32 * m + 8 * lq]));
                 float d[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 16 * I + 4 * lq + r;
-                    d[r] = (tr >= p0 && tr < p1) ? cur[32 + r] - acc[r] : 0.f;
+                    d[r] = (tr >= p0 && tr < p1) ? cur[80 + 4 * sl + r] - acc[r] : 0.f;
                 }
                 bf16_t hi[4], lo[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) split1(d[r], hi[r], lo[r]);
                 const int c0 = 16 * I + 4 * lq;
-                *reinterpret_cast<uint2 *>(&DH[li][c0]) =
+                *reinterpret_cast<uint2 *>(&DH[sr][c0]) =
                     make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
-                *reinterpret_cast<uint2 *>(&DL[li][c0]) =
+                *reinterpret_cast<uint2 *>(&DL[sr][c0]) =
                     make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
             }
             __syncthreads();  // D^T complete
-            // O = scale (Q Gamma S^T + P D)
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            // O = scale (Q Gamma S^T + P D) for each slice
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                mma3(acc, quad8(cur + 36 + 8 * m), quad8(cur + 36 + 8 * m + 4),
-                     lds8(&SH[b][li][32 * m + 8 * lq]), lds8(&SL[b][li][32 * m + 8 * lq]));
+            for (int sl = 0; sl < NSL; ++sl) {
+                const int sr = 16 * sl + li;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                mma3(acc, quad8(cur + 68 + 8 * m), quad8(cur + 68 + 8 * m + 4),
-                     lds8(&DH[li][32 * m + 8 * lq]), lds8(&DL[li][32 * m + 8 * lq]));
+                for (int m = 0; m < 4; ++m)
+                    mma3(acc, quad8(cur + 32 + 8 * m), quad8(cur + 32 + 8 * m + 4),
+                         lds8(&SH[b][sr][32 * m + 8 * lq]), lds8(&SL[b][sr][32 * m + 8 * lq]));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tr = 16 * I + 4 * lq + r;
-                if (tr >= p0 && tr < p1)
-                    st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + 16 * rs + li,
-                            a.scale * acc[r]);
+                for (int m = 0; m < 2; ++m)
+                    mma3(acc, quad8(cur + 64 + 8 * m), quad8(cur + 64 + 8 * m + 4),
+                         lds8(&DH[sr][32 * m + 8 * lq]), lds8(&DL[sr][32 * m + 8 * lq]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = 16 * I + 4 * lq + r;
+                    if (tr >= p0 && tr < p1)
+                        st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + row0 + sr,
+                                a.scale * acc[r]);
+                }
             }
         };
         if constexpr (PF) {
-            float bufA[kRowOps], bufB[kRowOps];
+            float bufA[kRowOpsN], bufB[kRowOpsN];
             if (ntiles > 0) load_ops(tb0, bufA);
             for (int it = 0; it < ntiles; it += 2) {
                 load_ops(min(tb0 + it + 1, tb1), bufB);
@@ -924,7 +936,7 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 4) prefill_chain_x3_ke
                 block(it + 1, bufB);
             }
         } else {
-            float buf[kRowOps];
+            float buf[kRowOpsN];
             for (int it = 0; it < ntiles; ++it) {
                 load_ops(tb0 + it, buf);
                 block(it, buf);
@@ -945,27 +957,35 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 4) prefill_chain_x3_ke
         auto block = [&](int it, const float *cur) {
             const int b = it & 1;
             __syncthreads();
-            float sc[2][4];  // this lane's old state entries, read while D is formed
+            float sc[NSL][2][4];  // this lane's old state entries, read while D is formed
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sc[q][r] = Sf[b][4 * lq + r][32 * I + 16 * q + li];
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sc[sl][q][r] = Sf[b][16 * sl + 4 * lq + r][32 * I + 16 * q + li];
             __syncthreads();  // D^T complete
             // new state columns: S Gamma_L + D^T K^
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    mma3(acc, lds8(&DH[li][32 * m + 8 * lq]), lds8(&DL[li][32 * m + 8 * lq]),
-                         quad8(cur + 16 * q + 8 * m), quad8(cur + 16 * q + 8 * m + 4));
                 const int c = 32 * I + 16 * q + li;
                 const float gm = exp_acc(cur[32 + q]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = fmaf(sc[q][r], gm, acc[r]);
-                    Sf[b ^ 1][4 * lq + r][c] = v;
-                    split1(v, SH[b ^ 1][4 * lq + r][c], SL[b ^ 1][4 * lq + r][c]);
+                for (int sl = 0; sl < NSL; ++sl) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+                        mma3(acc, lds8(&DH[16 * sl + li][32 * m + 8 * lq]),
+                             lds8(&DL[16 * sl + li][32 * m + 8 * lq]),
+                             quad8(cur + 16 * q + 8 * m), quad8(cur + 16 * q + 8 * m + 4));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * sl + 4 * lq + r;
+                        const float v = fmaf(sc[sl][q][r], gm, acc[r]);
+                        Sf[b ^ 1][row][c] = v;
+                        split1(v, SH[b ^ 1][row][c], SL[b ^ 1][row][c]);
+                    }
                 }
             }
         };
@@ -988,9 +1008,9 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 4) prefill_chain_x3_ke
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < 16 * DK; idx += kChainThreads) {
+    for (int idx = tid; idx < NR * DK; idx += kChainThreads) {
         const int i = idx / DK, c = idx % DK;
-        st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + 16 * rs + i) * DK + c,
+        st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + row0 + i) * DK + c,
                Sf[ntiles & 1][i][c]);
     }
 }
@@ -1022,11 +1042,12 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
         hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), g2, dim3(kChainThreads),
                            kChainLds, stream, a);
     else if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: prefetch
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, true>), g2, dim3(kChainThreads), 0,
-                           stream, a);
-    else  // many: two workgroups per CU
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, false>), g2, dim3(kChainThreads), 0,
-                           stream, a);
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, true, 1>), g2, dim3(kChainThreads),
+                           0, stream, a);
+    else  // many: 64 state rows per workgroup
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, false, 4>),
+                           dim3((unsigned)a.N, (unsigned)a.Hv, (unsigned)(DK / 64)),
+                           dim3(kChainThreads), 0, stream, a);
     return hipGetLastError();
 }
 
