@@ -389,6 +389,11 @@ def prefill_bench(dev, reps=10):
         la.kda_prefill_chunked(q, k, v, g, beta, cu, si, so, ssm_pool, out=outs[i], workspace=ws,
                                mode=mode)
 
+    def fused(i, mode=1):
+        x, g, beta, cu, si, so, _ = calls[i]
+        la.kda_prefill_conv(x, g, beta, cu, si, so, ssm_pool, Hqk=H, conv_w=w,
+                            conv_pool=conv_pool, out=outs[i], workspace=ws, mode=mode)
+
     def run_all(mode):
         for i in range(4):
             conv(i)
@@ -403,6 +408,9 @@ def prefill_bench(dev, reps=10):
         t_chunk = [time_graph(lambda i=i: [chunk(i, mode) for _ in range(reps)], reps, 4 * reps,
                               reps)[0] for i in range(4)]
         res_modes[mode] = (t_conv, t_chunk)
+    # the conv fused into the prefill's loads (one call per chunk, bf16x3)
+    t_fused = [time_graph(lambda i=i: [fused(i) for _ in range(reps)], reps, 4 * reps, reps)[0]
+               for i in range(4)]
     # primary: the bf16x3 mode (pre-split bf16 operands, fp32 accumulation;
     # meets 1e-4 on the fp32 end state like the fp32 mode)
     t_conv, t_chunk = res_modes[1]
@@ -444,6 +452,14 @@ def prefill_bench(dev, reps=10):
             "roofline": {"bound": "mfma", "achieved": f_tf, "peak": MFMA_FP32_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": f_tf / MFMA_FP32_PEAK_TFS,
                          "issued_mfma_flops": f_flops},
+        },
+        "fused_conv": {
+            "tokens_per_s": T_all / (sum(t_fused) * 1e-3),
+            "w1_13600_tokens_per_s": 13600 / (sum(t_fused[:3]) * 1e-3),
+            "w2_8x4096_tokens_per_s": 8 * 4096 / (t_fused[3] * 1e-3),
+            "calls_ms": t_fused,
+            "speedup_vs_separate_conv": (w1_ms + w2_ms) / sum(t_fused),
+            "note": "kda_prefill_conv: the short conv inside the prefill's loads, bf16x3 mode",
         },
         "timing": "each call replayed from a captured HIP graph; W1 = its three conv and "
                   "three chunked calls",

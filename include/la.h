@@ -185,6 +185,42 @@ int gdn_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const
                         float scale, int mode, void *workspace, size_t workspace_bytes,
                         void *stream);
 
+/* Chunked prefill with the short conv fused into its loads.  The extend path
+ * of "SGLang之KV Cache内存池机制" (yuyanqi.com) section 8.5 hands the chunked
+ * kernel the mixed q|k|v projections of a varlen batch, with the conv and SSM
+ * state of each request in the same pool slot; here the conv + SiLU of
+ * shortconv_prefill runs inside the prefill's loads instead of as a pass of
+ * its own (no [T, C] conv output is written or read back).
+ *   x [T, C] (io_dtype) pre-conv projections, C = 2 H_qk d_k + H_v d_v,
+ *     channel blocks [Q heads | K heads | V heads] as in kda_decode_step.
+ *   conv_w [C, 4], conv_b [C] or NULL; conv_pool rows [3, C] (conv_dtype)
+ *     at conv_pool + slot * conv_slot_stride, indexed by the same slot_in /
+ *     slot_out as ssm_pool: the history comes from slot_in (zeros when < 0)
+ *     and the last three pre-conv inputs go to slot_out, as in
+ *     shortconv_prefill (slot_in == slot_out is allowed).
+ *   Every other argument is that of kda_prefill_chunked.
+ * The conv activations stay fp32 between the conv and the prefill (the
+ * standalone pair rounds them to io_dtype in between).  Sequences whose
+ * slots are out of range get zero outputs and touch neither pool. */
+int kda_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *x,
+                     int io_dtype, const float *conv_w, const float *conv_b, void *conv_pool,
+                     int64_t conv_slot_stride, int conv_dtype, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const int32_t *slot_in,
+                     const int32_t *slot_out, int num_rows, void *ssm_pool,
+                     int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                     float scale, int mode, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* GDN form of kda_prefill_conv: g [T, H_v]. */
+int gdn_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *x,
+                     int io_dtype, const float *conv_w, const float *conv_b, void *conv_pool,
+                     int64_t conv_slot_stride, int conv_dtype, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const int32_t *slot_in,
+                     const int32_t *slot_out, int num_rows, void *ssm_pool,
+                     int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                     float scale, int mode, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* Host call: workspace bytes the prefill needs for N sequences and T tokens
  * (0 for invalid arguments). */
 size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode);

@@ -62,6 +62,10 @@ def load_library():
                                  P, F, F, I, P, Z, P], I),
         "gdn_prefill_chunked": ([I, I, I, I, I, I, P, L, P, L, P, L, I, P, P, P, P, P, I, P, L, I,
                                  P, F, F, I, P, Z, P], I),
+        "kda_prefill_conv": ([I, I, I, I, I, I, P, I, P, P, P, L, I, P, P, P, P, P, I, P, L, I,
+                              P, F, F, I, P, Z, P], I),
+        "gdn_prefill_conv": ([I, I, I, I, I, I, P, I, P, P, P, L, I, P, P, P, P, P, I, P, L, I,
+                              P, F, F, I, P, Z, P], I),
         "prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
         "kda_verify": ([I, I, P, I, I, I, I, P, I, P, P, P, L, I, P, P, P, I, P, L, I, P, P,
                         ctypes.POINTER(LaRing), P, F, F, P], I),
@@ -246,6 +250,46 @@ def kda_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_poo
 def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw):
     """Chunked GDN prefill; as :func:`kda_prefill_chunked` with g [T, Hv]."""
     return _prefill(False, q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw)
+
+
+def _prefill_conv(kda, x, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, *, Hqk, conv_w,
+                  conv_pool, conv_b=None, out=None, eps=1e-6, scale=1.0, mode=LA_PREFILL_FP32,
+                  workspace=None):
+    T, C = x.shape
+    _contig(x, "x")
+    rows, Hv, dv, dk = ssm_pool.shape
+    if C != 2 * Hqk * dk + Hv * dv:
+        raise ValueError(f"x has {C} channels, expected 2*Hqk*dk + Hv*dv")
+    N = cu_seqlens.shape[0] - 1
+    sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    cstride = _row_view(conv_pool, (3, C), "conv_pool")
+    out = torch.empty((T, Hv, dv), dtype=x.dtype, device=x.device) if out is None else out
+    need = prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fn = load_library().kda_prefill_conv if kda else load_library().gdn_prefill_conv
+    _check(fn(N, T, Hqk, Hv, dk, dv, _ptr(x), _dtype(x), _ptr(_contig(conv_w, "conv_w")),
+              _ptr(conv_b), _ptr(conv_pool), cstride, _dtype(conv_pool),
+              _ptr(_contig(g, "g")), _ptr(_contig(beta, "beta")),
+              _ptr(_contig(cu_seqlens, "cu_seqlens")), _ptr(_contig(slot_in, "slot_in")),
+              _ptr(_contig(slot_out, "slot_out")), rows, _ptr(ssm_pool), sstride,
+              _dtype(ssm_pool), _ptr(_contig(out, "out")), eps, scale, mode, _ptr(workspace),
+              ws_bytes, _stream(x.device)))
+    return out
+
+
+def kda_prefill_conv(x, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw):
+    """Chunked KDA prefill with the short conv fused into its loads.
+    x [T, C] pre-conv q|k|v projections; conv_w [C, 4]; conv_b [C] or None;
+    conv_pool [P+1, 3, C] (same slots as ssm_pool); Hqk keyword; the rest as
+    :func:`kda_prefill_chunked`.  Returns out [T, Hv, dv]."""
+    return _prefill_conv(True, x, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw)
+
+
+def gdn_prefill_conv(x, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw):
+    """GDN form of :func:`kda_prefill_conv` (g [T, Hv])."""
+    return _prefill_conv(False, x, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, **kw)
 
 
 # ------------------------------------------------------ speculative decode --

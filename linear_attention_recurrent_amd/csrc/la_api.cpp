@@ -139,15 +139,32 @@ int decode_common(bool kda, int B, int Hqk, int Hv, int dk, int dv, const void *
     return hip_status(la::launch_decode(a, dk, state_dtype, kda, st), fn);
 }
 
+// The fused short conv of kda_prefill_conv / gdn_prefill_conv.
+struct ConvIn {
+    const void *x;
+    const float *w, *bias;
+    void *pool;
+    int64_t stride;
+    int dtype;
+};
+
+// cv == nullptr: q, k, v are the post-conv inputs; otherwise they are unused
+// and the conv runs on cv->x inside the prefill.
 int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, const void *q,
                    int64_t q_stride, const void *k, int64_t k_stride, const void *v,
                    int64_t v_stride, int io_dtype, const float *g, const float *beta,
                    const int32_t *cu_seqlens, const int32_t *slot_in, const int32_t *slot_out,
                    int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
                    void *out, float eps, float scale, int mode, void *workspace,
-                   size_t workspace_bytes, void *stream)
+                   size_t workspace_bytes, void *stream, const ConvIn *cv = nullptr)
 {
-    const char *fn = kda ? "kda_prefill_chunked" : "gdn_prefill_chunked";
+    const char *fn = cv ? (kda ? "kda_prefill_conv" : "gdn_prefill_conv")
+                        : (kda ? "kda_prefill_chunked" : "gdn_prefill_chunked");
+    const int64_t C = 2LL * Hqk * dk + (int64_t)Hv * dv;
+    if (cv) {
+        q = k = v = cv->x;
+        q_stride = k_stride = v_stride = C;
+    }
     if (N < 0 || T < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || num_rows <= 0)
         return fail(LA_ERR_ARG, "%s: dimensions must be positive (N, T >= 0)", fn);
     if (Hv % Hqk != 0)
@@ -173,6 +190,18 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
     if (ssm_slot_stride < (int64_t)Hv * dv * dk || (ssm_slot_stride * dsize(state_dtype)) % 16)
         return fail(LA_ERR_ARG, "%s: ssm_slot_stride %lld too small or misaligned", fn,
                     (long long)ssm_slot_stride);
+    if (cv) {
+        if (!valid_dtype(cv->dtype))
+            return fail(LA_ERR_UNSUPPORTED, "%s: conv_dtype must be LA_F32 or LA_BF16", fn);
+        if (!cv->w || !cv->pool) return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
+        const void *cptrs[] = {cv->w, cv->bias, cv->pool};
+        for (const void *p : cptrs)
+            if (p && !aligned16(p))
+                return fail(LA_ERR_ARG, "%s: pointers must be 16-byte aligned", fn);
+        if (cv->stride < 3 * C)
+            return fail(LA_ERR_ARG, "%s: conv_slot_stride must be >= 3 C = %lld", fn,
+                        (long long)(3 * C));
+    }
     const size_t need = la::prefill_ws_bytes(N, T, Hqk, Hv, dk, mode);
     if (need && (!workspace || workspace_bytes < need ||
                  (reinterpret_cast<uintptr_t>(workspace) & 255u)))
@@ -197,7 +226,18 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
     a.ssm_pool = ssm_pool; a.ssm_stride = ssm_slot_stride; a.state_dtype = state_dtype;
     a.out = out; a.eps = eps; a.scale = scale; a.mode = mode; a.kda = kda;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
-    return hip_status(la::launch_prefill(a, st), fn);
+    if (!cv) return hip_status(la::launch_prefill(a, st), fn);
+    a.conv = true; a.x = cv->x; a.C = (int)C; a.w = cv->w; a.bias = cv->bias;
+    a.conv_pool = cv->pool; a.conv_stride = cv->stride; a.conv_dtype = cv->dtype;
+    if (int rc = hip_status(la::launch_prefill(a, st), fn)) return rc;
+    // the hand-off overwrites slot_out's history, so it runs after the
+    // prefill has read slot_in's
+    la::ConvPrefillArgs c{};
+    c.N = N; c.T = T; c.C = (int)C; c.x = cv->x; c.io_dtype = io_dtype;
+    c.cu = cu_seqlens; c.slot_in = slot_in; c.slot_out = slot_out; c.w = cv->w;
+    c.bias = cv->bias; c.conv_pool = cv->pool; c.conv_stride = cv->stride;
+    c.conv_dtype = cv->dtype; c.num_rows = num_rows; c.y = nullptr;
+    return hip_status(la::launch_shortconv_handoff(c, st), fn);
 }
 
 
@@ -481,6 +521,38 @@ int gdn_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const
                           io_dtype, g, beta, cu_seqlens, slot_in, slot_out, num_rows, ssm_pool,
                           ssm_slot_stride, state_dtype, out, eps, scale, mode, workspace,
                           workspace_bytes, stream);
+}
+
+int kda_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *x,
+                     int io_dtype, const float *conv_w, const float *conv_b, void *conv_pool,
+                     int64_t conv_slot_stride, int conv_dtype, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const int32_t *slot_in,
+                     const int32_t *slot_out, int num_rows, void *ssm_pool,
+                     int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                     float scale, int mode, void *workspace, size_t workspace_bytes,
+                     void *stream)
+{
+    const ConvIn cv{x, conv_w, conv_b, conv_pool, conv_slot_stride, conv_dtype};
+    return prefill_common(true, N, T, H_qk, H_v, d_k, d_v, nullptr, 0, nullptr, 0, nullptr, 0,
+                          io_dtype, g, beta, cu_seqlens, slot_in, slot_out, num_rows, ssm_pool,
+                          ssm_slot_stride, state_dtype, out, eps, scale, mode, workspace,
+                          workspace_bytes, stream, &cv);
+}
+
+int gdn_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *x,
+                     int io_dtype, const float *conv_w, const float *conv_b, void *conv_pool,
+                     int64_t conv_slot_stride, int conv_dtype, const float *g,
+                     const float *beta, const int32_t *cu_seqlens, const int32_t *slot_in,
+                     const int32_t *slot_out, int num_rows, void *ssm_pool,
+                     int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
+                     float scale, int mode, void *workspace, size_t workspace_bytes,
+                     void *stream)
+{
+    const ConvIn cv{x, conv_w, conv_b, conv_pool, conv_slot_stride, conv_dtype};
+    return prefill_common(false, N, T, H_qk, H_v, d_k, d_v, nullptr, 0, nullptr, 0, nullptr, 0,
+                          io_dtype, g, beta, cu_seqlens, slot_in, slot_out, num_rows, ssm_pool,
+                          ssm_slot_stride, state_dtype, out, eps, scale, mode, workspace,
+                          workspace_bytes, stream, &cv);
 }
 
 size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)

@@ -55,6 +55,9 @@ struct ConvPrefillArgs {
     void *y;
 };
 hipError_t launch_shortconv_prefill(const ConvPrefillArgs &a, hipStream_t stream);
+// Only the history hand-off of shortconv_prefill (the fused prefill computes
+// the outputs itself).
+hipError_t launch_shortconv_handoff(const ConvPrefillArgs &a, hipStream_t stream);
 
 struct PrefillArgs {
     int N, T, Hqk, Hv, G, D;
@@ -73,6 +76,15 @@ struct PrefillArgs {
     bool kda;
     void *ws;
     size_t ws_bytes;
+    // fused short conv: x holds the pre-conv q|k|v projections [T, C] and the
+    // conv + SiLU runs inside the prefill's loads (q, k, v unused)
+    bool conv;
+    const void *x;
+    int C;
+    const float *w, *bias;
+    const void *conv_pool;
+    int64_t conv_stride;
+    int conv_dtype;
 };
 size_t prefill_ws_bytes(int N, int T, int Hqk, int Hv, int D, int mode);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

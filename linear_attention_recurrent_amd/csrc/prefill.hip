@@ -264,14 +264,81 @@ template <> __device__ __forceinline__ void load16<bf16_t>(float *f, const void 
     }
 }
 
+// Fused short conv (pre-conv projections x [T, C]): conv + SiLU of channel ch
+// for the 16 tile tokens tq .. tq + 15 (tile starting at global token t0).
+// A token's window is rows tok - 3 .. tok of x; positions before its
+// sequence's start sst[tt] come from conv pool row ssl[tt] (< 0: zeros).  The
+// 19 rows slide along the thread's tokens, so every x element is loaded once
+// and the loads are coalesced over channels.  Tap order and sum order are
+// those of the standalone conv kernels.  The caller's wave shares tq, so the
+// per-token sequence data is wave-uniform: a wave whose windows all lie in
+// one sequence takes a branch-free path, the others test token by token.
+__device__ __forceinline__ float conv_tap4(const float4 wc, float bias, float h0, float h1,
+                                           float h2, float x)
+{
+    float acc = bias;
+    acc = fmaf(wc.x, h0, acc);
+    acc = fmaf(wc.y, h1, acc);
+    acc = fmaf(wc.z, h2, acc);
+    acc = fmaf(wc.w, x, acc);
+    return silu(acc);
+}
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The 19 rows (clamped into [0, T)); issued early, consumed by conv_apply.
+template <typename IOT>
+__device__ __forceinline__ void conv_rows(float *xr, const PrefillArgs &a, int t0, int tq, int ch)
+{
+    // opaque copy of the window start: without it the 19 row offsets are
+    // shared between calls and held live across the kernel's phases
+    int tb = t0 + tq - 3;
+    asm volatile("" : "+v"(tb));
+#pragma unroll
+    for (int r = 0; r < 19; ++r) {
+        const int64_t pos = max(min((int64_t)tb + r, (int64_t)a.T - 1), (int64_t)0);
+        xr[r] = ld<IOT>(a.x, pos * a.C + ch);
+    }
+}
+
+__device__ __forceinline__ void conv_apply(float *y, const float *xr, const PrefillArgs &a, int t0,
+                                           int tq, int ch, const int *sst, const int *ssl)
+{
+    const float4 wc = reinterpret_cast<const float4 *>(a.w)[ch];
+    const float bias = a.bias ? a.bias[ch] : 0.f;
+    const int s_first = wave_uniform(sst[tq]), s_last = wave_uniform(sst[tq + 15]);
+    if (s_first == s_last && s_first <= t0 + tq - 3) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            y[i] = conv_tap4(wc, bias, xr[i], xr[i + 1], xr[i + 2], xr[i + 3]);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tt = tq + i;
+        const int nh = wave_uniform(sst[tt]) - (t0 + tt - 3);  // window rows before the start
+        const int hrow = wave_uniform(ssl[tt]);
+        float win[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) win[r] = r >= nh ? xr[i + r] : 0.f;
+        if (nh > 0 && hrow >= 0) {
+            const int64_t hb = (int64_t)hrow * a.conv_stride + ch;
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+                if (r < nh) win[r] = load_elem(a.conv_pool, hb + (int64_t)(r + 3 - nh) * a.C,
+                                               a.conv_dtype);
+        }
+        y[i] = conv_tap4(wc, bias, win[0], win[1], win[2], win[3]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1: intra-block quantities, one workgroup (8 waves) per (tile, head).
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 512;
 constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
-constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + 2 * CB * sizeof(int);
+constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + 4 * CB * sizeof(int);
 
-template <typename IOT, bool KDA, int MODE>
+template <typename IOT, bool KDA, int MODE, bool CONV>
 __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArgs a)
 {
     extern __shared__ float sm[];
@@ -285,6 +352,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     float *scr = qsum + 4 * DK;      // per-wave 16x17 scratch
     int *pst = reinterpret_cast<int *>(scr + 8 * 16 * 17);  // piece start (tile-local)
     int *pen = pst + CB;                                      // piece end (inclusive)
+    int *sst = pen + CB;             // fused conv: the token's sequence start (global)
+    int *ssl = sst + CB;             // fused conv: its history row (-1: zeros)
     float *XtK = Qn, *XtV = Kn;      // transposed right-hand sides of phase 6
     float *KhTl = Nm;                // [128][LDJ] staging of K Gamma_L / Gamma, transposed
 
@@ -301,8 +370,15 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     const bool valid = t < nt;
     const int64_t tok = t0 + min(t, nt - 1);
     float qv[16], kv[16], gv[16];
-    load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
-    load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
+    int ps = t, pe = t, s0 = 0, hs = -1;
+    if (valid) {
+        const int n = find_seq_p(a.cu, a.N, t0 + t);
+        s0 = a.cu[n];
+        ps = max(s0, t0) - t0;
+        pe = min(a.cu[n + 1], t0 + CB) - 1 - t0;
+        const int si = a.slot_in[n];
+        hs = (si >= 0 && si < a.num_rows) ? si : -1;
+    }
     if constexpr (KDA) {
         load16<float>(gv, a.g + (tok * a.Hv + h) * DK + c0);
     } else {
@@ -311,11 +387,38 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         for (int e = 0; e < 16; ++e) gv[e] = g1;
     }
     const float bt = a.beta[tok * a.Hv + h];
-    int ps = t, pe = t;
-    if (valid) {
-        const int n = find_seq_p(a.cu, a.N, t0 + t);
-        ps = max(a.cu[n], t0) - t0;
-        pe = min(a.cu[n + 1], t0 + CB) - 1 - t0;
+    // fused conv: thread (channel cc, 16 tokens tc .. tc + 15); every lane of
+    // a wave shares tc, as conv_apply requires
+    const int cc = tid & (DK - 1), tc = 16 * (tid >> 7);
+    if constexpr (CONV) {
+        // conv of q and k into Qn / Kn, then back to the (token, chunk)
+        // mapping for the norms; both windows are in flight together
+        float xq[19], xk[19];
+        conv_rows<IOT>(xq, a, t0, tc, kh * DK + cc);
+        conv_rows<IOT>(xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
+        if (cq == 0) {
+            sst[t] = s0;
+            ssl[t] = hs;
+        }
+        __syncthreads();
+        float y[16];
+        conv_apply(y, xq, a, t0, tc, kh * DK + cc, sst, ssl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Qn[(tc + i) * LDK + cc] = y[i];
+        conv_apply(y, xk, a, t0, tc, a.Hqk * DK + kh * DK + cc, sst, ssl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Kn[(tc + i) * LDK + cc] = y[i];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(Qn + t * LDK + c0 + e);
+            const float4 k4 = *reinterpret_cast<const float4 *>(Kn + t * LDK + c0 + e);
+            qv[e] = q4.x; qv[e + 1] = q4.y; qv[e + 2] = q4.z; qv[e + 3] = q4.w;
+            kv[e] = k4.x; kv[e + 1] = k4.y; kv[e + 2] = k4.z; kv[e + 3] = k4.w;
+        }
+    } else {
+        load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
+        load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -422,6 +525,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     }
     __syncthreads();
     for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
+    // fused conv: the v window loads run under phases 4 and 5
+    float xvr[19];
+    if constexpr (CONV) conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
     __syncthreads();
 
     // ---- 4. A and P, one 16x16 tile pair (I, J <= I) per wave job; P is
@@ -551,11 +657,17 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     {   // thread (channel c, 16 tokens): rows of (beta V)^T, loads coalesced over c
         const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
         float xv[16];
+        if constexpr (CONV) {  // c, tq are cc, tc
+            conv_apply(xv, xvr, a, t0, tq, 2 * a.Hqk * DK + h * DK + c, sst, ssl);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tt = tq + i;
-            const int64_t tk = t0 + min(tt, nt - 1);
-            xv[i] = bet[tt] * ld<IOT>(a.v, tk * a.v_stride + h * DK + c);  // bet = 0 past nt
+            for (int i = 0; i < 16; ++i) xv[i] *= bet[tq + i];  // bet = 0 past nt
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int tt = tq + i;
+                const int64_t tk = t0 + min(tt, nt - 1);
+                xv[i] = bet[tt] * ld<IOT>(a.v, tk * a.v_stride + h * DK + c);  // bet = 0 past nt
+            }
         }
         __syncthreads();  // Kn is free
 #pragma unroll
@@ -1019,21 +1131,27 @@ template <typename IOT, typename ST, int MODE>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
     static const bool attr_done = [] {  // opt in to more than 64 KB of LDS per workgroup
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_intra_kernel<IOT, true, MODE>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIntraLds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_intra_kernel<IOT, false, MODE>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIntraLds);
+        const void *fns[] = {
+            reinterpret_cast<const void *>(&prefill_intra_kernel<IOT, true, MODE, false>),
+            reinterpret_cast<const void *>(&prefill_intra_kernel<IOT, false, MODE, false>),
+            reinterpret_cast<const void *>(&prefill_intra_kernel<IOT, true, MODE, true>),
+            reinterpret_cast<const void *>(&prefill_intra_kernel<IOT, false, MODE, true>)};
+        for (const void *f : fns)
+            (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIntraLds);
         return true;
     }();
     (void)attr_done;
     if (a.T > 0) {
         const dim3 g1((unsigned)((a.T + CB - 1) / CB), (unsigned)a.Hv);
-        if (a.kda)
-            hipLaunchKernelGGL((prefill_intra_kernel<IOT, true, MODE>), g1, dim3(kIntraThreads),
-                               kIntraLds, stream, a);
+        const dim3 b1(kIntraThreads);
+        if (a.kda && a.conv)
+            hipLaunchKernelGGL((prefill_intra_kernel<IOT, true, MODE, true>), g1, b1, kIntraLds, stream, a);
+        else if (a.kda)
+            hipLaunchKernelGGL((prefill_intra_kernel<IOT, true, MODE, false>), g1, b1, kIntraLds, stream, a);
+        else if (a.conv)
+            hipLaunchKernelGGL((prefill_intra_kernel<IOT, false, MODE, true>), g1, b1, kIntraLds, stream, a);
         else
-            hipLaunchKernelGGL((prefill_intra_kernel<IOT, false, MODE>), g1, dim3(kIntraThreads),
-                               kIntraLds, stream, a);
+            hipLaunchKernelGGL((prefill_intra_kernel<IOT, false, MODE, false>), g1, b1, kIntraLds, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

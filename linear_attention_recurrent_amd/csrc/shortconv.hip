@@ -281,4 +281,11 @@ hipError_t launch_shortconv_prefill(const ConvPrefillArgs &a, hipStream_t stream
     return hipGetLastError();
 }
 
+hipError_t launch_shortconv_handoff(const ConvPrefillArgs &a, hipStream_t stream)
+{
+    dim3 g2((unsigned)((a.C + 255) / 256), (unsigned)a.N);
+    hipLaunchKernelGGL(shortconv_prefill_state_kernel, g2, dim3(256), 0, stream, a, 0);
+    return hipGetLastError();
+}
+
 }  // namespace la

@@ -112,6 +112,33 @@ def test_prefill_validation(lib):
     assert lib.kda_prefill_chunked(*bad) == 0
 
 
+@pytest.mark.parametrize("fn", ["kda_prefill_conv", "gdn_prefill_conv"])
+def test_prefill_conv_validation(lib, fn):
+    fake = ctypes.c_void_p(0x1000)
+    T, H, d = 100, 12, 128
+    C = 3 * H * d
+    f = getattr(lib, fn)
+    args = [1, T, H, H, d, d, fake, 1, fake, None, fake, 3 * C, 1, fake, fake, fake, fake, fake,
+            5, fake, H * d * d, 0, fake, 1e-6, 1.0, 1, None, 0, None]
+    if lib.prefill_workspace_bytes(1, T, H, H, d, d, 1):
+        assert f(*args) == -3                             # workspace missing
+    bad = list(args)
+    bad[10] = None                                        # no conv pool
+    assert f(*bad) == -1
+    bad = list(args)
+    bad[11] = 3 * C - 8                                   # conv rows overlap
+    assert f(*bad) == -1 and b"conv_slot_stride" in lib.la_last_error()
+    bad = list(args)
+    bad[12] = 3                                           # unknown conv dtype
+    assert f(*bad) == -2
+    bad = list(args)
+    bad[8] = ctypes.c_void_p(0x1004)                      # misaligned taps
+    assert f(*bad) == -1
+    bad = list(args)
+    bad[0] = 0                                            # no sequences: no-op
+    assert f(*bad) == 0
+
+
 def test_shortconv_validation(lib):
     fake = ctypes.c_void_p(0x1000)
     assert lib.shortconv_update(4, 64, None, 1, fake, None, fake, 192, 1, 5, fake, fake, None) == -1
