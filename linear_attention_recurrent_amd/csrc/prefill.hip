@@ -530,56 +530,119 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     if constexpr (CONV) conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
     __syncthreads();
 
-    // ---- 4. A and P, one 16x16 tile pair (I, J <= I) per wave job; P is
-    //         kept in registers and staged through LDS once Q is dead
-    f32x4 pkeep[2];
+    // ---- 4. A and P.  Wave w contracts channel quarter qtr = w & 3 (32
+    //         channels) for the block pairs of two row blocks: even waves
+    //         take row block 3 (J = 0..3) and (0, 0), odd waves row blocks 2
+    //         and 1; that is five pairs each.  A row block's left factors (its k and
+    //         q rows decayed to the block's reference) are formed once for all
+    //         its pairs.  The four quarters' partial sums meet in LDS in a
+    //         fixed order once Q is dead, so the result does not depend on
+    //         which wave finishes first.
+    constexpr int KQ = DK / 4, W = Step<MODE>::W, NS = KQ / Step<MODE>::K;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+    const int qtr = wv >> 1, grp = wv & 1;  // a quarter's two waves sit on different SIMDs
+    f32x4 pa[5], pp[5];
+    auto rowblock = [&](int I, int nJ, int k0) {
+        const int ti = 16 * I + li;
+        float R[NS][W], fk[NS][W], fq[NS][W];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int job = wave + 8 * jj;
-        if (job >= 10) break;
-        // jobs in order of cost: (3,0..3), (2,0..2), (1,0..1), (0,0)
-        const int I = job < 4 ? 3 : job < 7 ? 2 : job < 9 ? 1 : 0;
-        const int J = job < 4 ? job : job < 7 ? job - 4 : job < 9 ? job - 7 : 0;
-        const int ti = 16 * I + li, tj = 16 * J + li;
-        constexpr int W = Step<MODE>::W;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
-#pragma unroll
-        for (int m = 0; m < DK / Step<MODE>::K; ++m) {
-            float fk[W], fq[W], fj[W];
+        for (int st = 0; st < NS; ++st)
 #pragma unroll
             for (int e = 0; e < W; ++e) {
-                const int c = frag_k<MODE, DK>(lq, m * W + e);
-                const float R = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
-                const float et = exp_acc(fminf(Gc[ti * LDK + c] - R, kExpClamp));
-                fk[e] = Kn[ti * LDK + c] * et;
-                fq[e] = Qn[ti * LDK + c] * et;
-                fj[e] = Kn[tj * LDK + c] * exp_acc(fminf(R - Gc[tj * LDK + c], kExpClamp));
+                const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
+                R[st][e] = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
+                const float et = exp_acc(fminf(Gc[ti * LDK + c] - R[st][e], kExpClamp));
+                fk[st][e] = Kn[ti * LDK + c] * et;
+                fq[st][e] = Qn[ti * LDK + c] * et;
             }
-            mma_step<MODE>(accA, fk, fj);
-            mma_step<MODE>(accP, fq, fj);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J >= nJ) break;
+            const int tj = 16 * J + li;
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                float fj[W];
+#pragma unroll
+                for (int e = 0; e < W; ++e) {
+                    const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
+                    fj[e] = Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp));
+                }
+                mma_step<MODE>(accA, fk[st], fj);
+                mma_step<MODE>(accP, fq[st], fj);
+            }
+            pa[k0 + J] = accA;
+            pp[k0 + J] = accP;
         }
+    };
+    if (grp == 0) {
+        rowblock(3, 4, 0);
+        rowblock(0, 1, 4);
+    } else {
+        rowblock(2, 3, 0);
+        rowblock(1, 2, 3);
+    }
+    // the wave's pairs in the order of pa / pp: (3,0..3), (0,0) for group 0;
+    // (2,0..2), (1,0..1) for group 1
+    auto pairI = [&](int k) { return grp ? (k < 3 ? 2 : 1) : (k < 4 ? 3 : 0); };
+    auto pairJ = [&](int k) { return grp ? (k < 3 ? k : k - 3) : (k < 4 ? k : 0); };
+    // masks and beta of the wave's elements, read once: A keeps beta[t] A
+    // where j < t in the same piece (else 0), P keeps j <= t in the same piece
+    float bA[5][4];
+    bool kA[5][4], kP[5][4];
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int tt = 16 * I + 4 * lq + r, j = 16 * J + li;
+            const int tt = 16 * pairI(k) + 4 * lq + r, j = 16 * pairJ(k) + li;
             const bool same = j >= pst[tt] && tt < nt;
-            Nm[tt * LDJ + j] = (same && j < tt) ? bet[tt] * accA[r] : 0.f;
-            pkeep[jj][r] = (same && j <= tt) ? accP[r] : 0.f;
+            bA[k][r] = bet[tt];
+            kA[k][r] = same && j < tt;
+            kP[k][r] = same && j <= tt;
         }
-    }
     __syncthreads();
     float *Ps = Qn;  // P [64][LDJ]; q_hat is no longer read
     for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {  // upper tiles of P are zero
         const int tt = idx / CB, j = idx % CB;
         if ((j >> 4) > (tt >> 4)) Ps[tt * LDJ + j] = 0.f;
     }
+    // quarter q adds its partial sums after quarters 0 .. q-1; the last one
+    // applies beta and the masks
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int job = wave + 8 * jj;
-        if (job >= 10) break;
-        const int I = job < 4 ? 3 : job < 7 ? 2 : job < 9 ? 1 : 0;
-        const int J = job < 4 ? job : job < 7 ? job - 4 : job < 9 ? job - 7 : 0;
+    for (int q = 0; q < 4; ++q) {
+        if (qtr == q) {
+            // every earlier partial is read before anything is written, so
+            // the reads go out together
+            float prevA[5][4], prevP[5][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Ps[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = pkeep[jj][r];
+            for (int k = 0; k < 5; ++k)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
+                    prevA[k][r] = q > 0 ? Nm[at] : 0.f;
+                    prevP[k][r] = q > 0 ? Ps[at] : 0.f;
+                }
+#pragma unroll
+            for (int k = 0; k < 5; ++k) {
+                const int I = pairI(k), J = pairJ(k);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tt = 16 * I + 4 * lq + r, j = 16 * J + li;
+                    float av = pa[k][r], pv = pp[k][r];
+                    if (q > 0) {
+                        av += prevA[k][r];
+                        pv += prevP[k][r];
+                    }
+                    if (q == 3) {
+                        av = kA[k][r] ? bA[k][r] * av : 0.f;
+                        pv = kP[k][r] ? pv : 0.f;
+                    }
+                    Nm[tt * LDJ + j] = av;
+                    Ps[tt * LDJ + j] = pv;
+                }
+            }
+        }
+        __syncthreads();
     }
 
     // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
