@@ -133,6 +133,18 @@ __device__ __forceinline__ void split8(const float *f, uint4 &hi, uint4 &lo)
     hi = __builtin_bit_cast(uint4, h);
     lo = __builtin_bit_cast(uint4, l);
 }
+// bf16x3 rows in LDS (row stride LDJ words): bf16 hi words 0..31 and lo words
+// 32..63 hold columns 0..63.  Writes columns k0 .. k0 + 15 of one row.
+__device__ __forceinline__ void store_row_split16(float *row, int k0, const float *v)
+{
+    uint4 h0, l0, h1, l1;
+    split8(v, h0, l0);
+    split8(v + 8, h1, l1);
+    *reinterpret_cast<uint4 *>(row + k0 / 2) = h0;
+    *reinterpret_cast<uint4 *>(row + k0 / 2 + 4) = h1;
+    *reinterpret_cast<uint4 *>(row + 32 + k0 / 2) = l0;
+    *reinterpret_cast<uint4 *>(row + 32 + k0 / 2 + 4) = l1;
+}
 // Writes the split 8-value group of step m of a lane into a fragment-major
 // block: the hi quad to run 2m, the lo quad to run 2m + 1 (bf16x3 layout).
 __device__ __forceinline__ void store_split(float *blk, int m, int lane, const float *v)
@@ -390,12 +402,17 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     // fused conv: thread (channel cc, 16 tokens tc .. tc + 15); every lane of
     // a wave shares tc, as conv_apply requires
     const int cc = tid & (DK - 1), tc = 16 * (tid >> 7);
-    if constexpr (CONV) {
-        // conv of q and k into Qn / Kn, then back to the (token, chunk)
-        // mapping for the norms; both windows are in flight together
-        float xq[19], xk[19];
+    float xq[19], xk[19];
+    if constexpr (CONV) {  // both windows in flight together
         conv_rows<IOT>(xq, a, t0, tc, kh * DK + cc);
         conv_rows<IOT>(xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
+    } else {
+        load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
+        load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
+    }
+    if constexpr (CONV) {
+        // conv of q and k into Qn / Kn, then back to the (token, chunk)
+        // mapping for the norms
         if (cq == 0) {
             sst[t] = s0;
             ssl[t] = hs;
@@ -416,9 +433,6 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             qv[e] = q4.x; qv[e + 1] = q4.y; qv[e + 2] = q4.z; qv[e + 3] = q4.w;
             kv[e] = k4.x; kv[e + 1] = k4.y; kv[e + 2] = k4.z; kv[e + 3] = k4.w;
         }
-    } else {
-        load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
-        load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -525,9 +539,19 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     }
     __syncthreads();
     for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
-    // fused conv: the v window loads run under phases 4 and 5
+    // the v loads of step 6 (its thread mapping: channel cc, tokens tc ..
+    // tc + 15) run under steps 4 and 5: the 19-row conv window when the conv
+    // is fused, else the 16 rows of v
     float xvr[19];
-    if constexpr (CONV) conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
+    if constexpr (CONV) {
+        conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t tk = t0 + min(tc + i, nt - 1);
+            xvr[i] = ld<IOT>(a.v, tk * a.v_stride + h * DK + cc);
+        }
+    }
     __syncthreads();
 
     // ---- 4. A and P.  Wave w contracts channel quarter qtr = w & 3 (32
@@ -701,7 +725,20 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         __syncthreads();
     }
 
-    // ---- 6. right-hand sides, transposed: (beta K Gamma)^T and (beta V)^T
+    // ---- 6. right-hand sides, transposed: (beta K Gamma)^T and (beta V)^T.
+    //         In bf16x3 mode they and T are stored split (bf16 hi / lo rows),
+    //         so step 7 reads its operands without converting them; T goes
+    //         to N's space, which is dead.
+    if constexpr (MODE != PM_F32) {
+        const int row = tid >> 3, k0 = 8 * (tid & 7);
+        const float4 t0v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0);
+        const float4 t1v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0 + 4);
+        const float tv[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+        uint4 hi, lo;
+        split8(tv, hi, lo);
+        *reinterpret_cast<uint4 *>(Nm + row * LDJ + k0 / 2) = hi;
+        *reinterpret_cast<uint4 *>(Nm + row * LDJ + 32 + k0 / 2) = lo;
+    }
     {
         const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
         float xk[16];
@@ -712,10 +749,14 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             xk[i] = bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c] - Gs);
         }
         __syncthreads();  // Qn is about to be overwritten
+        if constexpr (MODE == PM_F32) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 4)
-            *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + i) =
-                make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+            for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + i) =
+                    make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+        } else {
+            store_row_split16(XtK + c * LDJ, tq, xk);
+        }
     }
     {   // thread (channel c, 16 tokens): rows of (beta V)^T, loads coalesced over c
         const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
@@ -726,17 +767,17 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             for (int i = 0; i < 16; ++i) xv[i] *= bet[tq + i];  // bet = 0 past nt
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int tt = tq + i;
-                const int64_t tk = t0 + min(tt, nt - 1);
-                xv[i] = bet[tt] * ld<IOT>(a.v, tk * a.v_stride + h * DK + c);  // bet = 0 past nt
-            }
+            for (int i = 0; i < 16; ++i) xv[i] = bet[tq + i] * xvr[i];  // bet = 0 past nt
         }
         __syncthreads();  // Kn is free
+        if constexpr (MODE == PM_F32) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 4)
-            *reinterpret_cast<float4 *>(XtV + c * LDJ + tq + i) =
-                make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
+            for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<float4 *>(XtV + c * LDJ + tq + i) =
+                    make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
+        } else {
+            store_row_split16(XtV + c * LDJ, tq, xv);
+        }
     }
     __syncthreads();
 
@@ -753,11 +794,26 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const float *Trow = Tm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
-                auto fa = [&](int, int j) { return Trow[j]; };
-                auto fb = [&](int, int j) { return Xrow[j]; };
-                if (I < 2) mma_gen<MODE, 32>(acc, lq, fa, fb);  // T rows < 32: columns < 32
-                else mma_gen<MODE, 64>(acc, lq, fa, fb);
+                if constexpr (MODE == PM_F32) {
+                    const float *Trow = Tm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
+                    auto fa = [&](int, int j) { return Trow[j]; };
+                    auto fb = [&](int, int j) { return Xrow[j]; };
+                    if (I < 2) mma_gen<MODE, 32>(acc, lq, fa, fb);  // T rows < 32: columns < 32
+                    else mma_gen<MODE, 64>(acc, lq, fa, fb);
+                } else {  // split rows: step m, lane quad lq covers columns 32 m + 8 lq ..
+                    const float *Trow = Nm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
+#pragma unroll
+                    for (int m = 0; m < (I < 2 ? 1 : 2); ++m) {
+                        const int o = 16 * m + 4 * lq;
+                        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(Trow + o);
+                        const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(Trow + 32 + o);
+                        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(Xrow + o);
+                        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(Xrow + 32 + o);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+                    }
+                }
                 if (which == 0) {
                     *reinterpret_cast<f32x4 *>(ws.U + bh * kBlkDK + fidx(I * 8 + C, lane)) = acc;
                 } else {
