@@ -524,6 +524,38 @@ def copy_calibration(dev, nbytes=1 << 30, reps=5):
                       "gbs_rw": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def copy_reference(dev, same_size_bytes, big_bytes=2 << 30):
+    """Plain device copies as the practical HBM ceiling: one of big_bytes each
+    way (4 GiB moved), and one the size of a decode launch (half its bytes
+    each way) replayed over 16 rotated buffer pairs from a HIP graph, as the
+    decode is timed."""
+    src = torch.empty(big_bytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = events()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    big_gbs = 2 * big_bytes / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
+    del src, dst
+    half = (same_size_bytes // 2 + 15) // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev).fill_(1),
+              torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(16)]
+
+    def launch_all():
+        for a, b in pairs:
+            b.copy_(a)
+
+    ms, _ = time_graph(launch_all, len(pairs), 3200, 320)
+    small_gbs = 2 * half / (ms * 1e-3) / 1e9
+    del pairs
+    torch.cuda.empty_cache()
+    return big_gbs, small_gbs, ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -533,6 +565,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (PMC counter scaling)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the chunked-prefill workloads (for counter profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -545,8 +579,18 @@ def main():
         copy_calibration(dev)
         return
     la.load_library()
+    if args.prefill_only:
+        print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev)}), flush=True)
+        return
     log(f"headline KDA decode, {args.steps} launches after {args.warmup} warm-up")
     sh, res = headline(args, dev)
+    big_gbs, small_gbs, small_ms = copy_reference(dev, res["roofline"]["algorithmic_bytes_per_launch"])
+    res["roofline"]["copy_reference"] = {
+        "copy_4gib_gbs": big_gbs, "frac_of_copy_4gib": res["roofline"]["achieved"] / big_gbs,
+        "copy_same_size_gbs": small_gbs, "copy_same_size_ms": small_ms,
+        "frac_of_copy_same_size": res["roofline"]["achieved"] / small_gbs,
+        "note": "plain torch device copies on the same box: 2 GiB each way, and the decode "
+                "launch's bytes (half each way) rotated over 16 buffer pairs under graph replay"}
     extra = {}
     if not args.no_extra:
         extra["kda_decode_69_layers_h96_b128"] = decode_stack(
