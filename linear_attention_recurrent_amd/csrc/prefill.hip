@@ -1112,12 +1112,19 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
             // D = U - W S^T for each slice (ops words [8m, 8m+4) hi, [8m+4, 8m+8) lo)
 #pragma unroll
             for (int sl = 0; sl < NSL; ++sl) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                // two accumulators (even / odd 32-deep steps) halve the
+                // dependent matrix-core chain on the block's critical path
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
                 const int sr = 16 * sl + li;
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 4; m += 2) {
                     mma3(acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4),
                          lds8(&SH[b][sr][32 * m + 8 * lq]), lds8(&SL[b][sr][32 * m + 8 * lq]));
+                    mma3(acc1, quad8(cur + 8 * m + 8), quad8(cur + 8 * m + 12),
+                         lds8(&SH[b][sr][32 * m + 32 + 8 * lq]),
+                         lds8(&SL[b][sr][32 * m + 32 + 8 * lq]));
+                }
+                acc += acc1;
                 float d[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -1197,27 +1204,37 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
                     for (int r = 0; r < 4; ++r)
                         sc[sl][q][r] = Sf[b][16 * sl + 4 * lq + r][32 * I + 16 * q + li];
             __syncthreads();  // D^T complete
-            // new state columns: S Gamma_L + D^T K^
+            // new state columns: S Gamma_L + D^T K^.  The products of both
+            // 16-column halves are formed before either is written back, so
+            // their matrix-core chains overlap.
+            f32x4 acc[2][NSL];
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[q][sl] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const bf16x8_t dh = lds8(&DH[16 * sl + li][32 * m + 8 * lq]);
+                    const bf16x8_t dl = lds8(&DL[16 * sl + li][32 * m + 8 * lq]);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        mma3(acc[q][sl], dh, dl, quad8(cur + 16 * q + 8 * m),
+                             quad8(cur + 16 * q + 8 * m + 4));
+                }
+            }
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int c = 32 * I + 16 * q + li;
                 const float gm = exp_acc(cur[32 + q]);
 #pragma unroll
-                for (int sl = 0; sl < NSL; ++sl) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int m = 0; m < 2; ++m)
-                        mma3(acc, lds8(&DH[16 * sl + li][32 * m + 8 * lq]),
-                             lds8(&DL[16 * sl + li][32 * m + 8 * lq]),
-                             quad8(cur + 16 * q + 8 * m), quad8(cur + 16 * q + 8 * m + 4));
+                for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = 16 * sl + 4 * lq + r;
-                        const float v = fmaf(sc[sl][q][r], gm, acc[r]);
+                        const float v = fmaf(sc[sl][q][r], gm, acc[q][sl][r]);
                         Sf[b ^ 1][row][c] = v;
                         split1(v, SH[b ^ 1][row][c], SL[b ^ 1][row][c]);
                     }
-                }
             }
         };
         if constexpr (PF) {
