@@ -42,6 +42,10 @@
  *     for an out-of-range or duplicate non-zero slot.
  *   - Alignment: every pointer must be 16-byte aligned and every row stride
  *     a multiple of 16 bytes (LA_ERR_ARG otherwise).
+ *   - A prefill call with no tokens (T == 0) reads none of its per-token
+ *     buffers (q, k, v, x, g, beta, out, y), which may then be NULL; it still
+ *     hands each sequence's state (and conv history) from slot_in to
+ *     slot_out.
  *   - Errors: no exception crosses the ABI.  Calls return an LA_* status;
  *     la_last_error() gives a thread-local message for the last failure.
  */

@@ -176,8 +176,9 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
     if (dk != 128 || dv != 128)
         return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);
     if (N == 0) return ok();
-    if (!q || !k || !v || !g || !beta || !cu_seqlens || !slot_in || !slot_out || !ssm_pool ||
-        (T > 0 && !out))
+    // with no tokens the per-token buffers are not read and may be NULL
+    if (!cu_seqlens || !slot_in || !slot_out || !ssm_pool ||
+        (T > 0 && (!q || !k || !v || !g || !beta || !out)))
         return fail(LA_ERR_ARG, "%s: null pointer argument", fn);
     const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, out};
     for (const void *p : ptrs)
@@ -445,7 +446,7 @@ int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype, const in
     if (!valid_dtype(io_dtype) || !valid_dtype(conv_dtype))
         return fail(LA_ERR_UNSUPPORTED, "shortconv_prefill: dtype codes must be LA_F32 or LA_BF16");
     if (N == 0) return ok();
-    if (!x || !cu_seqlens || !slot_in || !slot_out || !w || !conv_pool || (T > 0 && !y))
+    if (!cu_seqlens || !slot_in || !slot_out || !w || !conv_pool || (T > 0 && (!x || !y)))
         return fail(LA_ERR_ARG, "shortconv_prefill: null pointer argument");
     const void *ptrs[] = {x, cu_seqlens, slot_in, slot_out, w, bias, conv_pool, y};
     for (const void *p : ptrs)

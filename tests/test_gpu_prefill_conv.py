@@ -201,3 +201,70 @@ def test_sampled_kda_prefill_conv_serving_shape(mode, dev):
                        "end states (sampled heads)")
     assert np.array_equal(f64(c["cpool"])[:, :, ch], cpool_ref)
     assert C == c["x"].shape[1]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_all_sequences_empty_hands_states_over(fused, dev):
+    """T = 0 with N = 3: no tokens, so each sequence's slot_out receives its
+    initial state (zeros when slot_in < 0) and, fused, its conv history."""
+    c = conv_case([0, 0, 0], 1, 1, 3207, dev, slot_in=[2, -1, 4], slot_out=[5, 6, 4], P=6)
+    cbefore, sbefore = c["cpool"].clone(), c["spool"].clone()
+    if fused:
+        out = run_fused(c, dev)
+    else:
+        Hqk, Hv = 1, 1
+        empty = torch.empty((0, Hqk, D), dtype=torch.bfloat16, device=dev)
+        out = la.kda_prefill_chunked(empty, empty, torch.empty((0, Hv, D), dtype=torch.bfloat16,
+                                                               device=dev),
+                                     c["g"], c["beta"], c["cu"], torch.from_numpy(c["si"]).to(dev),
+                                     torch.from_numpy(c["so"]).to(dev), c["spool"])
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+    assert torch.equal(c["spool"][5], sbefore[2])
+    assert torch.count_nonzero(c["spool"][6]) == 0
+    assert torch.equal(c["spool"][4], sbefore[4])
+    for r in (0, 1, 2, 3):
+        assert torch.equal(c["spool"][r], sbefore[r])
+    if fused:
+        assert torch.equal(c["cpool"][5], cbefore[2])
+        assert torch.count_nonzero(c["cpool"][6]) == 0
+        assert torch.equal(c["cpool"][4], cbefore[4])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_many_short_sequences_share_tiles(fused, dev):
+    """70 sequences of 1-3 tokens (seeded lengths), so a 64-token tile holds
+    dozens of pieces and the per-token sequence lookup runs deep; every
+    other one resumes from a pool slot."""
+    rng = np.random.default_rng(3208)
+    lens = [int(x) for x in rng.integers(1, 4, size=70)]
+    N = len(lens)
+    si = [n + 1 if n % 2 else -1 for n in range(N)]
+    so = [N + 1 + n for n in range(N)]
+    c = conv_case(lens, 1, 2, 3208, dev, kda=False, io="bf16", state="fp32", cdt="bf16",
+                  slot_in=si, slot_out=so, P=2 * N + 1)
+    if fused:
+        check(c, dev, "70 short sequences, fused", "bf16x3")
+        return
+    # unfused: the oracle's conv output (rounded to bf16 as a conv call would
+    # store it) is the prefill's input
+    sh = c["sh"]
+    T = sh.T
+    y, _ = oracle.shortconv_prefill(f64(c["x"]), c["cu"].cpu().numpy(), c["si"], c["so"],
+                                    f64(c["w"]), f64(c["b"]), f64(c["cpool"]),
+                                    conv_dtype="bf16", io_dtype="bf16")
+    yt = torch.from_numpy(y).to(torch.bfloat16).to(dev)
+    q = yt[:, :D].reshape(T, 1, D)
+    k = yt[:, D:2 * D].reshape(T, 1, D)
+    v = yt[:, 2 * D:].reshape(T, 2, D).contiguous()
+    sbefore = c["spool"].clone()
+    o_ref, s_ref = oracle.prefill(f64(q), f64(k), f64(v), f64(c["g"]), f64(c["beta"]),
+                                  c["cu"].cpu().numpy(), c["si"], c["so"], f64(sbefore),
+                                  kda=False, state_dtype="fp32", io_dtype="bf16")
+    out = la.gdn_prefill_chunked(q.contiguous(), k.contiguous(), v, c["g"], c["beta"], c["cu"],
+                                 torch.from_numpy(c["si"]).to(dev),
+                                 torch.from_numpy(c["so"]).to(dev), c["spool"],
+                                 mode=la.LA_PREFILL_BF16X3)
+    torch.cuda.synchronize()
+    assert_close_units(f64(out), o_ref, 2, "bf16", "70 short sequences outputs")
+    assert_close_units(f64(c["spool"])[c["so"]], s_ref[c["so"]], 2, "fp32", "end states")
