@@ -21,7 +21,7 @@
 //   S_L  = S_0 Diag(Gamma_L) + D^T (K . Gamma_L / Gamma)
 // U, W, P and the scaled Q, K do not depend on S_0: kernel 1 computes them for
 // every block in parallel; kernel 2 runs the block chain per (sequence, head,
-// 16-row slice of the state), rows of S being independent given the block.
+// slice of 16 or 64 state rows), rows of S being independent given the block.
 //
 // Blocks are the intersections of 64-token tiles of the packed token axis
 // with the sequences ("pieces").  Kernel 1 works per (tile, head) with a
