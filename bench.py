@@ -469,6 +469,47 @@ def prefill_bench(dev, reps=10):
     return res
 
 
+def gdn_prefill_bench(dev, reps=10):
+    """Chunked GDN prefill with the GDN decode configuration's heads (16 q/k
+    heads shared by 32 value heads, d=128), bf16 I/O, fp32 state, scalar
+    gate: eight 4,096-token sequences packed in one call, fresh states to
+    eight slots.  q, k, v are post-conv inputs (the chunked call alone), both
+    precision modes, each call replayed from a captured HIP graph."""
+    Hqk, Hv, D = 16, 32, 128
+    sh = synth.PrefillShape(seqlens=(4096,) * 8, Hqk=Hqk, Hv=Hv, dk=D, dv=D, kda=False)
+    log("GDN prefill: generating inputs")
+    inp = synth.prefill_inputs(sh, 1007, dev)
+    pool = torch.zeros((9, Hv, D, D), dtype=torch.float32, device=dev)
+    si = torch.full((8,), -1, dtype=torch.int32, device=dev)
+    so = torch.arange(1, 9, dtype=torch.int32, device=dev)
+    out = torch.empty((sh.T, Hv, D), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for mode, name in ((1, "bf16x3"), (0, "fp32")):
+        ws = torch.empty(la.prefill_workspace_bytes(8, sh.T, Hqk, Hv, D, D, mode),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            la.gdn_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   inp["cu_seqlens"], si, so, pool, out=out, workspace=ws,
+                                   mode=mode)
+
+        call()
+        torch.cuda.synchronize()
+        ms = time_graph(lambda: [call() for _ in range(reps)], reps, 4 * reps, reps)[0]
+        flops = prefill_mfma_flops(sh.seqlens, Hv, mode)
+        peak = MFMA_BF16_PEAK_TFS if mode else MFMA_FP32_PEAK_TFS
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"tokens_per_s": sh.T / (ms * 1e-3), "ms": ms,
+                     "roofline": {"bound": "mfma", "achieved": tf, "peak": peak,
+                                  "unit": "TFLOP/s", "frac": tf / peak,
+                                  "issued_mfma_flops": flops}}
+        del ws
+    res["workload"] = "gdn_prefill_8x4096_hqk16_hv32"
+    del inp, pool, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_prefill_rate(budget_tokens=1536):
     """The fp64 oracle's prefill on one head of `budget_tokens` tokens,
     scaled to tokens/s for all 12 heads (single thread)."""
@@ -580,7 +621,8 @@ def main():
         return
     la.load_library()
     if args.prefill_only:
-        print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev)}), flush=True)
+        print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev),
+                          "gdn_prefill_chunked_hqk16_hv32": gdn_prefill_bench(dev)}), flush=True)
         return
     log(f"headline KDA decode, {args.steps} launches after {args.warmup} warm-up")
     sh, res = headline(args, dev)
@@ -600,6 +642,7 @@ def main():
                               state="fp32", conv="fp32"), 48, 16, 1003, dev)
         log("prefill")
         extra["kda_prefill_chunked_h12"] = prefill_bench(dev)
+        extra["gdn_prefill_chunked_hqk16_hv32"] = gdn_prefill_bench(dev)
         extra["kda_speculative_b64_h12_d8"] = spec_bench(dev)
     if not args.no_cpu:
         log("CPU oracle baselines")

@@ -478,6 +478,18 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         for (int i = 0; i < 16; ++i) Gc[(16 * qq + i) * LDK + c] = run[i] + off;
     }
     __syncthreads();
+    // GDN: one decay per token, so the decay factors of steps 3 and 6 are
+    // per-token scalars, exp(G_end - G_t) and exp(G_t - G_start) over the
+    // token's piece, formed once here (qsum is free after step 2)
+    float *tabE = qsum, *tabS = qsum + CB;
+    if constexpr (!KDA) {
+        if (tid < CB) {
+            const float G = Gc[tid * LDK];
+            tabE[tid] = exp_acc(Gc[pen[tid] * LDK] - G);
+            tabS[tid] = exp_acc(G - (pst[tid] > 0 ? Gc[(pst[tid] - 1) * LDK] : 0.f));
+        }
+        __syncthreads();
+    }
 
     // ---- 3. K Gamma_L / Gamma transposed through LDS and the piece's total
     //         decay (global, at piece ends): thread (channel c, 16 tokens);
@@ -491,7 +503,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             const int pst_t = pst[tt], pen_t = pen[tt];
             const float G = Gc[tt * LDK + c];
             const float Ge = Gc[pen_t * LDK + c];
-            KhTl[c * LDJ + tt] = Kn[tt * LDK + c] * exp_acc(Ge - G);
+            KhTl[c * LDJ + tt] = Kn[tt * LDK + c] * (KDA ? exp_acc(Ge - G) : tabE[tt]);
             if (tt < nt && tt == pen_t) {
                 const float Gs = pst_t > 0 ? Gc[(pst_t - 1) * LDK + c] : 0.f;
                 ws.Ge[row(tt) * DK + c] = Ge - Gs;
@@ -503,12 +515,19 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
             const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
             const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
-            const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
-            float4 Gs = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (pst[tt] > 0) Gs = *reinterpret_cast<const float4 *>(Gc + (pst[tt] - 1) * LDK + k0);
+            float4 e4;
+            if constexpr (KDA) {
+                const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
+                float4 Gs = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (pst[tt] > 0) Gs = *reinterpret_cast<const float4 *>(Gc + (pst[tt] - 1) * LDK + k0);
+                e4 = make_float4(exp_acc(G.x - Gs.x), exp_acc(G.y - Gs.y), exp_acc(G.z - Gs.z),
+                                 exp_acc(G.w - Gs.w));
+            } else {
+                const float e = tabS[tt];
+                e4 = make_float4(e, e, e, e);
+            }
             *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
-                make_float4(qn.x * exp_acc(G.x - Gs.x), qn.y * exp_acc(G.y - Gs.y),
-                            qn.z * exp_acc(G.z - Gs.z), qn.w * exp_acc(G.w - Gs.w));
+                make_float4(qn.x * e4.x, qn.y * e4.y, qn.z * e4.z, qn.w * e4.w);
         }
     } else {  // split layout: thread = (row block I, step m, lane), 8 channels
         for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
@@ -518,7 +537,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                v[e] = Qn[tt * LDK + k0 + e] * exp_acc(Gc[tt * LDK + k0 + e] - (gs ? gs[e] : 0.f));
+                v[e] = Qn[tt * LDK + k0 + e] *
+                       (KDA ? exp_acc(Gc[tt * LDK + k0 + e] - (gs ? gs[e] : 0.f)) : tabS[tt]);
             store_split(ws.Qt + bh * kBlkDK + I * 2048, m, ln, v);
         }
     }
@@ -574,10 +594,15 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
             for (int e = 0; e < W; ++e) {
                 const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
-                R[st][e] = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
-                const float et = exp_acc(fminf(Gc[ti * LDK + c] - R[st][e], kExpClamp));
-                fk[st][e] = Kn[ti * LDK + c] * et;
-                fq[st][e] = Qn[ti * LDK + c] * et;
+                if constexpr (KDA) {
+                    R[st][e] = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
+                    const float et = exp_acc(fminf(Gc[ti * LDK + c] - R[st][e], kExpClamp));
+                    fk[st][e] = Kn[ti * LDK + c] * et;
+                    fq[st][e] = Qn[ti * LDK + c] * et;
+                } else {  // GDN: plain k and q rows; the decay is applied per element below
+                    fk[st][e] = Kn[ti * LDK + c];
+                    fq[st][e] = Qn[ti * LDK + c];
+                }
             }
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
@@ -590,7 +615,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
                 for (int e = 0; e < W; ++e) {
                     const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
-                    fj[e] = Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp));
+                    fj[e] = KDA ? Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp))
+                                : Kn[tj * LDK + c];
                 }
                 mma_step<MODE>(accA, fk[st], fj);
                 mma_step<MODE>(accP, fq[st], fj);
@@ -612,7 +638,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     auto pairJ = [&](int k) { return grp ? (k < 3 ? k : k - 3) : (k < 4 ? k : 0); };
     // masks and beta of the wave's elements, read once: A keeps beta[t] A
     // where j < t in the same piece (else 0), P keeps j <= t in the same piece
-    float bA[5][4];
+    // (GDN: also the element's decay exp(G_t - G_j), <= 1 where it is kept)
+    float bA[5][4], eP[5][4];
     bool kA[5][4], kP[5][4];
 #pragma unroll
     for (int k = 0; k < 5; ++k)
@@ -623,6 +650,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             bA[k][r] = bet[tt];
             kA[k][r] = same && j < tt;
             kP[k][r] = same && j <= tt;
+            eP[k][r] = KDA ? 1.f : exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
         }
     __syncthreads();
     float *Ps = Qn;  // P [64][LDJ]; q_hat is no longer read
@@ -658,6 +686,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                         pv += prevP[k][r];
                     }
                     if (q == 3) {
+                        if constexpr (!KDA) {
+                            av *= eP[k][r];
+                            pv *= eP[k][r];
+                        }
                         av = kA[k][r] ? bA[k][r] * av : 0.f;
                         pv = kP[k][r] ? pv : 0.f;
                     }
@@ -745,8 +777,12 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int tt = tq + i;
-            const float Gs = pst[tt] > 0 ? Gc[(pst[tt] - 1) * LDK + c] : 0.f;
-            xk[i] = bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c] - Gs);
+            if constexpr (KDA) {
+                const float Gs = pst[tt] > 0 ? Gc[(pst[tt] - 1) * LDK + c] : 0.f;
+                xk[i] = bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c] - Gs);
+            } else {
+                xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
+            }
         }
         __syncthreads();  // Qn is about to be overwritten
         if constexpr (MODE == PM_F32) {
