@@ -876,6 +876,27 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     }
 }
 
+// Chain workgroups: S row slices of each (sequence, head) pair, launched as a
+// 1-D grid of ceil(N Hv / 8) * 8 S workgroups.  Workgroup L takes pair
+// 8 (L / 8S) + L % 8 and slice (L / 8) % S, so the slices of a pair are 8 ids
+// apart: workgroups go to the 8 XCDs round-robin, so these share an XCD and
+// run at about the same time, and the block operands they all read come from
+// that XCD's L2 after the first.  Returns false for the padding workgroups.
+__device__ __forceinline__ bool chain_ids(const PrefillArgs &a, int S, int &n, int &h, int &rs)
+{
+    const int L = blockIdx.x;
+    const int pair = 8 * (L / (8 * S)) + (L & 7);
+    rs = (L >> 3) % S;
+    if (pair >= a.N * a.Hv) return false;
+    n = pair / a.Hv;
+    h = pair % a.Hv;
+    return true;
+}
+inline unsigned chain_grid(const PrefillArgs &a, int S)
+{
+    return (unsigned)(((int64_t)a.N * a.Hv + 7) / 8 * 8 * S);
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 2: the block chain, one workgroup per (sequence, head, 16 state rows).
 // Waves 0..3 ("row waves") own token rows 16I.. of D and O; waves 4..7
@@ -903,7 +924,8 @@ __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArg
     float *Sbuf = sm;                 // two state slices [16 rows][LDK]
     float *Dt = sm + 2 * 16 * LDK;    // D^T of the tile [16 rows][LDJ] (tile-local tokens)
 
-    const int n = blockIdx.x, h = blockIdx.y, rs = blockIdx.z;  // rows 16 rs .. 16 rs + 15
+    int n, h, rs;  // rows 16 rs .. 16 rs + 15
+    if (!chain_ids(a, DK / 16, n, h, rs)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int I = wave & 3;       // token block (row waves) / column pair (column waves)
@@ -1102,7 +1124,8 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
     __shared__ __attribute__((aligned(16))) bf16_t SH[2][NR][LDKH], SL[2][NR][LDKH];
     __shared__ __attribute__((aligned(16))) bf16_t DH[NR][LDJH], DL[NR][LDJH];
 
-    const int n = blockIdx.x, h = blockIdx.y, rs = blockIdx.z;  // rows NR rs .. NR rs + NR - 1
+    int n, h, rs;  // rows NR rs .. NR rs + NR - 1
+    if (!chain_ids(a, DK / NR, n, h, rs)) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int I = wave & 3;
@@ -1327,17 +1350,15 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 g2((unsigned)a.N, (unsigned)a.Hv, (unsigned)(DK / 16));
     if constexpr (MODE == PM_F32)
-        hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), g2, dim3(kChainThreads),
-                           kChainLds, stream, a);
+        hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), dim3(chain_grid(a, DK / 16)),
+                           dim3(kChainThreads), kChainLds, stream, a);
     else if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: prefetch
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, true, 1>), g2, dim3(kChainThreads),
-                           0, stream, a);
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, true, 1>),
+                           dim3(chain_grid(a, DK / 16)), dim3(kChainThreads), 0, stream, a);
     else  // many: 64 state rows per workgroup
         hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, false, 4>),
-                           dim3((unsigned)a.N, (unsigned)a.Hv, (unsigned)(DK / 64)),
-                           dim3(kChainThreads), 0, stream, a);
+                           dim3(chain_grid(a, DK / 64)), dim3(kChainThreads), 0, stream, a);
     return hipGetLastError();
 }
 
