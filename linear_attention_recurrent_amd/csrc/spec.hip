@@ -29,8 +29,9 @@
 // Work decomposition of verify and commit: one workgroup per (request, value
 // head), the head's state rows spread over the waves as in the decode kernel
 // (16-byte lane chunks, LPR lanes per row), held in fp32 registers across the
-// steps.  Verify computes the head's q|k|v conv outputs per step into a
-// double-buffered LDS area (one barrier per step).  Both kernels first stage
+// steps.  Verify forms a chunk's q|k|v conv outputs, decays, norms and ring
+// records up front, so its steps only update the state rows, with no barrier
+// between steps.  Both kernels first stage
 // the inputs of up to eight steps in LDS (verify: the pre-conv inputs of the
 // head's channels and the gates; commit: the ring records), with every load
 // issued back to back, so a step waits for memory once per eight steps.
@@ -94,9 +95,9 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
     constexpr int CPT = (NCH + NT - 1) / NT;   // channels per thread
     constexpr int XPT = (kChunk * NCH + NT - 1) / NT;  // staged inputs per thread
     constexpr int GPT = (kChunk * HD + NT - 1) / NT;   // staged gates per thread
-    __shared__ float ybuf[2][NCH];             // conv outputs per step parity (I/O-dtype values)
-    __shared__ float xs[kChunk][NCH];          // the chunk's pre-conv inputs of the head's channels
-    __shared__ float gs[kChunk][HD];           // the chunk's log-decays (GDN: broadcast)
+    __shared__ float xs[kChunk][NCH];          // the chunk's pre-conv inputs, then its q|k|v
+    __shared__ float nq[kChunk], nk[kChunk];   // the chunk's inverse q and k norms
+    __shared__ float gs[kChunk][HD];           // the chunk's log-decays, then exp of them (GDN: broadcast)
     __shared__ float bs[kChunk];               // the chunk's betas
 
     const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv, kh = h / a.G;
@@ -185,16 +186,20 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
         if (tid < kChunk) bs[tid] = bv;
         __syncthreads();
     }
-    for (int tt = 0; tt < nc; ++tt) {
-        const int t = t0 + tt;
-        const int pos = (a.ring_base[b] + t) & (R.L - 1);
-        const int64_t bt = (int64_t)b * a.D + t;
-        float *yb = ybuf[t & 1];
-        // ---- conv + SiLU of the owned channels, rounded to the I/O dtype
+    // ---- the chunk's conv outputs (rounded to the I/O dtype, in place over
+    //      the staged inputs), its decays alpha = exp(g) (in place over the
+    //      gates) and its ring records, before any state row is touched: the
+    //      conv history of each owned channel steps through the chunk in
+    //      registers
 #pragma unroll
-        for (int m = 0; m < CPT; ++m) {
-            if (!own[m]) continue;
-            const float x = xs[tt][tid + NT * m];
+    for (int m = 0; m < CPT; ++m) {
+        if (!own[m]) continue;
+        const int j = tid + NT * m;
+        for (int tt = 0; tt < nc; ++tt) {
+            const int t = t0 + tt;
+            const int pos = (a.ring_base[b] + t) & (R.L - 1);
+            const int64_t bt = (int64_t)b * a.D + t;
+            const float x = xs[tt][j];
             float y = x;
             if constexpr (CONV) {
                 float acc = bias[m];
@@ -214,49 +219,55 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
                 }
             }
             y = round_to<IOT>(y);
-            const int j = tid + NT * m;
-            yb[j] = y;
+            xs[tt][j] = y;
             if (j >= 2 * HD) st<IOT>(R.rawv, ring_at(slot, a.Hv, R.L, h, pos, HD) + (j - 2 * HD), y);
             else if (j >= HD) st<IOT>(R.rawk, ring_at(slot, a.Hv, R.L, h, pos, HD) + (j - HD), y);
         }
-        __syncthreads();  // this step's q|k|v complete (the other buffer is still being read)
-
-        // ---- norms (every wave computes the same values), normalised k in the ring
-        const float q0 = yb[lane], q1 = yb[lane + 64];
-        const float k0 = yb[HD + lane], k1 = yb[HD + lane + 64];
+    }
+    for (int i = tid; i < nc * HD; i += NT) {
+        const int tt = i / HD, c = i % HD;
+        const int pos = (a.ring_base[b] + t0 + tt) & (R.L - 1);
+        const float g = gs[tt][c];
+        if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
+        else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
+        if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
+        gs[tt][c] = fast_exp(g);
+    }
+    __syncthreads();  // the chunk's q|k|v and decays complete
+    // ---- the steps' norms, wave w taking steps w, w + NW, ..; normalised k
+    //      to the ring
+    for (int tt = wave; tt < nc; tt += Cfg::NW) {
+        const int pos = (a.ring_base[b] + t0 + tt) & (R.L - 1);
+        const float q0 = xs[tt][lane], q1 = xs[tt][lane + 64];
+        const float k0 = xs[tt][HD + lane], k1 = xs[tt][HD + lane + 64];
         const float inv_q = inv_norm128(q0, q1, a.eps);
         const float inv_k = inv_norm128(k0, k1, a.eps);
-        if (wave == 0) {
-            const int64_t kr = ring_at(slot, a.Hv, R.L, h, pos, HD);
-            st<IOT>(R.k, kr + lane, k0 * inv_k);
-            st<IOT>(R.k, kr + lane + 64, k1 * inv_k);
+        if (lane == 0) {
+            nq[tt] = inv_q;
+            nk[tt] = inv_k;
         }
+        const int64_t kr = ring_at(slot, a.Hv, R.L, h, pos, HD);
+        st<IOT>(R.k, kr + lane, k0 * inv_k);
+        st<IOT>(R.k, kr + lane + 64, k1 * inv_k);
+    }
+    __syncthreads();
+    // ---- the steps: only the state rows, with no barrier between steps
+    for (int tt = 0; tt < nc; ++tt) {
+        const int t = t0 + tt;
+        const int pos = (a.ring_base[b] + t) & (R.L - 1);
+        const float inv_q = nq[tt], inv_k = nk[tt];
         float kk[EPL], qq[EPL], al[EPL];
-        float gv[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) gv[e] = gs[tt][col0 + e];
-        const float beta = bs[tt];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            kk[e] = yb[HD + col0 + e] * inv_k;
-            qq[e] = yb[col0 + e] * inv_q;
-            al[e] = fast_exp(gv[e]);
+            kk[e] = xs[tt][HD + col0 + e] * inv_k;
+            qq[e] = xs[tt][col0 + e] * inv_q;
+            al[e] = gs[tt][col0 + e];
         }
-        if (tid < LPR) {  // one row group records the gates
-            if constexpr (KDA) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + col0 + e] = gv[e];
-            } else if (tid == 0) {
-                R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = gv[0];
-            }
-            if (tid == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = beta;
-        }
-
-        // ---- rows: the shared step, then o = scale S_t q
+        const float beta = bs[tt];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int r = (wave * NJ + j) * RPW + lane / LPR;
-            const float d = row_step<EPL, LPR>(s[j], al, kk, yb[2 * HD + r], beta);
+            const float d = row_step<EPL, LPR>(s[j], al, kk, xs[tt][2 * HD + r], beta);
             float p = 0.f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) p = fmaf(s[j][e], qq[e], p);
