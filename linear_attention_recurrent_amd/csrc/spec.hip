@@ -264,6 +264,9 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
             al[e] = gs[tt][col0 + e];
         }
         const float beta = bs[tt];
+        // every lane of a row group gets the row's sums; lane (l % LPR == j)
+        // keeps row instruction j's, so each lane stores once per step
+        float my_o = 0.f, my_d = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int r = (wave * NJ + j) * RPW + lane / LPR;
@@ -272,10 +275,15 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
 #pragma unroll
             for (int e = 0; e < EPL; ++e) p = fmaf(s[j][e], qq[e], p);
             p = group_sum<LPR>(p);
-            if (lane % LPR == 0) {
-                st<IOT>(a.out, out_at(t, r), a.scale * p);
-                st<IOT>(R.d, ring_at(slot, a.Hv, R.L, h, pos, HD) + r, d);
+            if (lane % LPR == j) {
+                my_o = p;
+                my_d = d;
             }
+        }
+        const int jl = lane % LPR, r = (wave * NJ + jl) * RPW + lane / LPR;
+        if (jl < NJ) {
+            st<IOT>(a.out, out_at(t, r), a.scale * my_o);
+            st<IOT>(R.d, ring_at(slot, a.Hv, R.L, h, pos, HD) + r, my_d);
         }
     }
     }
