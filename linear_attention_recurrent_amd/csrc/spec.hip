@@ -298,7 +298,7 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitA
     using Cfg = DecodeCfg<HD, ST>;
     constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
     constexpr int VPT = (kChunk * HD + NT - 1) / NT;  // staged ring values per thread
-    __shared__ float ks[kChunk][HD], vs[kChunk][HD], gsh[kChunk][HD], bsh[kChunk];
+    __shared__ float ks[kChunk][HD], vs[kChunk][HD], gsh[kChunk][HD], bsh[kChunk], nk[kChunk];
     const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int slot = a.slots[b];
@@ -344,13 +344,21 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitA
         }
         if (tid < kChunk) bsh[tid] = bv;
         __syncthreads();
-        for (int tt = 0; tt < nc; ++tt) {
+        // the chunk's inverse k norms (wave w: steps w, w + NW, ..) and its
+        // decays alpha = exp(g) (in place), formed once for all rows
+        for (int tt = wave; tt < nc; tt += Cfg::NW) {
             const float inv_k = inv_norm128(ks[tt][lane], ks[tt][lane + 64], a.eps);
+            if (lane == 0) nk[tt] = inv_k;
+        }
+        for (int i = tid; i < nc * HD; i += NT) gsh[i / HD][i % HD] = fast_exp(gsh[i / HD][i % HD]);
+        __syncthreads();
+        for (int tt = 0; tt < nc; ++tt) {
+            const float inv_k = nk[tt];
             float kk[EPL], al[EPL];
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 kk[e] = ks[tt][col0 + e] * inv_k;
-                al[e] = fast_exp(gsh[tt][col0 + e]);
+                al[e] = gsh[tt][col0 + e];
             }
             const float beta = bsh[tt];
 #pragma unroll
