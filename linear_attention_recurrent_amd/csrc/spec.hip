@@ -110,28 +110,23 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
         st<IOT>(a.out, out_at(i / HD, i % HD), 0.f);
     if (first_zero == 0) return;
 
-    // The channels this thread owns (local index j = tid + NT m over [q | k | v]
-    // of this head) and their conv history, carried across the steps.
-    int gch[CPT];
-    bool own[CPT], win_out[CPT];
-    float h0[CPT], h1[CPT], h2[CPT], bias[CPT];
-    float4 wc[CPT];
+    // The local channel j (over [q | k | v] of this head) -> global channel.
+    auto glob = [&](int j) {
+        return j < HD ? kh * HD + j
+             : j < 2 * HD ? a.Hqk * HD + kh * HD + (j - HD) : 2 * a.Hqk * HD + h * HD + (j - 2 * HD);
+    };
+    // The conv history of the channels this thread owns (local index
+    // j = tid + NT m), carried across the steps.  Everything else about a
+    // channel (its global index, weights, bias) is re-derived in each chunk,
+    // so only the history stays live across chunks.
+    float h0[CPT], h1[CPT], h2[CPT];
+    if constexpr (CONV) {
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) {
-        const int j = tid + NT * m, jj = min(j, NCH - 1);
-        own[m] = j < NCH;
-        gch[m] = jj < HD ? kh * HD + jj
-               : jj < 2 * HD ? a.Hqk * HD + kh * HD + (jj - HD)
-                             : 2 * a.Hqk * HD + h * HD + (jj - 2 * HD);
-        // q/k windows are written by the first value head of the group only
-        win_out[m] = own[m] && (jj >= 2 * HD || h % a.G == 0);
-        if constexpr (CONV) {
-            const int64_t row = (int64_t)slot * a.conv_stride;
-            h0[m] = ld<CT>(a.conv_pool, row + gch[m]);
-            h1[m] = ld<CT>(a.conv_pool, row + a.C + gch[m]);
-            h2[m] = ld<CT>(a.conv_pool, row + 2 * a.C + gch[m]);
-            wc[m] = reinterpret_cast<const float4 *>(a.w)[gch[m]];
-            bias[m] = a.bias ? a.bias[gch[m]] : 0.f;
+        for (int m = 0; m < CPT; ++m) {
+            const int64_t c = (int64_t)slot * a.conv_stride + glob(min(tid + NT * m, NCH - 1));
+            h0[m] = ld<CT>(a.conv_pool, c);
+            h1[m] = ld<CT>(a.conv_pool, c + a.C);
+            h2[m] = ld<CT>(a.conv_pool, c + 2 * a.C);
         }
     }
 
@@ -148,30 +143,39 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
     const int col0 = (lane % LPR) * EPL;
     const RingArgs &R = a.ring;
 
-    // The local channel j (over [q | k | v] of this head) -> global channel.
-    auto glob = [&](int j) {
-        return j < HD ? kh * HD + j
-             : j < 2 * HD ? a.Hqk * HD + kh * HD + (j - HD) : 2 * a.Hqk * HD + h * HD + (j - 2 * HD);
-    };
     for (int t0 = 0; t0 < n; t0 += kChunk) {
     // ---- stage the chunk's inputs and gates in LDS: every load issued back to
-    //      back (indices clamped into the chunk, so no branch around a load)
+    //      back (indices clamped into the chunk, so no branch around a load).
+    //      The staging indices are re-derived from an opaque copy of the
+    //      thread id in each chunk, so they are not kept live across chunks.
     const int nc = min(kChunk, n - t0);
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    float4 wc[CPT];
+    float bias[CPT];
     {
         float xv[XPT], gv2[GPT], bv = 0.f;
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
-            const int i = min(tid + q * NT, kChunk * NCH - 1);
+            const int i = min(ltid + q * NT, kChunk * NCH - 1);
             const int tt = min(i / NCH, nc - 1);
             xv[q] = ld<IOT>(a.x, ((int64_t)b * a.D + t0 + tt) * a.C + glob(i % NCH));
         }
 #pragma unroll
         for (int q = 0; q < GPT; ++q) {
-            const int i = min(tid + q * NT, kChunk * HD - 1);
+            const int i = min(ltid + q * NT, kChunk * HD - 1);
             const int64_t bt = (int64_t)b * a.D + t0 + min(i / HD, nc - 1);
             gv2[q] = KDA ? a.g[(bt * a.Hv + h) * HD + i % HD] : a.g[bt * a.Hv + h];
         }
         if (tid < kChunk) bv = a.beta[((int64_t)b * a.D + t0 + min(tid, nc - 1)) * a.Hv + h];
+        if constexpr (CONV) {
+#pragma unroll
+            for (int m = 0; m < CPT; ++m) {
+                const int gc = glob(min(ltid + NT * m, NCH - 1));
+                wc[m] = reinterpret_cast<const float4 *>(a.w)[gc];
+                bias[m] = a.bias ? a.bias[gc] : 0.f;
+            }
+        }
         __syncthreads();  // the previous chunk's staged values are no longer read
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
@@ -193,8 +197,11 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
     //      registers
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
-        if (!own[m]) continue;
-        const int j = tid + NT * m;
+        const int j = ltid + NT * m;
+        if (j >= NCH) continue;
+        const int gc = glob(j);
+        // q/k windows are written by the first value head of the group only
+        const bool win_out = j >= 2 * HD || h % a.G == 0;
         for (int tt = 0; tt < nc; ++tt) {
             const int t = t0 + tt;
             const int pos = (a.ring_base[b] + t) & (R.L - 1);
@@ -211,8 +218,8 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
                 h0[m] = h1[m];
                 h1[m] = h2[m];
                 h2[m] = round_to<CT>(x);
-                if (win_out[m]) {
-                    const int64_t wrow = bt * 3 * a.C + gch[m];
+                if (win_out) {
+                    const int64_t wrow = bt * 3 * a.C + gc;
                     st<CT>(a.windows, wrow, h0[m]);
                     st<CT>(a.windows, wrow + a.C, h1[m]);
                     st<CT>(a.windows, wrow + 2 * a.C, h2[m]);
