@@ -259,7 +259,11 @@ typedef struct la_ring {
  * tokens run from the conv history and state of pool row slots[b] -- neither
  * pool is modified -- through the short conv + SiLU (output rounded to
  * io_dtype, the dtype a separate conv kernel would store), the L2 norms and the
- * gated delta rule, the state carried in fp32 across the tokens.
+ * gated delta rule.  Two forms, chosen by D: up to 8 tokens the chunk form
+ * (the outputs and d from one product of the checkpoint with the steps'
+ * decayed keys and queries, plus the 8x8 intra-step terms: equal to the
+ * sequential rule up to rounding); beyond 8 the sequential form, the state
+ * carried in fp32 across the tokens with the commit's per-step arithmetic.
  *   x [B, D, C] (io_dtype); conv_w [C, 4] or NULL (x is then post-conv and
  *     conv_windows is not written); conv_b [C] or NULL.
  *   g [B, D, H_v, d_k] fp32; beta [B, D, H_v] fp32; slots, n_tok [B] int32.

@@ -23,18 +23,21 @@
 //              no replay of the delta rule (that page's d/k/g passage).
 // The conv output is rounded to the I/O dtype before the recurrence, as a
 // separate conv kernel's output tensor would be, so the ring holds exactly the
-// values verify used and the commit reproduces verify's arithmetic: both
-// kernels run the same per-row update code.
+// values verify used.
 //
-// Work decomposition of verify and commit: one workgroup per (request, value
-// head), the head's state rows spread over the waves as in the decode kernel
-// (16-byte lane chunks, LPR lanes per row), held in fp32 registers across the
-// steps.  Verify forms a chunk's q|k|v conv outputs, decays, norms and ring
-// records up front, so its steps only update the state rows, with no barrier
-// between steps.  Both kernels first stage
-// the inputs of up to eight steps in LDS (verify: the pre-conv inputs of the
-// head's channels and the gates; commit: the ring records), with every load
-// issued back to back, so a step waits for memory once per eight steps.
+// Verify has two forms.  Up to eight steps (the usual draft length) the chunk
+// form: the steps' outputs and d come from one matrix-core product of the
+// checkpoint with the steps' decayed keys and queries plus an 8x8 triangular
+// recurrence, so the state is read once and no per-element arithmetic is
+// spent on it.  Beyond eight steps the sequential form: one workgroup per
+// (request, value head), the head's state rows spread over the waves as in
+// the decode kernel (16-byte lane chunks, LPR lanes per row), held in fp32
+// registers across the steps, every step running the per-row update the
+// commit runs (the two agree bit for bit with an fp32 state).  It forms a
+// chunk's q|k|v conv outputs, decays, norms and ring records up front, so
+// its steps only update the state rows, with no barrier between steps.
+// Commit stages the ring records of up to eight steps in LDS, with every
+// load issued back to back, so a step waits for memory once per eight steps.
 #include "decode_kernel.h"
 #include "la_device.h"
 #include "la_internal.h"
@@ -51,6 +54,21 @@ template <> __device__ __forceinline__ float round_to<float>(float v) { return v
 template <> __device__ __forceinline__ float round_to<bf16_t>(float v)
 {
     return bf16_to_f32(f32_to_bf16(v));
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// v = hi + lo to about 16 significant bits: hi = bf16(v), lo = bf16(v - hi)
+// (both nearest even).
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8_t &hi, bf16x8_t &lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 x = static_cast<__bf16>(v[e]);
+        hi[e] = x;
+        lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(x));
+    }
 }
 
 __device__ __forceinline__ int64_t ring_at(int slot, int Hv, int L, int h, int pos, int n)
@@ -86,75 +104,80 @@ __device__ __forceinline__ float inv_norm128(float x0, float x1, float eps)
 // ---------------------------------------------------------------------------
 // verify
 // ---------------------------------------------------------------------------
-template <typename ST, typename IOT, typename CT, bool KDA, bool CONV>
-__global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyArgs a)
+// The per-chunk front half shared by both verify kernels.  For the steps
+// t0 .. t0 + nc - 1 of request b, value head h it
+//   - stages the pre-conv inputs of the head's q|k|v channels in xe rows
+//     3 .. 3 + nc - 1 below the three inputs before the chunk (rows 0 .. 2:
+//     the conv state for the first chunk, else the previous chunk's last
+//     three inputs), the gates in gs and the betas in bs;
+//   - runs the short conv into ys (rounded to the I/O dtype, as a separate
+//     conv kernel's output tensor would be), every (channel, step) from the
+//     staged rows alone, so the work splits evenly over the threads;
+//   - writes the conv windows (the history after each step: xe rows
+//     tt + 1 .. tt + 3) and the ring records (rawk, rawv, g, beta and the
+//     normalised k) with 16-byte stores where the rows allow;
+//   - leaves the inverse norms in nq / nk and the gates as exp(g) per step
+//     (CUM = false: the sequential update) or as the running sum G_t of g
+//     over the chunk (CUM = true: the chunk form).
+// Ends with a barrier after everything later phases read from LDS.
+constexpr int XLD = 3 * HD + 4;   // xe / ys row stride (floats): rows shift banks
+constexpr int GLD = HD + 4;       // gs row stride (floats)
+
+// 16 bytes of elements of type T from floats (nearest even for bf16).
+template <typename T> struct V16;
+template <> struct V16<float> {
+    static constexpr int N = 4;
+    __device__ static __forceinline__ uint4 pack(const float *v)
+    {
+        return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3]));
+    }
+};
+template <> struct V16<bf16_t> {
+    static constexpr int N = 8;
+    __device__ static __forceinline__ uint4 pack(const float *v)
+    {
+        return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+};
+template <typename T>
+__device__ __forceinline__ void store16(void *base, int64_t elem, const float *v)
 {
-    using Cfg = DecodeCfg<HD, ST>;
-    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
-    constexpr int NCH = 3 * HD;                // the head's q, k, v channels
-    constexpr int CPT = (NCH + NT - 1) / NT;   // channels per thread
-    constexpr int XPT = (kChunk * NCH + NT - 1) / NT;  // staged inputs per thread
-    constexpr int GPT = (kChunk * HD + NT - 1) / NT;   // staged gates per thread
-    __shared__ float xs[kChunk][NCH];          // the chunk's pre-conv inputs, then its q|k|v
-    __shared__ float nq[kChunk], nk[kChunk];   // the chunk's inverse q and k norms
-    __shared__ float gs[kChunk][HD];           // the chunk's log-decays, then exp of them (GDN: broadcast)
-    __shared__ float bs[kChunk];               // the chunk's betas
+    *reinterpret_cast<uint4 *>(static_cast<T *>(base) + elem) = V16<T>::pack(v);
+}
 
-    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv, kh = h / a.G;
+template <typename IOT, typename CT, bool KDA, bool CONV, int NT, bool CUM, class Issue>
+__device__ __forceinline__ void verify_front(const VerifyArgs &a, int b, int h, int kh, int slot,
+                                             int rb, int t0, int nc, float (*xe)[XLD],
+                                             float (*ys)[XLD], float (*gs)[GLD], float *bs,
+                                             float *nq, float *nk, Issue &&issue)
+{
+    constexpr int NCH = 3 * HD;                                // q, k, v channels
+    constexpr int XPT = (kChunk * NCH + NT - 1) / NT;          // staged inputs per thread
+    constexpr int GPT = (kChunk * HD + NT - 1) / NT;           // staged gates per thread
+    constexpr int HPT = (3 * NCH + NT - 1) / NT;               // history values per thread
+    constexpr int IPT = (2 * NCH + NT - 1) / NT;               // conv items per thread
+    constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = a.slots[b];
-    const int n = min(max(a.n_tok[b], 0), a.D);
-    auto out_at = [&](int t, int i) { return (((int64_t)b * a.D + t) * a.Hv + h) * HD + i; };
-    const int first_zero = (slot < 0 || slot >= a.num_rows) ? 0 : n;
-    for (int i = tid + first_zero * HD; i < a.D * HD; i += NT)  // steps past n (or a skipped entry)
-        st<IOT>(a.out, out_at(i / HD, i % HD), 0.f);
-    if (first_zero == 0) return;
-
+    const RingArgs &R = a.ring;
     // The local channel j (over [q | k | v] of this head) -> global channel.
     auto glob = [&](int j) {
         return j < HD ? kh * HD + j
              : j < 2 * HD ? a.Hqk * HD + kh * HD + (j - HD) : 2 * a.Hqk * HD + h * HD + (j - 2 * HD);
     };
-    // The conv history of the channels this thread owns (local index
-    // j = tid + NT m), carried across the steps.  Everything else about a
-    // channel (its global index, weights, bias) is re-derived in each chunk,
-    // so only the history stays live across chunks.
-    float h0[CPT], h1[CPT], h2[CPT];
-    if constexpr (CONV) {
-#pragma unroll
-        for (int m = 0; m < CPT; ++m) {
-            const int64_t c = (int64_t)slot * a.conv_stride + glob(min(tid + NT * m, NCH - 1));
-            h0[m] = ld<CT>(a.conv_pool, c);
-            h1[m] = ld<CT>(a.conv_pool, c + a.C);
-            h2[m] = ld<CT>(a.conv_pool, c + 2 * a.C);
-        }
-    }
-
-    // The head's state rows, unpacked to fp32 registers for the whole call.
-    const ST *S = static_cast<const ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride +
-                  (int64_t)h * HD * HD;
-    float s[NJ][EPL];
-    {
-        uint4 raw[NJ];
-        load_rows<HD, ST>(raw, S, wave, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
-    }
-    const int col0 = (lane % LPR) * EPL;
-    const RingArgs &R = a.ring;
-
-    for (int t0 = 0; t0 < n; t0 += kChunk) {
-    // ---- stage the chunk's inputs and gates in LDS: every load issued back to
-    //      back (indices clamped into the chunk, so no branch around a load).
-    //      The staging indices are re-derived from an opaque copy of the
-    //      thread id in each chunk, so they are not kept live across chunks.
-    const int nc = min(kChunk, n - t0);
+    // Conv items: item i = tid + NT m is channel i % NCH over the steps of
+    // half i / NCH of the chunk (steps 4 half .. 4 half + 3).
+    // ---- staging: every load issued back to back (indices clamped into the
+    //      chunk, so no branch around a load).  The staging indices are
+    //      re-derived from an opaque copy of the thread id in each chunk, so
+    //      they are not kept live across chunks.
     int ltid = tid;
     asm volatile("" : "+v"(ltid));
-    float4 wc[CPT];
-    float bias[CPT];
+    float4 wc[IPT];
+    float bias[IPT];
     {
-        float xv[XPT], gv2[GPT], bv = 0.f;
+        float xv[XPT], gv2[GPT], hv[HPT], bv = 0.f;
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
             const int i = min(ltid + q * NT, kChunk * NCH - 1);
@@ -170,17 +193,43 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
         if (tid < kChunk) bv = a.beta[((int64_t)b * a.D + t0 + min(tid, nc - 1)) * a.Hv + h];
         if constexpr (CONV) {
 #pragma unroll
-            for (int m = 0; m < CPT; ++m) {
-                const int gc = glob(min(ltid + NT * m, NCH - 1));
+            for (int m = 0; m < IPT; ++m) {
+                const int gc = glob(min(ltid + NT * m, 2 * NCH - 1) % NCH);
                 wc[m] = reinterpret_cast<const float4 *>(a.w)[gc];
                 bias[m] = a.bias ? a.bias[gc] : 0.f;
             }
+            if (t0 == 0) {  // the conv state: rows 0 .. 2
+#pragma unroll
+                for (int q = 0; q < HPT; ++q) {
+                    const int i = min(ltid + q * NT, 3 * NCH - 1);
+                    hv[q] = ld<CT>(a.conv_pool, (int64_t)slot * a.conv_stride +
+                                                    (int64_t)(i / NCH) * a.C + glob(i % NCH));
+                }
+            } else {        // the previous (full) chunk's last three inputs
+#pragma unroll
+                for (int q = 0; q < HPT; ++q) {
+                    const int i = min(tid + q * NT, 3 * NCH - 1);
+                    hv[q] = round_to<CT>(xe[kChunk + i / NCH][i % NCH]);
+                }
+            }
         }
+        // The caller's own loads (the state) go out behind the small staged
+        // ones: the waits for those then never wait on the state.
+        __builtin_amdgcn_sched_barrier(0);
+        issue();
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();  // the previous chunk's staged values are no longer read
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
             const int i = tid + q * NT;
-            if (i < kChunk * NCH) xs[i / NCH][i % NCH] = xv[q];
+            if (i < kChunk * NCH) xe[3 + i / NCH][i % NCH] = xv[q];
+        }
+        if constexpr (CONV) {
+#pragma unroll
+            for (int q = 0; q < HPT; ++q) {
+                const int i = tid + q * NT;
+                if (i < 3 * NCH) xe[i / NCH][i % NCH] = hv[q];
+            }
         }
 #pragma unroll
         for (int q = 0; q < GPT; ++q) {
@@ -190,109 +239,522 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
         if (tid < kChunk) bs[tid] = bv;
         __syncthreads();
     }
-    // ---- the chunk's conv outputs (rounded to the I/O dtype, in place over
-    //      the staged inputs), its decays alpha = exp(g) (in place over the
-    //      gates) and its ring records, before any state row is touched: the
-    //      conv history of each owned channel steps through the chunk in
-    //      registers
+    // ---- the conv outputs, rounded to the I/O dtype
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) {
-        const int j = ltid + NT * m;
-        if (j >= NCH) continue;
-        const int gc = glob(j);
-        // q/k windows are written by the first value head of the group only
-        const bool win_out = j >= 2 * HD || h % a.G == 0;
-        for (int tt = 0; tt < nc; ++tt) {
-            const int t = t0 + tt;
-            const int pos = (a.ring_base[b] + t) & (R.L - 1);
-            const int64_t bt = (int64_t)b * a.D + t;
-            const float x = xs[tt][j];
-            float y = x;
-            if constexpr (CONV) {
+    for (int m = 0; m < IPT; ++m) {
+        const int i = ltid + NT * m;
+        if (i >= 2 * NCH) continue;
+        const int j = i % NCH, t_lo = 4 * (i / NCH), t_hi = min(t_lo + 4, nc);
+        if constexpr (CONV) {
+            // taps: the history rounded to the conv dtype, the input as is
+            float x0 = round_to<CT>(xe[t_lo][j]), x1 = round_to<CT>(xe[t_lo + 1][j]);
+            float x2 = round_to<CT>(xe[t_lo + 2][j]);
+            for (int tt = t_lo; tt < t_hi; ++tt) {
+                const float x3 = xe[tt + 3][j];
                 float acc = bias[m];
-                acc = fmaf(wc[m].x, h0[m], acc);
-                acc = fmaf(wc[m].y, h1[m], acc);
-                acc = fmaf(wc[m].z, h2[m], acc);
-                acc = fmaf(wc[m].w, x, acc);
-                y = silu(acc);
-                h0[m] = h1[m];
-                h1[m] = h2[m];
-                h2[m] = round_to<CT>(x);
-                if (win_out) {
-                    const int64_t wrow = bt * 3 * a.C + gc;
-                    st<CT>(a.windows, wrow, h0[m]);
-                    st<CT>(a.windows, wrow + a.C, h1[m]);
-                    st<CT>(a.windows, wrow + 2 * a.C, h2[m]);
-                }
+                acc = fmaf(wc[m].x, x0, acc);
+                acc = fmaf(wc[m].y, x1, acc);
+                acc = fmaf(wc[m].z, x2, acc);
+                acc = fmaf(wc[m].w, x3, acc);
+                ys[tt][j] = round_to<IOT>(silu(acc));
+                x0 = x1;
+                x1 = x2;
+                x2 = round_to<CT>(x3);
             }
-            y = round_to<IOT>(y);
-            xs[tt][j] = y;
-            if (j >= 2 * HD) st<IOT>(R.rawv, ring_at(slot, a.Hv, R.L, h, pos, HD) + (j - 2 * HD), y);
-            else if (j >= HD) st<IOT>(R.rawk, ring_at(slot, a.Hv, R.L, h, pos, HD) + (j - HD), y);
+        } else {
+            for (int tt = t_lo; tt < t_hi; ++tt) ys[tt][j] = xe[tt + 3][j];
         }
     }
-    for (int i = tid; i < nc * HD; i += NT) {
-        const int tt = i / HD, c = i % HD;
-        const int pos = (a.ring_base[b] + t0 + tt) & (R.L - 1);
-        const float g = gs[tt][c];
-        if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
-        else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
-        if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
-        gs[tt][c] = fast_exp(g);
+    // ---- gates to the ring; then exp(g) per step, or the running sum of g
+    if constexpr (CUM) {
+        for (int c = tid; c < HD; c += NT) {
+            float G = 0.f;
+            for (int tt = 0; tt < nc; ++tt) {
+                const int pos = (rb + t0 + tt) & (R.L - 1);
+                const float g = gs[tt][c];
+                if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
+                else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
+                if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
+                G += g;
+                gs[tt][c] = G;
+            }
+        }
+    } else {
+        for (int i = tid; i < nc * HD; i += NT) {
+            const int tt = i / HD, c = i % HD;
+            const int pos = (rb + t0 + tt) & (R.L - 1);
+            const float g = gs[tt][c];
+            if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
+            else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
+            if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
+            gs[tt][c] = fast_exp(g);
+        }
     }
-    __syncthreads();  // the chunk's q|k|v and decays complete
-    // ---- the steps' norms, wave w taking steps w, w + NW, ..; normalised k
-    //      to the ring
-    for (int tt = wave; tt < nc; tt += Cfg::NW) {
-        const int pos = (a.ring_base[b] + t0 + tt) & (R.L - 1);
-        const float q0 = xs[tt][lane], q1 = xs[tt][lane + 64];
-        const float k0 = xs[tt][HD + lane], k1 = xs[tt][HD + lane + 64];
-        const float inv_q = inv_norm128(q0, q1, a.eps);
-        const float inv_k = inv_norm128(k0, k1, a.eps);
+    // ---- the conv windows: after step tt the history is xe rows
+    //      tt + 1 .. tt + 3; q/k windows come from the first value head of
+    //      the group only
+    if constexpr (CONV) {
+        constexpr int VN = V16<CT>::N, GR = HD / VN;  // channels per store, stores per block
+        const int nblk = h % a.G == 0 ? 3 : 1, blk0 = 3 - nblk;
+        for (int i = tid; i < nc * 3 * nblk * GR; i += NT) {
+            const int grp = i % GR, blk = blk0 + (i / GR) % nblk, rr = (i / (GR * nblk)) % 3;
+            const int tt = i / (GR * nblk * 3);
+            const int j = blk * HD + grp * VN;
+            float v[VN];
+#pragma unroll
+            for (int e = 0; e < VN; e += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(&xe[tt + 1 + rr][j + e]);
+                v[e] = round_to<CT>(f.x); v[e + 1] = round_to<CT>(f.y);
+                v[e + 2] = round_to<CT>(f.z); v[e + 3] = round_to<CT>(f.w);
+            }
+            store16<CT>(a.windows, (((int64_t)b * a.D + t0 + tt) * 3 + rr) * a.C + glob(j), v);
+        }
+    }
+    __syncthreads();  // ys, gs complete
+    // ---- the steps' norms, wave w taking steps w, w + NW, ..
+    for (int tt = wave; tt < nc; tt += NW) {
+        const float inv_q = inv_norm128(ys[tt][lane], ys[tt][lane + 64], a.eps);
+        const float inv_k = inv_norm128(ys[tt][HD + lane], ys[tt][HD + lane + 64], a.eps);
         if (lane == 0) {
             nq[tt] = inv_q;
             nk[tt] = inv_k;
         }
-        const int64_t kr = ring_at(slot, a.Hv, R.L, h, pos, HD);
-        st<IOT>(R.k, kr + lane, k0 * inv_k);
-        st<IOT>(R.k, kr + lane + 64, k1 * inv_k);
     }
-    __syncthreads();
-    // ---- the steps: only the state rows, with no barrier between steps
-    for (int tt = 0; tt < nc; ++tt) {
-        const int t = t0 + tt;
-        const int pos = (a.ring_base[b] + t) & (R.L - 1);
-        const float inv_q = nq[tt], inv_k = nk[tt];
-        float kk[EPL], qq[EPL], al[EPL];
+    __syncthreads();  // nq, nk complete
+    // ---- ring vectors rawk, rawv and the normalised k, 16 bytes a store
+    {
+        constexpr int VN = V16<IOT>::N, GR = HD / VN;
+        for (int i = tid; i < nc * 3 * GR; i += NT) {
+            const int grp = i % GR, which = (i / GR) % 3, tt = i / (3 * GR);
+            const int pos = (rb + t0 + tt) & (R.L - 1);
+            const int c = grp * VN, src = which == 1 ? 2 * HD + c : HD + c;
+            const float sc = which == 2 ? nk[tt] : 1.f;
+            float v[VN];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            kk[e] = xs[tt][HD + col0 + e] * inv_k;
-            qq[e] = xs[tt][col0 + e] * inv_q;
-            al[e] = gs[tt][col0 + e];
+            for (int e = 0; e < VN; e += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(&ys[tt][src + e]);
+                v[e] = f.x * sc; v[e + 1] = f.y * sc; v[e + 2] = f.z * sc; v[e + 3] = f.w * sc;
+            }
+            void *dst = which == 0 ? R.rawk : which == 1 ? R.rawv : R.k;
+            store16<IOT>(dst, ring_at(slot, a.Hv, R.L, h, pos, HD) + c, v);
         }
-        const float beta = bs[tt];
-        // every lane of a row group gets the row's sums; lane (l % LPR == j)
-        // keeps row instruction j's, so each lane stores once per step
-        float my_o = 0.f, my_d = 0.f;
+    }
+}
+
+// Sequential form, any number of steps: the state rows are carried in fp32
+// registers and every step runs the per-row update the commit runs.
+template <typename ST, typename IOT, typename CT, bool KDA, bool CONV>
+__global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyArgs a)
+{
+    using Cfg = DecodeCfg<HD, ST>;
+    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
+    __shared__ __align__(16) float xe[kChunk + 3][XLD];  // the chunk's inputs below the three before it
+    __shared__ __align__(16) float ys[kChunk][XLD];      // the chunk's q|k|v (conv outputs)
+    __shared__ float gs[kChunk][GLD];          // the chunk's decays exp(g) (GDN: broadcast)
+    __shared__ float nq[kChunk], nk[kChunk];   // the chunk's inverse q and k norms
+    __shared__ float bs[kChunk];               // the chunk's betas
+
+    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv, kh = h / a.G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int slot = a.slots[b], rb = a.ring_base[b];
+    const int n = min(max(a.n_tok[b], 0), a.D);
+    auto out_at = [&](int t, int i) { return (((int64_t)b * a.D + t) * a.Hv + h) * HD + i; };
+    const int first_zero = (slot < 0 || slot >= a.num_rows) ? 0 : n;
+    for (int i = tid + first_zero * HD; i < a.D * HD; i += NT)  // steps past n (or a skipped entry)
+        st<IOT>(a.out, out_at(i / HD, i % HD), 0.f);
+    if (first_zero == 0) return;
+
+    // The head's state rows, unpacked to fp32 registers for the whole call.
+    const ST *S = static_cast<const ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride +
+                  (int64_t)h * HD * HD;
+    float s[NJ][EPL];
+    {
+        uint4 raw[NJ];
+        load_rows<HD, ST>(raw, S, wave, lane);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int r = (wave * NJ + j) * RPW + lane / LPR;
-            const float d = row_step<EPL, LPR>(s[j], al, kk, xs[tt][2 * HD + r], beta);
-            float p = 0.f;
+        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
+    }
+    const int col0 = (lane % LPR) * EPL;
+    const RingArgs &R = a.ring;
+
+    for (int t0 = 0; t0 < n; t0 += kChunk) {
+        const int nc = min(kChunk, n - t0);
+        verify_front<IOT, CT, KDA, CONV, NT, false>(a, b, h, kh, slot, rb, t0, nc, xe, ys, gs, bs,
+                                                    nq, nk, [] {});
+        // ---- the steps: only the state rows, with no barrier between steps
+        for (int tt = 0; tt < nc; ++tt) {
+            const int t = t0 + tt;
+            const int pos = (rb + t) & (R.L - 1);
+            const float inv_q = nq[tt], inv_k = nk[tt];
+            float kk[EPL], qq[EPL], al[EPL];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) p = fmaf(s[j][e], qq[e], p);
-            p = group_sum<LPR>(p);
-            if (lane % LPR == j) {
-                my_o = p;
-                my_d = d;
+            for (int e = 0; e < EPL; ++e) {
+                kk[e] = ys[tt][HD + col0 + e] * inv_k;
+                qq[e] = ys[tt][col0 + e] * inv_q;
+                al[e] = gs[tt][col0 + e];
+            }
+            const float beta = bs[tt];
+            // every lane of a row group gets the row's sums; lane (l % LPR == j)
+            // keeps row instruction j's, so each lane stores once per step
+            float my_o = 0.f, my_d = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int r = (wave * NJ + j) * RPW + lane / LPR;
+                const float d = row_step<EPL, LPR>(s[j], al, kk, ys[tt][2 * HD + r], beta);
+                float p = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) p = fmaf(s[j][e], qq[e], p);
+                p = group_sum<LPR>(p);
+                if (lane % LPR == j) {
+                    my_o = p;
+                    my_d = d;
+                }
+            }
+            const int jl = lane % LPR, r = (wave * NJ + jl) * RPW + lane / LPR;
+            if (jl < NJ) {
+                st<IOT>(a.out, out_at(t, r), a.scale * my_o);
+                st<IOT>(R.d, ring_at(slot, a.Hv, R.L, h, pos, HD) + r, my_d);
             }
         }
-        const int jl = lane % LPR, r = (wave * NJ + jl) * RPW + lane / LPR;
-        if (jl < NJ) {
-            st<IOT>(a.out, out_at(t, r), a.scale * my_o);
-            st<IOT>(R.d, ring_at(slot, a.Hv, R.L, h, pos, HD) + r, my_d);
+    }
+}
+
+// Chunk form, at most kChunk steps (one chunk).  With G_t the running sum of
+// the log-decays over the steps (per channel; GDN: per head), k_t, q_t the
+// normalised keys and queries and S the checkpoint, the state the sequential
+// rule holds after its decay at step t is
+//   S'_t = S Diag(e^{G_t}) + sum_{j<t} d_j (k_j * e^{G_t - G_j})^T,
+// so with X = S [K~ | Q~]  (K~_t = k_t * e^{G_t}, Q~_t = q_t * e^{G_t}),
+//   A_tj = sum_c k_t[c] k_j[c] e^{G_t[c] - G_j[c]}   (j < t),
+//   P_tj = sum_c q_t[c] k_j[c] e^{G_t[c] - G_j[c]}   (j <= t):
+//   d_t = beta_t (v_t - X[:, t] - sum_{j<t} A_tj d_j),
+//   o_t = scale (X[:, 8 + t] + sum_{j<=t} P_tj d_j).
+// Every exponent is <= 0.  The one product that touches the state, X, is a
+// 128 x 16 x 128 matrix-core product per head (bf16 state: the state is the
+// exact bf16 operand and [K~ | Q~] a two-term bf16 split; fp32 state:
+// v_mfma_f32_16x16x4f32), so the state crosses HBM once and no per-element
+// arithmetic is spent on it.
+//
+// Phases (three workgroup barriers):
+//   1. staging: 16-byte loads of the head's inputs, conv state, conv weights
+//      and gates (then the state fragments); the gates' running sums and
+//      their ring records by 32 lanes holding four channels each;
+//   2. per (step, q|k|v block) unit, one wave: the conv of the block's 128
+//      channels at that step (two per lane), its ring records and conv
+//      window, and for q and k the norm (a wave sum) and the row of
+//      [K~ | Q~];
+//   3. the matrix-core product (every wave) and A, P (four lanes per pair);
+//   4. the d recurrence and the outputs per value row.
+template <typename T> __device__ __forceinline__ void store2(void *base, int64_t elem, float v0, float v1);
+template <> __device__ __forceinline__ void store2<float>(void *base, int64_t elem, float v0, float v1)
+{
+    *reinterpret_cast<float2 *>(static_cast<float *>(base) + elem) = make_float2(v0, v1);
+}
+template <> __device__ __forceinline__ void store2<bf16_t>(void *base, int64_t elem, float v0, float v1)
+{
+    *reinterpret_cast<uint32_t *>(static_cast<bf16_t *>(base) + elem) = pack_bf16x2(v0, v1);
+}
+// 16 bytes of T as floats.
+template <typename T> __device__ __forceinline__ void unpack16(const uint4 &r, float *v);
+template <> __device__ __forceinline__ void unpack16<float>(const uint4 &r, float *v)
+{
+    v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y);
+    v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+}
+template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4 &r, float *v)
+{
+    Stor<bf16_t>::unpack(r, v);
+}
+
+template <typename ST, typename IOT, typename CT, bool KDA, bool CONV>
+__global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
+{
+    constexpr int NT = 256;
+    constexpr int LDB = HD + 4;                     // [K~ | Q~] row stride (floats)
+    constexpr int LDX = 17;                         // X row stride (floats)
+    constexpr int FR = HD * (int)sizeof(ST) / 64;   // 64-byte row pieces: 4 (bf16) or 8 (fp32)
+    constexpr int NCH = 3 * HD;
+    __shared__ __align__(16) float xe[kChunk + 3][XLD];  // conv state rows 0..2, inputs below
+    __shared__ __align__(16) float ys[kChunk][XLD];      // q|k|v conv outputs
+    __shared__ __align__(16) float Gs[kChunk][GLD];      // running sums of the log-decays
+    __shared__ __align__(16) float Bm[16][LDB];          // rows t: K~_t, rows 8 + t: Q~_t
+    // X = S [K~ | Q~]^T after the product; the conv weights and biases before
+    __shared__ __align__(16) float Xw[HD * LDX > 5 * NCH ? HD * LDX : 5 * NCH];
+    __shared__ float Am[kChunk][kChunk], Pm[kChunk][kChunk];
+    __shared__ float nq[kChunk], nk[kChunk], bs[kChunk];
+    float4 *w4 = reinterpret_cast<float4 *>(Xw);     // [NCH] conv weights
+    float *wb = Xw + 4 * NCH;                         // [NCH] conv biases
+
+    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv, kh = h / a.G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const int slot = a.slots[b], rb = a.ring_base[b];
+    const int n = min(max(a.n_tok[b], 0), a.D);
+    auto out_at = [&](int t, int i) { return (((int64_t)b * a.D + t) * a.Hv + h) * HD + i; };
+    const int first_zero = (slot < 0 || slot >= a.num_rows) ? 0 : n;
+    for (int i = tid + first_zero * HD; i < a.D * HD; i += NT)  // steps past n (or a skipped entry)
+        st<IOT>(a.out, out_at(i / HD, i % HD), 0.f);
+    if (first_zero == 0) return;
+
+    const RingArgs &R = a.ring;
+    // first global channel of block blk (0 = q, 1 = k, 2 = v) of this head
+    auto gbase = [&](int blk) {
+        return blk == 0 ? kh * HD : blk == 1 ? (a.Hqk + kh) * HD : 2 * a.Hqk * HD + h * HD;
+    };
+    auto pos_of = [&](int t) { return (rb + t) & (R.L - 1); };
+
+    // ---- 1. staging ------------------------------------------------------
+    constexpr int VX = V16<IOT>::N, GX = HD / VX, NX = kChunk * 3 * GX, XI = (NX + NT - 1) / NT;
+    constexpr int VH = V16<CT>::N, GH = HD / VH, NH = 3 * 3 * GH, HI = (NH + NT - 1) / NT;
+    static_assert(NCH <= 2 * NT, "two conv weight vectors per thread");
+    uint4 xr[XI], hr[HI];
+    float4 g4[kChunk], wr0, wr1, br = make_float4(0.f, 0.f, 0.f, 0.f);
+    float bv = 0.f;
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+        const int i = min(tid + q * NT, NX - 1), grp = i % GX, blk = (i / GX) % 3;
+        const int tt = min(i / (3 * GX), n - 1);
+        xr[q] = *reinterpret_cast<const uint4 *>(static_cast<const IOT *>(a.x) +
+                                                 ((int64_t)b * a.D + tt) * a.C + gbase(blk) + grp * VX);
+    }
+    if (tid < 32) {  // lane l: channels 4 l .. 4 l + 3 of every step
+#pragma unroll
+        for (int tt = 0; tt < kChunk; ++tt) {
+            const int64_t bt = (int64_t)b * a.D + min(tt, n - 1);
+            if constexpr (KDA) {
+                g4[tt] = *reinterpret_cast<const float4 *>(a.g + (bt * a.Hv + h) * HD + 4 * tid);
+            } else {
+                const float g1 = a.g[bt * a.Hv + h];
+                g4[tt] = make_float4(g1, g1, g1, g1);
+            }
         }
     }
+    if (tid < kChunk) bv = a.beta[((int64_t)b * a.D + min(tid, n - 1)) * a.Hv + h];
+    if constexpr (CONV) {
+#pragma unroll
+        for (int q = 0; q < HI; ++q) {
+            const int i = min(tid + q * NT, NH - 1), grp = i % GH, blk = (i / GH) % 3, r = i / (3 * GH);
+            hr[q] = *reinterpret_cast<const uint4 *>(static_cast<const CT *>(a.conv_pool) +
+                                                     (int64_t)slot * a.conv_stride + (int64_t)r * a.C +
+                                                     gbase(blk) + grp * VH);
+        }
+        {
+            const int j0 = tid, j1 = min(tid + NT, NCH - 1);
+            wr0 = reinterpret_cast<const float4 *>(a.w)[gbase(j0 / HD) + j0 % HD];
+            wr1 = reinterpret_cast<const float4 *>(a.w)[gbase(j1 / HD) + j1 % HD];
+        }
+        if (tid < NCH / 4 && a.bias)
+            br = *reinterpret_cast<const float4 *>(a.bias + gbase(tid / (HD / 4)) + 4 * (tid % (HD / 4)));
+    }
+    // The state as matrix-core operand fragments, behind the staged loads:
+    // wave w owns rows 32w .. 32w + 31 (two 16-row tiles); lane (li, lq)
+    // holds 16 bytes at byte 64 f + 16 lq of row 16 T + li.  bf16: fragment
+    // f is k = 32 f + 8 lq + e (e < 8), one 16x16x32 step; fp32: fragment f
+    // is k = 16 f + 4 lq + e (e < 4), four 16x16x4 steps.
+    __builtin_amdgcn_sched_barrier(0);
+    const char *S = static_cast<const char *>(a.ssm_pool) +
+                    ((int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD) * sizeof(ST);
+    uint4 fr[2][FR];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int f = 0; f < FR; ++f)
+            fr[T][f] = ld_stream(S + (int64_t)(32 * wave + 16 * T + li) * HD * sizeof(ST) + 64 * f + 16 * lq);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+        const int i = tid + q * NT, grp = i % GX, blk = (i / GX) % 3, tt = i / (3 * GX);
+        if (i < NX && tt < n) {
+            float v[VX];
+            unpack16<IOT>(xr[q], v);
+#pragma unroll
+            for (int e = 0; e < VX; e += 4)
+                *reinterpret_cast<float4 *>(&xe[3 + tt][blk * HD + grp * VX + e]) =
+                    make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+        }
+    }
+    if constexpr (CONV) {
+#pragma unroll
+        for (int q = 0; q < HI; ++q) {
+            const int i = tid + q * NT, grp = i % GH, blk = (i / GH) % 3, r = i / (3 * GH);
+            if (i < NH) {
+                float v[VH];
+                unpack16<CT>(hr[q], v);
+#pragma unroll
+                for (int e = 0; e < VH; e += 4)
+                    *reinterpret_cast<float4 *>(&xe[r][blk * HD + grp * VH + e]) =
+                        make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+            }
+        }
+        w4[tid] = wr0;
+        if (tid + NT < NCH) w4[tid + NT] = wr1;
+        if (tid < NCH / 4) *reinterpret_cast<float4 *>(&wb[4 * tid]) = br;
+    }
+    if (tid < kChunk) {
+        bs[tid] = bv;
+        if (tid < n) R.beta[ring_at(slot, a.Hv, R.L, h, pos_of(tid), 1)] = bv;
+    }
+    if (tid < 32) {
+        float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int tt = 0; tt < kChunk; ++tt) {
+            if (tt < n) {
+                if constexpr (KDA)
+                    *reinterpret_cast<float4 *>(R.g + ring_at(slot, a.Hv, R.L, h, pos_of(tt), HD) + 4 * tid) = g4[tt];
+                else if (tid == 0)
+                    R.g[ring_at(slot, a.Hv, R.L, h, pos_of(tt), 1)] = g4[tt].x;
+                G.x += g4[tt].x; G.y += g4[tt].y; G.z += g4[tt].z; G.w += g4[tt].w;
+                *reinterpret_cast<float4 *>(&Gs[tt][4 * tid]) = G;
+            }
+        }
+    }
+    for (int i = tid; i < 16 * (HD / 4); i += NT) {  // rows of [K~ | Q~] past n are zero
+        const int r = i / (HD / 4);
+        if ((r & (kChunk - 1)) >= n)
+            *reinterpret_cast<float4 *>(&Bm[r][4 * (i % (HD / 4))]) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+
+    // ---- 2. units (step tt, block blk), one per wave at a time ------------
+    for (int u = wave; u < 3 * n; u += NT / 64) {
+        const int tt = u / 3, blk = u - 3 * tt, j = blk * HD + 2 * lane;
+        const float2 r3 = *reinterpret_cast<const float2 *>(&xe[tt + 3][j]);
+        float y0 = r3.x, y1 = r3.y;
+        float2 r1, r2;
+        if constexpr (CONV) {
+            const float2 r0 = *reinterpret_cast<const float2 *>(&xe[tt][j]);
+            r1 = *reinterpret_cast<const float2 *>(&xe[tt + 1][j]);
+            r2 = *reinterpret_cast<const float2 *>(&xe[tt + 2][j]);
+            const float4 wa = w4[j], wc = w4[j + 1];
+            const float2 bb = *reinterpret_cast<const float2 *>(&wb[j]);
+            float acc0 = bb.x, acc1 = bb.y;
+            acc0 = fmaf(wa.x, round_to<CT>(r0.x), acc0);
+            acc0 = fmaf(wa.y, round_to<CT>(r1.x), acc0);
+            acc0 = fmaf(wa.z, round_to<CT>(r2.x), acc0);
+            acc0 = fmaf(wa.w, r3.x, acc0);
+            acc1 = fmaf(wc.x, round_to<CT>(r0.y), acc1);
+            acc1 = fmaf(wc.y, round_to<CT>(r1.y), acc1);
+            acc1 = fmaf(wc.z, round_to<CT>(r2.y), acc1);
+            acc1 = fmaf(wc.w, r3.y, acc1);
+            y0 = round_to<IOT>(silu(acc0));
+            y1 = round_to<IOT>(silu(acc1));
+        }
+        *reinterpret_cast<float2 *>(&ys[tt][j]) = make_float2(y0, y1);
+        const int64_t rr = ring_at(slot, a.Hv, R.L, h, pos_of(tt), HD) + 2 * lane;
+        if (blk < 2) {
+            const float inv = 1.0f / sqrtf(wave_sum(fmaf(y1, y1, y0 * y0)) + a.eps);
+            if (lane == 0) (blk == 0 ? nq : nk)[tt] = inv;
+            const float2 G = *reinterpret_cast<const float2 *>(&Gs[tt][2 * lane]);
+            *reinterpret_cast<float2 *>(&Bm[blk == 1 ? tt : kChunk + tt][2 * lane]) =
+                make_float2(y0 * inv * fast_exp(G.x), y1 * inv * fast_exp(G.y));
+            if (blk == 1) {
+                store2<IOT>(R.rawk, rr, y0, y1);
+                store2<IOT>(R.k, rr, y0 * inv, y1 * inv);
+            }
+        } else {
+            store2<IOT>(R.rawv, rr, y0, y1);
+        }
+        if constexpr (CONV) {  // the history after step tt; q/k windows from the group's first head
+            if (blk == 2 || h % a.G == 0) {
+                const int64_t wrow = ((int64_t)b * a.D + tt) * 3 * a.C + gbase(blk) + 2 * lane;
+                store2<CT>(a.windows, wrow, round_to<CT>(r1.x), round_to<CT>(r1.y));
+                store2<CT>(a.windows, wrow + a.C, round_to<CT>(r2.x), round_to<CT>(r2.y));
+                store2<CT>(a.windows, wrow + 2 * a.C, round_to<CT>(r3.x), round_to<CT>(r3.y));
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. X = S [K~ | Q~]^T on the matrix cores (lane (li, lq) ends with
+    //      X[32 w + 16 T + 4 lq + r][li] in acc[T][r]), and A, P
+    f32x4 acc[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(ST) == 2) {
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+            const float4 b0 = *reinterpret_cast<const float4 *>(&Bm[li][32 * f + 8 * lq]);
+            const float4 b1 = *reinterpret_cast<const float4 *>(&Bm[li][32 * f + 8 * lq + 4]);
+            const float bv8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            bf16x8_t bh, bl;
+            split_bf16x8(bv8, bh, bl);
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fr[T][f]);
+                acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[T], 0, 0, 0);
+                acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[T], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+            const float4 bq = *reinterpret_cast<const float4 *>(&Bm[li][16 * f + 4 * lq]);
+            const float bv4[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int T = 0; T < 2; ++T) {
+                    const uint32_t w = e == 0 ? fr[T][f].x : e == 1 ? fr[T][f].y : e == 2 ? fr[T][f].z : fr[T][f].w;
+                    acc[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w), bv4[e], acc[T], 0, 0, 0);
+                }
+        }
+    }
+    float (*Xs)[LDX] = reinterpret_cast<float (*)[LDX]>(Xw);  // the weights are no longer read
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xs[32 * wave + 16 * T + 4 * lq + r][li] = acc[T][r];
+    // A and P: pair p of the 36 pairs (t, j <= t) on threads 112 + 4 p ..
+    // 112 + 4 p + 3, the four lanes of a quad splitting the channels
+    if (tid >= NT - 4 * 36) {
+        const int p = (tid - (NT - 4 * 36)) >> 2, qc = tid & 3;
+        int t = 0;
+        while ((t + 1) * (t + 2) / 2 <= p) ++t;
+        const int j = p - t * (t + 1) / 2;
+        float sa = 0.f, sp = 0.f;
+        if (t < n) {
+            for (int m = 0; m < HD / 4; ++m) {
+                const int c = qc + 4 * m;
+                const float w = ys[j][HD + c] * fast_exp(Gs[t][c] - Gs[j][c]);
+                sa = fmaf(ys[t][HD + c], w, sa);
+                sp = fmaf(ys[t][c], w, sp);
+            }
+        }
+        sa = group_sum<4>(sa);
+        sp = group_sum<4>(sp);
+        if (qc == 0 && t < n) {
+            Am[t][j] = j < t ? sa * nk[t] * nk[j] : 0.f;
+            Pm[t][j] = sp * nq[t] * nk[j];
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. per value row r: the d recurrence (both halves of the block),
+    //      then the outputs of steps 4 half .. 4 half + 3
+    {
+        const int r = tid & (HD - 1), half = tid / HD;
+        float d[kChunk];
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+            d[t] = 0.f;
+            if (t < n) {
+                float u = Xs[r][t];
+#pragma unroll
+                for (int jj = 0; jj < t; ++jj) u = fmaf(Am[t][jj], d[jj], u);
+                d[t] = bs[t] * (ys[t][2 * HD + r] - u);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+            if (t / (kChunk / 2) == half && t < n) {
+                float o = Xs[r][kChunk + t];
+#pragma unroll
+                for (int jj = 0; jj <= t; ++jj) o = fmaf(Pm[t][jj], d[jj], o);
+                st<IOT>(a.out, out_at(t, r), a.scale * o);
+                st<IOT>(R.d, ring_at(slot, a.Hv, R.L, h, pos_of(t), HD) + r, d[t]);
+            }
+        }
     }
 }
 
@@ -534,7 +996,15 @@ __global__ void __launch_bounds__(256) track_copy_kernel(TrackArgs a)
 template <typename ST, typename IOT, typename CT, bool KDA>
 hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(a.B * a.Hv)), block(DecodeCfg<HD, ST>::NT);
+    const dim3 grid((unsigned)(a.B * a.Hv));
+    if (a.D <= kChunk) {  // one chunk: the matrix-core form
+        if (a.w)
+            hipLaunchKernelGGL((verify_chunk_kernel<ST, IOT, CT, KDA, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((verify_chunk_kernel<ST, IOT, CT, KDA, false>), grid, dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
+    const dim3 block(DecodeCfg<HD, ST>::NT);
     if (a.w)
         hipLaunchKernelGGL((verify_kernel<ST, IOT, CT, KDA, true>), grid, block, 0, stream, a);
     else

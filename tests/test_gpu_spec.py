@@ -6,9 +6,12 @@ Bars: every step's output, the ring's vectors and the committed state within
 the relative-L2 tolerance of their storage dtype (1e-4 fp32, 2e-2 bf16) per
 (request, step, head) or (request, head); conv windows, the ring's gates, the
 scattered conv rows, the tracking copies and every untouched pool row
-bit-exact.  With an fp32 state, committing a verify's first steps and
+bit-exact.  Verify has two forms: up to 8 draft tokens the chunk form (one
+matrix-core product with the checkpoint), beyond that the sequential form;
+both are checked against the oracle.  Committing a verify's first steps and
 verifying the rest from the committed state reproduces the first call's later
-outputs bit for bit (commit and verify run the same arithmetic).
+outputs: bit for bit in the sequential form (commit and verify run the same
+per-row arithmetic there), within the fp32 bar in the chunk form.
 """
 import numpy as np
 import pytest
@@ -66,11 +69,12 @@ CASES = [  # kda, Hqk, Hv, io, state, conv
 ]
 
 
+@pytest.mark.parametrize("D", [8, 12])   # the chunk form, the sequential form
 @pytest.mark.parametrize("kda,Hqk,Hv,io,state,conv", CASES)
-def test_verify_and_commit_match_oracle(kda, Hqk, Hv, io, state, conv, dev):
-    B, D, P = 4, 8, 10
-    c = make_case(7100 + Hv + 10 * kda, B, D, Hqk, Hv, kda, io, state, conv, P, dev)
-    n_tok = [8, 5, 1, 0]
+def test_verify_and_commit_match_oracle(kda, Hqk, Hv, io, state, conv, D, dev):
+    B, P = 4, 10
+    c = make_case(7100 + Hv + 10 * kda + D, B, D, Hqk, Hv, kda, io, state, conv, P, dev)
+    n_tok = [D, 5, 1, 0]
     base = [0, 13, 7, 3]                      # wraps around the 16-deep ring
     conv0, ssm0 = c["conv_pool"].clone(), c["ssm_pool"].clone()
     out, win = run_verify(kda, c, n_tok, base, Hqk, dev)
@@ -104,21 +108,34 @@ def test_verify_and_commit_match_oracle(kda, Hqk, Hv, io, state, conv, dev):
     np.testing.assert_array_equal(got[untouched], f64(ssm0)[untouched])
 
 
-def test_commit_then_verify_continues_bit_exactly(dev):
-    """fp32 state: verify 5 tokens; commit 3 and scatter the conv window of
-    step 2; verify the remaining 2 tokens from the committed pools: their
-    outputs equal the first call's steps 3 and 4 bit for bit."""
-    B, D, Hqk, Hv, P = 3, 5, 2, 2, 8
-    c = make_case(7200, B, D, Hqk, Hv, True, "bf16", "fp32", "bf16", P, dev)
-    out1, win1 = run_verify(True, c, [5, 5, 5], [0, 0, 0], Hqk, dev)
-    a = 3
+def continue_after_commit(D, a, io, dev):
+    """fp32 state: verify D tokens; commit a and scatter the conv window of
+    step a - 1; verify the remaining D - a tokens from the committed pools.
+    Returns the first call's outputs of steps a.. and the second call's."""
+    B, Hqk, Hv, P = 3, 2, 2, 8
+    c = make_case(7200 + D, B, D, Hqk, Hv, True, io, "fp32", "bf16", P, dev)
+    out1, win1 = run_verify(True, c, [D] * B, [0] * B, Hqk, dev)
     la.kda_commit(i32([a] * B, dev), c["slots"], c["ssm_pool"], c["ring"], i32([0] * B, dev))
     la.conv_window_scatter(win1, c["slots"], i32([a - 1] * B, dev), c["conv_pool"])
     c2 = dict(c, x=c["x"][:, a:].contiguous(), g=c["g"][:, a:].contiguous(),
               beta=c["beta"][:, a:].contiguous())
-    out2, _ = run_verify(True, c2, [2, 2, 2], [a] * B, Hqk, dev)
+    out2, _ = run_verify(True, c2, [D - a] * B, [a] * B, Hqk, dev)
     torch.cuda.synchronize()
-    assert torch.equal(out2, out1[:, a:])
+    return out1[:, a:], out2
+
+
+def test_commit_then_verify_continues_bit_exactly_sequential(dev):
+    """12 tokens, commit 3, then 9 more: both calls take the sequential form,
+    whose steps run the commit's arithmetic, so the outputs agree bit for bit."""
+    first, second = continue_after_commit(12, 3, "bf16", dev)
+    assert torch.equal(second, first)
+
+
+def test_commit_then_verify_continues_chunk_form(dev):
+    """5 tokens, commit 3, then 2 more, fp32 I/O: both calls take the chunk
+    form; the continuation agrees with the first call within the fp32 bar."""
+    first, second = continue_after_commit(5, 3, "fp32", dev)
+    assert_close_units(f64(second), f64(first), 2, "fp32", "continued outputs")
 
 
 def test_conv_window_scatter_and_track_copy_are_bit_exact(dev):
