@@ -144,7 +144,7 @@ template <> struct V16<bf16_t> {
 template <typename T>
 __device__ __forceinline__ void store16(void *base, int64_t elem, const float *v)
 {
-    *reinterpret_cast<uint4 *>(static_cast<T *>(base) + elem) = V16<T>::pack(v);
+    st_stream(static_cast<T *>(base) + elem, V16<T>::pack(v));
 }
 
 template <typename IOT, typename CT, bool KDA, bool CONV, int NT, bool CUM, class Issue>
@@ -435,24 +435,28 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
 // v_mfma_f32_16x16x4f32), so the state crosses HBM once and no per-element
 // arithmetic is spent on it.
 //
-// Phases (three workgroup barriers):
+// Phases (three workgroup barriers; records and outputs are written with
+// non-temporal stores):
 //   1. staging: 16-byte loads of the head's inputs, conv state, conv weights
-//      and gates (then the state fragments); the gates' running sums and
-//      their ring records by 32 lanes holding four channels each;
-//   2. per (step, q|k|v block) unit, one wave: the conv of the block's 128
+//      and gates; the gates' running sums and their ring records by 32 lanes
+//      holding four channels each;
+//   2. the state fragments are issued (they stream in under this phase);
+//      per (step, q|k|v block) unit, one wave: the conv of the block's 128
 //      channels at that step (two per lane), its ring records and conv
 //      window, and for q and k the norm (a wave sum) and the row of
 //      [K~ | Q~];
-//   3. the matrix-core product (every wave) and A, P (four lanes per pair);
+//   3. the matrix-core product (every wave) and A, P (eight lanes per pair);
 //   4. the d recurrence and the outputs per value row.
 template <typename T> __device__ __forceinline__ void store2(void *base, int64_t elem, float v0, float v1);
 template <> __device__ __forceinline__ void store2<float>(void *base, int64_t elem, float v0, float v1)
 {
-    *reinterpret_cast<float2 *>(static_cast<float *>(base) + elem) = make_float2(v0, v1);
+    float *p = static_cast<float *>(base) + elem;
+    __builtin_nontemporal_store(v0, p);
+    __builtin_nontemporal_store(v1, p + 1);
 }
 template <> __device__ __forceinline__ void store2<bf16_t>(void *base, int64_t elem, float v0, float v1)
 {
-    *reinterpret_cast<uint32_t *>(static_cast<bf16_t *>(base) + elem) = pack_bf16x2(v0, v1);
+    __builtin_nontemporal_store(pack_bf16x2(v0, v1), reinterpret_cast<uint32_t *>(static_cast<bf16_t *>(base) + elem));
 }
 // 16 bytes of T as floats.
 template <typename T> __device__ __forceinline__ void unpack16(const uint4 &r, float *v);
@@ -466,10 +470,16 @@ template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4 &r, flo
     Stor<bf16_t>::unpack(r, v);
 }
 
+constexpr int kChunkNT = 512;   // threads of the chunk-form verify workgroup
+
 template <typename ST, typename IOT, typename CT, bool KDA, bool CONV>
-__global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
+__global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
 {
-    constexpr int NT = 256;
+    constexpr int NT = kChunkNT, NW = NT / 64;
+    constexpr int TPW = HD / 16 / NW;               // 16-row state tiles per wave
+    constexpr int LPP = NT >= 512 ? 8 : 4;          // lanes per (t, j) pair of A and P
+    constexpr int PARTS = NT / HD;                  // threads per value row in the last phase
+    static_assert(TPW * NW * 16 == HD && PARTS * HD == NT && kChunk % PARTS == 0, "layout");
     constexpr int LDB = HD + 4;                     // [K~ | Q~] row stride (floats)
     constexpr int LDX = 17;                         // X row stride (floats)
     constexpr int FR = HD * (int)sizeof(ST) / 64;   // 64-byte row pieces: 4 (bf16) or 8 (fp32)
@@ -508,7 +518,7 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
     constexpr int VH = V16<CT>::N, GH = HD / VH, NH = 3 * 3 * GH, HI = (NH + NT - 1) / NT;
     static_assert(NCH <= 2 * NT, "two conv weight vectors per thread");
     uint4 xr[XI], hr[HI];
-    float4 g4[kChunk], wr0, wr1, br = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 g4[kChunk], wr0, wr1 = make_float4(0.f, 0.f, 0.f, 0.f), br = make_float4(0.f, 0.f, 0.f, 0.f);
     float bv = 0.f;
 #pragma unroll
     for (int q = 0; q < XI; ++q) {
@@ -539,28 +549,13 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
                                                      gbase(blk) + grp * VH);
         }
         {
-            const int j0 = tid, j1 = min(tid + NT, NCH - 1);
+            const int j0 = min(tid, NCH - 1), j1 = min(tid + NT, NCH - 1);
             wr0 = reinterpret_cast<const float4 *>(a.w)[gbase(j0 / HD) + j0 % HD];
-            wr1 = reinterpret_cast<const float4 *>(a.w)[gbase(j1 / HD) + j1 % HD];
+            if constexpr (NT < NCH) wr1 = reinterpret_cast<const float4 *>(a.w)[gbase(j1 / HD) + j1 % HD];
         }
         if (tid < NCH / 4 && a.bias)
             br = *reinterpret_cast<const float4 *>(a.bias + gbase(tid / (HD / 4)) + 4 * (tid % (HD / 4)));
     }
-    // The state as matrix-core operand fragments, behind the staged loads:
-    // wave w owns rows 32w .. 32w + 31 (two 16-row tiles); lane (li, lq)
-    // holds 16 bytes at byte 64 f + 16 lq of row 16 T + li.  bf16: fragment
-    // f is k = 32 f + 8 lq + e (e < 8), one 16x16x32 step; fp32: fragment f
-    // is k = 16 f + 4 lq + e (e < 4), four 16x16x4 steps.
-    __builtin_amdgcn_sched_barrier(0);
-    const char *S = static_cast<const char *>(a.ssm_pool) +
-                    ((int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD) * sizeof(ST);
-    uint4 fr[2][FR];
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int f = 0; f < FR; ++f)
-            fr[T][f] = ld_stream(S + (int64_t)(32 * wave + 16 * T + li) * HD * sizeof(ST) + 64 * f + 16 * lq);
-    __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
     for (int q = 0; q < XI; ++q) {
@@ -587,7 +582,7 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
                         make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
             }
         }
-        w4[tid] = wr0;
+        if (tid < NCH) w4[tid] = wr0;
         if (tid + NT < NCH) w4[tid + NT] = wr1;
         if (tid < NCH / 4) *reinterpret_cast<float4 *>(&wb[4 * tid]) = br;
     }
@@ -616,8 +611,24 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
     }
     __syncthreads();
 
+    // The state as matrix-core operand fragments, issued after the staged
+    // inputs have landed, so they stream in while the units below run: wave
+    // w owns the TPW 16-row tiles from row 16 TPW w; lane (li, lq) holds 16
+    // bytes at byte 64 f + 16 lq of row li of a tile.  bf16: fragment f is
+    // k = 32 f + 8 lq + e (e < 8), one 16x16x32 step; fp32: fragment f is
+    // k = 16 f + 4 lq + e (e < 4), four 16x16x4 steps.
+    __builtin_amdgcn_sched_barrier(0);
+    const char *S = static_cast<const char *>(a.ssm_pool) +
+                    ((int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD) * sizeof(ST);
+    uint4 fr[TPW][FR];
+#pragma unroll
+    for (int T = 0; T < TPW; ++T)
+#pragma unroll
+        for (int f = 0; f < FR; ++f)
+            fr[T][f] = ld_stream(S + (int64_t)(16 * (TPW * wave + T) + li) * HD * sizeof(ST) + 64 * f + 16 * lq);
+    __builtin_amdgcn_sched_barrier(0);
     // ---- 2. units (step tt, block blk), one per wave at a time ------------
-    for (int u = wave; u < 3 * n; u += NT / 64) {
+    for (int u = wave; u < 3 * n; u += NW) {
         const int tt = u / 3, blk = u - 3 * tt, j = blk * HD + 2 * lane;
         const float2 r3 = *reinterpret_cast<const float2 *>(&xe[tt + 3][j]);
         float y0 = r3.x, y1 = r3.y;
@@ -667,10 +678,10 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
     __syncthreads();
 
     // ---- 3. X = S [K~ | Q~]^T on the matrix cores (lane (li, lq) ends with
-    //      X[32 w + 16 T + 4 lq + r][li] in acc[T][r]), and A, P
-    f32x4 acc[2];
+    //      X[16 (TPW w + T) + 4 lq + r][li] in acc[T][r]), and A, P
+    f32x4 acc[TPW];
 #pragma unroll
-    for (int T = 0; T < 2; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int T = 0; T < TPW; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (sizeof(ST) == 2) {
 #pragma unroll
         for (int f = 0; f < FR; ++f) {
@@ -680,7 +691,7 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
             bf16x8_t bh, bl;
             split_bf16x8(bv8, bh, bl);
 #pragma unroll
-            for (int T = 0; T < 2; ++T) {
+            for (int T = 0; T < TPW; ++T) {
                 const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fr[T][f]);
                 acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[T], 0, 0, 0);
                 acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[T], 0, 0, 0);
@@ -694,7 +705,7 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int T = 0; T < 2; ++T) {
+                for (int T = 0; T < TPW; ++T) {
                     const uint32_t w = e == 0 ? fr[T][f].x : e == 1 ? fr[T][f].y : e == 2 ? fr[T][f].z : fr[T][f].w;
                     acc[T] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w), bv4[e], acc[T], 0, 0, 0);
                 }
@@ -702,27 +713,27 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
     }
     float (*Xs)[LDX] = reinterpret_cast<float (*)[LDX]>(Xw);  // the weights are no longer read
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+    for (int T = 0; T < TPW; ++T)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Xs[32 * wave + 16 * T + 4 * lq + r][li] = acc[T][r];
-    // A and P: pair p of the 36 pairs (t, j <= t) on threads 112 + 4 p ..
-    // 112 + 4 p + 3, the four lanes of a quad splitting the channels
-    if (tid >= NT - 4 * 36) {
-        const int p = (tid - (NT - 4 * 36)) >> 2, qc = tid & 3;
+        for (int r = 0; r < 4; ++r) Xs[16 * (TPW * wave + T) + 4 * lq + r][li] = acc[T][r];
+    // A and P: pair p of the 36 pairs (t, j <= t) on the LPP aligned lanes
+    // from thread NT - 36 LPP + LPP p, which split the channels
+    if (tid >= NT - LPP * 36) {
+        const int p = (tid - (NT - LPP * 36)) / LPP, qc = tid % LPP;
         int t = 0;
         while ((t + 1) * (t + 2) / 2 <= p) ++t;
         const int j = p - t * (t + 1) / 2;
         float sa = 0.f, sp = 0.f;
         if (t < n) {
-            for (int m = 0; m < HD / 4; ++m) {
-                const int c = qc + 4 * m;
+            for (int m = 0; m < HD / LPP; ++m) {
+                const int c = qc + LPP * m;
                 const float w = ys[j][HD + c] * fast_exp(Gs[t][c] - Gs[j][c]);
                 sa = fmaf(ys[t][HD + c], w, sa);
                 sp = fmaf(ys[t][c], w, sp);
             }
         }
-        sa = group_sum<4>(sa);
-        sp = group_sum<4>(sp);
+        sa = group_sum<LPP>(sa);
+        sp = group_sum<LPP>(sp);
         if (qc == 0 && t < n) {
             Am[t][j] = j < t ? sa * nk[t] * nk[j] : 0.f;
             Pm[t][j] = sp * nq[t] * nk[j];
@@ -730,10 +741,10 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
     }
     __syncthreads();
 
-    // ---- 4. per value row r: the d recurrence (both halves of the block),
-    //      then the outputs of steps 4 half .. 4 half + 3
+    // ---- 4. per value row r: the d recurrence (every part of the block),
+    //      then the outputs of this part's steps
     {
-        const int r = tid & (HD - 1), half = tid / HD;
+        const int r = tid % HD, part = tid / HD;
         float d[kChunk];
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
@@ -747,7 +758,7 @@ __global__ void __launch_bounds__(256) verify_chunk_kernel(VerifyArgs a)
         }
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
-            if (t / (kChunk / 2) == half && t < n) {
+            if (t / (kChunk / PARTS) == part && t < n) {
                 float o = Xs[r][kChunk + t];
 #pragma unroll
                 for (int jj = 0; jj <= t; ++jj) o = fmaf(Pm[t][jj], d[jj], o);
@@ -999,9 +1010,9 @@ hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t stream)
     const dim3 grid((unsigned)(a.B * a.Hv));
     if (a.D <= kChunk) {  // one chunk: the matrix-core form
         if (a.w)
-            hipLaunchKernelGGL((verify_chunk_kernel<ST, IOT, CT, KDA, true>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((verify_chunk_kernel<ST, IOT, CT, KDA, true>), grid, dim3(kChunkNT), 0, stream, a);
         else
-            hipLaunchKernelGGL((verify_chunk_kernel<ST, IOT, CT, KDA, false>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((verify_chunk_kernel<ST, IOT, CT, KDA, false>), grid, dim3(kChunkNT), 0, stream, a);
         return hipGetLastError();
     }
     const dim3 block(DecodeCfg<HD, ST>::NT);
