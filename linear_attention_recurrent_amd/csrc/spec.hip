@@ -59,18 +59,6 @@ template <> __device__ __forceinline__ float round_to<bf16_t>(float v)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
-// v = hi + lo to about 16 significant bits: hi = bf16(v), lo = bf16(v - hi)
-// (both nearest even).
-__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8_t &hi, bf16x8_t &lo)
-{
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 x = static_cast<__bf16>(v[e]);
-        hi[e] = x;
-        lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(x));
-    }
-}
-
 __device__ __forceinline__ int64_t ring_at(int slot, int Hv, int L, int h, int pos, int n)
 {
     return (((int64_t)slot * Hv + h) * L + pos) * n;
@@ -478,16 +466,26 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
     constexpr int NT = kChunkNT, NW = NT / 64;
     constexpr int TPW = HD / 16 / NW;               // 16-row state tiles per wave
     constexpr int LPP = NT >= 512 ? 8 : 4;          // lanes per (t, j) pair of A and P
-    constexpr int PARTS = NT / HD;                  // threads per value row in the last phase
-    static_assert(TPW * NW * 16 == HD && PARTS * HD == NT && kChunk % PARTS == 0, "layout");
+    static_assert(TPW * NW * 16 == HD && HD <= NT, "layout");
     constexpr int LDB = HD + 4;                     // [K~ | Q~] row stride (floats)
+    constexpr int LDBH = HD + 8;                    // its bf16 hi / lo row stride (elements)
+    constexpr bool kBf16B = sizeof(ST) == 2;        // [K~ | Q~] kept as bf16 hi + lo
+    constexpr int BSZ = kBf16B ? 16 * LDBH : 16 * LDB;  // floats
+    // taps from the inputs need rounding to the conv dtype only when it is
+    // narrower than the I/O dtype
+    constexpr bool kRoundTaps = std::is_same<CT, bf16_t>::value && !std::is_same<IOT, CT>::value;
     constexpr int LDX = 17;                         // X row stride (floats)
     constexpr int FR = HD * (int)sizeof(ST) / 64;   // 64-byte row pieces: 4 (bf16) or 8 (fp32)
     constexpr int NCH = 3 * HD;
     __shared__ __align__(16) float xe[kChunk + 3][XLD];  // conv state rows 0..2, inputs below
     __shared__ __align__(16) float ys[kChunk][XLD];      // q|k|v conv outputs
     __shared__ __align__(16) float Gs[kChunk][GLD];      // running sums of the log-decays
-    __shared__ __align__(16) float Bm[16][LDB];          // rows t: K~_t, rows 8 + t: Q~_t
+    // [K~ | Q~]: rows t: K~_t, rows 8 + t: Q~_t; fp32 (fp32 state) or the
+    // bf16 hi rows followed by the bf16 lo rows (bf16 state)
+    __shared__ __align__(16) float Braw[BSZ];
+    float (*Bm)[LDB] = reinterpret_cast<float (*)[LDB]>(Braw);
+    bf16_t (*Bh)[LDBH] = reinterpret_cast<bf16_t (*)[LDBH]>(Braw);
+    bf16_t (*Bl)[LDBH] = Bh + 16;
     // X = S [K~ | Q~]^T after the product; the conv weights and biases before
     __shared__ __align__(16) float Xw[HD * LDX > 5 * NCH ? HD * LDX : 5 * NCH];
     __shared__ float Am[kChunk][kChunk], Pm[kChunk][kChunk];
@@ -605,9 +603,15 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
         }
     }
     for (int i = tid; i < 16 * (HD / 4); i += NT) {  // rows of [K~ | Q~] past n are zero
-        const int r = i / (HD / 4);
-        if ((r & (kChunk - 1)) >= n)
-            *reinterpret_cast<float4 *>(&Bm[r][4 * (i % (HD / 4))]) = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int r = i / (HD / 4), c = 4 * (i % (HD / 4));
+        if ((r & (kChunk - 1)) >= n) {
+            if constexpr (kBf16B) {
+                *reinterpret_cast<uint2 *>(&Bh[r][c]) = make_uint2(0, 0);
+                *reinterpret_cast<uint2 *>(&Bl[r][c]) = make_uint2(0, 0);
+            } else {
+                *reinterpret_cast<float4 *>(&Bm[r][c]) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
     }
     __syncthreads();
 
@@ -639,14 +643,15 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
             r2 = *reinterpret_cast<const float2 *>(&xe[tt + 2][j]);
             const float4 wa = w4[j], wc = w4[j + 1];
             const float2 bb = *reinterpret_cast<const float2 *>(&wb[j]);
+            auto tap = [](float x) { return kRoundTaps ? round_to<CT>(x) : x; };
             float acc0 = bb.x, acc1 = bb.y;
-            acc0 = fmaf(wa.x, round_to<CT>(r0.x), acc0);
-            acc0 = fmaf(wa.y, round_to<CT>(r1.x), acc0);
-            acc0 = fmaf(wa.z, round_to<CT>(r2.x), acc0);
+            acc0 = fmaf(wa.x, tap(r0.x), acc0);
+            acc0 = fmaf(wa.y, tap(r1.x), acc0);
+            acc0 = fmaf(wa.z, tap(r2.x), acc0);
             acc0 = fmaf(wa.w, r3.x, acc0);
-            acc1 = fmaf(wc.x, round_to<CT>(r0.y), acc1);
-            acc1 = fmaf(wc.y, round_to<CT>(r1.y), acc1);
-            acc1 = fmaf(wc.z, round_to<CT>(r2.y), acc1);
+            acc1 = fmaf(wc.x, tap(r0.y), acc1);
+            acc1 = fmaf(wc.y, tap(r1.y), acc1);
+            acc1 = fmaf(wc.z, tap(r2.y), acc1);
             acc1 = fmaf(wc.w, r3.y, acc1);
             y0 = round_to<IOT>(silu(acc0));
             y1 = round_to<IOT>(silu(acc1));
@@ -654,11 +659,19 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
         *reinterpret_cast<float2 *>(&ys[tt][j]) = make_float2(y0, y1);
         const int64_t rr = ring_at(slot, a.Hv, R.L, h, pos_of(tt), HD) + 2 * lane;
         if (blk < 2) {
-            const float inv = 1.0f / sqrtf(wave_sum(fmaf(y1, y1, y0 * y0)) + a.eps);
+            const float inv = __builtin_amdgcn_rsqf(wave_sum(fmaf(y1, y1, y0 * y0)) + a.eps);
             if (lane == 0) (blk == 0 ? nq : nk)[tt] = inv;
             const float2 G = *reinterpret_cast<const float2 *>(&Gs[tt][2 * lane]);
-            *reinterpret_cast<float2 *>(&Bm[blk == 1 ? tt : kChunk + tt][2 * lane]) =
-                make_float2(y0 * inv * fast_exp(G.x), y1 * inv * fast_exp(G.y));
+            const float b0 = y0 * inv * fast_exp(G.x), b1 = y1 * inv * fast_exp(G.y);
+            const int row = blk == 1 ? tt : kChunk + tt;
+            if constexpr (kBf16B) {  // the two-term split: hi = bf16(b), lo = bf16(b - hi)
+                const uint32_t hp = pack_bf16x2(b0, b1);
+                *reinterpret_cast<uint32_t *>(&Bh[row][2 * lane]) = hp;
+                *reinterpret_cast<uint32_t *>(&Bl[row][2 * lane]) =
+                    pack_bf16x2(b0 - bf16_lo(hp), b1 - bf16_hi(hp));
+            } else {
+                *reinterpret_cast<float2 *>(&Bm[row][2 * lane]) = make_float2(b0, b1);
+            }
             if (blk == 1) {
                 store2<IOT>(R.rawk, rr, y0, y1);
                 store2<IOT>(R.k, rr, y0 * inv, y1 * inv);
@@ -669,9 +682,9 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
         if constexpr (CONV) {  // the history after step tt; q/k windows from the group's first head
             if (blk == 2 || h % a.G == 0) {
                 const int64_t wrow = ((int64_t)b * a.D + tt) * 3 * a.C + gbase(blk) + 2 * lane;
-                store2<CT>(a.windows, wrow, round_to<CT>(r1.x), round_to<CT>(r1.y));
-                store2<CT>(a.windows, wrow + a.C, round_to<CT>(r2.x), round_to<CT>(r2.y));
-                store2<CT>(a.windows, wrow + 2 * a.C, round_to<CT>(r3.x), round_to<CT>(r3.y));
+                store2<CT>(a.windows, wrow, r1.x, r1.y);  // the store rounds to the conv dtype
+                store2<CT>(a.windows, wrow + a.C, r2.x, r2.y);
+                store2<CT>(a.windows, wrow + 2 * a.C, r3.x, r3.y);
             }
         }
     }
@@ -685,11 +698,8 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
     if constexpr (sizeof(ST) == 2) {
 #pragma unroll
         for (int f = 0; f < FR; ++f) {
-            const float4 b0 = *reinterpret_cast<const float4 *>(&Bm[li][32 * f + 8 * lq]);
-            const float4 b1 = *reinterpret_cast<const float4 *>(&Bm[li][32 * f + 8 * lq + 4]);
-            const float bv8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            bf16x8_t bh, bl;
-            split_bf16x8(bv8, bh, bl);
+            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&Bh[li][32 * f + 8 * lq]);
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&Bl[li][32 * f + 8 * lq]);
 #pragma unroll
             for (int T = 0; T < TPW; ++T) {
                 const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fr[T][f]);
@@ -741,10 +751,9 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
     }
     __syncthreads();
 
-    // ---- 4. per value row r: the d recurrence (every part of the block),
-    //      then the outputs of this part's steps
-    {
-        const int r = tid % HD, part = tid / HD;
+    // ---- 4. per value row r: the d recurrence, then the outputs
+    if (tid < HD) {
+        const int r = tid;
         float d[kChunk];
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
@@ -758,7 +767,7 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
         }
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
-            if (t / (kChunk / PARTS) == part && t < n) {
+            if (t < n) {
                 float o = Xs[r][kChunk + t];
 #pragma unroll
                 for (int jj = 0; jj <= t; ++jj) o = fmaf(Pm[t][jj], d[jj], o);
