@@ -429,10 +429,9 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
 //      and gates; the gates' running sums and their ring records by 32 lanes
 //      holding four channels each;
 //   2. the state fragments are issued (they stream in under this phase);
-//      per (step, q|k|v block) unit, one wave: the conv of the block's 128
-//      channels at that step (two per lane), its ring records and conv
-//      window, and for q and k the norm (a wave sum) and the row of
-//      [K~ | Q~];
+//      one step per wave: the conv of the step's q, k and v channels (two
+//      of each per lane), the q and k norms (wave sums), the ring records,
+//      the conv window and the step's rows of [K~ | Q~];
 //   3. the matrix-core product (every wave) and A, P (eight lanes per pair);
 //   4. the d recurrence and the outputs per value row.
 template <typename T> __device__ __forceinline__ void store2(void *base, int64_t elem, float v0, float v1);
@@ -631,38 +630,62 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
         for (int f = 0; f < FR; ++f)
             fr[T][f] = ld_stream(S + (int64_t)(16 * (TPW * wave + T) + li) * HD * sizeof(ST) + 64 * f + 16 * lq);
     __builtin_amdgcn_sched_barrier(0);
-    // ---- 2. units (step tt, block blk), one per wave at a time ------------
-    for (int u = wave; u < 3 * n; u += NW) {
-        const int tt = u / 3, blk = u - 3 * tt, j = blk * HD + 2 * lane;
-        const float2 r3 = *reinterpret_cast<const float2 *>(&xe[tt + 3][j]);
-        float y0 = r3.x, y1 = r3.y;
-        float2 r1, r2;
-        if constexpr (CONV) {
-            const float2 r0 = *reinterpret_cast<const float2 *>(&xe[tt][j]);
-            r1 = *reinterpret_cast<const float2 *>(&xe[tt + 1][j]);
-            r2 = *reinterpret_cast<const float2 *>(&xe[tt + 2][j]);
-            const float4 wa = w4[j], wc = w4[j + 1];
-            const float2 bb = *reinterpret_cast<const float2 *>(&wb[j]);
-            auto tap = [](float x) { return kRoundTaps ? round_to<CT>(x) : x; };
-            float acc0 = bb.x, acc1 = bb.y;
-            acc0 = fmaf(wa.x, tap(r0.x), acc0);
-            acc0 = fmaf(wa.y, tap(r1.x), acc0);
-            acc0 = fmaf(wa.z, tap(r2.x), acc0);
-            acc0 = fmaf(wa.w, r3.x, acc0);
-            acc1 = fmaf(wc.x, tap(r0.y), acc1);
-            acc1 = fmaf(wc.y, tap(r1.y), acc1);
-            acc1 = fmaf(wc.z, tap(r2.y), acc1);
-            acc1 = fmaf(wc.w, r3.y, acc1);
-            y0 = round_to<IOT>(silu(acc0));
-            y1 = round_to<IOT>(silu(acc1));
-        }
-        *reinterpret_cast<float2 *>(&ys[tt][j]) = make_float2(y0, y1);
+    // ---- 2. one step per wave: the conv of the step's q, k and v channels
+    //      (two of each block per lane), norms, records and window
+    const bool qk_win = h % a.G == 0;  // q/k windows come from the group's first head
+    for (int tt = wave; tt < n; tt += NW) {
         const int64_t rr = ring_at(slot, a.Hv, R.L, h, pos_of(tt), HD) + 2 * lane;
-        if (blk < 2) {
-            const float inv = __builtin_amdgcn_rsqf(wave_sum(fmaf(y1, y1, y0 * y0)) + a.eps);
-            if (lane == 0) (blk == 0 ? nq : nk)[tt] = inv;
-            const float2 G = *reinterpret_cast<const float2 *>(&Gs[tt][2 * lane]);
-            const float b0 = y0 * inv * fast_exp(G.x), b1 = y1 * inv * fast_exp(G.y);
+        const int64_t wrow = ((int64_t)b * a.D + tt) * 3 * a.C + 2 * lane;
+        float yq0 = 0.f, yq1 = 0.f, yk0 = 0.f, yk1 = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk) {
+            const int j = blk * HD + 2 * lane;
+            const float2 r3 = *reinterpret_cast<const float2 *>(&xe[tt + 3][j]);
+            float y0 = r3.x, y1 = r3.y;
+            if constexpr (CONV) {
+                const float2 r0 = *reinterpret_cast<const float2 *>(&xe[tt][j]);
+                const float2 r1 = *reinterpret_cast<const float2 *>(&xe[tt + 1][j]);
+                const float2 r2 = *reinterpret_cast<const float2 *>(&xe[tt + 2][j]);
+                const float4 wa = w4[j], wc = w4[j + 1];
+                const float2 bb = *reinterpret_cast<const float2 *>(&wb[j]);
+                auto tap = [](float x) { return kRoundTaps ? round_to<CT>(x) : x; };
+                float acc0 = bb.x, acc1 = bb.y;
+                acc0 = fmaf(wa.x, tap(r0.x), acc0);
+                acc0 = fmaf(wa.y, tap(r1.x), acc0);
+                acc0 = fmaf(wa.z, tap(r2.x), acc0);
+                acc0 = fmaf(wa.w, r3.x, acc0);
+                acc1 = fmaf(wc.x, tap(r0.y), acc1);
+                acc1 = fmaf(wc.y, tap(r1.y), acc1);
+                acc1 = fmaf(wc.z, tap(r2.y), acc1);
+                acc1 = fmaf(wc.w, r3.y, acc1);
+                y0 = round_to<IOT>(silu(acc0));
+                y1 = round_to<IOT>(silu(acc1));
+                // the history after step tt (the store rounds to the conv dtype)
+                if (blk == 2 || qk_win) {
+                    const int64_t w0 = wrow + gbase(blk);
+                    store2<CT>(a.windows, w0, r1.x, r1.y);
+                    store2<CT>(a.windows, w0 + a.C, r2.x, r2.y);
+                    store2<CT>(a.windows, w0 + 2 * a.C, r3.x, r3.y);
+                }
+            }
+            *reinterpret_cast<float2 *>(&ys[tt][j]) = make_float2(y0, y1);
+            if (blk == 0) { yq0 = y0; yq1 = y1; }
+            if (blk == 1) { yk0 = y0; yk1 = y1; store2<IOT>(R.rawk, rr, y0, y1); }
+            if (blk == 2) store2<IOT>(R.rawv, rr, y0, y1);
+            __builtin_amdgcn_sched_barrier(0);  // one block's operands live at a time
+        }
+        const float iq = __builtin_amdgcn_rsqf(wave_sum(fmaf(yq1, yq1, yq0 * yq0)) + a.eps);
+        const float ik = __builtin_amdgcn_rsqf(wave_sum(fmaf(yk1, yk1, yk0 * yk0)) + a.eps);
+        if (lane == 0) {
+            nq[tt] = iq;
+            nk[tt] = ik;
+        }
+        store2<IOT>(R.k, rr, yk0 * ik, yk1 * ik);
+        const float2 G = *reinterpret_cast<const float2 *>(&Gs[tt][2 * lane]);
+        const float e0 = fast_exp(G.x), e1 = fast_exp(G.y);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const float b0 = (blk ? yk0 * ik : yq0 * iq) * e0, b1 = (blk ? yk1 * ik : yq1 * iq) * e1;
             const int row = blk == 1 ? tt : kChunk + tt;
             if constexpr (kBf16B) {  // the two-term split: hi = bf16(b), lo = bf16(b - hi)
                 const uint32_t hp = pack_bf16x2(b0, b1);
@@ -671,20 +694,6 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
                     pack_bf16x2(b0 - bf16_lo(hp), b1 - bf16_hi(hp));
             } else {
                 *reinterpret_cast<float2 *>(&Bm[row][2 * lane]) = make_float2(b0, b1);
-            }
-            if (blk == 1) {
-                store2<IOT>(R.rawk, rr, y0, y1);
-                store2<IOT>(R.k, rr, y0 * inv, y1 * inv);
-            }
-        } else {
-            store2<IOT>(R.rawv, rr, y0, y1);
-        }
-        if constexpr (CONV) {  // the history after step tt; q/k windows from the group's first head
-            if (blk == 2 || h % a.G == 0) {
-                const int64_t wrow = ((int64_t)b * a.D + tt) * 3 * a.C + gbase(blk) + 2 * lane;
-                store2<CT>(a.windows, wrow, r1.x, r1.y);  // the store rounds to the conv dtype
-                store2<CT>(a.windows, wrow + a.C, r2.x, r2.y);
-                store2<CT>(a.windows, wrow + 2 * a.C, r3.x, r3.y);
             }
         }
     }
