@@ -790,28 +790,38 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
 // ---------------------------------------------------------------------------
 // commit
 // ---------------------------------------------------------------------------
-template <typename ST, typename IOT, bool KDA>
-__global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitArgs a)
-{
-    using Cfg = DecodeCfg<HD, ST>;
-    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
-    constexpr int VPT = (kChunk * HD + NT - 1) / NT;  // staged ring values per thread
-    __shared__ float ks[kChunk][HD], vs[kChunk][HD], gsh[kChunk][HD], bsh[kChunk], nk[kChunk];
-    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = a.slots[b];
-    const int na = min(a.accepted[b], a.ring.L);
-    if (slot < 0 || slot >= a.num_rows || na <= 0) return;  // nothing accepted: row unchanged
+// One 512-thread workgroup per (request, value head).  Up to eight accepted
+// steps take the chunk form below; more take the sequential replay, whose
+// per-row arithmetic is the sequential verify's (bit for bit with an fp32
+// state).
+constexpr int kCommitNT = 512;
 
+// Rows of a head spread over NW waves as in the decode kernel: LPR lanes of
+// EPL elements (16 bytes) per row, NJ row instructions per lane.
+template <typename ST, int NW_> struct RowCfg {
+    static constexpr int NW = NW_;
+    static constexpr int EPL = Stor<ST>::kPer16B, LPR = HD / EPL, RPW = 64 / LPR;
+    static constexpr int NJ = HD / RPW / NW;
+    static_assert(NJ * RPW * NW == HD, "rows split evenly over the waves");
+};
+
+// The sequential replay of na (> 0) ring steps onto the state row.
+template <typename ST, typename IOT, bool KDA>
+__device__ __forceinline__ void commit_sequential(const CommitArgs &a, int b, int h, int slot, int na,
+                                                  float (*ks)[HD], float (*vs)[HD], float (*gsh)[HD],
+                                                  float *bsh, float *nk)
+{
+    using Cfg = RowCfg<ST, kCommitNT / 64>;
+    constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = kCommitNT;
+    constexpr int VPT = (kChunk * HD + NT - 1) / NT;  // staged ring values per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rb = a.ring_base[b];
     ST *S = static_cast<ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD;
-    float s[NJ][EPL];
-    {
-        uint4 raw[NJ];
-        load_rows<HD, ST>(raw, S, wave, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
-    }
     const int col0 = (lane % LPR) * EPL;
+    auto row_of = [&](int j) { return (wave * NJ + j) * RPW + lane / LPR; };
+    float s[NJ][EPL];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(ld_stream(S + (int64_t)row_of(j) * HD + col0), s[j]);
     const RingArgs &R = a.ring;
     for (int t0 = 0; t0 < na; t0 += kChunk) {
         // stage the chunk's ring records in LDS, all loads back to back
@@ -820,16 +830,13 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitA
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
             const int i = min(tid + q * NT, kChunk * HD - 1);
-            const int pos = (a.ring_base[b] + t0 + min(i / HD, nc - 1)) & (R.L - 1);
+            const int pos = (rb + t0 + min(i / HD, nc - 1)) & (R.L - 1);
             const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD) + i % HD;
             kv[q] = ld<IOT>(R.rawk, vr);
             vv[q] = ld<IOT>(R.rawv, vr);
             gv[q] = KDA ? R.g[vr] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
         }
-        if (tid < kChunk) {
-            const int pos = (a.ring_base[b] + t0 + min(tid, nc - 1)) & (R.L - 1);
-            bv = R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)];
-        }
+        if (tid < kChunk) bv = R.beta[ring_at(slot, a.Hv, R.L, h, (rb + t0 + min(tid, nc - 1)) & (R.L - 1), 1)];
         __syncthreads();  // the previous chunk's records are no longer read
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
@@ -860,17 +867,272 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) commit_kernel(CommitA
             }
             const float beta = bsh[tt];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int r = (wave * NJ + j) * RPW + lane / LPR;
-                row_step<EPL, LPR>(s[j], al, kk, vs[tt][r], beta);
+            for (int j = 0; j < NJ; ++j) row_step<EPL, LPR>(s[j], al, kk, vs[tt][row_of(j)], beta);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) st_stream(S + (int64_t)row_of(j) * HD + col0, Stor<ST>::pack(s[j]));
+}
+
+// Chunk form of the commit of na <= 8 steps.  With G_t the running sum of
+// the steps' log-decays, k_t the normalised keys and S the checkpoint, d_t
+// follows from X = S K~^T (K~_t = k_t * e^{G_t}) and the 8x8 A of the verify's
+// chunk form, and the committed state is
+//   S_na = S Diag(e^{G_na}) + sum_t d_t (k_t * e^{G_na - G_t})^T,
+// the second term a rank-8 product on the matrix cores.  Wave w owns state
+// rows 16 w .. 16 w + 15; lane (m, g) holds row 16 w + m, columns
+// 32 c + 8 g .. 32 c + 8 g + 7 for c < 4, in fp32 after loading.
+//   X:      bf16 state: v_mfma_f32_16x16x32_bf16, the state exact and K~ split
+//           into bf16 hi + lo; fp32 state: v_mfma_f32_16x16x4f32 with lane
+//           group g supplying column 32 c + 8 g + e for step (c, e);
+//   update: for each column block c and half hf, D[i][m] = sum_t KD_t[col(i)]
+//           d_t[row m] with col(i) = 32 c + 8 (i / 4) + 4 hf + i % 4, so lane
+//           (m, g) receives columns 32 c + 8 g + 4 hf .. + 3 of its own row,
+//           accumulated onto S e^{G_na} of the same elements.
+template <typename ST, typename IOT, bool KDA>
+__global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
+{
+    constexpr int NT = kCommitNT;
+    constexpr int LDB = HD + 4, LDBH = HD + 8, LDX = kChunk + 1;
+    constexpr bool kBf16 = sizeof(ST) == 2;
+    __shared__ __align__(16) float ks[kChunk][HD];   // rawk (the sequential form: the same)
+    __shared__ __align__(16) float vs[kChunk][HD];   // rawv
+    __shared__ __align__(16) float gsh[kChunk][HD];  // G_t (the sequential form: g, exp g)
+    __shared__ float bsh[kChunk], nk[kChunk];
+    __shared__ __align__(16) float Braw[kBf16 ? kChunk * LDBH : kChunk * LDB];  // K~
+    __shared__ __align__(16) float KD[kChunk][LDB];  // k_t e^{G_na - G_t}
+    __shared__ __align__(16) float Ds[kChunk][HD];   // d_t
+    __shared__ float Xs[HD][LDX];
+    __shared__ float Am[kChunk][kChunk];
+    __shared__ __align__(16) float Ee[HD];           // e^{G_na}
+    float (*Bm)[LDB] = reinterpret_cast<float (*)[LDB]>(Braw);
+    bf16_t (*Bh)[LDBH] = reinterpret_cast<bf16_t (*)[LDBH]>(Braw);
+    bf16_t (*Bl)[LDBH] = reinterpret_cast<bf16_t (*)[LDBH]>(Braw) + kChunk;
+
+    const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int slot = a.slots[b];
+    const int na = min(a.accepted[b], a.ring.L);
+    if (slot < 0 || slot >= a.num_rows || na <= 0) return;  // nothing accepted: row unchanged
+    if (na > kChunk) {
+        commit_sequential<ST, IOT, KDA>(a, b, h, slot, na, ks, vs, gsh, bsh, nk);
+        return;
+    }
+    const RingArgs &R = a.ring;
+    const int rb = a.ring_base[b];
+    auto pos_of = [&](int t) { return (rb + t) & (R.L - 1); };
+
+    // ---- 1. staging: rawk / rawv rows (16-byte loads), gates, betas
+    constexpr int VI = V16<IOT>::N, GI = HD / VI, NI = kChunk * 2 * GI, II = (NI + NT - 1) / NT;
+    uint4 xr[II];
+    float4 g4[kChunk];
+    float bv = 0.f;
+#pragma unroll
+    for (int q = 0; q < II; ++q) {
+        const int i = min(tid + q * NT, NI - 1), grp = i % GI, which = (i / GI) % 2;
+        const int t = min(i / (2 * GI), na - 1);
+        xr[q] = *reinterpret_cast<const uint4 *>(static_cast<const IOT *>(which ? R.rawv : R.rawk) +
+                                                 ring_at(slot, a.Hv, R.L, h, pos_of(t), HD) + grp * VI);
+    }
+    if (tid < 32) {  // lane l: channels 4 l .. 4 l + 3 of every step
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+            const int pos = pos_of(min(t, na - 1));
+            if constexpr (KDA) {
+                g4[t] = *reinterpret_cast<const float4 *>(R.g + ring_at(slot, a.Hv, R.L, h, pos, HD) + 4 * tid);
+            } else {
+                const float g1 = R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
+                g4[t] = make_float4(g1, g1, g1, g1);
             }
         }
     }
-    const int c0 = col0;
+    if (tid < kChunk) bv = R.beta[ring_at(slot, a.Hv, R.L, h, pos_of(min(tid, na - 1)), 1)];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int r = (wave * NJ + j) * RPW + lane / LPR;
-        st_stream(S + (int64_t)r * HD + c0, Stor<ST>::pack(s[j]));
+    for (int q = 0; q < II; ++q) {
+        const int i = tid + q * NT, grp = i % GI, which = (i / GI) % 2, t = i / (2 * GI);
+        if (i < NI && t < na) {
+            float v[VI];
+            unpack16<IOT>(xr[q], v);
+            float *dst = which ? &vs[t][grp * VI] : &ks[t][grp * VI];
+#pragma unroll
+            for (int e = 0; e < VI; e += 4)
+                *reinterpret_cast<float4 *>(dst + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+        }
+    }
+    if (tid < kChunk) bsh[tid] = bv;
+    if (tid < 32) {
+        float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+            if (t < na) {
+                G.x += g4[t].x; G.y += g4[t].y; G.z += g4[t].z; G.w += g4[t].w;
+                *reinterpret_cast<float4 *>(&gsh[t][4 * tid]) = G;
+            }
+        }
+        *reinterpret_cast<float4 *>(&Ee[4 * tid]) =
+            make_float4(fast_exp(G.x), fast_exp(G.y), fast_exp(G.z), fast_exp(G.w));
+    }
+    for (int i = tid; i < kChunk * (HD / 4); i += NT) {  // rows past na are zero
+        const int t = i / (HD / 4), c = 4 * (i % (HD / 4));
+        if (t >= na) {
+            *reinterpret_cast<float4 *>(&KD[t][c]) = make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4 *>(&Ds[t][c]) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (kBf16) {
+                *reinterpret_cast<uint2 *>(&Bh[t][c]) = make_uint2(0, 0);
+                *reinterpret_cast<uint2 *>(&Bl[t][c]) = make_uint2(0, 0);
+            } else {
+                *reinterpret_cast<float4 *>(&Bm[t][c]) = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. the state (streams in under this phase); per step wave: the k
+    //      norm, the row of K~ and the row of KD
+    const char *Sb = static_cast<const char *>(a.ssm_pool) +
+                     ((int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD) * sizeof(ST);
+    const char *Srow = Sb + (int64_t)(16 * wave + m) * HD * sizeof(ST);
+    constexpr int LPB = kBf16 ? 1 : 2;   // 16-byte loads per 8-column block
+    uint4 fr[4][LPB];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int l = 0; l < LPB; ++l)
+            fr[c][l] = ld_stream(Srow + (int64_t)(32 * c + 8 * g) * sizeof(ST) + 16 * l);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = wave; t < na; t += NT / 64) {
+        const float2 kr = *reinterpret_cast<const float2 *>(&ks[t][2 * lane]);
+        const float ik = __builtin_amdgcn_rsqf(wave_sum(fmaf(kr.y, kr.y, kr.x * kr.x)) + a.eps);
+        if (lane == 0) nk[t] = ik;
+        const float2 G = *reinterpret_cast<const float2 *>(&gsh[t][2 * lane]);
+        const float k0 = kr.x * ik, k1 = kr.y * ik;
+        const float b0 = k0 * fast_exp(G.x), b1 = k1 * fast_exp(G.y);
+        if constexpr (kBf16) {  // the two-term split: hi = bf16(b), lo = bf16(b - hi)
+            const uint32_t hp = pack_bf16x2(b0, b1);
+            *reinterpret_cast<uint32_t *>(&Bh[t][2 * lane]) = hp;
+            *reinterpret_cast<uint32_t *>(&Bl[t][2 * lane]) = pack_bf16x2(b0 - bf16_lo(hp), b1 - bf16_hi(hp));
+        } else {
+            *reinterpret_cast<float2 *>(&Bm[t][2 * lane]) = make_float2(b0, b1);
+        }
+        // e^{G_na - G_t} as a quotient of exponentials would overflow for
+        // strong decays; formed directly it is <= 1
+        const float2 Gn = *reinterpret_cast<const float2 *>(&gsh[na - 1][2 * lane]);
+        *reinterpret_cast<float2 *>(&KD[t][2 * lane]) =
+            make_float2(k0 * fast_exp(Gn.x - G.x), k1 * fast_exp(Gn.y - G.y));
+    }
+    __syncthreads();
+
+    // ---- 3. X = S K~^T: K~ has 8 rows, so the tile's lanes m >= 8 repeat
+    //      rows m - 8 and those columns of the result are dropped; and A
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int bn = m & (kChunk - 1);
+    if constexpr (kBf16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&Bh[bn][32 * c + 8 * g]);
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&Bl[bn][32 * c + 8 * g]);
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, fr[c][0]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int l = 0; l < 2; ++l) {
+                const float4 bq = *reinterpret_cast<const float4 *>(&Bm[bn][32 * c + 8 * g + 4 * l]);
+                const float bv4[4] = {bq.x, bq.y, bq.z, bq.w};
+                const uint32_t w4[4] = {fr[c][l].x, fr[c][l].y, fr[c][l].z, fr[c][l].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(w4[e]), bv4[e], acc, 0, 0, 0);
+            }
+    }
+    if (m < kChunk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xs[16 * wave + 4 * g + r][m] = acc[r];
+    }
+    // A_tj = k_t . k_j e^{G_t - G_j} (j < t): 28 pairs on eight lanes each
+    if (tid >= NT - 8 * 28) {
+        const int p = (tid - (NT - 8 * 28)) / 8, qc = tid % 8;
+        int t = 1;
+        while (t * (t + 1) / 2 <= p) ++t;
+        const int j = p - t * (t - 1) / 2;
+        float sa = 0.f;
+        if (t < na) {
+            for (int mm = 0; mm < HD / 8; ++mm) {
+                const int c = qc + 8 * mm;
+                sa = fmaf(ks[t][c], ks[j][c] * fast_exp(gsh[t][c] - gsh[j][c]), sa);
+            }
+        }
+        sa = group_sum<8>(sa);
+        if (qc == 0 && t < na) Am[t][j] = sa;  // unnormalised: scaled below
+    }
+    __syncthreads();
+
+    // ---- 4. per value row r: the d recurrence
+    if (tid < HD) {
+        const int r = tid;
+        float d[kChunk];
+#pragma unroll
+        for (int t = 0; t < kChunk; ++t) {
+            d[t] = 0.f;
+            if (t < na) {
+                float u = Xs[r][t];
+#pragma unroll
+                for (int jj = 0; jj < t; ++jj) u = fmaf(Am[t][jj] * nk[t] * nk[jj], d[jj], u);
+                d[t] = bsh[t] * (vs[t][r] - u);
+                Ds[t][r] = d[t];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. S_na = S e^{G_na} + sum_t d_t KD_t^T, per (column block, half)
+    {
+        float sv[4][8];  // the lane's state elements in fp32
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (kBf16) {
+                Stor<bf16_t>::unpack(fr[c][0], sv[c]);
+            } else {
+                Stor<float>::unpack(fr[c][0], sv[c]);
+                Stor<float>::unpack(fr[c][1], sv[c] + 4);
+            }
+        }
+        const int row = 16 * wave + m;
+        const float d_lo = Ds[g][row], d_hi = Ds[4 + g][row];  // B operand: d_{g}, d_{4+g} of row m
+        float out[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4 e0 = *reinterpret_cast<const float4 *>(&Ee[32 * c + 8 * g]);
+            const float4 e1 = *reinterpret_cast<const float4 *>(&Ee[32 * c + 8 * g + 4]);
+            const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4 u;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[r] = sv[c][4 * hf + r] * ev[4 * hf + r];
+                // A operand: lane (m, g) supplies KD_t[col(m)] for t = g (then 4 + g)
+                const int colm = 32 * c + 8 * (m >> 2) + 4 * hf + (m & 3);
+                u = __builtin_amdgcn_mfma_f32_16x16x4f32(KD[g][colm], d_lo, u, 0, 0, 0);
+                u = __builtin_amdgcn_mfma_f32_16x16x4f32(KD[4 + g][colm], d_hi, u, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[c][4 * hf + r] = u[r];
+            }
+        }
+        char *Sw = const_cast<char *>(Srow);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (kBf16) {
+                st_stream(Sw + (int64_t)(32 * c + 8 * g) * 2, Stor<bf16_t>::pack(out[c]));
+            } else {
+                st_stream(Sw + (int64_t)(32 * c + 8 * g) * 4, Stor<float>::pack(out[c]));
+                st_stream(Sw + (int64_t)(32 * c + 8 * g) * 4 + 16, Stor<float>::pack(out[c] + 4));
+            }
+        }
     }
 }
 
@@ -1052,7 +1314,7 @@ template <typename ST, typename IOT, bool KDA>
 hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream)
 {
     hipLaunchKernelGGL((commit_kernel<ST, IOT, KDA>), dim3((unsigned)(a.B * a.Hv)),
-                       dim3(DecodeCfg<HD, ST>::NT), 0, stream, a);
+                       dim3(kCommitNT), 0, stream, a);
     return hipGetLastError();
 }
 
