@@ -885,6 +885,8 @@ __device__ __forceinline__ void commit_sequential(const CommitArgs &a, int b, in
 //   X:      bf16 state: v_mfma_f32_16x16x32_bf16, the state exact and K~ split
 //           into bf16 hi + lo; fp32 state: v_mfma_f32_16x16x4f32 with lane
 //           group g supplying column 32 c + 8 g + e for step (c, e);
+//   A (the 28 pairs j < t) is formed beside the K~ / KD rows; after that
+//   barrier each wave runs X, d and the update for its own rows alone.
 //   update: for each column block c and half hf, D[i][m] = sum_t KD_t[col(i)]
 //           d_t[row m] with col(i) = 32 c + 8 (i / 4) + 4 hf + i % 4, so lane
 //           (m, g) receives columns 32 c + 8 g + 4 hf .. + 3 of its own row,
@@ -1022,10 +1024,33 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
         *reinterpret_cast<float2 *>(&KD[t][2 * lane]) =
             make_float2(k0 * fast_exp(Gn.x - G.x), k1 * fast_exp(Gn.y - G.y));
     }
+    // A_tj = k_t . k_j e^{G_t - G_j} (j < t): 28 pairs on eight lanes each
+    if (tid >= NT - 8 * 28) {
+        const int p = (tid - (NT - 8 * 28)) / 8, qc = tid % 8;
+        int t = 1;
+        while (t * (t + 1) / 2 <= p) ++t;
+        const int j = p - t * (t - 1) / 2;
+        float sa = 0.f;
+        if (t < na) {
+            for (int mm = 0; mm < HD / 8; ++mm) {
+                const int c = qc + 8 * mm;
+                sa = fmaf(ks[t][c], ks[j][c] * fast_exp(gsh[t][c] - gsh[j][c]), sa);
+            }
+        }
+        sa = group_sum<8>(sa);
+        if (qc == 0 && t < na) Am[t][j] = sa;  // unnormalised: scaled below
+    }
     __syncthreads();
+    // From here each wave works on its own 16 rows alone: its rows of X and
+    // d go through LDS within the wave only, so a wave runs on as soon as
+    // its part of the state has landed.
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    };
 
     // ---- 3. X = S K~^T: K~ has 8 rows, so the tile's lanes m >= 8 repeat
-    //      rows m - 8 and those columns of the result are dropped; and A
+    //      rows m - 8 and those columns of the result are dropped
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const int bn = m & (kChunk - 1);
     if constexpr (kBf16) {
@@ -1054,27 +1079,11 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) Xs[16 * wave + 4 * g + r][m] = acc[r];
     }
-    // A_tj = k_t . k_j e^{G_t - G_j} (j < t): 28 pairs on eight lanes each
-    if (tid >= NT - 8 * 28) {
-        const int p = (tid - (NT - 8 * 28)) / 8, qc = tid % 8;
-        int t = 1;
-        while (t * (t + 1) / 2 <= p) ++t;
-        const int j = p - t * (t - 1) / 2;
-        float sa = 0.f;
-        if (t < na) {
-            for (int mm = 0; mm < HD / 8; ++mm) {
-                const int c = qc + 8 * mm;
-                sa = fmaf(ks[t][c], ks[j][c] * fast_exp(gsh[t][c] - gsh[j][c]), sa);
-            }
-        }
-        sa = group_sum<8>(sa);
-        if (qc == 0 && t < na) Am[t][j] = sa;  // unnormalised: scaled below
-    }
-    __syncthreads();
+    wave_sync();
 
-    // ---- 4. per value row r: the d recurrence
-    if (tid < HD) {
-        const int r = tid;
+    // ---- 4. per value row r of the wave: the d recurrence
+    if (lane < 16) {
+        const int r = 16 * wave + lane;
         float d[kChunk];
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
@@ -1088,7 +1097,7 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
             }
         }
     }
-    __syncthreads();
+    wave_sync();
 
     // ---- 5. S_na = S e^{G_na} + sum_t d_t KD_t^T, per (column block, half)
     {
