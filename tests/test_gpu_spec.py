@@ -142,6 +142,46 @@ def test_commit_then_verify_continues_chunk_form(dev):
     assert_close_units(f64(second), f64(first), 2, "fp32", "continued outputs")
 
 
+@pytest.mark.parametrize("kda", [True, False])
+def test_chunk_forms_at_extreme_decays(kda, dev):
+    """The chunk forms of verify and commit where the decay is extreme: no
+    decay at all (g = 0), a decay strong enough to underflow exp(G) within
+    the chunk (g = -30 per step), and the two alternating per channel (KDA)
+    or per step (GDN).  Every exponent the chunk form takes is <= 0, so
+    nothing overflows; outputs, ring d and the committed state stay within
+    the fp32 bar of the oracle."""
+    B, D, Hqk, Hv, P = 3, 8, 2, 2, 6
+    c = make_case(7600 + kda, B, D, Hqk, Hv, kda, "fp32", "fp32", "fp32", P, dev)
+    shape = c["g"].shape
+    g = torch.zeros(shape, dtype=torch.float32)
+    g[1] = -30.0                                       # request 1: strong decay
+    if kda:
+        g[2, :, :, 1::2] = -30.0                       # request 2: alternating channels
+    else:
+        g[2, 1::2] = -30.0                             # request 2: alternating steps
+    c["g"] = g.to(dev)
+    n_tok, base = [D, D, D], [0, 5, 11]
+    ssm0 = c["ssm_pool"].clone()
+    out, _ = run_verify(kda, c, n_tok, base, Hqk, dev)
+    torch.cuda.synchronize()
+    o_ref, _, r_ref = oracle_verify(kda, c, n_tok, base, Hqk, Hv, "fp32", "fp32")
+    assert np.all(np.isfinite(f64(out)))
+    assert_close_units(f64(out), o_ref, 3, "fp32", "verify outputs")
+    slots = c["slots"].cpu().numpy()
+    ring = {k: f64(v) for k, v in c["ring"].items()}
+    for b in range(B):
+        pos = [(base[b] + t) % 16 for t in range(D)]
+        assert_close_units(ring["d"][slots[b]][:, pos], r_ref["d"][slots[b]][:, pos], 2, "fp32", "ring d")
+    accepted = [8, 8, 5]
+    fn = la.kda_commit if kda else la.gdn_commit
+    fn(i32(accepted, dev), c["slots"], c["ssm_pool"], c["ring"], i32(base, dev))
+    torch.cuda.synchronize()
+    p_ref = oracle.commit(accepted, slots, f64(ssm0), ring, base, kda=kda, state_dtype="fp32")
+    got = f64(c["ssm_pool"])
+    assert np.all(np.isfinite(got))
+    assert_close_units(got[slots], p_ref[slots], 2, "fp32", "committed state")
+
+
 def test_conv_window_scatter_and_track_copy_are_bit_exact(dev):
     B, D, C, P = 5, 4, 768, 12
     conv = synth.to_torch(synth.normal(7300, 0, (P + 1, 3, C)), "bf16", dev)
