@@ -23,17 +23,16 @@
 // LPR-lane group, bit-identical in every lane), the update is applied in
 // registers and the row is stored back: the state crosses HBM once each way.
 //
-// Latency hiding.  Every wave runs independently until the very end: it
-// issues its few prologue loads (x, conv history, conv weights, gates),
-// computes the conv + SiLU + L2-norm prologue (each wave recomputes the q/k
-// conv; the copies are bit-identical), then issues all of its state-row
-// loads and consumes the rows in issue order, storing each as soon as it is
-// updated.  (Issuing the rows before the prologue compute, so they are in
-// flight meanwhile, measured 0.35 us slower on a 55 MB launch: the prologue
-// loads then wait behind every workgroup's rows.)  The only workgroup barrier sits at the end: the
-// q/k conv history is shared by all waves, so it is rolled only after every
-// wave has read it.  With G > 1 the next head's loads are issued before the
-// current head is computed.
+// Latency hiding.  Each wave issues its few prologue loads (x, conv
+// history, conv weights, gates) and computes its share of the conv + SiLU
+// prologue: the waves split the q and k channels, and the one workgroup
+// barrier publishes the q/k conv outputs, from which every wave forms the
+// L2 norms.  Only then does a wave issue all of its state-row loads; it
+// consumes the rows in issue order, storing each as soon as it is updated.
+// (Issuing the rows before the prologue, so they are in flight meanwhile,
+// was slower: the small prologue loads then wait behind every workgroup's
+// rows.)  With G > 1 the next head's loads are issued before the current
+// head is computed.
 #pragma once
 
 #include "la_device.h"
@@ -53,8 +52,9 @@ template <int D, typename ST> struct DecodeCfg {
     static constexpr int NJ = RI / NW;              // row instructions per lane
     static constexpr int NT = 64 * NW;              // threads per workgroup
     static constexpr int RW = D < NJ * RPW ? D : NJ * RPW;  // rows per wave per head
-    static constexpr int QKL = (D + 63) / 64;       // q (or k) channels per lane
-    static constexpr int LDS_PER_WAVE = 2 * D + RW; // floats: q, k, v band
+    static constexpr int QS = D / NW;               // q (and k) channels each wave convolves
+    static constexpr int LDS_FLOATS = 2 * D + NW * RW;  // shared q, k conv outputs; v bands
+    static_assert(QS * NW == D && QS <= 32, "q/k channels split over the waves, 32 lanes each");
     static_assert(LPR >= 1 && LPR <= 32, "row must fit in half a wave");
     static_assert(RI % NW == 0, "rows must split evenly over waves");
     static_assert(NJ <= LPR, "one output lane per row instruction");
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
 {
     using Cfg = DecodeCfg<D, ST>;
     constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ;
-    constexpr int RW = Cfg::RW, QKL = Cfg::QKL;
+    constexpr int RW = Cfg::RW, QS = Cfg::QS;
     extern __shared__ float lds[];
 
     const int b = blockIdx.x / a.Hqk, kh = blockIdx.x % a.Hqk;
@@ -181,9 +181,9 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
         return;
     }
 
-    float *wq = lds + wave * Cfg::LDS_PER_WAVE;  // this wave's private LDS band
-    float *wk = wq + D;
-    float *wv = wk + D;
+    float *wq = lds;                      // the head's q conv outputs (all waves)
+    float *wk = lds + D;                  // its k conv outputs
+    float *wv = lds + 2 * D + wave * RW;  // this wave's private v band
     CT *cs = CONV ? static_cast<CT *>(a.conv_pool) + (int64_t)slot * a.conv_stride : nullptr;
     const int64_t xrow = (int64_t)b * a.C;
     const float bias_on = a.bias ? 1.f : 0.f;
@@ -193,15 +193,17 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
     const int cv0 = 2 * a.Hqk * D + kh * G * D;   // first v channel of the group
 
     // ---- 1. prologue loads (small) ----
+    // The q and k channels are split over the waves: wave w convolves q
+    // channels QS w .. QS w + QS - 1 on lanes 0..31 and the same k channels
+    // on lanes 32..63, so it alone reads (and rolls) their conv history.
     // Indices are clamped instead of branched on, so every lane issues the
     // same loads and no control-flow join forces an early wait.
-    ConvIn<IOT, CT> qi[QKL], ki[QKL], vi;
-#pragma unroll
-    for (int t = 0; t < QKL; ++t) {
-        const int i = min(lane + 64 * t, D - 1);
-        load_conv_in<IOT, CT, CONV>(qi[t], a, cs, xrow, cq0 + i);
-        load_conv_in<IOT, CT, CONV>(ki[t], a, cs, xrow, ck0 + i);
-    }
+    const bool is_k = lane >= 32;
+    const int qk_i = QS * wave + min(lane & 31, QS - 1);  // channel within the block
+    const bool qk_on = (lane & 31) < QS;
+    const int qk_c = (is_k ? ck0 : cq0) + qk_i;
+    ConvIn<IOT, CT> qki, vi;
+    load_conv_in<IOT, CT, CONV>(qki, a, cs, xrow, qk_c);
     const int vl = min(lane, RW - 1);  // this lane's v channel in the band
     load_conv_in<IOT, CT, CONV>(vi, a, cs, xrow, cv0 + rband + vl);
     float gl[EPL], beta;
@@ -209,22 +211,25 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. prologue compute, before any state row is requested ----
-    float sq = 0.f, sk = 0.f, sqk = 0.f;
-#pragma unroll
-    for (int t = 0; t < QKL; ++t) {
-        const int i = lane + 64 * t;
-        if (i < D) {
-            const float yq = conv_out<CONV>(qi[t], bias_on), yk = conv_out<CONV>(ki[t], bias_on);
-            wq[i] = yq;
-            wk[i] = yk;
-            sq = fmaf(yq, yq, sq);
-            sk = fmaf(yk, yk, sk);
-            sqk = fmaf(yq, yk, sqk);
-        }
+    if (qk_on) {
+        (is_k ? wk : wq)[qk_i] = conv_out<CONV>(qki, bias_on);
+        if constexpr (CONV) roll_history<IOT, CT>(qki, a, cs, qk_c);  // only this lane reads it
     }
     if (lane < RW) {
         wv[lane] = conv_out<CONV>(vi, bias_on);
         if constexpr (CONV) roll_history<IOT, CT>(vi, a, cs, cv0 + rband + lane);  // only this wave reads it
+    }
+    __syncthreads();  // every wave's q/k conv outputs written
+    float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int t = 0; t < (D + 63) / 64; ++t) {
+        const int i = lane + 64 * t;
+        if (i < D) {
+            const float yq = wq[i], yk = wk[i];
+            sq = fmaf(yq, yq, sq);
+            sk = fmaf(yk, yk, sk);
+            sqk = fmaf(yq, yk, sqk);
+        }
     }
     sq = wave_sum(sq);
     sk = wave_sum(sk);
@@ -232,7 +237,6 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
     const float inv_q = 1.0f / sqrtf(sq + a.eps);
     const float inv_k = 1.0f / sqrtf(sk + a.eps);
     const float kq = sqk * inv_q * inv_k;
-    __builtin_amdgcn_wave_barrier();  // LDS band written above, read below (same wave)
     float kk[EPL], qq[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -330,21 +334,6 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
         for (int hg = 0; hg + 1 < G; ++hg) step(hg);
     }
     head(G - 1, buf, gl, beta);
-
-    // ---- 5. roll the shared q/k history once every wave has read it ----
-    if constexpr (CONV) {
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int t = 0; t < QKL; ++t) {
-                const int i = lane + 64 * t;
-                if (i < D) {
-                    roll_history<IOT, CT>(qi[t], a, cs, cq0 + i);
-                    roll_history<IOT, CT>(ki[t], a, cs, ck0 + i);
-                }
-            }
-        }
-    }
 }
 
 
@@ -354,7 +343,7 @@ template <int D, typename ST, typename IOT, typename CT, bool KDA, bool CONV>
 inline hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream)
 {
     using Cfg = DecodeCfg<D, ST>;
-    const size_t lds = (size_t)Cfg::NW * Cfg::LDS_PER_WAVE * sizeof(float);
+    const size_t lds = (size_t)Cfg::LDS_FLOATS * sizeof(float);
     const dim3 grid((unsigned)(a.B * a.Hqk)), block(Cfg::NT);
     if (a.G == 1)
         hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 1, CONV>), grid, block, lds,
