@@ -24,10 +24,12 @@
 // registers and the row is stored back: the state crosses HBM once each way.
 //
 // Latency hiding.  Each wave issues its few prologue loads (x, conv
-// history, conv weights, gates) and computes its share of the conv + SiLU
-// prologue: the waves split the q and k channels, and the one workgroup
-// barrier publishes the q/k conv outputs, from which every wave forms the
-// L2 norms.  Only then does a wave issue all of its state-row loads; it
+// history, conv weights, gates) and computes the conv + SiLU prologue: with
+// one value head per workgroup the waves split the q and k channels and one
+// workgroup barrier publishes the q/k conv outputs (with several heads per
+// workgroup every wave convolves all of them itself, and the shared q/k
+// history is rolled after a barrier at the end); every wave forms the L2
+// norms.  Only then does a wave issue all of its state-row loads; it
 // consumes the rows in issue order, storing each as soon as it is updated.
 // (Issuing the rows before the prologue, so they are in flight meanwhile,
 // was slower: the small prologue loads then wait behind every workgroup's
@@ -52,8 +54,10 @@ template <int D, typename ST> struct DecodeCfg {
     static constexpr int NJ = RI / NW;              // row instructions per lane
     static constexpr int NT = 64 * NW;              // threads per workgroup
     static constexpr int RW = D < NJ * RPW ? D : NJ * RPW;  // rows per wave per head
-    static constexpr int QS = D / NW;               // q (and k) channels each wave convolves
-    static constexpr int LDS_FLOATS = 2 * D + NW * RW;  // shared q, k conv outputs; v bands
+    static constexpr int QKL = (D + 63) / 64;       // q (or k) channels per lane, whole-head prologue
+    static constexpr int QS = D / NW;               // q (and k) channels per wave, split prologue
+    static constexpr int LDS_SPLIT = 2 * D + NW * RW;   // floats: shared q, k outputs; v bands
+    static constexpr int LDS_WHOLE = NW * (2 * D + RW); // floats: per wave q, k, v band
     static_assert(QS * NW == D && QS <= 32, "q/k channels split over the waves, 32 lanes each");
     static_assert(LPR >= 1 && LPR <= 32, "row must fit in half a wave");
     static_assert(RI % NW == 0, "rows must split evenly over waves");
@@ -166,7 +170,13 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
 {
     using Cfg = DecodeCfg<D, ST>;
     constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ;
-    constexpr int RW = Cfg::RW, QS = Cfg::QS;
+    constexpr int RW = Cfg::RW, QS = Cfg::QS, QKL = Cfg::QKL;
+    // One value head per workgroup: the waves split the q/k prologue (one
+    // barrier).  Several heads per workgroup (GQA groups): every wave runs the
+    // whole q/k prologue itself, so no wave waits for another before its
+    // state stream -- these launches run one workgroup per CU in many rounds,
+    // where that wait is exposed.
+    constexpr bool kSplit = GT == 1;
     extern __shared__ float lds[];
 
     const int b = blockIdx.x / a.Hqk, kh = blockIdx.x % a.Hqk;
@@ -181,9 +191,9 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
         return;
     }
 
-    float *wq = lds;                      // the head's q conv outputs (all waves)
-    float *wk = lds + D;                  // its k conv outputs
-    float *wv = lds + 2 * D + wave * RW;  // this wave's private v band
+    float *wq = kSplit ? lds : lds + wave * (2 * D + RW);  // q conv outputs
+    float *wk = wq + D;                                     // k conv outputs
+    float *wv = kSplit ? lds + 2 * D + wave * RW : wk + D;  // this wave's v band
     CT *cs = CONV ? static_cast<CT *>(a.conv_pool) + (int64_t)slot * a.conv_stride : nullptr;
     const int64_t xrow = (int64_t)b * a.C;
     const float bias_on = a.bias ? 1.f : 0.f;
@@ -193,17 +203,28 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
     const int cv0 = 2 * a.Hqk * D + kh * G * D;   // first v channel of the group
 
     // ---- 1. prologue loads (small) ----
-    // The q and k channels are split over the waves: wave w convolves q
-    // channels QS w .. QS w + QS - 1 on lanes 0..31 and the same k channels
-    // on lanes 32..63, so it alone reads (and rolls) their conv history.
+    // Split prologue: wave w convolves q channels QS w .. QS w + QS - 1 on
+    // lanes 0..31 and the same k channels on lanes 32..63, so it alone reads
+    // (and rolls) their conv history.  Whole prologue: lane l convolves q and
+    // k channels l, l + 64, ..; the shared history is rolled at the end.
     // Indices are clamped instead of branched on, so every lane issues the
     // same loads and no control-flow join forces an early wait.
     const bool is_k = lane >= 32;
     const int qk_i = QS * wave + min(lane & 31, QS - 1);  // channel within the block
     const bool qk_on = (lane & 31) < QS;
     const int qk_c = (is_k ? ck0 : cq0) + qk_i;
-    ConvIn<IOT, CT> qki, vi;
-    load_conv_in<IOT, CT, CONV>(qki, a, cs, xrow, qk_c);
+    constexpr int NQK = kSplit ? 1 : QKL;
+    ConvIn<IOT, CT> qi[NQK], ki[NQK], vi;
+    if constexpr (kSplit) {
+        load_conv_in<IOT, CT, CONV>(qi[0], a, cs, xrow, qk_c);
+    } else {
+#pragma unroll
+        for (int t = 0; t < QKL; ++t) {
+            const int i = min(lane + 64 * t, D - 1);
+            load_conv_in<IOT, CT, CONV>(qi[t], a, cs, xrow, cq0 + i);
+            load_conv_in<IOT, CT, CONV>(ki[t], a, cs, xrow, ck0 + i);
+        }
+    }
     const int vl = min(lane, RW - 1);  // this lane's v channel in the band
     load_conv_in<IOT, CT, CONV>(vi, a, cs, xrow, cv0 + rband + vl);
     float gl[EPL], beta;
@@ -211,15 +232,27 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. prologue compute, before any state row is requested ----
-    if (qk_on) {
-        (is_k ? wk : wq)[qk_i] = conv_out<CONV>(qki, bias_on);
-        if constexpr (CONV) roll_history<IOT, CT>(qki, a, cs, qk_c);  // only this lane reads it
+    if constexpr (kSplit) {
+        if (qk_on) {
+            (is_k ? wk : wq)[qk_i] = conv_out<CONV>(qi[0], bias_on);
+            if constexpr (CONV) roll_history<IOT, CT>(qi[0], a, cs, qk_c);  // only this lane reads it
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < QKL; ++t) {
+            const int i = lane + 64 * t;
+            if (i < D) {
+                wq[i] = conv_out<CONV>(qi[t], bias_on);
+                wk[i] = conv_out<CONV>(ki[t], bias_on);
+            }
+        }
     }
     if (lane < RW) {
         wv[lane] = conv_out<CONV>(vi, bias_on);
         if constexpr (CONV) roll_history<IOT, CT>(vi, a, cs, cv0 + rband + lane);  // only this wave reads it
     }
-    __syncthreads();  // every wave's q/k conv outputs written
+    if constexpr (kSplit) __syncthreads();  // every wave's q/k conv outputs written
+    else __builtin_amdgcn_wave_barrier();   // this wave's LDS band written above, read below
     float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
     for (int t = 0; t < (D + 63) / 64; ++t) {
@@ -334,6 +367,22 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
         for (int hg = 0; hg + 1 < G; ++hg) step(hg);
     }
     head(G - 1, buf, gl, beta);
+
+    // ---- 5. whole prologue: roll the shared q/k history once every wave
+    //      has read it ----
+    if constexpr (CONV && !kSplit) {
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int t = 0; t < QKL; ++t) {
+                const int i = lane + 64 * t;
+                if (i < D) {
+                    roll_history<IOT, CT>(qi[t], a, cs, cq0 + i);
+                    roll_history<IOT, CT>(ki[t], a, cs, ck0 + i);
+                }
+            }
+        }
+    }
 }
 
 
@@ -343,16 +392,17 @@ template <int D, typename ST, typename IOT, typename CT, bool KDA, bool CONV>
 inline hipError_t launch_decode_cfg(const DecodeArgs &a, hipStream_t stream)
 {
     using Cfg = DecodeCfg<D, ST>;
-    const size_t lds = (size_t)Cfg::LDS_FLOATS * sizeof(float);
+    const size_t lds_split = (size_t)Cfg::LDS_SPLIT * sizeof(float);
+    const size_t lds_whole = (size_t)Cfg::LDS_WHOLE * sizeof(float);
     const dim3 grid((unsigned)(a.B * a.Hqk)), block(Cfg::NT);
     if (a.G == 1)
-        hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 1, CONV>), grid, block, lds,
+        hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 1, CONV>), grid, block, lds_split,
                            stream, a);
     else if (a.G == 2)
-        hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 2, CONV>), grid, block, lds,
+        hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 2, CONV>), grid, block, lds_whole,
                            stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 0, CONV>), grid, block, lds,
+        hipLaunchKernelGGL((decode_kernel<D, ST, IOT, CT, KDA, 0, CONV>), grid, block, lds_whole,
                            stream, a);
     return hipGetLastError();
 }
