@@ -382,15 +382,6 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     const bool valid = t < nt;
     const int64_t tok = t0 + min(t, nt - 1);
     float qv[16], kv[16], gv[16];
-    int ps = t, pe = t, s0 = 0, hs = -1;
-    if (valid) {
-        const int n = find_seq_p(a.cu, a.N, t0 + t);
-        s0 = a.cu[n];
-        ps = max(s0, t0) - t0;
-        pe = min(a.cu[n + 1], t0 + CB) - 1 - t0;
-        const int si = a.slot_in[n];
-        hs = (si >= 0 && si < a.num_rows) ? si : -1;
-    }
     if constexpr (KDA) {
         load16<float>(gv, a.g + (tok * a.Hv + h) * DK + c0);
     } else {
@@ -409,6 +400,17 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     } else {
         load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
         load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
+    }
+    // the token's sequence (a short search over cu_seqlens): after the data
+    // loads, so its dependent round trips overlap them
+    int ps = t, pe = t, s0 = 0, hs = -1;
+    if (valid) {
+        const int n = find_seq_p(a.cu, a.N, t0 + t);
+        s0 = a.cu[n];
+        ps = max(s0, t0) - t0;
+        pe = min(a.cu[n + 1], t0 + CB) - 1 - t0;
+        const int si = a.slot_in[n];
+        hs = (si >= 0 && si < a.num_rows) ? si : -1;
     }
     if constexpr (CONV) {
         // conv of q and k into Qn / Kn, then back to the (token, chunk)
