@@ -92,7 +92,7 @@ __device__ __forceinline__ float inv_norm128(float x0, float x1, float eps)
 // ---------------------------------------------------------------------------
 // verify
 // ---------------------------------------------------------------------------
-// The per-chunk front half shared by both verify kernels.  For the steps
+// The per-chunk front half of the sequential verify.  For the steps
 // t0 .. t0 + nc - 1 of request b, value head h it
 //   - stages the pre-conv inputs of the head's q|k|v channels in xe rows
 //     3 .. 3 + nc - 1 below the three inputs before the chunk (rows 0 .. 2:
@@ -104,9 +104,7 @@ __device__ __forceinline__ float inv_norm128(float x0, float x1, float eps)
 //   - writes the conv windows (the history after each step: xe rows
 //     tt + 1 .. tt + 3) and the ring records (rawk, rawv, g, beta and the
 //     normalised k) with 16-byte stores where the rows allow;
-//   - leaves the inverse norms in nq / nk and the gates as exp(g) per step
-//     (CUM = false: the sequential update) or as the running sum G_t of g
-//     over the chunk (CUM = true: the chunk form).
+//   - leaves the inverse norms in nq / nk and the decays exp(g) in gs.
 // Ends with a barrier after everything later phases read from LDS.
 constexpr int XLD = 3 * HD + 4;   // xe / ys row stride (floats): rows shift banks
 constexpr int GLD = HD + 4;       // gs row stride (floats)
@@ -135,11 +133,11 @@ __device__ __forceinline__ void store16(void *base, int64_t elem, const float *v
     st_stream(static_cast<T *>(base) + elem, V16<T>::pack(v));
 }
 
-template <typename IOT, typename CT, bool KDA, bool CONV, int NT, bool CUM, class Issue>
+template <typename IOT, typename CT, bool KDA, bool CONV, int NT>
 __device__ __forceinline__ void verify_front(const VerifyArgs &a, int b, int h, int kh, int slot,
                                              int rb, int t0, int nc, float (*xe)[XLD],
                                              float (*ys)[XLD], float (*gs)[GLD], float *bs,
-                                             float *nq, float *nk, Issue &&issue)
+                                             float *nq, float *nk)
 {
     constexpr int NCH = 3 * HD;                                // q, k, v channels
     constexpr int XPT = (kChunk * NCH + NT - 1) / NT;          // staged inputs per thread
@@ -201,11 +199,6 @@ __device__ __forceinline__ void verify_front(const VerifyArgs &a, int b, int h, 
                 }
             }
         }
-        // The caller's own loads (the state) go out behind the small staged
-        // ones: the waits for those then never wait on the state.
-        __builtin_amdgcn_sched_barrier(0);
-        issue();
-        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();  // the previous chunk's staged values are no longer read
 #pragma unroll
         for (int q = 0; q < XPT; ++q) {
@@ -253,30 +246,15 @@ __device__ __forceinline__ void verify_front(const VerifyArgs &a, int b, int h, 
             for (int tt = t_lo; tt < t_hi; ++tt) ys[tt][j] = xe[tt + 3][j];
         }
     }
-    // ---- gates to the ring; then exp(g) per step, or the running sum of g
-    if constexpr (CUM) {
-        for (int c = tid; c < HD; c += NT) {
-            float G = 0.f;
-            for (int tt = 0; tt < nc; ++tt) {
-                const int pos = (rb + t0 + tt) & (R.L - 1);
-                const float g = gs[tt][c];
-                if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
-                else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
-                if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
-                G += g;
-                gs[tt][c] = G;
-            }
-        }
-    } else {
-        for (int i = tid; i < nc * HD; i += NT) {
-            const int tt = i / HD, c = i % HD;
-            const int pos = (rb + t0 + tt) & (R.L - 1);
-            const float g = gs[tt][c];
-            if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
-            else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
-            if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
-            gs[tt][c] = fast_exp(g);
-        }
+    // ---- gates to the ring; then exp(g) per step
+    for (int i = tid; i < nc * HD; i += NT) {
+        const int tt = i / HD, c = i % HD;
+        const int pos = (rb + t0 + tt) & (R.L - 1);
+        const float g = gs[tt][c];
+        if constexpr (KDA) R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + c] = g;
+        else if (c == 0) R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)] = g;
+        if (c == 0) R.beta[ring_at(slot, a.Hv, R.L, h, pos, 1)] = bs[tt];
+        gs[tt][c] = fast_exp(g);
     }
     // ---- the conv windows: after step tt the history is xe rows
     //      tt + 1 .. tt + 3; q/k windows come from the first value head of
@@ -367,8 +345,7 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) verify_kernel(VerifyA
 
     for (int t0 = 0; t0 < n; t0 += kChunk) {
         const int nc = min(kChunk, n - t0);
-        verify_front<IOT, CT, KDA, CONV, NT, false>(a, b, h, kh, slot, rb, t0, nc, xe, ys, gs, bs,
-                                                    nq, nk, [] {});
+        verify_front<IOT, CT, KDA, CONV, NT>(a, b, h, kh, slot, rb, t0, nc, xe, ys, gs, bs, nq, nk);
         // ---- the steps: only the state rows, with no barrier between steps
         for (int tt = 0; tt < nc; ++tt) {
             const int t = t0 + tt;
@@ -458,6 +435,13 @@ template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4 &r, flo
 }
 
 constexpr int kChunkNT = 512;   // threads of the chunk-form verify workgroup
+
+// Floor of a log decay inside the chunk-form running sums.  Both chunk forms
+// use differences G_t - G_j of running sums, which a gate of -inf (a full
+// reset of the state) would turn into -inf - -inf.  exp(-128) is below the
+// smallest fp32 denormal, so a single step's decay is already exactly 0 at the
+// floor: the floor changes no result, while every running sum stays finite.
+constexpr float kGFloor = -128.f;
 
 template <typename ST, typename IOT, typename CT, bool KDA, bool CONV>
 __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
@@ -596,7 +580,8 @@ __global__ void __launch_bounds__(kChunkNT) verify_chunk_kernel(VerifyArgs a)
                     *reinterpret_cast<float4 *>(R.g + ring_at(slot, a.Hv, R.L, h, pos_of(tt), HD) + 4 * tid) = g4[tt];
                 else if (tid == 0)
                     R.g[ring_at(slot, a.Hv, R.L, h, pos_of(tt), 1)] = g4[tt].x;
-                G.x += g4[tt].x; G.y += g4[tt].y; G.z += g4[tt].z; G.w += g4[tt].w;
+                G.x += fmaxf(g4[tt].x, kGFloor); G.y += fmaxf(g4[tt].y, kGFloor);
+                G.z += fmaxf(g4[tt].z, kGFloor); G.w += fmaxf(g4[tt].w, kGFloor);
                 *reinterpret_cast<float4 *>(&Gs[tt][4 * tid]) = G;
             }
         }
@@ -968,7 +953,8 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
             if (t < na) {
-                G.x += g4[t].x; G.y += g4[t].y; G.z += g4[t].z; G.w += g4[t].w;
+                G.x += fmaxf(g4[t].x, kGFloor); G.y += fmaxf(g4[t].y, kGFloor);
+                G.z += fmaxf(g4[t].z, kGFloor); G.w += fmaxf(g4[t].w, kGFloor);
                 *reinterpret_cast<float4 *>(&gsh[t][4 * tid]) = G;
             }
         }

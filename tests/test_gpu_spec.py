@@ -182,6 +182,48 @@ def test_chunk_forms_at_extreme_decays(kda, dev):
     assert_close_units(got[slots], p_ref[slots], 2, "fp32", "committed state")
 
 
+@pytest.mark.parametrize("kda", [1, 0], ids=["kda", "gdn"])
+def test_chunk_forms_with_a_full_reset(kda, dev):
+    """A gate of -inf empties the state at that step (exp(-inf) = 0), so the
+    outputs after it depend on the later steps only.  The chunk forms of
+    verify and commit take differences of running gate sums; the reset must
+    not turn those into NaN.  Request 0 resets mid-chunk, request 1 at its
+    first step, request 2 at its last step; for KDA request 0 resets only the
+    even key channels."""
+    B, D, Hqk, Hv, P = 3, 8, 2, 2, 6
+    c = make_case(7700 + kda, B, D, Hqk, Hv, kda, "fp32", "fp32", "fp32", P, dev)
+    g = c["g"].cpu().clone()
+    if kda:
+        g[0, 3, :, 0::2] = float("-inf")
+        g[1, 0] = float("-inf")
+        g[2, D - 1] = float("-inf")
+    else:
+        g[0, 3] = float("-inf")
+        g[1, 0] = float("-inf")
+        g[2, D - 1] = float("-inf")
+    c["g"] = g.to(dev)
+    n_tok, base = [D, D, D], [0, 5, 11]
+    ssm0 = c["ssm_pool"].clone()
+    out, _ = run_verify(kda, c, n_tok, base, Hqk, dev)
+    torch.cuda.synchronize()
+    o_ref, _, r_ref = oracle_verify(kda, c, n_tok, base, Hqk, Hv, "fp32", "fp32")
+    assert np.all(np.isfinite(f64(out)))
+    assert_close_units(f64(out), o_ref, 3, "fp32", "verify outputs")
+    slots = c["slots"].cpu().numpy()
+    ring = {k: f64(v) for k, v in c["ring"].items()}
+    for b in range(B):
+        pos = [(base[b] + t) % 16 for t in range(D)]
+        assert_close_units(ring["d"][slots[b]][:, pos], r_ref["d"][slots[b]][:, pos], 2, "fp32", "ring d")
+    accepted = [6, 8, 8]
+    fn = la.kda_commit if kda else la.gdn_commit
+    fn(i32(accepted, dev), c["slots"], c["ssm_pool"], c["ring"], i32(base, dev))
+    torch.cuda.synchronize()
+    p_ref = oracle.commit(accepted, slots, f64(ssm0), ring, base, kda=kda, state_dtype="fp32")
+    got = f64(c["ssm_pool"])
+    assert np.all(np.isfinite(got))
+    assert_close_units(got[slots], p_ref[slots], 2, "fp32", "committed state")
+
+
 def test_conv_window_scatter_and_track_copy_are_bit_exact(dev):
     B, D, C, P = 5, 4, 768, 12
     conv = synth.to_torch(synth.normal(7300, 0, (P + 1, 3, C)), "bf16", dev)
