@@ -615,7 +615,7 @@ def main():
                     help="only the chunked-prefill workloads (for counter profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
