@@ -922,6 +922,9 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
         xr[q] = *reinterpret_cast<const uint4 *>(static_cast<const IOT *>(which ? R.rawv : R.rawk) +
                                                  ring_at(slot, a.Hv, R.L, h, pos_of(t), HD) + grp * VI);
     }
+    // the betas before the gates: wave 0 waits for its first gate load at
+    // the end of the branch below, and its beta load is then already out
+    if (tid < kChunk) bv = R.beta[ring_at(slot, a.Hv, R.L, h, pos_of(min(tid, na - 1)), 1)];
     if (tid < 32) {  // lane l: channels 4 l .. 4 l + 3 of every step
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
@@ -934,7 +937,6 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
             }
         }
     }
-    if (tid < kChunk) bv = R.beta[ring_at(slot, a.Hv, R.L, h, pos_of(min(tid, na - 1)), 1)];
 #pragma unroll
     for (int q = 0; q < II; ++q) {
         const int i = tid + q * NT, grp = i % GI, which = (i / GI) % 2, t = i / (2 * GI);
