@@ -1140,15 +1140,90 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
 // cumulative log decay of the first j folded steps: the unrolled sum of the
 // ReplaySSM d/k/g passage, 16 steps per LDS pass (passes compose).
 constexpr int kFold = 16;
+// One pass of the fold over nc <= kFold ring steps from step t0.  Staging:
+// the records as 16-byte loads, d and k in units of V16<IOT>::N values, the
+// gates in units of four channels (GDN: the step's gate four times).
+// Indices are clamped, so every load is issued with no branch; rows past
+// the pass's last step repeat it and are never read.
+template <typename IOT, bool KDA, int NT> struct FoldStage {
+    static constexpr int VI = V16<IOT>::N, ND = kFold * HD / VI, NG = kFold * HD / 4;
+    static constexpr int UD = (ND + NT - 1) / NT, UG = (NG + NT - 1) / NT;
+    uint4 d[UD], k[UD], g[UG];
+
+    __device__ __forceinline__ void load(const FoldArgs &a, int slot, int h, int rb, int t0, int nc,
+                                         int tid)
+    {
+        const RingArgs &R = a.ring;
+#pragma unroll
+        for (int q = 0; q < UD; ++q) {
+            const int e = min(tid + q * NT, ND - 1) * VI;
+            const int pos = (rb + t0 + min(e / HD, nc - 1)) & (R.L - 1);
+            const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD) + e % HD;
+            d[q] = *reinterpret_cast<const uint4 *>(static_cast<const IOT *>(R.d) + vr);
+            k[q] = *reinterpret_cast<const uint4 *>(static_cast<const IOT *>(R.k) + vr);
+        }
+#pragma unroll
+        for (int q = 0; q < UG; ++q) {
+            const int e = min(tid + q * NT, NG - 1) * 4;
+            const int pos = (rb + t0 + min(e / HD, nc - 1)) & (R.L - 1);
+            if constexpr (KDA) {
+                g[q] = *reinterpret_cast<const uint4 *>(R.g + ring_at(slot, a.Hv, R.L, h, pos, HD) + e % HD);
+            } else {
+                const uint32_t g1 = __float_as_uint(R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)]);
+                g[q] = make_uint4(g1, g1, g1, g1);
+            }
+        }
+    }
+
+    // The staged records to LDS, then per channel the cumulative decay and
+    // the decayed keys; starts and ends with a barrier.
+    __device__ __forceinline__ void tables(float (*dsh)[HD], float (*esh)[HD], float (*gsh)[HD],
+                                           float *eend, int nc, int tid) const
+    {
+        __syncthreads();  // the previous pass's tables are no longer read
+#pragma unroll
+        for (int q = 0; q < UD; ++q) {
+            const int u = tid + q * NT;
+            if (u < ND) {
+                const int t = u * VI / HD, c = u * VI % HD;
+                float v[VI];
+                unpack16<IOT>(d[q], v);
+#pragma unroll
+                for (int e = 0; e < VI; e += 4)
+                    *reinterpret_cast<float4 *>(&dsh[t][c + e]) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+                unpack16<IOT>(k[q], v);
+#pragma unroll
+                for (int e = 0; e < VI; e += 4)
+                    *reinterpret_cast<float4 *>(&esh[t][c + e]) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < UG; ++q) {
+            const int u = tid + q * NT;
+            if (u < NG) *reinterpret_cast<uint4 *>(&gsh[4 * u / HD][4 * u % HD]) = g[q];
+        }
+        __syncthreads();
+        if (tid < HD) {
+            float G = 0.f;
+            for (int t = 0; t < nc; ++t) {
+                G += gsh[t][tid];
+                gsh[t][tid] = G;
+            }
+            eend[tid] = fast_exp(G);
+            for (int t = 0; t < nc; ++t) esh[t][tid] *= fast_exp(G - gsh[t][tid]);
+        }
+        __syncthreads();
+    }
+};
+
 template <typename ST, typename IOT, bool KDA, bool PROJ>
 __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) fold_kernel(FoldArgs a)
 {
     using Cfg = DecodeCfg<HD, ST>;
     constexpr int EPL = Cfg::EPL, LPR = Cfg::LPR, RPW = Cfg::RPW, NJ = Cfg::NJ, NT = Cfg::NT;
-    constexpr int VPT = (kFold * HD + NT - 1) / NT;
-    __shared__ float dsh[kFold][HD];  // d_j
-    __shared__ float esh[kFold][HD];  // k_j, then k_j exp(G_end - G_j)
-    __shared__ float gsh[kFold][HD];  // g_j, then G_j
+    __shared__ __align__(16) float dsh[kFold][HD];  // d_j
+    __shared__ __align__(16) float esh[kFold][HD];  // k_j, then k_j exp(G_end - G_j)
+    __shared__ __align__(16) float gsh[kFold][HD];  // g_j, then G_j
     __shared__ float eend[HD];        // exp(G_end)
     const int b = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1161,48 +1236,11 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) fold_kernel(FoldArgs 
     const int m = min(max(a.m[b], 0), a.ring.L);
     const ST *S0 = static_cast<const ST *>(a.ssm_pool) + (int64_t)slot * a.ssm_stride +
                    (int64_t)h * HD * HD;
-    float s[NJ][EPL];
-    {
-        uint4 raw[NJ];
-        load_rows<HD, ST>(raw, S0, wave, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
-    }
     const int col0 = (lane % LPR) * EPL;
-    const RingArgs &R = a.ring;
-    for (int t0 = 0; t0 < m; t0 += kFold) {
-        const int nc = min(kFold, m - t0);
-        float dv_[VPT], kv[VPT], gv[VPT];
-#pragma unroll
-        for (int q = 0; q < VPT; ++q) {  // clamped indices: every load issued, no branch
-            const int i = min(tid + q * NT, kFold * HD - 1);
-            const int pos = (a.ring_base[b] + t0 + min(i / HD, nc - 1)) & (R.L - 1);
-            const int64_t vr = ring_at(slot, a.Hv, R.L, h, pos, HD) + i % HD;
-            dv_[q] = ld<IOT>(R.d, vr);
-            kv[q] = ld<IOT>(R.k, vr);
-            gv[q] = KDA ? R.g[vr] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
-        }
-        __syncthreads();  // the previous pass's tables are no longer read
-#pragma unroll
-        for (int q = 0; q < VPT; ++q) {
-            const int i = tid + q * NT;
-            if (i < kFold * HD) {
-                dsh[i / HD][i % HD] = dv_[q];
-                esh[i / HD][i % HD] = kv[q];
-                gsh[i / HD][i % HD] = gv[q];
-            }
-        }
-        __syncthreads();
-        if (tid < HD) {  // per channel: cumulative decay, then the decayed keys
-            float G = 0.f;
-            for (int t = 0; t < nc; ++t) {
-                G += gsh[t][tid];
-                gsh[t][tid] = G;
-            }
-            eend[tid] = fast_exp(G);
-            for (int t = 0; t < nc; ++t) esh[t][tid] *= fast_exp(G - gsh[t][tid]);
-        }
-        __syncthreads();
+    const int rb = a.ring_base[b];
+    float s[NJ][EPL];
+    // s = s Diag(exp(G_end)) + sum_t d_t (k_t exp(G_end - G_t))^T over a pass
+    auto apply = [&](int nc) {
         float ee[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) ee[e] = eend[col0 + e];
@@ -1221,6 +1259,31 @@ __global__ void __launch_bounds__((DecodeCfg<HD, ST>::NT)) fold_kernel(FoldArgs 
                 for (int e = 0; e < EPL; ++e) s[j][e] = fmaf(dt, kt[e], s[j][e]);
             }
         }
+    };
+    // First pass: its records go out first and the state rows right behind
+    // them (loads complete in issue order, so waiting for the records does
+    // not wait for the rows); the rows are unpacked only once the tables are
+    // built, so they land under the staging.  With m = 0 the records loaded
+    // are unused and the checkpoint is copied.
+    const int nc0 = min(kFold, m);
+    {
+        uint4 raw[NJ];
+        FoldStage<IOT, KDA, NT> fs;
+        fs.load(a, slot, h, rb, 0, max(nc0, 1), tid);
+        __builtin_amdgcn_sched_barrier(0);
+        load_rows<HD, ST>(raw, S0, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m > 0) fs.tables(dsh, esh, gsh, eend, nc0, tid);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) Stor<ST>::unpack(raw[j], s[j]);
+    }
+    if (m > 0) apply(nc0);
+    for (int t0 = kFold; t0 < m; t0 += kFold) {
+        const int nc = min(kFold, m - t0);
+        FoldStage<IOT, KDA, NT> fs;
+        fs.load(a, slot, h, rb, t0, nc, tid);
+        fs.tables(dsh, esh, gsh, eend, nc, tid);
+        apply(nc);
     }
     ST *Sd = static_cast<ST *>(a.ssm_pool) + (int64_t)dst * a.ssm_stride + (int64_t)h * HD * HD;
 #pragma unroll
