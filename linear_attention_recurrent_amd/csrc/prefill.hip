@@ -347,6 +347,9 @@ __device__ __forceinline__ void conv_apply(float *y, const float *xr, const Pref
 // Kernel 1: intra-block quantities, one workgroup (8 waves) per (tile, head).
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 512;
+constexpr int kSeqTab = 512;  // sequences whose cu_seqlens / slot_in kernel 1 stages in LDS
+static_assert(kSeqTab <= kIntraThreads && 2 * kSeqTab <= CB * LDJ,
+              "one table entry per thread, both tables inside N's space");
 constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
 constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + 4 * CB * sizeof(int);
 
@@ -381,6 +384,15 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     const int t = tid >> 3, cq = tid & 7, c0 = 16 * cq;
     const bool valid = t < nt;
     const int64_t tok = t0 + min(t, nt - 1);
+    // With fewer than kSeqTab sequences, cu_seqlens and slot_in go to LDS in
+    // one parallel round (Nm is free until step 3) and each token searches
+    // them there; issued before the data loads, so waiting for them does not
+    // wait for the data (loads complete in issue order).  Larger batches
+    // search cu_seqlens in global memory.
+    int *cut = reinterpret_cast<int *>(Nm), *sit = cut + kSeqTab;
+    const bool tab = a.N < kSeqTab;
+    const int cuv = a.cu[min(tid, a.N)], siv = a.slot_in[min(tid, a.N - 1)];
+    __builtin_amdgcn_sched_barrier(0);
     float qv[16], kv[16], gv[16];
     if constexpr (KDA) {
         load16<float>(gv, a.g + (tok * a.Hv + h) * DK + c0);
@@ -401,15 +413,36 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
         load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
     }
-    // the token's sequence (a short search over cu_seqlens): after the data
-    // loads, so its dependent round trips overlap them
+    // the token's sequence: a search of the LDS table, else of cu_seqlens in
+    // global memory (after the data loads, so its round trips overlap them)
+    cut[tid] = cuv;  // entries past N repeat the last one and are never read
+    sit[tid] = siv;
+    __syncthreads();
     int ps = t, pe = t, s0 = 0, hs = -1;
     if (valid) {
-        const int n = find_seq_p(a.cu, a.N, t0 + t);
-        s0 = a.cu[n];
+        int n, s1, si;
+        if (tab) {
+            int lo = 0, hi = a.N - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (cut[mid] <= t0 + t) lo = mid;
+                else hi = mid - 1;
+            }
+            n = lo;
+            s0 = cut[n];
+            s1 = cut[n + 1];
+            si = sit[n];
+            // keeps these LDS reads from being merged with the global ones
+            // below into one generic load, which would wait for every load
+            asm volatile("" : "+v"(s0), "+v"(s1), "+v"(si));
+        } else {
+            n = find_seq_p(a.cu, a.N, t0 + t);
+            s0 = a.cu[n];
+            s1 = a.cu[n + 1];
+            si = a.slot_in[n];
+        }
         ps = max(s0, t0) - t0;
-        pe = min(a.cu[n + 1], t0 + CB) - 1 - t0;
-        const int si = a.slot_in[n];
+        pe = min(s1, t0 + CB) - 1 - t0;
         hs = (si >= 0 && si < a.num_rows) ? si : -1;
     }
     if constexpr (CONV) {

@@ -120,6 +120,22 @@ def test_empty_and_single_token_sequences(dev):
     assert torch.equal(pool[7], before[4])
 
 
+@pytest.mark.parametrize("N", [511, 600])
+def test_sequence_table_edge_and_global_search(N, dev):
+    """Kernel 1 stages cu_seqlens and slot_in in LDS for fewer than 512
+    sequences (511 fills the table) and searches cu_seqlens in global memory
+    beyond (600).  Seeded lengths of 0-3 tokens put dozens of pieces in a
+    tile; every other sequence resumes from a pool slot."""
+    rng = np.random.default_rng(3300 + N)
+    lens = [int(x) for x in rng.integers(0, 4, size=N)]
+    si = [n + 1 if n % 2 else -1 for n in range(N)]
+    so = [N + 1 + n for n in range(N)]
+    sh, inp, pool, si, so = prefill_case(lens, 1, 1, 3300 + N, dev, slot_in=si, slot_out=so,
+                                         P=2 * N + 1)
+    print(f"[prefill parity] {N} sequences, T={sum(lens)}", flush=True)
+    check(sh, inp, pool, si, so, what=f"{N} sequences", mode=la.LA_PREFILL_BF16X3)
+
+
 @pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
 def test_strong_decay_diagonal_factorisation(mode, dev):
     """Log decays near -4 per token (16-token spread ~64, inside the
