@@ -436,8 +436,8 @@ template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4 &r, flo
 
 constexpr int kChunkNT = 512;   // threads of the chunk-form verify workgroup
 
-// Floor of a log decay inside the chunk-form running sums.  Both chunk forms
-// use differences G_t - G_j of running sums, which a gate of -inf (a full
+// Floor of a log decay inside the running sums of the chunk forms and the
+// fold.  They use differences G_t - G_j of running sums, which a gate of -inf (a full
 // reset of the state) would turn into -inf - -inf.  exp(-128) is below the
 // smallest fp32 denormal, so a single step's decay is already exactly 0 at the
 // floor: the floor changes no result, while every running sum stays finite.
@@ -1203,10 +1203,10 @@ template <typename IOT, bool KDA, int NT> struct FoldStage {
             if (u < NG) *reinterpret_cast<uint4 *>(&gsh[4 * u / HD][4 * u % HD]) = g[q];
         }
         __syncthreads();
-        if (tid < HD) {
+        if (tid < HD) {  // per channel: running sums (floored gates), decayed keys
             float G = 0.f;
             for (int t = 0; t < nc; ++t) {
-                G += gsh[t][tid];
+                G += fmaxf(gsh[t][tid], kGFloor);
                 gsh[t][tid] = G;
             }
             eend[tid] = fast_exp(G);

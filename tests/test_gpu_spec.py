@@ -186,8 +186,8 @@ def test_chunk_forms_at_extreme_decays(kda, dev):
 def test_chunk_forms_with_a_full_reset(kda, dev):
     """A gate of -inf empties the state at that step (exp(-inf) = 0), so the
     outputs after it depend on the later steps only.  The chunk forms of
-    verify and commit take differences of running gate sums; the reset must
-    not turn those into NaN.  Request 0 resets mid-chunk, request 1 at its
+    verify and commit, and the fold, take differences of running gate sums;
+    the reset must not turn those into NaN.  Request 0 resets mid-chunk, request 1 at its
     first step, request 2 at its last step; for KDA request 0 resets only the
     even key channels."""
     B, D, Hqk, Hv, P = 3, 8, 2, 2, 6
@@ -222,6 +222,19 @@ def test_chunk_forms_with_a_full_reset(kda, dev):
     got = f64(c["ssm_pool"])
     assert np.all(np.isfinite(got))
     assert_close_units(got[slots], p_ref[slots], 2, "fp32", "committed state")
+    # the fast rebuild of the same records, from the checkpoint
+    pool = ssm0.clone()
+    q = synth.to_torch(synth.normal(7701, 0, (B, Hv, D_HEAD)), "fp32", dev)
+    m = [8, 8, 6]
+    ffn = la.kda_ring_fold if kda else la.gdn_ring_fold
+    out = ffn(i32(m, dev), c["slots"], pool, c["ring"], i32(base, dev), q=q)
+    torch.cuda.synchronize()
+    f_ref, fo_ref = oracle.ring_fold(m, slots, slots, f64(ssm0), ring, base, f64(q), kda=kda,
+                                     state_dtype="fp32", io_dtype="fp32", scale=1.0)
+    got = f64(pool)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(f64(out)))
+    assert_close_units(got[slots], f_ref[slots], 2, "fp32", "folded state")
+    assert_close_units(f64(out), fo_ref, 2, "fp32", "fold projection")
 
 
 def test_conv_window_scatter_and_track_copy_are_bit_exact(dev):
