@@ -76,6 +76,25 @@ def test_decode_step_matches_oracle(name, sh, dev):
     check_step(sh, inp, dev)
 
 
+@pytest.mark.parametrize("kda", [True, False], ids=["kda", "gdn"])
+def test_decode_full_reset_gate(kda, dev):
+    """g = -inf empties the state at this step (exp(-inf) = 0): for KDA on
+    every other key channel of request 0 and all channels of request 2, for
+    GDN on the heads of requests 0 and 2."""
+    sh = synth.DecodeShape(B=4, Hqk=2, Hv=2, dk=128, dv=128, P=6, kda=kda, io="fp32",
+                           state="fp32", conv="fp32")
+    inp = synth.decode_inputs(sh, 1190 + kda, dev)
+    g = inp["g"].cpu().clone()
+    if kda:
+        g[0, :, 0::2] = float("-inf")
+    else:
+        g[0] = float("-inf")
+    g[2] = float("-inf")
+    inp["g"] = g.to(dev)
+    out = check_step(sh, inp, dev)
+    assert torch.isfinite(out).all()
+
+
 def test_decode_without_conv(dev):
     sh = synth.DecodeShape(B=4, Hqk=2, Hv=2, dk=128, dv=128, P=5, io="fp32", state="fp32",
                            conv="fp32")
