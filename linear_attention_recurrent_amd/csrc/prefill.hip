@@ -671,70 +671,57 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     // (2,0..2), (1,0..1) for group 1
     auto pairI = [&](int k) { return grp ? (k < 3 ? 2 : 1) : (k < 4 ? 3 : 0); };
     auto pairJ = [&](int k) { return grp ? (k < 3 ? k : k - 3) : (k < 4 ? k : 0); };
-    // masks and beta of the wave's elements, read once: A keeps beta[t] A
-    // where j < t in the same piece (else 0), P keeps j <= t in the same piece
-    // (GDN: also the element's decay exp(G_t - G_j), <= 1 where it is kept)
-    float bA[5][4], eP[5][4];
-    bool kA[5][4], kP[5][4];
-#pragma unroll
-    for (int k = 0; k < 5; ++k)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tt = 16 * pairI(k) + 4 * lq + r, j = 16 * pairJ(k) + li;
-            const bool same = j >= pst[tt] && tt < nt;
-            bA[k][r] = bet[tt];
-            kA[k][r] = same && j < tt;
-            kP[k][r] = same && j <= tt;
-            eP[k][r] = KDA ? 1.f : exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
-        }
     __syncthreads();
-    float *Ps = Qn;  // P [64][LDJ]; q_hat is no longer read
-    for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {  // upper tiles of P are zero
-        const int tt = idx / CB, j = idx % CB;
-        if ((j >> 4) > (tt >> 4)) Ps[tt * LDJ + j] = 0.f;
-    }
-    // quarter q adds its partial sums after quarters 0 .. q-1; the last one
-    // applies beta and the masks
+    float *Ps = Qn;            // P [64][LDJ]; q_hat is no longer read
+    float *Ps2 = Qn + CB * LDJ;  // second half of Q's space: P partial of quarters 2 + 3
+    float *Nm2 = Tm;           // A partial of quarters 2 + 3 (T's lower tiles, rewritten in step 5)
+    // The quarters' partial sums meet in a fixed order, (q0 + q1) + (q2 + q3):
+    // quarters 0 and 2 store theirs, quarters 1 and 3 add theirs in place,
+    // then every thread combines the two halves of its elements.
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (qtr == q) {
-            // every earlier partial is read before anything is written, so
-            // the reads go out together
+    for (int st = 0; st < 2; ++st) {
+        if ((qtr & 1) == st) {
+            float *dA = qtr < 2 ? Nm : Nm2, *dP = qtr < 2 ? Ps : Ps2;
             float prevA[5][4], prevP[5][4];
 #pragma unroll
             for (int k = 0; k < 5; ++k)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
-                    prevA[k][r] = q > 0 ? Nm[at] : 0.f;
-                    prevP[k][r] = q > 0 ? Ps[at] : 0.f;
+                    prevA[k][r] = st ? dA[at] : 0.f;
+                    prevP[k][r] = st ? dP[at] : 0.f;
                 }
 #pragma unroll
-            for (int k = 0; k < 5; ++k) {
-                const int I = pairI(k), J = pairJ(k);
+            for (int k = 0; k < 5; ++k)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int tt = 16 * I + 4 * lq + r, j = 16 * J + li;
-                    float av = pa[k][r], pv = pp[k][r];
-                    if (q > 0) {
-                        av += prevA[k][r];
-                        pv += prevP[k][r];
-                    }
-                    if (q == 3) {
-                        if constexpr (!KDA) {
-                            av *= eP[k][r];
-                            pv *= eP[k][r];
-                        }
-                        av = kA[k][r] ? bA[k][r] * av : 0.f;
-                        pv = kP[k][r] ? pv : 0.f;
-                    }
-                    Nm[tt * LDJ + j] = av;
-                    Ps[tt * LDJ + j] = pv;
+                    const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
+                    dA[at] = st ? prevA[k][r] + pa[k][r] : pa[k][r];
+                    dP[at] = st ? prevP[k][r] + pp[k][r] : pp[k][r];
                 }
-            }
         }
         __syncthreads();
     }
+    // A keeps beta[t] A where j < t in the same piece (else 0), P keeps
+    // j <= t in the same piece (GDN: also the element's decay
+    // exp(G_t - G_j), <= 1 where it is kept); upper tiles of P are zero
+    for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {
+        const int tt = idx / CB, j = idx % CB, at = tt * LDJ + j;
+        if ((j >> 4) > (tt >> 4)) {
+            Ps[at] = 0.f;
+            continue;
+        }
+        float av = Nm[at] + Nm2[at], pv = Ps[at] + Ps2[at];
+        if constexpr (!KDA) {
+            const float e = exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
+            av *= e;
+            pv *= e;
+        }
+        const bool same = j >= pst[tt] && tt < nt;
+        Nm[at] = same && j < tt ? bet[tt] * av : 0.f;
+        Ps[at] = same && j <= tt ? pv : 0.f;
+    }
+    __syncthreads();
 
     // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
     //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
