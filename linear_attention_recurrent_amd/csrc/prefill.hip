@@ -360,8 +360,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     float *Qn = sm;                  // q_hat [64][LDK]; later (beta K Gamma)^T [128][LDJ]
     float *Kn = Qn + kRegion;        // k_hat [64][LDK]; later (beta V)^T [128][LDJ]
     float *Gc = Kn + kRegion;        // cumulative log decay over the tile
-    float *Nm = Gc + kRegion;        // N = Diag(beta) A (strictly lower, masked); earlier K^ T
-    float *Tm = Nm + CB * LDJ;       // T = (I + N)^-1
+    float *Nm = Gc + kRegion;        // N = Diag(beta) A (strictly lower, masked); earlier the
+                                     // sequence table (step 1), then K Gamma_L / Gamma (step 3)
+    float *Tm = Nm + CB * LDJ;       // T = (I + N)^-1; in step 4 also a partial of A
     float *bet = Tm + CB * LDJ;      // beta
     float *qsum = bet + CB;          // [4][128] partial sums of the tile scan
     float *scr = qsum + 4 * DK;      // per-wave 16x17 scratch
