@@ -328,3 +328,39 @@ def test_shortconv_prefill_then_decode_continues_history(dev):
     torch.cuda.synchronize()
     assert torch.equal(y_last[0], y_all[L])
     assert torch.equal(pool[1], pool[2])
+
+
+def test_graph_replay_matches_eager(dev):
+    """Chunked prefill (bf16x3) captured in a HIP graph and replayed several
+    times, each replay continuing the states in place, with eager work and
+    synchronisations between replays: bit-identical to eager calls at every
+    replay."""
+    lens = [40, 100, 7]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3400, dev, slot_in=[1, 2, 3],
+                                         slot_out=[1, 2, 3], P=4)
+    si_t, so_t = torch.from_numpy(si).to(dev), torch.from_numpy(so).to(dev)
+    pool_b = pool.clone()
+    mode = la.LA_PREFILL_BF16X3
+    ws = torch.empty(la.prefill_workspace_bytes(len(lens), sum(lens), 2, 2, D, D, mode),
+                     dtype=torch.uint8, device=dev)
+    out_b = torch.empty((sum(lens), 2, D), dtype=inp["q"].dtype, device=dev)
+
+    def call(p, out=None, workspace=None):
+        return la.kda_prefill_chunked(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                      inp["cu_seqlens"], si_t, so_t, p, mode=mode, out=out,
+                                      workspace=workspace)
+
+    call(pool_b, out_b, ws)   # warm-up outside capture
+    call(pool)                # keep the two pools in step
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(pool_b, out_b, ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        out_a = call(pool)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), rep
+        assert torch.equal(pool, pool_b), rep

@@ -320,3 +320,39 @@ def test_ring_fold_matches_oracle(kda, Hqk, Hv, io, state, L, D, dev):
         exact = oracle.commit(m, slots, f64(ssm0), ring, base, kda=kda, state_dtype="fp64")
         for b in (0, 3):
             assert_close_units(got[dst[b]], exact[slots[b]], 1, "fp32", "fold vs exact commit")
+
+
+def test_graph_replay_verify_commit_matches_eager(dev):
+    """Verify then commit (chunk forms, bf16) captured in one HIP graph and
+    replayed several times, each replay committing onto the state the last
+    one left, with eager work between replays: bit-identical to eager calls
+    at every replay."""
+    B, D, Hqk, Hv, P = 4, 8, 2, 2, 6
+    c = make_case(7800, B, D, Hqk, Hv, 1, "bf16", "bf16", "bf16", P, dev)
+    cb = dict(c, ssm_pool=c["ssm_pool"].clone(), conv_pool=c["conv_pool"].clone(),
+              ring={k: v.clone() for k, v in c["ring"].items()})
+    n_tok, base, acc = i32([D] * B, dev), i32([0, 3, 8, 5], dev), i32([8, 5, 1, 8], dev)
+    outs = {}
+
+    def call(cc, key):
+        outs[key] = la.kda_verify(cc["x"], cc["g"], cc["beta"], cc["slots"], n_tok, cc["ssm_pool"],
+                                  cc["ring"], base, Hqk=Hqk, conv_w=cc["w"],
+                                  conv_pool=cc["conv_pool"], out=outs.get(key))[0]
+        la.kda_commit(acc, cc["slots"], cc["ssm_pool"], cc["ring"], base)
+
+    call(cb, "b")   # warm-up outside capture
+    call(c, "a")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(cb, "b")
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        call(c, "a")
+        torch.cuda.synchronize()
+        assert torch.equal(outs["a"], outs["b"]), rep
+        assert torch.equal(c["ssm_pool"], cb["ssm_pool"]), rep
+        for k in c["ring"]:
+            assert torch.equal(c["ring"][k], cb["ring"][k]), (rep, k)
