@@ -7,10 +7,12 @@
  *     S' = S Diag(alpha),  d = beta (v - S' k),  S = S' + d k^T,  o = scale S q
  * with alpha = exp(g).  KDA has one log-decay g per key channel; GDN has one
  * scalar per value head.  q and k are L2-normalised, x / sqrt(|x|^2 + eps).
- * Gates.  g <= 0 is the decay regime.  The decode, verify, commit and fold
- * calls also take g = -inf, a full reset of those channels at that step.  The
- * chunked prefill is exact while the decay accumulated over any 16
- * consecutive tokens stays above -80 (an average g above -5).
+ * Gates.  Every call takes any g <= 0, including g = -inf: a full reset of
+ * those channels at that token (exp(-inf) = 0).  The chunked prefill forms
+ * the same result as the token-by-token rule over that whole range (no
+ * regime bound): a full reset of every key channel starts a new segment of
+ * its decay bookkeeping, and 16-token blocks whose decay is too strong for
+ * a factorised product form their decay factors element by element.
  * Sources: the decode kernel's steps and the in-place slot update in
  * "SGLang之KV Cache内存池机制" (yuyanqi.com) section 8.5; the state and conv
  * pool layouts in its section 8.2; the per-key-channel alpha of KDA and the

@@ -25,20 +25,33 @@
 //
 // Blocks are the intersections of 64-token tiles of the packed token axis
 // with the sequences ("pieces").  Kernel 1 works per (tile, head) with a
-// same-sequence mask on A and P, so one launch covers every sequence; the
-// cumulative decay G runs continuously over the tile and only differences of
-// G between tokens of one piece enter the results.  Kernel 2 walks a
-// sequence's tiles and treats each piece as the full 64-token tile with the
-// other rows masked to zero, so every access stays tile-aligned.
+// same-sequence mask on A and P, so one launch covers every sequence.  The
+// cumulative decay G is a segmented sum over the tile: it starts again from
+// zero at every piece start, so a piece's decay factors never see another
+// request's gates and their magnitude is that of the piece's own decay.
+// A gate at or below -128 (exp underflows to 0 in fp32; -inf is a reset)
+// empties those state channels at that token.  When every key channel of a
+// token is reset (always so for GDN), the token starts a new "sub-piece":
+// no pair across it interacts, the sum restarts from zero there, the state
+// entering the tile reaches no token from it on, and the piece's decay of
+// that state is zero.  A reset of some channels only is floored at -128 in
+// those channels' sums, which keeps every difference finite and gives the
+// same zero factors across it.  Kernel 2 walks a sequence's
+// tiles and treats each piece as the full 64-token tile with the other rows
+// masked to zero, so every access stays tile-aligned.
 //
-// Overflow-safe factorisation of A and P.  For row sub-block I (tokens
-// 16I..16I+15) the reference R_I = G_{16I-1} (0 for I = 0) splits
-//   exp(G_t - G_j) = exp(G_t - R_I) exp(R_I - G_j)
-// with both factors <= 1 whenever j < 16I <= t, so the off-diagonal 16x16
-// tiles are plain matrix products.  On the diagonal tile the j-side factor is
-// >= 1 and bounded by exp of the decay accumulated over 16 tokens; exponents
-// are clamped at 80 (e^80 ~ 5.5e34), which is exact while that accumulated
-// decay stays below 80 (an average |g| < 5 per token).
+// Factorisation of A and P (KDA).  Row t of 16-token sub-block I takes the
+// reference R_t = G_{16I-1} when its piece began before the sub-block and 0
+// (the piece's own start) otherwise, and
+//   exp(G_t - G_j) = exp(G_t - R_t) exp(R_t - G_j),
+// where G_t - R_t <= 0 is the decay accumulated inside the sub-block.  Off
+// the diagonal (j < 16I <= t, one piece) both factors are <= 1, so those
+// 16x16 tiles are plain matrix products whatever the decay.  On the diagonal
+// the j-side factor is >= 1, bounded by exp of the sub-block's largest
+// in-block decay ("span").  Sub-blocks whose span stays within kSpanMax use
+// the factorised product; the others (strong decay, resets) form
+// exp(G_t - G_j) <= 1 per element instead, which is exact for any g <= 0.
+// GDN has one decay per token and always scales per element.
 //
 // Matrix cores.  Every contraction is an "NT" product C[i][j] =
 // sum_k A[i][k] B[j][k] of 16x16 output tiles with both operands row-major
@@ -69,7 +82,13 @@ constexpr int DK = 128;        // head dim (d_k = d_v)
 constexpr int LDK = DK + 4;    // [* x 128] arrays
 constexpr int LDJ = CB + 4;    // [* x 64] arrays
 constexpr int kRegion = 128 * LDJ > CB * LDK ? 128 * LDJ : CB * LDK;  // one [64 x 128] or [128 x 64] array
+// Largest in-sub-block decay taken by the factorised diagonal product:
+// exp(-64) keeps the t-side factor and the low bf16 part of its split far
+// above the fp32 subnormals.  kExpClamp only keeps factors of masked
+// (cross-piece) pairs finite.
+constexpr float kSpanMax = 64.f;
 constexpr float kExpClamp = 80.f;
+constexpr float kGateFloor = -128.f;  // exp(-128) == 0 in fp32
 enum { PM_F32 = 0, PM_BF16X3 = 1 };
 
 // exp(x) as 2^(x log2 e) with the product carried in two pieces before the
@@ -351,7 +370,12 @@ constexpr int kSeqTab = 512;  // sequences whose cu_seqlens / slot_in kernel 1 s
 static_assert(kSeqTab <= kIntraThreads && 2 * kSeqTab <= CB * LDJ,
               "one table entry per thread, both tables inside N's space");
 constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
-constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + 4 * CB * sizeof(int);
+constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + (5 * CB + 8) * sizeof(int);
+// per-token flags of kernel 1 (sub-pieces)
+enum { TF_OPEN = 1,      // no full reset between the piece start and the token
+       TF_LAST = 2,      // no full reset after the token up to the piece end
+       TF_PRESET = 4,    // the token's piece holds a full reset
+       TF_RESET = 8 };   // the token itself resets every key channel
 
 template <typename IOT, bool KDA, int MODE, bool CONV>
 __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArgs a)
@@ -366,10 +390,13 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     float *bet = Tm + CB * LDJ;      // beta
     float *qsum = bet + CB;          // [4][128] partial sums of the tile scan
     float *scr = qsum + 4 * DK;      // per-wave 16x17 scratch
-    int *pst = reinterpret_cast<int *>(scr + 8 * 16 * 17);  // piece start (tile-local)
+    int *pst = reinterpret_cast<int *>(scr + 8 * 16 * 17);  // piece start, then sub-piece
+                                                              // start (tile-local)
     int *pen = pst + CB;                                      // piece end (inclusive)
     int *sst = pen + CB;             // fused conv: the token's sequence start (global)
     int *ssl = sst + CB;             // fused conv: its history row (-1: zeros)
+    int *bigw = ssl + CB;            // [8] KDA: wave w saw a sub-block span above kSpanMax
+    int *tfl = bigw + 8;             // TF_* flags per token
     float *XtK = Qn, *XtV = Kn;      // transposed right-hand sides of phase 6
     float *KhTl = Nm;                // [128][LDJ] staging of K Gamma_L / Gamma, transposed
 
@@ -470,15 +497,17 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             kv[e] = k4.x; kv[e + 1] = k4.y; kv[e + 2] = k4.z; kv[e + 3] = k4.w;
         }
     }
-    float sq = 0.f, sk = 0.f;
+    float sq = 0.f, sk = 0.f, live = 0.f;  // live: channels not reset
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         if (!valid) { qv[e] = 0.f; kv[e] = 0.f; gv[e] = 0.f; }
         sq = fmaf(qv[e], qv[e], sq);
         sk = fmaf(kv[e], kv[e], sk);
+        live += gv[e] > kGateFloor ? 1.f : 0.f;
     }
     sq = group_sum<8>(sq);
     sk = group_sum<8>(sk);
+    live = group_sum<8>(live);
     const float iq = 1.f / sqrtf(sq + a.eps), ik = 1.f / sqrtf(sk + a.eps);
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
@@ -487,42 +516,85 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         *reinterpret_cast<float4 *>(Kn + t * LDK + c0 + e) =
             make_float4(kv[e] * ik, kv[e + 1] * ik, kv[e + 2] * ik, kv[e + 3] * ik);
         *reinterpret_cast<float4 *>(Gc + t * LDK + c0 + e) =
-            make_float4(gv[e], gv[e + 1], gv[e + 2], gv[e + 3]);
+            make_float4(fmaxf(gv[e], kGateFloor), fmaxf(gv[e + 1], kGateFloor),
+                        fmaxf(gv[e + 2], kGateFloor), fmaxf(gv[e + 3], kGateFloor));
     }
     if (cq == 0) {
         bet[t] = valid ? bt : 0.f;
         pst[t] = ps;
         pen[t] = pe;
+        tfl[t] = TF_OPEN | TF_LAST | (live == 0.f ? TF_RESET : 0);  // final unless a reset
     }
     __syncthreads();
+    // sub-pieces: with a full reset in the tile (rm, the same in every wave),
+    // lane t of wave 0 finds the last reset at or before t and the last one
+    // of its piece, then one more barrier publishes them
+    const uint64_t rm = __ballot(tfl[lane] & TF_RESET);
+    if (rm != 0 && wave == 0) {
+        const bool rs = (rm >> lane) & 1;
+        const int ps_l = pst[lane], pe_l = pen[lane];
+        const uint64_t upto = rm & ((2ull << lane) - 1ull), upto_e = rm & ((2ull << pe_l) - 1ull);
+        const int r = upto ? 63 - __builtin_clzll(upto) : -1;       // last reset <= t
+        const int rl = upto_e ? 63 - __builtin_clzll(upto_e) : -1;  // last reset <= piece end
+        pst[lane] = max(ps_l, r);
+        tfl[lane] = (r < ps_l ? TF_OPEN : 0) | (rl <= lane ? TF_LAST : 0) |
+                    (rl >= ps_l ? TF_PRESET : 0) | (rs ? TF_RESET : 0);
+    }
+    if (rm != 0) __syncthreads();
 
-    // ---- 2. cumulative decay over the tile: 4 quarters of 16 tokens per channel
+    // ---- 2. cumulative decay over the tile, segmented at piece starts: four
+    //         quarters (the 16-token sub-blocks) of 16 tokens per channel.
+    //         run is the sum inside the quarter since its last piece start;
+    //         a quarter's tokens before its first sub-piece start continue the
+    //         previous quarters' running sum.  -min(run) is the largest decay
+    //         inside the sub-block, the span that bounds the factorised
+    //         diagonal product of step 4.
     {
         const int c = tid & (DK - 1), qq = tid >> 7;
+        // wave-uniform bit masks over the tile's tokens: sub-piece starts,
+        // and full resets (those sub-pieces start from zero: the token's own
+        // gate only empties what came before it)
+        const uint64_t sm = __ballot(pst[lane] == lane);
+        const uint32_t smq = (uint32_t)(sm >> (16 * qq)) & 0xFFFFu;
+        const uint32_t rmq = (uint32_t)(rm >> (16 * qq)) & 0xFFFFu;
+        const int first = smq ? __builtin_ctz(smq) : 16;  // first sub-piece start in the quarter
         float run[16];
-        float acc = 0.f;
+        float acc = 0.f, mn = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            acc += Gc[(16 * qq + i) * LDK + c];
+            const float gi = Gc[(16 * qq + i) * LDK + c];
+            acc = ((smq >> i) & 1) ? (((rmq >> i) & 1) ? 0.f : gi) : acc + gi;
             run[i] = acc;
+            mn = fminf(mn, acc);
         }
         qsum[qq * DK + c] = acc;
+        if constexpr (KDA) {
+            const bool big = __ballot(-mn > kSpanMax) != 0;
+            if (lane == 0) bigw[wave] = big;
+        }
         __syncthreads();
+        // carry into the quarter: the running sum of the sub-piece open at
+        // its start (quarter p restarts iff its last sub-piece began inside
+        // it; quarter 0 always does, at the tile start)
         float off = 0.f;
-        for (int p = 0; p < qq; ++p) off += qsum[p * DK + c];
+        for (int p = 0; p < qq; ++p)
+            off = ((sm >> (16 * p)) & 0xFFFFu) ? qsum[p * DK + c] : off + qsum[p * DK + c];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Gc[(16 * qq + i) * LDK + c] = run[i] + off;
+        for (int i = 0; i < 16; ++i)
+            Gc[(16 * qq + i) * LDK + c] = i < first ? run[i] + off : run[i];
     }
     __syncthreads();
     // GDN: one decay per token, so the decay factors of steps 3 and 6 are
     // per-token scalars, exp(G_end - G_t) and exp(G_t - G_start) over the
-    // token's piece, formed once here (qsum is free after step 2)
+    // token's piece (zero across a reset), formed once here (qsum is free
+    // after step 2)
     float *tabE = qsum, *tabS = qsum + CB;
     if constexpr (!KDA) {
         if (tid < CB) {
             const float G = Gc[tid * LDK];
-            tabE[tid] = exp_acc(Gc[pen[tid] * LDK] - G);
-            tabS[tid] = exp_acc(G - (pst[tid] > 0 ? Gc[(pst[tid] - 1) * LDK] : 0.f));
+            const int f = tfl[tid];
+            tabE[tid] = (f & TF_LAST) ? exp_acc(Gc[pen[tid] * LDK] - G) : 0.f;
+            tabS[tid] = (f & TF_OPEN) ? exp_acc(G) : 0.f;
         }
         __syncthreads();
     }
@@ -536,14 +608,14 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll 4
         for (int i = 0; i < 16; ++i) {
             const int tt = tq + i;
-            const int pst_t = pst[tt], pen_t = pen[tt];
+            const int pen_t = pen[tt], f = tfl[tt];
             const float G = Gc[tt * LDK + c];
             const float Ge = Gc[pen_t * LDK + c];
-            KhTl[c * LDJ + tt] = Kn[tt * LDK + c] * (KDA ? exp_acc(Ge - G) : tabE[tt]);
-            if (tt < nt && tt == pen_t) {
-                const float Gs = pst_t > 0 ? Gc[(pst_t - 1) * LDK + c] : 0.f;
-                ws.Ge[row(tt) * DK + c] = Ge - Gs;
-            }
+            KhTl[c * LDJ + tt] =
+                Kn[tt * LDK + c] * (KDA ? ((f & TF_LAST) ? exp_acc(Ge - G) : 0.f) : tabE[tt]);
+            // the piece's decay of the state entering the tile (none left
+            // after a full reset)
+            if (tt < nt && tt == pen_t) ws.Ge[row(tt) * DK + c] = (f & TF_PRESET) ? kGateFloor : Ge;
         }
     }
     if constexpr (MODE == PM_F32) {
@@ -554,10 +626,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             float4 e4;
             if constexpr (KDA) {
                 const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
-                float4 Gs = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (pst[tt] > 0) Gs = *reinterpret_cast<const float4 *>(Gc + (pst[tt] - 1) * LDK + k0);
-                e4 = make_float4(exp_acc(G.x - Gs.x), exp_acc(G.y - Gs.y), exp_acc(G.z - Gs.z),
-                                 exp_acc(G.w - Gs.w));
+                e4 = (tfl[tt] & TF_OPEN)
+                         ? make_float4(exp_acc(G.x), exp_acc(G.y), exp_acc(G.z), exp_acc(G.w))
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
             } else {
                 const float e = tabS[tt];
                 e4 = make_float4(e, e, e, e);
@@ -569,12 +640,12 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
             const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
             const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
-            const float *gs = pst[tt] > 0 ? Gc + (pst[tt] - 1) * LDK + k0 : nullptr;
+            const bool open = tfl[tt] & TF_OPEN;
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 v[e] = Qn[tt * LDK + k0 + e] *
-                       (KDA ? exp_acc(Gc[tt * LDK + k0 + e] - (gs ? gs[e] : 0.f)) : tabS[tt]);
+                       (KDA ? (open ? exp_acc(Gc[tt * LDK + k0 + e]) : 0.f) : tabS[tt]);
             store_split(ws.Qt + bh * kBlkDK + I * 2048, m, ln, v);
         }
     }
@@ -624,7 +695,13 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     f32x4 pa[5], pp[5];
     auto rowblock = [&](int I, int nJ, int k0) {
         const int ti = 16 * I + li;
-        float R[NS][W], fk[NS][W], fq[NS][W];
+        // the row's reference: G_{16I-1} if its piece began before the
+        // sub-block, else 0 (the piece starts inside it)
+        const bool cont = I > 0 && pst[ti] < 16 * I;
+        // sub-block span above kSpanMax: the diagonal pair is formed per element
+        const bool exact_diag =
+            KDA && __builtin_amdgcn_readfirstlane(bigw[2 * I] | bigw[2 * I + 1]);
+        float R[NS][W], fk[NS][W], fq[NS][W], fd[NS][W];
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
@@ -632,12 +709,16 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
                 if constexpr (KDA) {
                     R[st][e] = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
-                    const float et = exp_acc(fminf(Gc[ti * LDK + c] - R[st][e], kExpClamp));
+                    const float x = Gc[ti * LDK + c] - (cont ? R[st][e] : 0.f);  // <= 0
+                    const float et = exp_acc(fminf(x, kExpClamp));
                     fk[st][e] = Kn[ti * LDK + c] * et;
                     fq[st][e] = Qn[ti * LDK + c] * et;
+                    // the diagonal's j-side factor (its column token is this row)
+                    fd[st][e] = Kn[ti * LDK + c] * exp_acc(fminf(-x, kExpClamp));
                 } else {  // GDN: plain k and q rows; the decay is applied per element below
                     fk[st][e] = Kn[ti * LDK + c];
                     fq[st][e] = Qn[ti * LDK + c];
+                    fd[st][e] = fk[st][e];
                 }
             }
 #pragma unroll
@@ -645,17 +726,46 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             if (J >= nJ) break;
             const int tj = 16 * J + li;
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+            if (J == I && exact_diag) {
+                // exp(G_t - G_j) per element, t = 16I + 4 lq + r, j = tj: the
+                // result tile layout of the matrix-core path; pairs of other
+                // pieces or with j > t are masked later and only kept finite
+#pragma unroll 2
+                for (int c = qtr * KQ; c < qtr * KQ + KQ; c += 4) {
+                    const float4 kj = *reinterpret_cast<const float4 *>(Kn + tj * LDK + c);
+                    const float4 gj = *reinterpret_cast<const float4 *>(Gc + tj * LDK + c);
+                    const float kjv[4] = {kj.x, kj.y, kj.z, kj.w}, gjv[4] = {gj.x, gj.y, gj.z, gj.w};
 #pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                float fj[W];
+                    for (int r = 0; r < 4; ++r) {
+                        const int tr = 16 * I + 4 * lq + r;
+                        const float4 kt = *reinterpret_cast<const float4 *>(Kn + tr * LDK + c);
+                        const float4 qt = *reinterpret_cast<const float4 *>(Qn + tr * LDK + c);
+                        const float4 gt = *reinterpret_cast<const float4 *>(Gc + tr * LDK + c);
+                        const float ktv[4] = {kt.x, kt.y, kt.z, kt.w};
+                        const float qtv[4] = {qt.x, qt.y, qt.z, qt.w};
+                        const float gtv[4] = {gt.x, gt.y, gt.z, gt.w};
 #pragma unroll
-                for (int e = 0; e < W; ++e) {
-                    const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
-                    fj[e] = KDA ? Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp))
-                                : Kn[tj * LDK + c];
+                        for (int e = 0; e < 4; ++e) {
+                            const float kd = kjv[e] * exp_acc(fminf(gtv[e] - gjv[e], 0.f));
+                            accA[r] = fmaf(ktv[e], kd, accA[r]);
+                            accP[r] = fmaf(qtv[e], kd, accP[r]);
+                        }
+                    }
                 }
-                mma_step<MODE>(accA, fk[st], fj);
-                mma_step<MODE>(accP, fq[st], fj);
+            } else {
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    float fj[W];
+#pragma unroll
+                    for (int e = 0; e < W; ++e) {
+                        const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
+                        fj[e] = J == I ? fd[st][e]
+                              : KDA ? Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp))
+                                    : Kn[tj * LDK + c];
+                    }
+                    mma_step<MODE>(accA, fk[st], fj);
+                    mma_step<MODE>(accP, fq[st], fj);
+                }
             }
             pa[k0 + J] = accA;
             pp[k0 + J] = accP;
@@ -801,8 +911,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         for (int i = 0; i < 16; ++i) {
             const int tt = tq + i;
             if constexpr (KDA) {
-                const float Gs = pst[tt] > 0 ? Gc[(pst[tt] - 1) * LDK + c] : 0.f;
-                xk[i] = bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c] - Gs);
+                xk[i] = (tfl[tt] & TF_OPEN) ? bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c])
+                                            : 0.f;
             } else {
                 xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
             }

@@ -14,7 +14,7 @@ import torch
 import oracle
 from linear_attention_recurrent_amd import binding as la
 from linear_attention_recurrent_amd import synth
-from parity_util import assert_close_units, f64
+from parity_util import assert_close_seqs, assert_close_units, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -43,12 +43,14 @@ def run_gpu(sh, inp, pool, si, so, **kw):
 
 
 def run_oracle(sh, inp, pool, si, so, heads=None):
-    """Oracle on all heads, or on a subset of value heads (and their q/k heads)."""
+    """Oracle on all heads, or on a subset of value heads.  A sampled value
+    head h takes its q/k head h // (Hv / Hqk) along, so the oracle runs the
+    subset with one q/k head per value head."""
     q, k, v, g, beta = (f64(inp[x]) for x in ("q", "k", "v", "g", "beta"))
     p = f64(pool)
     if heads is not None:
-        assert sh.Hv == sh.Hqk, "head sampling keeps one q/k head per value head"
-        q, k = q[:, heads], k[:, heads]
+        kh = [h // (sh.Hv // sh.Hqk) for h in heads]
+        q, k = q[:, kh], k[:, kh]
         v, g, beta = v[:, heads], g[:, heads], beta[:, heads]
         p = p[:, heads]
     return oracle.prefill(q, k, v, g, beta, inp["cu_seqlens"].cpu().numpy(), si, so, p,
@@ -56,11 +58,6 @@ def run_oracle(sh, inp, pool, si, so, heads=None):
 
 
 MODES = {"fp32": la.LA_PREFILL_FP32, "bf16x3": la.LA_PREFILL_BF16X3}
-
-
-def tol_class(dtype, mode):
-    """Both precision modes are held to the bar of the tensor's storage dtype."""
-    return dtype
 
 
 def check(sh, inp, pool, si, so, heads=None, what="", mode=la.LA_PREFILL_FP32):
@@ -73,8 +70,9 @@ def check(sh, inp, pool, si, so, heads=None, what="", mode=la.LA_PREFILL_FP32):
     if heads is not None:
         o, p = o[:, heads], p[:, heads]
     # outputs per (token, head); states per (slot, head)
-    assert_close_units(o, o_ref, 2, tol_class(sh.io, mode), f"{what} outputs")
-    assert_close_units(p[so], p_ref[so], 2, tol_class(sh.state, mode), f"{what} final states")
+    # both precision modes are held to the bar of the tensor's storage dtype
+    assert_close_seqs(o, o_ref, inp["cu_seqlens"].cpu().numpy(), sh.io, f"{what} outputs")
+    assert_close_units(p[so], p_ref[so], 2, sh.state, f"{what} final states")
     untouched = np.setdiff1d(np.arange(pool.shape[0]), so)
     assert np.array_equal(f64(pool)[untouched], f64(before)[untouched])
     return out
@@ -147,6 +145,91 @@ def test_strong_decay_diagonal_factorisation(mode, dev):
     check(sh, inp, pool, si, so, what="strong decay", mode=MODES[mode])
 
 
+# --------------------------------------------------- the gate's whole range --
+# The decay gate is alpha = exp(g) for any g <= 0; g = -inf empties those
+# state channels at that token ("SGLang之KV Cache内存池机制" section 8.5,
+# h *= exp(g); the ReplaySSM exact-commit passage of xxmr.cn/news/181459).
+# Token positions below: 37 is inside a 16-token sub-block, 64 a tile
+# boundary, 80 a sub-block boundary.
+
+def set_gates(inp, fn):
+    g = f64(inp["g"]).astype(np.float32)
+    fn(g)
+    inp["g"] = torch.from_numpy(g).to(inp["g"].device)
+
+
+def gate_pattern(g, pattern, kda, lens):
+    cu = synth.cu_seqlens(lens)
+    a, b = cu[0], cu[1]          # the first sequence takes the pattern
+    if pattern == "minus30":
+        g[a:b] = -30.0
+    elif pattern == "alternating":  # -30 / 0 per key channel (KDA), per token (GDN)
+        if kda:
+            g[a:b, :, 0::2] = -30.0
+            g[a:b, :, 1::2] = 0.0
+        else:
+            g[a:b:2] = -30.0
+            g[a + 1:b:2] = 0.0
+    elif pattern == "resets":
+        for t in (37, 64, 80):
+            g[a + t] = -np.inf
+        if kda:
+            g[a + 100, :, ::3] = -np.inf  # a reset of some key channels only
+        g[cu[2] + 5] = -np.inf        # and one inside the third sequence
+    else:
+        raise ValueError(pattern)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("kda", [True, False], ids=["kda", "gdn"])
+@pytest.mark.parametrize("pattern", ["minus30", "alternating", "resets"])
+def test_prefill_exact_over_the_gate_range(pattern, kda, mode, dev):
+    """g = -30 per token, -30 / 0 alternating, and -inf resets (mid
+    sub-block, at a tile boundary, at a sub-block boundary, on some channels
+    only) match the oracle in both modes; the mild sequences packed after
+    the first are unaffected."""
+    lens = [150, 40, 70]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3010, dev, kda=kda, io="fp32",
+                                         state="fp32", slot_in=[1, -1, 2], slot_out=[3, 4, 5],
+                                         P=5)
+    set_gates(inp, lambda g: gate_pattern(g, pattern, kda, lens))
+    print(f"[prefill gates] {pattern} kda={kda} mode={mode}", flush=True)
+    check(sh, inp, pool, si, so, what=f"{pattern} kda={kda} {mode}", mode=MODES[mode])
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("kda", [True, False], ids=["kda", "gdn"])
+def test_strong_decay_sequence_packed_beside_a_mild_one(kda, mode, dev):
+    """Sequence A (10 tokens, g = -30, a -inf reset at its token 5) and
+    sequence B (mild gates) share the first tile and its first 16-token
+    sub-block; B, and A too, match the oracle.  A third sequence starts in
+    the same tile after a -inf gate at its first token."""
+    lens = [10, 30, 60, 20]
+    sh, inp, pool, si, so = prefill_case(lens, 1, 1, 3011, dev, kda=kda, io="fp32",
+                                         state="fp32", slot_in=[1, 2, -1, 3],
+                                         slot_out=[4, 5, 6, 7], P=7)
+
+    def pattern(g):
+        g[0:10] = -30.0
+        g[5] = -np.inf
+        g[40] = -np.inf
+    set_gates(inp, pattern)
+    check(sh, inp, pool, si, so, what=f"packed strong/mild kda={kda}", mode=MODES[mode])
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_bf16_io_with_resets(mode, dev):
+    """bf16 I/O with every tenth token a -inf reset of all channels."""
+    lens = [200, 57]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3012, dev, slot_in=[1, -1],
+                                         slot_out=[2, 3], P=3)
+
+    def pattern(g):
+        g[::10] = -np.inf
+    set_gates(inp, pattern)
+    check(sh, inp, pool, si, so, what=f"bf16 resets {mode}", mode=MODES[mode])
+
+
 def test_split_through_slots_equals_one_call(dev):
     """One sequence processed in three scheduler chunks (128 + 100 + 72
     tokens), each chunk's end state handed to the next through a pool slot,
@@ -166,7 +249,7 @@ def test_split_through_slots_equals_one_call(dev):
                             np.array([2], np.int32)))
     torch.cuda.synchronize()
     split = torch.cat(outs)
-    assert_close_units(f64(split), f64(one), 2, "bf16", "split vs one call outputs")
+    assert_close_seqs(f64(split), f64(one), [0, 300], "bf16", "split vs one call outputs")
     assert_close_units(f64(pool2[2]), f64(pool[1]), 1, "fp32", "split vs one call state")
 
 
@@ -240,7 +323,7 @@ def test_sampled_kda_prefill_long_sequence_in_scheduler_chunks(mode, dev):
                             mode=MODES[mode]))
     torch.cuda.synchronize()
     out = f64(torch.cat(outs))[:, heads]
-    assert_close_units(out, o_ref, 2, "bf16", "13600-token outputs (sampled heads)")
+    assert_close_seqs(out, o_ref, [0, 13600], "bf16", "13600-token outputs (sampled heads)")
     assert_close_units(f64(pool[3])[heads], p_ref[1], 1, "fp32", "end state (sampled heads)")
 
 
@@ -258,8 +341,30 @@ def test_sampled_kda_prefill_eight_packed_sequences(mode, dev):
     o_ref, p_ref = run_oracle(sh, inp, pool, si, so, heads)
     out = run_gpu(sh, inp, pool, si, so, mode=MODES[mode])
     torch.cuda.synchronize()
-    assert_close_units(f64(out)[:, heads], o_ref, 2, "bf16", "packed outputs (sampled heads)")
+    assert_close_seqs(f64(out)[:, heads], o_ref, synth.cu_seqlens(sh.seqlens), "bf16",
+                      "packed outputs (sampled heads)")
     assert_close_units(f64(pool)[1:, heads], p_ref[1:], 2, "fp32", "packed end states")
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+def test_sampled_gdn_prefill_gqa_eight_packed_sequences(mode, dev):
+    """GDN prefill at its benchmarked shape: 16 q/k heads shared by 32 value
+    heads, eight 4,096-token sequences packed into one call, bf16 I/O, fp32
+    states.  Value heads 10 and 11 (both reading q/k head 5) and 31 are
+    checked against the oracle."""
+    sh = synth.PrefillShape(seqlens=(4096,) * 8, Hqk=16, Hv=32, dk=D, dv=D, kda=False)
+    inp = synth.prefill_inputs(sh, 1007, dev)
+    pool = torch.zeros((9, 32, D, D), dtype=torch.float32, device=dev)
+    si = np.full(8, -1, np.int32)
+    so = np.arange(1, 9, dtype=np.int32)
+    heads = [10, 11, 31]
+    o_ref, p_ref = run_oracle(sh, inp, pool, si, so, heads)
+    print(f"[prefill parity] gdn 16/32 heads 8x4096 mode={mode}", flush=True)
+    out = run_gpu(sh, inp, pool, si, so, mode=MODES[mode])
+    torch.cuda.synchronize()
+    assert_close_seqs(f64(out)[:, heads], o_ref, synth.cu_seqlens(sh.seqlens), "bf16",
+                      "gdn packed outputs (sampled heads)")
+    assert_close_units(f64(pool)[1:, heads], p_ref[1:], 2, "fp32", "gdn packed end states")
 
 
 # ------------------------------------------------------------ short conv ---
