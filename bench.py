@@ -2,29 +2,34 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
 
-Headline (`value`): KDA decode at the single-layer serving shape -- 64
-requests, 12 heads, d_k = d_v = 128, bf16 state in an 80-slot pool, bf16 conv
-state, per-channel decay.  One step = one fused decode launch (short conv +
-SiLU + L2 norm + gated delta rule) for the 64-request batch.  The 34 MB working
-set would sit in the 256 MB on-die cache, so the K timed steps rotate over R
-independent copies of pools and inputs (>= 1 GB in all), as consecutive layers
-of a model do; the rotation is captured once as a HIP graph and replayed.
-`value` = 64 K / elapsed (tokens/s).  Inputs are resident in HBM before the
-timed region starts.
+Headline (`value`): KDA decode tokens/s on the 69-layer stack -- 128
+requests, 96 heads, d_k = d_v = 128, bf16 state and conv state in per-layer
+pools of 129 rows, per-channel decay.  One step = one fused decode launch
+(short conv + SiLU + L2 norm + gated delta rule) per layer, 69 launches,
+for the 128-request batch: 128 tokens.  The step is captured once as a HIP
+graph; W untimed replays, then exactly K timed replays, each bracketed by
+HIP events on the launch stream.  `value` = 128 K / (elapsed over the K
+replays); the per-step median is reported beside it.  The layer inputs are
+generated once and reused every step while the states evolve; inputs and
+pools (31 GB) are resident in HBM before the timed region starts.
 
-`roofline` is the decode kernel's: algorithmic bytes per launch (every state
-row read and written once, the conv history read and written, x, gates,
-output and weights moved once) over the average launch time from hipEvents on
-the launch stream, against 8 TB/s; `traffic` is the HBM bytes per launch
-measured with rocprofv3 counters (FETCH_SIZE x the copy-calibrated factor,
-plus WRITE_SIZE) when they were taken for the current kernel source.
-`cpu_baseline` is the fp64 C oracle on the same workload, single-threaded.
+`roofline` is the decode kernel's at that shape: algorithmic bytes per
+launch (every state row read and written once, the conv history read and
+written, x, gates, output and weights moved once) over the average launch
+time (step time / 69), against 8 TB/s; `traffic` is the HBM bytes per launch
+measured with rocprofv3 counters (FETCH_SIZE and WRITE_SIZE scaled by a
+plain copy's readings) when they were taken for the current kernel source.
+`cpu_baseline` is the fp64 C oracle on a bounded sample of the same workload
+(see cpu_decode_rate), on every host core and single-threaded.
 
-`extra` holds the other workloads: the 69-layer KDA decode (H=96, 128
-requests), the 48-layer GDN fp32 decode (16 q/k heads shared by 32 value
-heads, 256 requests) and the chunked prefill (one 13,600-token sequence in
-6,144 / 6,144 / 1,312-token scheduler chunks plus eight packed 4,096-token
-sequences, H=12), each with its own roofline line.
+`extra` holds the other workloads, each timed the same way (median of at
+least 20 graph replays) with its own roofline and CPU baseline: the
+single-layer KDA decode (64 requests x 12 heads, pools rotated over >= 1 GiB
+of copies so nothing is served from the on-die cache), the 48-layer GDN fp32
+decode (16 q/k heads shared by 32 value heads, 256 requests), the chunked
+prefill (one 13,600-token sequence in 6,144 / 6,144 / 1,312-token scheduler
+chunks plus eight packed 4,096-token sequences, H = 12; GDN with 16/32
+heads) and the speculative-decode calls.
 """
 from __future__ import annotations
 
@@ -48,6 +53,10 @@ from linear_attention_recurrent_amd import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFS = 157.3
 MFMA_BF16_PEAK_TFS = 2500.0
+# algorithmic matrix work of the chunked prefill per token and value head
+# (blocks of 64: A, P, T RHS, P D at 64^2 d each, (K Gamma) S^T, (Q Gamma) S^T
+# and D^T K at 64 d^2 each; 10.5 MFLOP per 64-token block)
+PREFILL_ALG_FLOPS_PER_TOKEN_HEAD = (8 * 64 * 64 * 128 + 6 * 64 * 128 * 128) / 64
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -112,84 +121,38 @@ def run_decode(sh, inp, out, layer=None):
        Hqk=sh.Hqk, conv_w=pick(inp["w"]), conv_pool=pick(inp["conv_pool"]), out=out)
 
 
-def time_graph(launch_all, n_launch, steps, warmup):
-    """Captures `launch_all` (n_launch kernel launches) as a HIP graph and
-    replays it until >= `steps` launches; returns (ms per launch, launches)."""
+def time_replays(launch_all, n_launch, reps, warmup):
+    """Captures `launch_all` (n_launch kernel launches) as a HIP graph,
+    replays it `warmup` times untimed, then exactly `reps` times, each replay
+    between two HIP events on the current stream (the stream the library
+    launches on).  Returns per-launch times: the mean over the whole timed
+    span (ms_per_launch), the median and extremes over replays."""
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         launch_all()
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // n_launch))
-    for _ in range(max(1, -(-warmup // n_launch))):
+    for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = events()
     stream = torch.cuda.current_stream()
-    e0.record(stream)
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
         graph.replay()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * n_launch), reps * n_launch
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]) / n_launch
+    total = ev[0].elapsed_time(ev[reps])
+    del graph
+    return {"ms_per_launch": total / (reps * n_launch), "median_ms_per_launch": float(np.median(per)),
+            "min_ms_per_launch": float(per.min()), "max_ms_per_launch": float(per.max()),
+            "replays": reps, "launches_per_replay": n_launch, "elapsed_ms": total}
 
 
-def headline(args, dev):
-    sh = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
-    per_copy = (sh.P + 1) * (sh.Hv * sh.dv * sh.dk + 3 * sh.C) * 2
-    n = max(16, -(-(1 << 30) // per_copy))
-    copies = [synth.decode_inputs(sh, 1001 + 7919 * i, dev) for i in range(n)]
-    outs = [torch.empty((sh.B, sh.Hv, sh.dv), dtype=torch.bfloat16, device=dev) for _ in copies]
-    for i in range(n):  # eager warm-up (and eager timing for reference)
-        run_decode(sh, copies[i], outs[i])
-    torch.cuda.synchronize()
-    e0, e1 = events()
-    e0.record()
-    for i in range(4 * n):
-        run_decode(sh, copies[i % n], outs[i % n])
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / (4 * n)
-
-    def launch_all():
-        for i in range(n):
-            run_decode(sh, copies[i], outs[i])
-
-    ms, steps = time_graph(launch_all, n, args.steps, args.warmup)
-    nbytes = decode_bytes(sh)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    traffic = measured_traffic("decode_kda_b64_h12_bf16", source_hash(*DECODE_SOURCES))
-    res = {
-        "metric": "KDA decode tokens/s (single layer, 64 requests, H=12, d=128, bf16 state)",
-        "value": sh.B / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": f"synthetic (seeded SplitMix64/Box-Muller; random pools rotated over {n} copies)",
-        "config": {"workload": "kda_decode_single_layer", "batch": sh.B, "H": sh.Hv,
-                   "d_k": sh.dk, "d_v": sh.dv, "state_dtype": sh.state, "pool_slots": sh.P,
-                   "conv_kernel": 4, "pool_copies_rotated": n},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "decode_kernel<128, bf16 state, bf16 io, bf16 conv, KDA, G=1>",
-                     "algorithmic_bytes_per_launch": nbytes},
-        "eager_ms_per_step": eager_ms,
-        "launch": "HIP graph of one decode launch per pool copy, replayed",
-    }
-    del copies, outs
-    torch.cuda.empty_cache()
-    return sh, res
-
-
-def decode_stack(sh, layers, steps, seed, dev):
+def decode_stack(sh, layers, steps, warmup, seed, dev):
     """`layers` stacked layers, each with its own pools and inputs; one step =
-    one decode launch per layer (captured as one graph).  Returns a dict."""
+    one decode launch per layer (one graph replay).  Returns a dict."""
     L, B, C = layers, sh.B, sh.C
     log(f"decode stack: {L} layers, B={B}, H_qk={sh.Hqk}, H_v={sh.Hv}, {sh.state} state")
     n_ssm = (sh.P + 1) * sh.Hv * sh.dv * sh.dk
@@ -222,22 +185,58 @@ def decode_stack(sh, layers, steps, seed, dev):
         for l in range(L):
             run_decode(sh, inp, outs[l], layer=l)
 
-    ms_launch, launches = time_graph(launch_all, L, steps * L, 2 * L)
-    step_ms = ms_launch * L
-    nbytes = decode_bytes(sh) * L
-    gbs = nbytes / (step_ms * 1e-3) / 1e9
+    t = time_replays(launch_all, L, steps, warmup)
+    step_ms = t["ms_per_launch"] * L
+    nbytes = decode_bytes(sh)
+    gbs = nbytes / (t["ms_per_launch"] * 1e-3) / 1e9
     del inp, ssm, conv, outs
     torch.cuda.empty_cache()
-    return {"tokens_per_s": B / (step_ms * 1e-3), "ms_per_step": step_ms,
-            "steps": launches // L, "layers": L, "batch": B,
+    return {"tokens_per_s": B / (step_ms * 1e-3),
+            "median_tokens_per_s": B / (t["median_ms_per_launch"] * L * 1e-3),
+            "ms_per_step": step_ms, "median_ms_per_step": t["median_ms_per_launch"] * L,
+            "steps": t["replays"], "warmup": warmup, "layers": L, "batch": B,
+            "timing": t,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS,
-                         "algorithmic_bytes_per_step": nbytes}}
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                         "launch_us": t["ms_per_launch"] * 1e3}}
+
+
+def decode_single_layer(sh, reps, dev):
+    """One decode launch per step at a single layer's shape; the 34 MB
+    working set would sit in the on-die cache, so a replay launches the
+    decode once on each of n independent pool + input copies (>= 1 GiB in
+    all), as consecutive layers of a model would."""
+    per_copy = (sh.P + 1) * (sh.Hv * sh.dv * sh.dk + 3 * sh.C) * esize(sh.state)
+    n = max(16, -(-(1 << 30) // per_copy))
+    log(f"single-layer decode: B={sh.B}, H={sh.Hv}, {n} rotated copies")
+    copies = [synth.decode_inputs(sh, 1001 + 7919 * i, dev) for i in range(n)]
+    outs = [torch.empty((sh.B, sh.Hv, sh.dv), dtype=synth.TORCH_DTYPE[sh.io], device=dev)
+            for _ in copies]
+    for i in range(n):
+        run_decode(sh, copies[i], outs[i])
+    torch.cuda.synchronize()
+
+    def launch_all():
+        for i in range(n):
+            run_decode(sh, copies[i], outs[i])
+
+    t = time_replays(launch_all, n, reps, 2)
+    nbytes = decode_bytes(sh)
+    gbs = nbytes / (t["median_ms_per_launch"] * 1e-3) / 1e9
+    traffic = measured_traffic("decode_kda_b64_h12_bf16", source_hash(*DECODE_SOURCES))
+    del copies, outs
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": sh.B / (t["median_ms_per_launch"] * 1e-3),
+            "us_per_launch": t["median_ms_per_launch"] * 1e3, "batch": sh.B, "heads": sh.Hv,
+            "pool_copies_rotated": n, "timing": t,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                         "algorithmic_bytes_per_launch": nbytes}}
 
 
 # ----------------------------------------------------- speculative decode ----
 
-def spec_bench(dev, D=8, L=16, reps=200):
+def spec_bench(dev, D=8, L=16, reps=20):
     """Speculative verify of D draft tokens and the exact commit at the
     single-layer serving shape (64 requests x 12 heads, d=128, bf16 I/O, state,
     conv and ring), plus the tracking copy and the conv-window scatter of the
@@ -302,7 +301,7 @@ def spec_bench(dev, D=8, L=16, reps=200):
     }
     for name, fn in (("verify", verify), ("commit", commit), ("ring_fold", fold),
                      ("conv_window_scatter", scatter), ("state_track_copy", track)):
-        ms, _ = time_graph(lambda: [fn(c) for c in copies], n, reps, n)
+        ms = time_replays(lambda: [fn(c) for c in copies], n, reps, 2)["median_ms_per_launch"]
         gbs = nbytes[name] / (ms * 1e-3) / 1e9
         res[name] = {"us": ms * 1e3, "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -339,7 +338,7 @@ def prefill_mfma_flops(seqlens, Hv, mode=0) -> float:
     return intra + chain_tiles * 8 * Hv * per_chain_tile   # eight 16-row state slices per head
 
 
-def prefill_bench(dev, reps=10):
+def prefill_bench(dev, reps=20, per_graph=10):
     """Chunked KDA prefill, H=12, d=128, bf16 I/O, fp32 state: W1 = one
     13,600-token sequence in 6,144 / 6,144 / 1,312-token calls chained through
     a pool slot; W2 = eight 4,096-token sequences packed in one call.  Each call
@@ -371,7 +370,7 @@ def prefill_bench(dev, reps=10):
                       i32([c + 1]), (b - a,)))
     calls.append((x2, g2, b2, i32(list(range(0, 8 * 4096 + 1, 4096))), i32([-1] * 8),
                   i32(list(range(2, 10))), (4096,) * 8))
-    ws = torch.empty(la.prefill_workspace_bytes(8, 8 * 4096, H, H, D, D), dtype=torch.uint8,
+    ws = torch.empty(la.kda_prefill_workspace_bytes(8, 8 * 4096, H, H, D, D), dtype=torch.uint8,
                      device=dev)
     ys = [torch.empty((cl[0].shape[0], C), dtype=torch.bfloat16, device=dev) for cl in calls]
     outs = [torch.empty((cl[0].shape[0], H, D), dtype=torch.bfloat16, device=dev) for cl in calls]
@@ -403,30 +402,32 @@ def prefill_bench(dev, reps=10):
     for mode in (0, 1):
         run_all(mode)  # every slot a call reads now holds its predecessor's hand-off
         torch.cuda.synchronize()
-        t_conv = [time_graph(lambda i=i: [conv(i) for _ in range(reps)], reps, 4 * reps, reps)[0]
-                  for i in range(4)]
-        t_chunk = [time_graph(lambda i=i: [chunk(i, mode) for _ in range(reps)], reps, 4 * reps,
-                              reps)[0] for i in range(4)]
+        t_conv = [time_replays(lambda i=i: [conv(i) for _ in range(per_graph)], per_graph, reps,
+                               2)["median_ms_per_launch"] for i in range(4)]
+        t_chunk = [time_replays(lambda i=i: [chunk(i, mode) for _ in range(per_graph)], per_graph,
+                                reps, 2)["median_ms_per_launch"] for i in range(4)]
         res_modes[mode] = (t_conv, t_chunk)
     # the conv fused into the prefill's loads (one call per chunk, bf16x3)
-    t_fused = [time_graph(lambda i=i: [fused(i) for _ in range(reps)], reps, 4 * reps, reps)[0]
-               for i in range(4)]
+    t_fused = [time_replays(lambda i=i: [fused(i) for _ in range(per_graph)], per_graph, reps,
+                            2)["median_ms_per_launch"] for i in range(4)]
     # primary: the bf16x3 mode (pre-split bf16 operands, fp32 accumulation;
     # meets 1e-4 on the fp32 end state like the fp32 mode)
     t_conv, t_chunk = res_modes[1]
     w1_ms = sum(t_conv[:3]) + sum(t_chunk[:3])
     w2_ms = t_conv[3] + t_chunk[3]
+    T_all = 13600 + 8 * 4096
+    alg = PREFILL_ALG_FLOPS_PER_TOKEN_HEAD * T_all * H
     flops = sum(prefill_mfma_flops(cl[6], H, 1) for cl in calls)
     chunk_ms = sum(t_chunk)
-    tf = flops / (chunk_ms * 1e-3) / 1e12
+    tf = alg / (chunk_ms * 1e-3) / 1e12
+    tf_issued = flops / (chunk_ms * 1e-3) / 1e12
     conv_bytes = sum(2 * cl[0].numel() * 2 for cl in calls)  # x read + y written, bf16
     conv_gbs = conv_bytes / (sum(t_conv) * 1e-3) / 1e9
     f_conv, f_chunk = res_modes[0]
     f_w1 = sum(f_conv[:3]) + sum(f_chunk[:3])
     f_w2 = f_conv[3] + f_chunk[3]
     f_flops = sum(prefill_mfma_flops(cl[6], H, 0) for cl in calls)
-    f_tf = f_flops / (sum(f_chunk) * 1e-3) / 1e12
-    T_all = 13600 + 8 * 4096
+    f_tf = alg / (sum(f_chunk) * 1e-3) / 1e12
     res = {
         "tokens_per_s": T_all / ((w1_ms + w2_ms) * 1e-3),
         "w1_13600_tokens_per_s": 13600 / (w1_ms * 1e-3),
@@ -437,11 +438,14 @@ def prefill_bench(dev, reps=10):
                 "per 32-deep step, fp32 accumulation)",
         "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFS,
-                     "issued_mfma_flops": flops,
-                     "algorithmic_flops": 164e3 * T_all * H,
-                     "note": "prefill kernels only; issued flops count the three bf16 products "
-                             "of every split step; the chain over 213 dependent blocks of the "
-                             "13,600-token sequence bounds W1"},
+                     "algorithmic_flops": alg,
+                     "issued_mfma_flops": flops, "issued_tflops": tf_issued,
+                     "issued_frac": tf_issued / MFMA_BF16_PEAK_TFS,
+                     "note": "chunked-prefill kernels only (conv separate); achieved = "
+                             "algorithmic flops (164 kFLOP per token-head) / time; issued "
+                             "flops count the three bf16 products of every split step; the "
+                             "chain over 213 dependent blocks of the 13,600-token sequence "
+                             "bounds W1"},
         "conv_roofline": {"bound": "hbm", "achieved": conv_gbs, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS},
         "fp32_mode": {
@@ -451,7 +455,8 @@ def prefill_bench(dev, reps=10):
             "chunked_calls_ms": f_chunk,
             "roofline": {"bound": "mfma", "achieved": f_tf, "peak": MFMA_FP32_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": f_tf / MFMA_FP32_PEAK_TFS,
-                         "issued_mfma_flops": f_flops},
+                         "algorithmic_flops": alg, "issued_mfma_flops": f_flops,
+                         "issued_frac": f_flops / (sum(f_chunk) * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFS},
         },
         "fused_conv": {
             "tokens_per_s": T_all / (sum(t_fused) * 1e-3),
@@ -461,15 +466,15 @@ def prefill_bench(dev, reps=10):
             "speedup_vs_separate_conv": (w1_ms + w2_ms) / sum(t_fused),
             "note": "kda_prefill_conv: the short conv inside the prefill's loads, bf16x3 mode",
         },
-        "timing": "each call replayed from a captured HIP graph; W1 = its three conv and "
-                  "three chunked calls",
+        "timing": f"median over {reps} replays of a captured HIP graph of {per_graph} copies "
+                  "of each call; W1 = its three conv and three chunked calls",
     }
     del x1, x2, g1, g2, b1, b2, ws, ys, outs, calls
     torch.cuda.empty_cache()
     return res
 
 
-def gdn_prefill_bench(dev, reps=10):
+def gdn_prefill_bench(dev, reps=20, per_graph=10):
     """Chunked GDN prefill with the GDN decode configuration's heads (16 q/k
     heads shared by 32 value heads, d=128), bf16 I/O, fp32 state, scalar
     gate: eight 4,096-token sequences packed in one call, fresh states to
@@ -485,7 +490,7 @@ def gdn_prefill_bench(dev, reps=10):
     out = torch.empty((sh.T, Hv, D), dtype=torch.bfloat16, device=dev)
     res = {}
     for mode, name in ((1, "bf16x3"), (0, "fp32")):
-        ws = torch.empty(la.prefill_workspace_bytes(8, sh.T, Hqk, Hv, D, D, mode),
+        ws = torch.empty(la.gdn_prefill_workspace_bytes(8, sh.T, Hqk, Hv, D, D, mode),
                          dtype=torch.uint8, device=dev)
 
         def call():
@@ -495,14 +500,17 @@ def gdn_prefill_bench(dev, reps=10):
 
         call()
         torch.cuda.synchronize()
-        ms = time_graph(lambda: [call() for _ in range(reps)], reps, 4 * reps, reps)[0]
+        ms = time_replays(lambda: [call() for _ in range(per_graph)], per_graph, reps,
+                          2)["median_ms_per_launch"]
         flops = prefill_mfma_flops(sh.seqlens, Hv, mode)
+        alg = PREFILL_ALG_FLOPS_PER_TOKEN_HEAD * sh.T * Hv
         peak = MFMA_BF16_PEAK_TFS if mode else MFMA_FP32_PEAK_TFS
-        tf = flops / (ms * 1e-3) / 1e12
+        tf = alg / (ms * 1e-3) / 1e12
         res[name] = {"tokens_per_s": sh.T / (ms * 1e-3), "ms": ms,
                      "roofline": {"bound": "mfma", "achieved": tf, "peak": peak,
-                                  "unit": "TFLOP/s", "frac": tf / peak,
-                                  "issued_mfma_flops": flops}}
+                                  "unit": "TFLOP/s", "frac": tf / peak, "algorithmic_flops": alg,
+                                  "issued_mfma_flops": flops,
+                                  "issued_frac": flops / (ms * 1e-3) / 1e12 / peak}}
         del ws
     res["workload"] = "gdn_prefill_8x4096_hqk16_hv32"
     del inp, pool, out
@@ -510,46 +518,115 @@ def gdn_prefill_bench(dev, reps=10):
     return res
 
 
-def cpu_prefill_rate(tokens=6144, budget_s=10.0):
-    """The fp64 oracle's prefill of the first `tokens`-token scheduler chunk of
-    the long-sequence workload, all 12 heads, repeated for at least
-    `budget_s` seconds; single-threaded.  Returns (tokens/s, calls, seconds)."""
+def host_threads() -> int:
+    """Worker threads for the all-core CPU baselines: every logical CPU the
+    process may use, capped at 16 (a GPU machine's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _repeat(fn, budget_s):
+    """Runs fn() until budget_s seconds have passed; returns (calls, seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return reps, el
+
+
+def _threaded(fn, threads, budget_s):
+    """fn() repeated for budget_s seconds on each of `threads` threads at once
+    (the oracle's C calls release the interpreter lock); returns (calls,
+    seconds of the slowest thread)."""
+    import threading
+    res = [None] * threads
+
+    def work(i):
+        res[i] = _repeat(fn, budget_s)
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    return sum(r[0] for r in res), max(r[1] for r in res)
+
+
+def cpu_decode_rate(sh, layers, seed, b_sample, budget_s=8.0):
+    """The fp64 C oracle (token by token, as it stands) on a bounded sample of
+    a decode workload: one layer's decode step for b_sample requests x all
+    value heads, with the workload's shapes, dtypes and value distributions,
+    repeated for budget_s seconds single-threaded and then on every host
+    core.  A token of the workload needs that update for all `layers`
+    layers, so tokens/s = requests updated per second / layers (an
+    extrapolation from the sample, labelled as such)."""
+    import oracle
+    sub = synth.DecodeShape(B=b_sample, Hqk=sh.Hqk, Hv=sh.Hv, dk=sh.dk, dv=sh.dv, P=b_sample,
+                            kda=sh.kda, io=sh.io, state=sh.state, conv=sh.conv)
+    inp = synth.decode_inputs(sub, seed, "cpu")
+    f = {k: v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()
+         for k, v in inp.items()}
+
+    def step():
+        oracle.decode(f["x"], f["w"], None, f["conv_pool"], f["g"], f["beta"], f["slots"],
+                      f["ssm_pool"], Hqk=sub.Hqk, Hv=sub.Hv, dk=sub.dk, dv=sub.dv, kda=sub.kda,
+                      conv_dtype=sub.conv, state_dtype=sub.state, io_dtype=sub.io)
+
+    step()  # builds / loads the oracle before any thread starts
+    reps1, el1 = _repeat(step, budget_s)
+    nt = host_threads()
+    repsn, eln = _threaded(step, nt, budget_s)
+    one = b_sample * reps1 / el1 / layers
+    alln = b_sample * repsn / eln / layers
+    what = (f"fp64 C oracle, token by token: one layer's decode step for {b_sample} requests x "
+            f"{sh.Hv} value heads (d={sh.dk}, {sh.state} state), repeated for {budget_s:.0f} s; "
+            f"tokens/s = requests updated per s / {layers} layers (extrapolated from the sample)")
+    return {"value": alln, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"{what}; {repsn} steps on {nt} threads in {eln:.1f} s",
+            "extrapolated": True,
+            "single_thread": {"value": one, "cores": 1, "steps": reps1, "seconds": el1},
+            "host": {"logical_cpus": os.cpu_count(), "machine": platform.machine(),
+                     "processor": platform.processor()}}
+
+
+def cpu_prefill_rate(tokens=6144, budget_s=8.0):
+    """The fp64 C oracle's prefill of the first `tokens`-token scheduler chunk
+    of the long-sequence workload (H=12, d=128), repeated for budget_s
+    seconds: single-threaded over all 12 heads, and on every host core with
+    each thread running one head (tokens/s of the 12-head workload =
+    head-tokens per s / 12)."""
     import oracle
     H, D = 12, 128
     sh = synth.PrefillShape(seqlens=(tokens,), Hqk=H, Hv=H, dk=D, dv=D)
     inp = synth.prefill_inputs(sh, 77, "cpu")
     f = {k: v.to(torch.float64).numpy() for k, v in inp.items() if k != "cu_seqlens"}
     pool = np.zeros((2, H, D, D))
-    reps, t0 = 0, time.perf_counter()
-    while True:
+
+    def all_heads():
         oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], [0, tokens], [-1], [1], pool)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return tokens * reps / el, reps, el
 
+    one_head = {k: np.ascontiguousarray(v[:, :1]) for k, v in f.items()}
+    pool1 = np.zeros((2, 1, D, D))
 
-def cpu_oracle_decode_rate(sh, seed, budget_s=12.0):
-    """The fp64 oracle on the headline workload, repeated for `budget_s`
-    seconds; single-threaded."""
-    import oracle
-    inp = synth.decode_inputs(sh, seed, "cpu")
-    f = {k: v.to(torch.float64).numpy() if v.is_floating_point() else v.numpy()
-         for k, v in inp.items()}
-    rows = np.concatenate([[0], f["slots"]])  # compact pools: the batch's rows only
-    f["conv_pool"], f["ssm_pool"] = f["conv_pool"][rows], f["ssm_pool"][rows]
-    f["slots"] = np.arange(1, sh.B + 1, dtype=np.int32)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode(f["x"], f["w"], None, f["conv_pool"], f["g"], f["beta"], f["slots"],
-                      f["ssm_pool"], Hqk=sh.Hqk, Hv=sh.Hv, dk=sh.dk, dv=sh.dv, kda=sh.kda,
-                      conv_dtype=sh.conv, state_dtype=sh.state, io_dtype=sh.io)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return sh.B * reps / el, reps, el
+    def head():
+        oracle.prefill(one_head["q"], one_head["k"], one_head["v"], one_head["g"],
+                       one_head["beta"], [0, tokens], [-1], [1], pool1)
+
+    head()
+    reps1, el1 = _repeat(all_heads, budget_s)
+    nt = host_threads()
+    repsn, eln = _threaded(head, nt, budget_s)
+    return {"value": tokens * repsn / eln / H, "unit": "tokens/s", "cores": nt, "kind": "oracle",
+            "sample": f"fp64 C oracle, token by token: the first {tokens}-token scheduler chunk "
+                      f"of the 13,600-token sequence; {nt} threads each running one head "
+                      f"({repsn} head-calls in {eln:.1f} s; tokens/s = head-tokens per s / {H})",
+            "single_thread": {"value": tokens * reps1 / el1, "cores": 1, "calls": reps1,
+                              "seconds": el1, "sample": "all 12 heads per call"}}
 
 
 def copy_calibration(dev, nbytes=1 << 30, reps=5):
@@ -595,18 +672,22 @@ def copy_reference(dev, same_size_bytes, big_bytes=2 << 30):
         for a, b in pairs:
             b.copy_(a)
 
-    ms, _ = time_graph(launch_all, len(pairs), 3200, 320)
+    ms = time_replays(launch_all, len(pairs), 20, 2)["median_ms_per_launch"]
     small_gbs = 2 * half / (ms * 1e-3) / 1e9
     del pairs
     torch.cuda.empty_cache()
     return big_gbs, small_gbs, ms
 
 
+BASELINE_METRIC = "KDA decode tokens/s + achieved HBM GB/s (% peak); chunked-prefill tokens/s"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3200)
-    ap.add_argument("--warmup", type=int, default=320)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed decode steps (one step = 69 layer launches, 128 tokens)")
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extra", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -616,6 +697,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -629,41 +713,67 @@ def main():
         print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev),
                           "gdn_prefill_chunked_hqk16_hv32": gdn_prefill_bench(dev)}), flush=True)
         return
-    log(f"headline KDA decode, {args.steps} launches after {args.warmup} warm-up")
-    sh, res = headline(args, dev)
-    big_gbs, small_gbs, small_ms = copy_reference(dev, res["roofline"]["algorithmic_bytes_per_launch"])
+    sh = synth.DecodeShape(B=128, Hqk=96, Hv=96, dk=128, dv=128, P=128)
+    layers = 69
+    log(f"headline: KDA decode, {layers} layers, {args.steps} timed steps after {args.warmup}")
+    st = decode_stack(sh, layers, args.steps, args.warmup, 1002, dev)
+    nbytes = decode_bytes(sh)
+    traffic = measured_traffic("decode_kda_69layers_h96_b128_bf16", source_hash(*DECODE_SOURCES))
+    res = {
+        "metric": BASELINE_METRIC,
+        "value": st["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": st["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": st["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64 / Box-Muller draws; random bf16 pools, "
+                "g = -softplus(randn), beta = sigmoid(randn))",
+        "config": {"workload": "kda_decode_69_layers_h96_b128", "layers": layers,
+                   "batch": sh.B, "H": sh.Hv, "d_k": sh.dk, "d_v": sh.dv,
+                   "state_dtype": sh.state, "conv_dtype": sh.conv, "io_dtype": sh.io,
+                   "pool_rows_per_layer": sh.P + 1, "conv_kernel": 4,
+                   "tokens_per_step": sh.B},
+        "median_tokens_per_s": st["median_tokens_per_s"],
+        "median_ms_per_step": st["median_ms_per_step"],
+        "roofline": dict(st["roofline"], traffic=traffic,
+                         kernel="decode_kernel<128, bf16 state, bf16 io, bf16 conv, KDA, G=1>"),
+        "timing": dict(st["timing"], method="one HIP graph of the 69 layer launches; W untimed "
+                       "replays, then K replays each between HIP events on the launch stream"),
+    }
+    big_gbs, small_gbs, small_ms = copy_reference(dev, nbytes)
     res["roofline"]["copy_reference"] = {
         "copy_4gib_gbs": big_gbs, "frac_of_copy_4gib": res["roofline"]["achieved"] / big_gbs,
         "copy_same_size_gbs": small_gbs, "copy_same_size_ms": small_ms,
         "frac_of_copy_same_size": res["roofline"]["achieved"] / small_gbs,
-        "note": "plain torch device copies on the same box: 2 GiB each way, and the decode "
+        "note": "plain torch device copies on the same box: 2 GiB each way, and one decode "
                 "launch's bytes (half each way) rotated over 16 buffer pairs under graph replay"}
     extra = {}
     if not args.no_extra:
-        extra["kda_decode_69_layers_h96_b128"] = decode_stack(
-            synth.DecodeShape(B=128, Hqk=96, Hv=96, dk=128, dv=128, P=128), 69, 16, 1002, dev)
-        extra["gdn_decode_48_layers_fp32_b256"] = decode_stack(
-            synth.DecodeShape(B=256, Hqk=16, Hv=32, dk=128, dv=128, P=256, kda=False, io="fp32",
-                              state="fp32", conv="fp32"), 48, 16, 1003, dev)
+        s2 = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
+        extra["kda_decode_single_layer_b64_h12"] = decode_single_layer(s2, max(20, args.steps),
+                                                                        dev)
+        s4 = synth.DecodeShape(B=256, Hqk=16, Hv=32, dk=128, dv=128, P=256, kda=False, io="fp32",
+                               state="fp32", conv="fp32")
+        extra["gdn_decode_48_layers_fp32_b256"] = decode_stack(s4, 48, max(20, args.steps), 2,
+                                                               1003, dev)
         log("prefill")
         extra["kda_prefill_chunked_h12"] = prefill_bench(dev)
         extra["gdn_prefill_chunked_hqk16_hv32"] = gdn_prefill_bench(dev)
         extra["kda_speculative_b64_h12_d8"] = spec_bench(dev)
     if not args.no_cpu:
         log("CPU oracle baselines")
-        rate, reps, el = cpu_oracle_decode_rate(sh, 1001)
-        res["cpu_baseline"] = {
-            "value": rate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 C oracle, {reps} full decode steps of the 64-request, 12-head "
-                      f"batch in {el:.1f} s, one thread on {platform.machine()} "
-                      f"(host has {os.cpu_count()} logical CPUs)"}
-        if "kda_prefill_chunked_h12" in extra:
-            prate, preps, pel = cpu_prefill_rate()
-            extra["kda_prefill_chunked_h12"]["cpu_baseline"] = {
-                "value": prate, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"fp64 C oracle, token by token: the first 6,144-token scheduler "
-                          f"chunk of the 13,600-token sequence (12 heads), {preps} calls in "
-                          f"{pel:.1f} s, one thread"}
+        res["cpu_baseline"] = cpu_decode_rate(sh, layers, 1002, b_sample=8)
+        if extra:
+            extra["kda_decode_single_layer_b64_h12"]["cpu_baseline"] = cpu_decode_rate(
+                s2, 1, 1001, b_sample=16)
+            extra["gdn_decode_48_layers_fp32_b256"]["cpu_baseline"] = cpu_decode_rate(
+                s4, 48, 1003, b_sample=8)
+            extra["kda_prefill_chunked_h12"]["cpu_baseline"] = cpu_prefill_rate()
     res["extra"] = extra
     print(json.dumps(res), flush=True)
 

@@ -40,12 +40,15 @@
  *     row is addressed as base + slot * slot_stride (elements), so per-layer
  *     views of a [layers, P+1, ...] tensor work.  Inner dims are contiguous.
  *   - Pools are read and written in place, only at the rows named by the
- *     slots.  Non-zero slots within one call must be distinct (else the
- *     result is undefined).  Slots outside [0, num_rows) are skipped by the
- *     kernels (their outputs are written as zeros and no pool row is
+ *     slots.  Non-zero slots that a call writes must be distinct (else the
+ *     result is undefined).  Prefill calls read slot_in and write slot_out:
+ *     slot_in values may repeat (a row only read) and slot_in[n] ==
+ *     slot_out[n] is allowed, but no sequence may read (slot_in >= 1) a row
+ *     that another sequence writes.  Slots outside [0, num_rows) are skipped
+ *     by the kernels (their outputs are written as zeros and no pool row is
  *     touched); with the environment variable LA_CHECK=1 the call instead
  *     copies the slots to the host, synchronously, and returns LA_ERR_SLOT
- *     for an out-of-range or duplicate non-zero slot.
+ *     for a slot out of range or a breach of these rules.
  *   - Alignment: every pointer must be 16-byte aligned and every row stride
  *     a multiple of 16 bytes (LA_ERR_ARG otherwise).
  *   - A prefill call with no tokens (T == 0) reads none of its per-token
@@ -93,7 +96,9 @@ int la_version(void);
 const char *la_last_error(void);
 
 /* Host call.  Bytes of the conv and SSM state pools for `layers` layers and
- * `slots` usable slots (slots + 1 rows each, row 0 = padding):
+ * `slots` usable slots (slots + 1 rows each, row 0 = padding), the sizes the
+ * allocation logs print (hotelren.com/news/5417338 section 4.2; the ReplaySSM
+ * allocation log of xxmr.cn/news/181459):
  *   ssm  = layers (slots+1) H_v d_v d_k  size(state_dtype)
  *   conv = layers (slots+1) 3 C          size(conv_dtype)
  * (section 8.2 of the pool page gives the [layers, pool_size+1, ...] shapes;
@@ -102,7 +107,24 @@ const char *la_last_error(void);
 int la_pool_bytes(int layers, int slots, int H_v, int d_v, int d_k, int conv_channels,
                   int state_dtype, int conv_dtype, int64_t *ssm_bytes, int64_t *conv_bytes);
 
-/* One decode token of the short conv + SiLU, standalone.
+/* Host call.  Bytes of each buffer of the ReplaySSM ring (la_ring below) for
+ * `layers` layers, `slots` usable slots (slots + 1 rows, as the pools),
+ * H_v value heads and L positions: d_bytes for d and for rawv
+ * ([rows, H_v, L, d_v] in io_dtype), k_bytes for k and for rawk
+ * ([rows, H_v, L, d_k] in io_dtype), g_bytes for g (fp32, [rows, H_v, L,
+ * d_k] with kda != 0, else [rows, H_v, L]) and beta_bytes for beta (fp32,
+ * [rows, H_v, L]).  Source: the ring shapes [69, 120, 12, 16, 128] and the
+ * "ring buffers allocated (L16)" log of the ReplaySSM passage of
+ * xxmr.cn/news/181459.  Any output pointer may be NULL.  Returns LA_OK, or
+ * LA_ERR_ARG for a negative size or unknown dtype. */
+int la_ring_bytes(int layers, int slots, int H_v, int L, int d_k, int d_v, int io_dtype, int kda,
+                  int64_t *d_bytes, int64_t *k_bytes, int64_t *g_bytes, int64_t *beta_bytes);
+
+/* One decode token of the short conv + SiLU, standalone.  Source: the
+ * causal_conv1d_update step of forward_decode in "SGLang之KV Cache内存池机制"
+ * section 8.5 (in place on the conv pool rows named by the cache indices) and
+ * the "Conv state" passage of xxmr.cn/news/181459 (a 3-token history per
+ * request).
  *   x [B, C] (x_dtype) input projections of the current token;
  *   w [C, 4], bias [C] or NULL;
  *   conv_pool rows [3, C] (conv_dtype) at conv_pool + slot * conv_slot_stride;
@@ -117,6 +139,10 @@ int shortconv_update(int B, int C, const void *x, int x_dtype, const float *w,
 /* One KDA decode token per request, fused: short conv + SiLU over x, split
  * into q [H_qk, d_k] | k [H_qk, d_k] | v [H_v, d_v], L2 norm of q and k, then
  * the gated delta rule with a per-key-channel decay, in place on the state.
+ * Source: forward_decode in "SGLang之KV Cache内存池机制" section 8.5 (conv
+ * update, then the recurrence reading and writing the state pool rows in
+ * place: h *= exp(g), the delta correction, h += k v, o = h q) and the "KDA
+ * recurrent update" passage of xxmr.cn/news/181459 (alpha per key channel).
  *   x [B, C] (io_dtype); C = 2 H_qk d_k + H_v d_v.
  *   conv_w [C, 4] or NULL: NULL means x already holds the post-conv q|k|v;
  *     the conv, the SiLU and the conv pool are then skipped (conv_pool may be
@@ -139,7 +165,11 @@ int kda_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, i
                     float scale, void *stream);
 
 /* GDN decode: as kda_decode_step with one log-decay per value head,
- * g [B, H_v] fp32 (the decay Diag(alpha) is alpha I). */
+ * g [B, H_v] fp32 (the decay Diag(alpha) is alpha I).  Source: the "KDA
+ * recurrent update" passage of xxmr.cn/news/181459, which sets KDA's
+ * per-key-channel alpha against the one scalar per head of the other linear
+ * layers, and the forward_decode steps of "SGLang之KV Cache内存池机制"
+ * section 8.5. */
 int gdn_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, int io_dtype,
                     const float *conv_w, const float *conv_b, void *conv_pool,
                     int64_t conv_slot_stride, int conv_dtype, const float *g,
@@ -147,7 +177,10 @@ int gdn_decode_step(int B, int H_qk, int H_v, int d_k, int d_v, const void *x, i
                     int64_t ssm_slot_stride, int state_dtype, void *out, float eps,
                     float scale, void *stream);
 
-/* Short conv + SiLU over N packed sequences (prefill).  Sequence n covers
+/* Short conv + SiLU over N packed sequences (prefill).  Source: the conv of
+ * forward_extend in "SGLang之KV Cache内存池机制" section 8.5 (varlen over
+ * cu_seqlens, history read from and written back to each request's slot).
+ * Sequence n covers
  * tokens [cu_seqlens[n], cu_seqlens[n+1]) of x [T, C] (io_dtype); its history
  * comes from conv-pool row slot_in[n] (zeros when slot_in[n] < 0) and the last
  * three pre-conv inputs (older history shifted in when the sequence is
@@ -162,7 +195,11 @@ int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype,
 
 /* Chunked KDA prefill over N packed sequences (extend: the initial state is
  * read from the pool, the final state written back; the result is that of
- * the token-by-token recurrence, computed by blocks of 64 tokens).
+ * the token-by-token recurrence, computed by blocks of 64 tokens).  Source:
+ * forward_extend in "SGLang之KV Cache内存池机制" section 8.5 (chunk size 64,
+ * inter-chunk recurrence plus intra-chunk parallel work, state read from and
+ * written to the pool by cache index) and the unrolled sum of the ReplaySSM
+ * fast-rebuild passage of xxmr.cn/news/181459 (the block algebra).
  *   q [T, H_qk, d_k], k [T, H_qk, d_k], v [T, H_v, d_v] (io_dtype; raw,
  *     post-conv: q and k are L2-normalised inside) with token strides
  *     q_stride, k_stride, v_stride in elements (>= the row size; lets q|k|v be
@@ -172,7 +209,7 @@ int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype,
  *     ssm_pool [H_v, d_v, d_k] (state_dtype).
  *   out [T, H_v, d_v] (io_dtype).
  *   mode: LA_PREFILL_FP32 or LA_PREFILL_BF16X3.
- *   workspace: device scratch of at least prefill_workspace_bytes(...)
+ *   workspace: device scratch of at least kda_prefill_workspace_bytes(...)
  *     bytes, 256-byte aligned; contents need no initialisation.
  * Supported: d_k == d_v == 128; H_v a multiple of H_qk. */
 int kda_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
@@ -185,7 +222,8 @@ int kda_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const
                         void *stream);
 
 /* GDN prefill: as kda_prefill_chunked with g [T, H_v] (one log-decay per
- * value head). */
+ * value head) and a workspace of gdn_prefill_workspace_bytes(...).  Source:
+ * forward_extend in "SGLang之KV Cache内存池机制" section 8.5. */
 int gdn_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
                         int64_t q_stride, const void *k, int64_t k_stride, const void *v,
                         int64_t v_stride, int io_dtype, const float *g, const float *beta,
@@ -231,9 +269,13 @@ int gdn_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const vo
                      float scale, int mode, void *workspace, size_t workspace_bytes,
                      void *stream);
 
-/* Host call: workspace bytes the prefill needs for N sequences and T tokens
- * (0 for invalid arguments). */
-size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode);
+/* Host calls: workspace bytes kda_prefill_chunked / kda_prefill_conv and
+ * gdn_prefill_chunked / gdn_prefill_conv need for N sequences and T tokens
+ * (0 for invalid arguments).  The workspace holds the per-block quantities
+ * the inter-block chain reads (the intra-chunk part of forward_extend in
+ * "SGLang之KV Cache内存池机制" section 8.5). */
+size_t kda_prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode);
+size_t gdn_prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode);
 
 /* ---- Speculative decode (multi-token verify with an exact commit) --------
  * Sources: the ReplaySSM passages of xxmr.cn/news/181459 (verify computes

@@ -66,7 +66,9 @@ def load_library():
                               P, F, F, I, P, Z, P], I),
         "gdn_prefill_conv": ([I, I, I, I, I, I, P, I, P, P, P, L, I, P, P, P, P, P, I, P, L, I,
                               P, F, F, I, P, Z, P], I),
-        "prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "kda_prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "gdn_prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
+        "la_ring_bytes": ([I, I, I, I, I, I, I, I, P, P, P, P], I),
         "kda_verify": ([I, I, P, I, I, I, I, P, I, P, P, P, L, I, P, P, P, I, P, L, I, P, P,
                         ctypes.POINTER(LaRing), P, F, F, P], I),
         "gdn_verify": ([I, I, P, I, I, I, I, P, I, P, P, P, L, I, P, P, P, I, P, L, I, P, P,
@@ -106,9 +108,49 @@ def _dtype(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
+# ---- argument checks (before any launch: a wrong dtype, length or device
+#      would otherwise make a kernel read past an allocation) ----
+
+F32, I32 = torch.float32, torch.int32
+_FLOATS = (torch.float32, torch.bfloat16)
+
+
+def _arg(t, what, *, dtype=None, shape=None, contig=True):
+    """Checks a tensor argument's dtype (one dtype or a tuple), exact shape
+    and contiguity; returns it."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor, got {type(t).__name__}")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if contig and not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _opt(t, what, **kw):
+    return None if t is None else _arg(t, what, **kw)
+
+
+def _devices(ref: torch.Tensor, **named):
+    """Every named tensor (None skipped) must sit on ref's GPU."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU (got {ref.device})")
+    for what, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{what} is on {t.device}, the pools on {ref.device}")
+
+
 def _row_view(pool: torch.Tensor, inner: tuple, what: str) -> int:
     """Checks a pool [rows, *inner] has contiguous inner dims; returns the row
     stride in elements."""
+    if not isinstance(pool, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if pool.dtype not in _FLOATS:
+        raise ValueError(f"{what}: dtype {pool.dtype}, expected fp32 or bf16")
     if tuple(pool.shape[1:]) != tuple(inner):
         raise ValueError(f"{what}: expected rows of shape {inner}, got {tuple(pool.shape[1:])}")
     if not pool[0].is_contiguous():
@@ -136,38 +178,70 @@ def pool_bytes(layers: int, slots: int, Hv: int, dv: int, dk: int, conv_channels
     return s.value, c.value
 
 
+def ring_bytes(layers: int, slots: int, Hv: int, L: int, dk: int, dv: int,
+               io_dtype: str = "bf16", kda: bool = True) -> dict:
+    """Bytes of each ReplaySSM ring buffer (slots + 1 rows): d, k, rawv, rawk,
+    g, beta."""
+    d, k, g, b = (ctypes.c_int64() for _ in range(4))
+    _check(load_library().la_ring_bytes(layers, slots, Hv, L, dk, dv, _DT_NAME[io_dtype],
+                                        int(kda), ctypes.byref(d), ctypes.byref(k),
+                                        ctypes.byref(g), ctypes.byref(b)))
+    return {"d": d.value, "k": k.value, "rawv": d.value, "rawk": k.value, "g": g.value,
+            "beta": b.value}
+
+
 def shortconv_update(x, w, conv_pool, slots, bias=None, y=None):
     """One decode token of the short conv + SiLU; rolls conv_pool rows in place.
     x [B, C]; w [C, 4] fp32; conv_pool [P+1, 3, C]; slots [B] int32."""
+    _arg(x, "x", dtype=_FLOATS)
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [B, C], got {tuple(x.shape)}")
     B, C = x.shape
-    _contig(x, "x")
-    y = torch.empty_like(x) if y is None else y
     stride = _row_view(conv_pool, (3, C), "conv_pool")
+    _arg(w, "w", dtype=F32, shape=(C, 4))
+    _opt(bias, "bias", dtype=F32, shape=(C,))
+    _arg(slots, "slots", dtype=I32, shape=(B,))
+    _opt(y, "y", dtype=x.dtype, shape=(B, C))
+    _devices(conv_pool, x=x, w=w, bias=bias, slots=slots, y=y)
+    y = torch.empty_like(x) if y is None else y
     _check(load_library().shortconv_update(
-        B, C, _ptr(x), _dtype(x), _ptr(_contig(w, "w")), _ptr(bias), _ptr(conv_pool), stride,
-        _dtype(conv_pool), conv_pool.shape[0], _ptr(_contig(slots, "slots")), _ptr(y),
-        _stream(x.device)))
+        B, C, _ptr(x), _dtype(x), _ptr(w), _ptr(bias), _ptr(conv_pool), stride,
+        _dtype(conv_pool), conv_pool.shape[0], _ptr(slots), _ptr(y), _stream(x.device)))
     return y
 
 
 def _decode(kda, x, g, beta, slots, ssm_pool, *, Hqk, conv_w=None, conv_b=None,
             conv_pool=None, out=None, eps=1e-6, scale=1.0):
+    _arg(x, "x", dtype=_FLOATS)
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [B, C], got {tuple(x.shape)}")
     B, C = x.shape
-    _contig(x, "x")
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
     rows, Hv, dv, dk = ssm_pool.shape
     if C != 2 * Hqk * dk + Hv * dv:
         raise ValueError(f"x has {C} channels, expected 2*Hqk*dk + Hv*dv")
     sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    _arg(g, "g", dtype=F32, shape=(B, Hv, dk) if kda else (B, Hv))
+    _arg(beta, "beta", dtype=F32, shape=(B, Hv))
+    _arg(slots, "slots", dtype=I32, shape=(B,))
+    _opt(out, "out", dtype=x.dtype, shape=(B, Hv, dv))
     cstride, cdt = 0, LA_F32
     if conv_w is not None:
+        if conv_pool is None:
+            raise ValueError("conv_pool is required with conv_w")
         cstride = _row_view(conv_pool, (3, C), "conv_pool")
         cdt = _dtype(conv_pool)
+        _arg(conv_w, "conv_w", dtype=F32, shape=(C, 4))
+        _opt(conv_b, "conv_b", dtype=F32, shape=(C,))
+    _devices(ssm_pool, x=x, g=g, beta=beta, slots=slots, out=out, conv_w=conv_w, conv_b=conv_b,
+             conv_pool=conv_pool)
     out = torch.empty((B, Hv, dv), dtype=x.dtype, device=x.device) if out is None else out
     fn = load_library().kda_decode_step if kda else load_library().gdn_decode_step
     _check(fn(B, Hqk, Hv, dk, dv, _ptr(x), _dtype(x), _ptr(conv_w), _ptr(conv_b),
-              _ptr(conv_pool), cstride, cdt, _ptr(_contig(g, "g")), _ptr(_contig(beta, "beta")),
-              _ptr(_contig(slots, "slots")), rows, _ptr(ssm_pool), sstride, _dtype(ssm_pool),
-              _ptr(_contig(out, "out")), eps, scale, _stream(x.device)))
+              _ptr(conv_pool), cstride, cdt, _ptr(g), _ptr(beta), _ptr(slots), rows,
+              _ptr(ssm_pool), sstride, _dtype(ssm_pool), _ptr(out), eps, scale,
+              _stream(x.device)))
     return out
 
 
@@ -188,55 +262,99 @@ def gdn_decode_step(x, g, beta, slots, ssm_pool, *, Hqk, conv_w=None, conv_b=Non
                    conv_pool=conv_pool, out=out, eps=eps, scale=scale)
 
 
+def _seq_args(cu_seqlens, slot_in, slot_out):
+    """cu_seqlens [N+1], slot_in / slot_out [N], all int32; returns N."""
+    _arg(cu_seqlens, "cu_seqlens", dtype=I32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens: expected [N+1]")
+    N = cu_seqlens.shape[0] - 1
+    _arg(slot_in, "slot_in", dtype=I32, shape=(N,))
+    _arg(slot_out, "slot_out", dtype=I32, shape=(N,))
+    return N
+
+
 def shortconv_prefill(x, cu_seqlens, slot_in, slot_out, w, conv_pool, bias=None, y=None):
     """Short conv + SiLU over packed sequences.  x [T, C]; cu_seqlens [N+1];
     slot_in/slot_out [N] int32; conv_pool [P+1, 3, C].  Returns y [T, C]."""
+    _arg(x, "x", dtype=_FLOATS)
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [T, C], got {tuple(x.shape)}")
     T, C = x.shape
-    _contig(x, "x")
-    N = cu_seqlens.shape[0] - 1
-    y = torch.empty_like(x) if y is None else y
+    N = _seq_args(cu_seqlens, slot_in, slot_out)
     stride = _row_view(conv_pool, (3, C), "conv_pool")
+    _arg(w, "w", dtype=F32, shape=(C, 4))
+    _opt(bias, "bias", dtype=F32, shape=(C,))
+    _opt(y, "y", dtype=x.dtype, shape=(T, C))
+    _devices(conv_pool, x=x, cu_seqlens=cu_seqlens, slot_in=slot_in, slot_out=slot_out, w=w,
+             bias=bias, y=y)
+    y = torch.empty_like(x) if y is None else y
     _check(load_library().shortconv_prefill(
-        N, T, C, _ptr(x), _dtype(x), _ptr(_contig(cu_seqlens, "cu_seqlens")),
-        _ptr(_contig(slot_in, "slot_in")), _ptr(_contig(slot_out, "slot_out")),
-        _ptr(_contig(w, "w")), _ptr(bias), _ptr(conv_pool), stride, _dtype(conv_pool),
-        conv_pool.shape[0], _ptr(y), _stream(x.device)))
+        N, T, C, _ptr(x), _dtype(x), _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), _ptr(w),
+        _ptr(bias), _ptr(conv_pool), stride, _dtype(conv_pool), conv_pool.shape[0], _ptr(y),
+        _stream(x.device)))
     return y
 
 
-def prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode=LA_PREFILL_FP32) -> int:
-    return load_library().prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode)
+def kda_prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode=LA_PREFILL_FP32) -> int:
+    return load_library().kda_prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode)
 
 
-def _token_view(t, heads, d, what):
-    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != d:
-        raise ValueError(f"{what}: expected [T, {heads}, {d}]")
+def gdn_prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode=LA_PREFILL_FP32) -> int:
+    return load_library().gdn_prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode)
+
+
+def prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode=LA_PREFILL_FP32, kda=True) -> int:
+    """Workspace bytes of the KDA (kda=True) or GDN prefill calls."""
+    fn = kda_prefill_workspace_bytes if kda else gdn_prefill_workspace_bytes
+    return fn(N, T, Hqk, Hv, dk, dv, mode)
+
+
+def _token_view(t, T, heads, d, dtype, what):
+    _arg(t, what, dtype=dtype, contig=False)
+    if t.dim() != 3 or tuple(t.shape) != (T, heads, d):
+        raise ValueError(f"{what}: expected [{T}, {heads}, {d}], got {tuple(t.shape)}")
     if t.stride(2) != 1 or t.stride(1) != d:
         raise ValueError(f"{what}: heads and channels must be contiguous inside a token")
     return t.stride(0)
 
 
+def _workspace(workspace, need, dev):
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    _arg(workspace, "workspace")
+    if workspace.device != dev:
+        raise ValueError(f"workspace is on {workspace.device}, the pools on {dev}")
+    return workspace
+
+
 def _prefill(kda, q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, *, out=None,
              eps=1e-6, scale=1.0, mode=LA_PREFILL_FP32, workspace=None):
+    _arg(q, "q", dtype=_FLOATS, contig=False)
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [T, Hqk, dk], got {tuple(q.shape)}")
     T, Hqk, dk = q.shape
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
     rows, Hv, dv, _ = ssm_pool.shape
-    N = cu_seqlens.shape[0] - 1
-    qs = _token_view(q, Hqk, dk, "q")
-    ks = _token_view(k, Hqk, dk, "k")
-    vs = _token_view(v, Hv, dv, "v")
+    N = _seq_args(cu_seqlens, slot_in, slot_out)
+    qs = _token_view(q, T, Hqk, dk, q.dtype, "q")
+    ks = _token_view(k, T, Hqk, dk, q.dtype, "k")
+    vs = _token_view(v, T, Hv, dv, q.dtype, "v")
     sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    _arg(g, "g", dtype=F32, shape=(T, Hv, dk) if kda else (T, Hv))
+    _arg(beta, "beta", dtype=F32, shape=(T, Hv))
+    _opt(out, "out", dtype=q.dtype, shape=(T, Hv, dv))
+    _devices(ssm_pool, q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, slot_in=slot_in,
+             slot_out=slot_out, out=out)
     out = torch.empty((T, Hv, dv), dtype=q.dtype, device=q.device) if out is None else out
-    need = prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode, kda),
+                           ssm_pool.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = load_library().kda_prefill_chunked if kda else load_library().gdn_prefill_chunked
     _check(fn(N, T, Hqk, Hv, dk, dv, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _dtype(q),
-              _ptr(_contig(g, "g")), _ptr(_contig(beta, "beta")),
-              _ptr(_contig(cu_seqlens, "cu_seqlens")), _ptr(_contig(slot_in, "slot_in")),
-              _ptr(_contig(slot_out, "slot_out")), rows, _ptr(ssm_pool), sstride,
-              _dtype(ssm_pool), _ptr(_contig(out, "out")), eps, scale, mode, _ptr(workspace),
-              ws_bytes, _stream(q.device)))
+              _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), rows,
+              _ptr(ssm_pool), sstride, _dtype(ssm_pool), _ptr(out), eps, scale, mode,
+              _ptr(workspace), ws_bytes, _stream(q.device)))
     return out
 
 
@@ -255,27 +373,35 @@ def gdn_prefill_chunked(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_poo
 def _prefill_conv(kda, x, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, *, Hqk, conv_w,
                   conv_pool, conv_b=None, out=None, eps=1e-6, scale=1.0, mode=LA_PREFILL_FP32,
                   workspace=None):
+    _arg(x, "x", dtype=_FLOATS)
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [T, C], got {tuple(x.shape)}")
     T, C = x.shape
-    _contig(x, "x")
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
     rows, Hv, dv, dk = ssm_pool.shape
     if C != 2 * Hqk * dk + Hv * dv:
         raise ValueError(f"x has {C} channels, expected 2*Hqk*dk + Hv*dv")
-    N = cu_seqlens.shape[0] - 1
+    N = _seq_args(cu_seqlens, slot_in, slot_out)
     sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
     cstride = _row_view(conv_pool, (3, C), "conv_pool")
+    _arg(conv_w, "conv_w", dtype=F32, shape=(C, 4))
+    _opt(conv_b, "conv_b", dtype=F32, shape=(C,))
+    _arg(g, "g", dtype=F32, shape=(T, Hv, dk) if kda else (T, Hv))
+    _arg(beta, "beta", dtype=F32, shape=(T, Hv))
+    _opt(out, "out", dtype=x.dtype, shape=(T, Hv, dv))
+    _devices(ssm_pool, x=x, g=g, beta=beta, cu_seqlens=cu_seqlens, slot_in=slot_in,
+             slot_out=slot_out, conv_w=conv_w, conv_b=conv_b, conv_pool=conv_pool, out=out)
     out = torch.empty((T, Hv, dv), dtype=x.dtype, device=x.device) if out is None else out
-    need = prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace(workspace, prefill_workspace_bytes(N, T, Hqk, Hv, dk, dv, mode, kda),
+                           ssm_pool.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = load_library().kda_prefill_conv if kda else load_library().gdn_prefill_conv
-    _check(fn(N, T, Hqk, Hv, dk, dv, _ptr(x), _dtype(x), _ptr(_contig(conv_w, "conv_w")),
-              _ptr(conv_b), _ptr(conv_pool), cstride, _dtype(conv_pool),
-              _ptr(_contig(g, "g")), _ptr(_contig(beta, "beta")),
-              _ptr(_contig(cu_seqlens, "cu_seqlens")), _ptr(_contig(slot_in, "slot_in")),
-              _ptr(_contig(slot_out, "slot_out")), rows, _ptr(ssm_pool), sstride,
-              _dtype(ssm_pool), _ptr(_contig(out, "out")), eps, scale, mode, _ptr(workspace),
-              ws_bytes, _stream(x.device)))
+    _check(fn(N, T, Hqk, Hv, dk, dv, _ptr(x), _dtype(x), _ptr(conv_w), _ptr(conv_b),
+              _ptr(conv_pool), cstride, _dtype(conv_pool), _ptr(g), _ptr(beta),
+              _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), rows, _ptr(ssm_pool), sstride,
+              _dtype(ssm_pool), _ptr(out), eps, scale, mode, _ptr(workspace), ws_bytes,
+              _stream(x.device)))
     return out
 
 
@@ -306,37 +432,62 @@ def new_ring(num_rows, Hv, L, dk, dv, *, kda=True, dtype=torch.bfloat16, device=
             "beta": z(num_rows, Hv, L, dt=torch.float32)}
 
 
-def _ring_struct(ring):
-    for k in ("d", "k", "rawv", "rawk", "g", "beta"):
-        _contig(ring[k], f"ring[{k!r}]")
-    return LaRing(ring["d"].shape[2], ring["d"].data_ptr(), ring["k"].data_ptr(),
-                  ring["rawv"].data_ptr(), ring["rawk"].data_ptr(), ring["g"].data_ptr(),
-                  ring["beta"].data_ptr())
+def _ring_struct(ring, rows, Hv, dk, dv, kda, io_dtype, ref):
+    """Checks the ring's buffers against the pool (rows, heads, dims), the
+    I/O dtype and the device; returns the la_ring struct."""
+    d = _arg(ring["d"], "ring['d']", dtype=io_dtype)
+    if d.dim() != 4:
+        raise ValueError("ring['d']: expected [rows, Hv, L, dv]")
+    L = d.shape[2]
+    _arg(d, "ring['d']", shape=(rows, Hv, L, dv))
+    _arg(ring["rawv"], "ring['rawv']", dtype=io_dtype, shape=(rows, Hv, L, dv))
+    _arg(ring["k"], "ring['k']", dtype=io_dtype, shape=(rows, Hv, L, dk))
+    _arg(ring["rawk"], "ring['rawk']", dtype=io_dtype, shape=(rows, Hv, L, dk))
+    _arg(ring["g"], "ring['g']", dtype=F32, shape=(rows, Hv, L, dk) if kda else (rows, Hv, L))
+    _arg(ring["beta"], "ring['beta']", dtype=F32, shape=(rows, Hv, L))
+    _devices(ref, **{f"ring[{k!r}]": ring[k] for k in ("d", "k", "rawv", "rawk", "g", "beta")})
+    return LaRing(L, ring["d"].data_ptr(), ring["k"].data_ptr(), ring["rawv"].data_ptr(),
+                  ring["rawk"].data_ptr(), ring["g"].data_ptr(), ring["beta"].data_ptr())
 
 
 def _verify(kda, x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, *, Hqk, conv_w=None,
             conv_b=None, conv_pool=None, out=None, windows=None, eps=1e-6, scale=1.0):
+    _arg(x, "x", dtype=_FLOATS)
+    if x.dim() != 3:
+        raise ValueError(f"x: expected [B, D, C], got {tuple(x.shape)}")
     B, D, C = x.shape
-    _contig(x, "x")
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
     rows, Hv, dv, dk = ssm_pool.shape
     if C != 2 * Hqk * dk + Hv * dv:
         raise ValueError(f"x has {C} channels, expected 2*Hqk*dk + Hv*dv")
     sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    _arg(g, "g", dtype=F32, shape=(B, D, Hv, dk) if kda else (B, D, Hv))
+    _arg(beta, "beta", dtype=F32, shape=(B, D, Hv))
+    _arg(slots, "slots", dtype=I32, shape=(B,))
+    _arg(n_tok, "n_tok", dtype=I32, shape=(B,))
+    _arg(ring_base, "ring_base", dtype=I32, shape=(B,))
+    _opt(out, "out", dtype=x.dtype, shape=(B, D, Hv, dv))
     cstride, cdt = 0, LA_F32
     if conv_w is not None:
+        if conv_pool is None:
+            raise ValueError("conv_pool is required with conv_w")
         cstride = _row_view(conv_pool, (3, C), "conv_pool")
         cdt = _dtype(conv_pool)
-        if windows is None:
-            windows = torch.empty((B, D, 3, C), dtype=conv_pool.dtype, device=x.device)
+        _arg(conv_w, "conv_w", dtype=F32, shape=(C, 4))
+        _opt(conv_b, "conv_b", dtype=F32, shape=(C,))
+        _opt(windows, "windows", dtype=conv_pool.dtype, shape=(B, D, 3, C))
+    r = _ring_struct(ring, rows, Hv, dk, dv, kda, x.dtype, ssm_pool)
+    _devices(ssm_pool, x=x, g=g, beta=beta, slots=slots, n_tok=n_tok, ring_base=ring_base,
+             out=out, conv_w=conv_w, conv_b=conv_b, conv_pool=conv_pool, windows=windows)
+    if conv_w is not None and windows is None:
+        windows = torch.empty((B, D, 3, C), dtype=conv_pool.dtype, device=x.device)
     out = torch.empty((B, D, Hv, dv), dtype=x.dtype, device=x.device) if out is None else out
-    r = _ring_struct(ring)
     fn = load_library().kda_verify if kda else load_library().gdn_verify
-    _check(fn(B, D, _ptr(_contig(n_tok, "n_tok")), Hqk, Hv, dk, dv, _ptr(x), _dtype(x),
-              _ptr(conv_w), _ptr(conv_b), _ptr(conv_pool), cstride, cdt, _ptr(_contig(g, "g")),
-              _ptr(_contig(beta, "beta")), _ptr(_contig(slots, "slots")), rows, _ptr(ssm_pool),
-              sstride, _dtype(ssm_pool), _ptr(_contig(out, "out")), _ptr(windows),
-              ctypes.byref(r), _ptr(_contig(ring_base, "ring_base")), eps, scale,
-              _stream(x.device)))
+    _check(fn(B, D, _ptr(n_tok), Hqk, Hv, dk, dv, _ptr(x), _dtype(x), _ptr(conv_w),
+              _ptr(conv_b), _ptr(conv_pool), cstride, cdt, _ptr(g), _ptr(beta), _ptr(slots),
+              rows, _ptr(ssm_pool), sstride, _dtype(ssm_pool), _ptr(out), _ptr(windows),
+              ctypes.byref(r), _ptr(ring_base), eps, scale, _stream(x.device)))
     return out, windows
 
 
@@ -354,13 +505,24 @@ def gdn_verify(x, g, beta, slots, n_tok, ssm_pool, ring, ring_base, **kw):
 
 
 def _commit(kda, accepted, slots, ssm_pool, ring, ring_base, eps=1e-6):
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
     rows, Hv, dv, dk = ssm_pool.shape
     sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
-    r = _ring_struct(ring)
+    _arg(slots, "slots", dtype=I32)
+    if slots.dim() != 1:
+        raise ValueError("slots: expected [B]")
+    B = slots.shape[0]
+    _arg(accepted, "accepted", dtype=I32, shape=(B,))
+    _arg(ring_base, "ring_base", dtype=I32, shape=(B,))
+    io = ring["d"].dtype
+    if io not in _FLOATS:
+        raise ValueError(f"ring['d']: dtype {io}, expected fp32 or bf16")
+    r = _ring_struct(ring, rows, Hv, dk, dv, kda, io, ssm_pool)
+    _devices(ssm_pool, accepted=accepted, slots=slots, ring_base=ring_base)
     fn = load_library().kda_commit if kda else load_library().gdn_commit
-    _check(fn(slots.shape[0], _ptr(_contig(accepted, "accepted")), Hv, dk, dv,
-              _ptr(_contig(slots, "slots")), rows, _ptr(ssm_pool), sstride, _dtype(ssm_pool),
-              _dtype(ring["d"]), ctypes.byref(r), _ptr(_contig(ring_base, "ring_base")), eps,
+    _check(fn(B, _ptr(accepted), Hv, dk, dv, _ptr(slots), rows, _ptr(ssm_pool), sstride,
+              _dtype(ssm_pool), _DT[io], ctypes.byref(r), _ptr(ring_base), eps,
               _stream(ssm_pool.device)))
 
 
@@ -375,48 +537,83 @@ def gdn_commit(accepted, slots, ssm_pool, ring, ring_base, eps=1e-6):
     _commit(False, accepted, slots, ssm_pool, ring, ring_base, eps)
 
 
+def _mask(mask, B):
+    if mask is None:
+        return None
+    if mask.dtype not in (torch.uint8, torch.bool):
+        raise ValueError(f"mask: dtype {mask.dtype}, expected uint8 or bool")
+    return _arg(mask.to(torch.uint8), "mask", shape=(B,))
+
+
 def conv_window_scatter(windows, slots, step, conv_pool, mask=None):
     """conv_pool[slots[b]] = windows[b, step[b]] where mask[b] (uint8 or bool;
     None = all) and 0 <= step[b] < D."""
-    B, D, three, C = windows.shape
+    _arg(windows, "windows", dtype=_FLOATS)
+    if windows.dim() != 4 or windows.shape[2] != 3:
+        raise ValueError(f"windows: expected [B, D, 3, C], got {tuple(windows.shape)}")
+    B, D, _, C = windows.shape
     stride = _row_view(conv_pool, (3, C), "conv_pool")
-    if mask is not None:
-        mask = _contig(mask.to(torch.uint8), "mask")
+    if windows.dtype != conv_pool.dtype:
+        raise ValueError("windows must have the conv pool's dtype")
+    _arg(slots, "slots", dtype=I32, shape=(B,))
+    _arg(step, "step", dtype=I32, shape=(B,))
+    mask = _mask(mask, B)
+    _devices(conv_pool, windows=windows, slots=slots, step=step, mask=mask)
     _check(load_library().conv_window_scatter(
-        B, D, C, _ptr(mask), _ptr(_contig(slots, "slots")), _ptr(_contig(step, "step")),
-        _ptr(_contig(windows, "windows")), _ptr(conv_pool), stride, _dtype(conv_pool),
-        conv_pool.shape[0], _stream(conv_pool.device)))
+        B, D, C, _ptr(mask), _ptr(slots), _ptr(step), _ptr(windows), _ptr(conv_pool), stride,
+        _dtype(conv_pool), conv_pool.shape[0], _stream(conv_pool.device)))
 
 
 def state_track_copy(src, dst, conv_pool, ssm_pool, mask=None):
     """Rows dst[b] of both pools become copies of rows src[b] where mask[b]."""
+    for pool, what in ((conv_pool, "conv_pool"), (ssm_pool, "ssm_pool")):
+        if not isinstance(pool, torch.Tensor) or pool.dtype not in _FLOATS:
+            raise ValueError(f"{what}: expected an fp32 or bf16 tensor")
+        if not pool[0].is_contiguous():
+            raise ValueError("pool rows must be contiguous")
+    if conv_pool.shape[0] != ssm_pool.shape[0]:
+        raise ValueError("conv_pool and ssm_pool must have the same number of rows")
+    _arg(src, "src", dtype=I32)
+    if src.dim() != 1:
+        raise ValueError("src: expected [B]")
+    B = src.shape[0]
+    _arg(dst, "dst", dtype=I32, shape=(B,))
+    mask = _mask(mask, B)
+    _devices(ssm_pool, conv_pool=conv_pool, src=src, dst=dst, mask=mask)
     crow = conv_pool[0].numel()
     srow = ssm_pool[0].numel()
-    if not conv_pool[0].is_contiguous() or not ssm_pool[0].is_contiguous():
-        raise ValueError("pool rows must be contiguous")
-    if mask is not None:
-        mask = _contig(mask.to(torch.uint8), "mask")
     _check(load_library().state_track_copy(
-        src.shape[0], _ptr(mask), _ptr(_contig(src, "src")), _ptr(_contig(dst, "dst")),
-        _ptr(conv_pool), conv_pool.stride(0), crow, _dtype(conv_pool), _ptr(ssm_pool),
-        ssm_pool.stride(0), srow, _dtype(ssm_pool), ssm_pool.shape[0],
-        _stream(ssm_pool.device)))
+        B, _ptr(mask), _ptr(src), _ptr(dst), _ptr(conv_pool), conv_pool.stride(0), crow,
+        _dtype(conv_pool), _ptr(ssm_pool), ssm_pool.stride(0), srow, _dtype(ssm_pool),
+        ssm_pool.shape[0], _stream(ssm_pool.device)))
 
 
 def _fold(kda, m, slots, ssm_pool, ring, ring_base, dst=None, q=None, out=None, eps=1e-6,
           scale=1.0):
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
     rows, Hv, dv, dk = ssm_pool.shape
     sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    _arg(slots, "slots", dtype=I32)
+    if slots.dim() != 1:
+        raise ValueError("slots: expected [B]")
     B = slots.shape[0]
+    _arg(m, "m", dtype=I32, shape=(B,))
+    _arg(ring_base, "ring_base", dtype=I32, shape=(B,))
+    _opt(dst, "dst", dtype=I32, shape=(B,))
+    io = ring["d"].dtype
+    if io not in _FLOATS:
+        raise ValueError(f"ring['d']: dtype {io}, expected fp32 or bf16")
+    _opt(q, "q", dtype=io, shape=(B, Hv, dk))
+    _opt(out, "out", dtype=io, shape=(B, Hv, dv))
+    r = _ring_struct(ring, rows, Hv, dk, dv, kda, io, ssm_pool)
+    _devices(ssm_pool, m=m, slots=slots, ring_base=ring_base, dst=dst, q=q, out=out)
     if q is not None and out is None:
         out = torch.empty((B, Hv, dv), dtype=q.dtype, device=q.device)
-    r = _ring_struct(ring)
     fn = load_library().kda_ring_fold if kda else load_library().gdn_ring_fold
-    _check(fn(B, _ptr(_contig(m, "m")), Hv, dk, dv, _ptr(_contig(slots, "slots")),
-              _ptr(dst if dst is None else _contig(dst, "dst")), rows, _ptr(ssm_pool), sstride,
-              _dtype(ssm_pool), _dtype(ring["d"]), ctypes.byref(r),
-              _ptr(_contig(ring_base, "ring_base")), _ptr(q if q is None else _contig(q, "q")),
-              _ptr(out), eps, scale, _stream(ssm_pool.device)))
+    _check(fn(B, _ptr(m), Hv, dk, dv, _ptr(slots), _ptr(dst), rows, _ptr(ssm_pool), sstride,
+              _dtype(ssm_pool), _DT[io], ctypes.byref(r), _ptr(ring_base), _ptr(q), _ptr(out),
+              eps, scale, _stream(ssm_pool.device)))
     return out
 
 

@@ -3,13 +3,14 @@
 // Host side only: argument validation, the optional checked mode (LA_CHECK=1:
 // slots and sequence offsets copied to the host and verified), dtype / head
 // dim dispatch and error reporting.  Every computation happens in the HIP
-// kernels; nothing here allocates, frees or synchronises outside checked mode.
+// kernels; nothing here allocates, frees or synchronises outside checked mode
+// (the error text lives in a fixed thread-local buffer).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
-#include <string>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -18,22 +19,20 @@
 
 namespace {
 
-thread_local std::string g_err;
+thread_local char g_err[512];
 
 int fail(int code, const char *fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
-    g_err = buf;
     return code;
 }
 
 int ok()
 {
-    g_err.clear();
+    g_err[0] = 0;
     return LA_OK;
 }
 
@@ -80,6 +79,35 @@ int check_slots(const std::vector<int32_t> &s, int num_rows, bool allow_negative
             return fail(LA_ERR_SLOT, "%s[%zu] = %d outside [0, %d)", name, i, v, num_rows);
         if (v != 0 && !seen.insert(v).second)
             return fail(LA_ERR_SLOT, "%s[%zu] = %d repeats a slot of this call", name, i, v);
+    }
+    return LA_OK;
+}
+
+// Prefill slots: slot_out entries in [0, num_rows), non-zero ones distinct;
+// slot_in entries < 0 (fresh) or in [0, num_rows), repeats allowed (a row
+// only read); and no sequence may read (slot_in >= 1) a row that another
+// sequence writes (its slot_out), since the write of one workgroup would race
+// the read of another.  slot_in[n] == slot_out[n] is the in-place default.
+int check_prefill_slots(const std::vector<int32_t> &si, const std::vector<int32_t> &so,
+                        int num_rows)
+{
+    std::unordered_map<int32_t, size_t> writer;
+    for (size_t m = 0; m < so.size(); ++m) {
+        const int32_t v = so[m];
+        if (v < 0 || v >= num_rows)
+            return fail(LA_ERR_SLOT, "slot_out[%zu] = %d outside [0, %d)", m, v, num_rows);
+        if (v != 0 && !writer.emplace(v, m).second)
+            return fail(LA_ERR_SLOT, "slot_out[%zu] = %d repeats a slot of this call", m, v);
+    }
+    for (size_t n = 0; n < si.size(); ++n) {
+        const int32_t v = si[n];
+        if (v >= num_rows)
+            return fail(LA_ERR_SLOT, "slot_in[%zu] = %d outside [0, %d)", n, v, num_rows);
+        if (v < 1) continue;
+        const auto it = writer.find(v);
+        if (it != writer.end() && it->second != n)
+            return fail(LA_ERR_SLOT, "slot_in[%zu] = %d is slot_out[%zu] of another sequence", n,
+                        v, it->second);
     }
     return LA_OK;
 }
@@ -215,8 +243,7 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
         if (int rc = check_cu(cu, T)) return rc;
         if (int rc = fetch_i32(slot_in, N, si, st)) return rc;
         if (int rc = fetch_i32(slot_out, N, so, st)) return rc;
-        if (int rc = check_slots(si, num_rows, true, "slot_in")) return rc;
-        if (int rc = check_slots(so, num_rows, false, "slot_out")) return rc;
+        if (int rc = check_prefill_slots(si, so, num_rows)) return rc;
     }
     la::PrefillArgs a{};
     a.N = N; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.G = Hv / Hqk; a.D = dk;
@@ -391,7 +418,7 @@ extern "C" {
 
 int la_version(void) { return LA_VERSION; }
 
-const char *la_last_error(void) { return g_err.c_str(); }
+const char *la_last_error(void) { return g_err; }
 
 int la_pool_bytes(int layers, int slots, int H_v, int d_v, int d_k, int conv_channels,
                   int state_dtype, int conv_dtype, int64_t *ssm_bytes, int64_t *conv_bytes)
@@ -461,8 +488,7 @@ int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype, const in
         if (int rc = check_cu(cu, T)) return rc;
         if (int rc = fetch_i32(slot_in, N, si, st)) return rc;
         if (int rc = fetch_i32(slot_out, N, so, st)) return rc;
-        if (int rc = check_slots(si, num_rows, true, "slot_in")) return rc;
-        if (int rc = check_slots(so, num_rows, false, "slot_out")) return rc;
+        if (int rc = check_prefill_slots(si, so, num_rows)) return rc;
     }
     la::ConvPrefillArgs a{};
     a.N = N; a.T = T; a.C = C; a.x = x; a.io_dtype = io_dtype;
@@ -556,10 +582,36 @@ int gdn_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const vo
                           workspace_bytes, stream, &cv);
 }
 
-size_t prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)
+static size_t prefill_ws(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)
 {
     if (N < 0 || T < 0 || H_qk <= 0 || H_v <= 0 || H_v % H_qk || d_k != d_v) return 0;
+    if (mode != LA_PREFILL_FP32 && mode != LA_PREFILL_BF16X3) return 0;
     return la::prefill_ws_bytes(N, T, H_qk, H_v, d_k, mode);
+}
+
+size_t kda_prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)
+{
+    return prefill_ws(N, T, H_qk, H_v, d_k, d_v, mode);
+}
+
+size_t gdn_prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)
+{
+    return prefill_ws(N, T, H_qk, H_v, d_k, d_v, mode);
+}
+
+int la_ring_bytes(int layers, int slots, int H_v, int L, int d_k, int d_v, int io_dtype, int kda,
+                  int64_t *d_bytes, int64_t *k_bytes, int64_t *g_bytes, int64_t *beta_bytes)
+{
+    if (layers < 0 || slots < 0 || H_v < 0 || L < 0 || d_k < 0 || d_v < 0)
+        return fail(LA_ERR_ARG, "la_ring_bytes: negative size");
+    if (!valid_dtype(io_dtype))
+        return fail(LA_ERR_ARG, "la_ring_bytes: io_dtype must be LA_F32 or LA_BF16");
+    const int64_t steps = (int64_t)layers * (slots + 1) * H_v * L;  // records per buffer
+    if (d_bytes) *d_bytes = steps * d_v * dsize(io_dtype);
+    if (k_bytes) *k_bytes = steps * d_k * dsize(io_dtype);
+    if (g_bytes) *g_bytes = steps * (kda ? d_k : 1) * (int64_t)sizeof(float);
+    if (beta_bytes) *beta_bytes = steps * (int64_t)sizeof(float);
+    return ok();
 }
 
 

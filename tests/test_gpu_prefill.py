@@ -289,6 +289,24 @@ def test_strided_qkv_views_of_conv_output(dev):
     assert torch.equal(pool, pool2)
 
 
+def test_checked_mode_prefill_slot_rule(dev, monkeypatch):
+    """LA_CHECK=1: a sequence may not read a row another sequence writes
+    (their workgroups would race); repeated slot_in values (rows only read)
+    and slot_in == slot_out of the same sequence are allowed and match the
+    oracle."""
+    monkeypatch.setenv("LA_CHECK", "1")
+    sh, inp, pool, si, so = prefill_case([30, 50, 20], 1, 1, 3013, dev, slot_in=[1, 4, 1],
+                                         slot_out=[2, 3, 1], P=5)
+    # sequence 0 reads row 1, which sequence 2 writes (and 1 reads row 2 of 0)
+    with pytest.raises(la.LAError, match="slot_out"):
+        run_gpu(sh, inp, pool, np.array([1, 2, 5], np.int32), so)
+    with pytest.raises(la.LAError, match="repeats"):
+        run_gpu(sh, inp, pool, si, np.array([2, 3, 2], np.int32))
+    # sequences 0 and 1 both read row 4; sequence 2 updates row 1 in place
+    check(sh, inp, pool, np.array([4, 4, 1], np.int32), np.array([2, 3, 1], np.int32),
+          what="checked slots")
+
+
 def test_workspace_too_small_is_rejected(dev):
     sh, inp, pool, si, so = prefill_case([64], 1, 1, 3008, dev, P=2)
     with pytest.raises(la.LAError, match="workspace"):

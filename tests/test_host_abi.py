@@ -6,12 +6,14 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 from linear_attention_recurrent_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden", "pool_bytes.json")
+RING_GOLDEN = os.path.join(ROOT, "tests", "golden", "ring_bytes.json")
 HEADER = os.path.join(ROOT, "include", "la.h")
 
 
@@ -50,6 +52,29 @@ def test_pool_bytes_reproduce_printed_figures(lib):
         ssm, conv = binding.pool_bytes(L, case["slots"], H, d, d, C, case["state"], case["conv"])
         assert round(ssm / 2**30, 2) == case["ssm_gib"], case
         assert round(conv / 2**30, 2) == case["conv_gib"], case
+
+
+def test_ring_bytes_reproduce_printed_figures(lib):
+    """The ReplaySSM ring sizes of the pages' allocation log (L = 16, 119
+    slots + 1 rows, 69 layers, 12 heads, head dim 128)."""
+    gold = json.load(open(RING_GOLDEN))
+    got = binding.ring_bytes(gold["layers"], gold["slots"], gold["H_v"], gold["L"], gold["d"],
+                             gold["d"], gold["io_dtype"], gold["kda"])
+    for name, shape in gold["shapes"].items():
+        elem = 2 if name in ("d", "k", "rawv", "rawk") else 4
+        assert got[name] == int(np.prod(shape)) * elem, name
+        assert round(got[name] / 2**30, 3) == gold["gib"][name], name
+    # GDN keeps one gate per head and step
+    gdn = binding.ring_bytes(gold["layers"], gold["slots"], gold["H_v"], gold["L"], gold["d"],
+                             gold["d"], "bf16", False)
+    assert gdn["g"] == got["beta"] and gdn["d"] == got["d"]
+
+
+def test_ring_bytes_rejects_bad_args(lib):
+    out = ctypes.c_int64()
+    assert lib.la_ring_bytes(1, -1, 1, 16, 128, 128, 1, 1, ctypes.byref(out), None, None,
+                             None) == -1
+    assert lib.la_ring_bytes(1, 1, 1, 16, 128, 128, 5, 1, None, None, None, None) == -1
 
 
 def test_pool_bytes_rejects_bad_args(lib):
@@ -94,7 +119,7 @@ def test_prefill_validation(lib):
     T, H, d = 100, 12, 128
     args = [1, T, H, H, d, d, fake, H * d, fake, H * d, fake, H * d, 1, fake, fake, fake, fake,
             fake, 5, fake, H * d * d, 0, fake, 1e-6, 1.0, 0, None, 0, None]
-    need = lib.prefill_workspace_bytes(1, T, H, H, d, d, 0)
+    need = lib.kda_prefill_workspace_bytes(1, T, H, H, d, d, 0)
     if need:
         assert lib.kda_prefill_chunked(*args) == -3       # workspace missing
         assert b"workspace" in lib.la_last_error()
@@ -120,7 +145,7 @@ def test_prefill_conv_validation(lib, fn):
     f = getattr(lib, fn)
     args = [1, T, H, H, d, d, fake, 1, fake, None, fake, 3 * C, 1, fake, fake, fake, fake, fake,
             5, fake, H * d * d, 0, fake, 1e-6, 1.0, 1, None, 0, None]
-    if lib.prefill_workspace_bytes(1, T, H, H, d, d, 1):
+    if lib.kda_prefill_workspace_bytes(1, T, H, H, d, d, 1):
         assert f(*args) == -3                             # workspace missing
     bad = list(args)
     bad[10] = None                                        # no conv pool
