@@ -269,6 +269,26 @@ int gdn_prefill_conv(int N, int T, int H_qk, int H_v, int d_k, int d_v, const vo
                      float scale, int mode, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/* kda_prefill_chunked without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a 128 MiB device
+ * array inside the library, one per GPU, held from this call's first use on
+ * that GPU until the process ends; its address is looked up once per device
+ * (the current device must be the stream's).  Arguments, layouts and results
+ * are those of kda_prefill_chunked.  The call allocates and frees nothing;
+ * LA_CHECK=1 does not apply to it (its host copies would allocate).
+ * Returns LA_ERR_WORKSPACE when kda_prefill_workspace_bytes(...) exceeds
+ * 128 MiB (about 47,000 token x value-head pairs; 3,900 tokens at 12
+ * heads).  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised. */
+int kda_prefill_chunked_noalloc(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
+                                int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                                int64_t v_stride, int io_dtype, const float *g,
+                                const float *beta, const int32_t *cu_seqlens,
+                                const int32_t *slot_in, const int32_t *slot_out, int num_rows,
+                                void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+                                void *out, float eps, float scale, int mode, void *stream);
+
 /* Host calls: workspace bytes kda_prefill_chunked / kda_prefill_conv and
  * gdn_prefill_chunked / gdn_prefill_conv need for N sequences and T tokens
  * (0 for invalid arguments).  The workspace holds the per-block quantities

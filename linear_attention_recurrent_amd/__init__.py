@@ -12,7 +12,7 @@ from __future__ import annotations
 
 _BINDING_NAMES = {
     "kda_decode_step", "gdn_decode_step", "shortconv_update", "shortconv_prefill",
-    "kda_prefill_chunked", "gdn_prefill_chunked", "kda_prefill_conv", "gdn_prefill_conv",
+    "kda_prefill_chunked", "kda_prefill_chunked_noalloc", "gdn_prefill_chunked", "kda_prefill_conv", "gdn_prefill_conv",
     "prefill_workspace_bytes", "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
     "pool_bytes", "ring_bytes", "version", "LAError", "load_library", "library_path",
     "kda_verify", "gdn_verify", "kda_commit", "gdn_commit", "conv_window_scatter",

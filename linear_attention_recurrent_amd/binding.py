@@ -66,6 +66,8 @@ def load_library():
                               P, F, F, I, P, Z, P], I),
         "gdn_prefill_conv": ([I, I, I, I, I, I, P, I, P, P, P, L, I, P, P, P, P, P, I, P, L, I,
                               P, F, F, I, P, Z, P], I),
+        "kda_prefill_chunked_noalloc": ([I, I, I, I, I, I, P, L, P, L, P, L, I, P, P, P, P, P, I,
+                                         P, L, I, P, F, F, I, P], I),
         "kda_prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
         "gdn_prefill_workspace_bytes": ([I, I, I, I, I, I, I], Z),
         "la_ring_bytes": ([I, I, I, I, I, I, I, I, P, P, P, P], I),
@@ -355,6 +357,35 @@ def _prefill(kda, q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, *, 
               _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), rows,
               _ptr(ssm_pool), sstride, _dtype(ssm_pool), _ptr(out), eps, scale, mode,
               _ptr(workspace), ws_bytes, _stream(q.device)))
+    return out
+
+
+def kda_prefill_chunked_noalloc(q, k, v, g, beta, cu_seqlens, slot_in, slot_out, ssm_pool, *,
+                                out, eps=1e-6, scale=1.0, mode=LA_PREFILL_FP32):
+    """kda_prefill_chunked with the library's own 128 MiB per-GPU scratch in
+    place of a workspace: the call allocates nothing (``out`` [T, Hv, dv] is
+    the caller's).  Calls that overlap on one GPU race."""
+    _arg(q, "q", dtype=_FLOATS, contig=False)
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [T, Hqk, dk], got {tuple(q.shape)}")
+    T, Hqk, dk = q.shape
+    if ssm_pool.dim() != 4:
+        raise ValueError("ssm_pool: expected [P+1, Hv, dv, dk]")
+    rows, Hv, dv, _ = ssm_pool.shape
+    N = _seq_args(cu_seqlens, slot_in, slot_out)
+    qs = _token_view(q, T, Hqk, dk, q.dtype, "q")
+    ks = _token_view(k, T, Hqk, dk, q.dtype, "k")
+    vs = _token_view(v, T, Hv, dv, q.dtype, "v")
+    sstride = _row_view(ssm_pool, (Hv, dv, dk), "ssm_pool")
+    _arg(g, "g", dtype=F32, shape=(T, Hv, dk))
+    _arg(beta, "beta", dtype=F32, shape=(T, Hv))
+    _arg(out, "out", dtype=q.dtype, shape=(T, Hv, dv))
+    _devices(ssm_pool, q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, slot_in=slot_in,
+             slot_out=slot_out, out=out)
+    _check(load_library().kda_prefill_chunked_noalloc(
+        N, T, Hqk, Hv, dk, dv, _ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _dtype(q), _ptr(g),
+        _ptr(beta), _ptr(cu_seqlens), _ptr(slot_in), _ptr(slot_out), rows, _ptr(ssm_pool),
+        sstride, _dtype(ssm_pool), _ptr(out), eps, scale, mode, _stream(q.device)))
     return out
 
 

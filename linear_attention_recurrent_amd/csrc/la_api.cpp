@@ -4,9 +4,11 @@
 // slots and sequence offsets copied to the host and verified), dtype / head
 // dim dispatch and error reporting.  Every computation happens in the HIP
 // kernels; nothing here allocates, frees or synchronises outside checked mode
-// (the error text lives in a fixed thread-local buffer).
+// (the error text lives in a fixed thread-local buffer).  The one device
+// object defined here is the scratch array of kda_prefill_chunked_noalloc.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -184,7 +186,8 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
                    const int32_t *cu_seqlens, const int32_t *slot_in, const int32_t *slot_out,
                    int num_rows, void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
                    void *out, float eps, float scale, int mode, void *workspace,
-                   size_t workspace_bytes, void *stream, const ConvIn *cv = nullptr)
+                   size_t workspace_bytes, void *stream, const ConvIn *cv = nullptr,
+                   bool may_check = true)
 {
     const char *fn = cv ? (kda ? "kda_prefill_conv" : "gdn_prefill_conv")
                         : (kda ? "kda_prefill_chunked" : "gdn_prefill_chunked");
@@ -237,7 +240,7 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
         return fail(LA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)",
                     fn, need, workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (checked_mode()) {
+    if (may_check && checked_mode()) {
         std::vector<int32_t> cu, si, so;
         if (int rc = fetch_i32(cu_seqlens, N + 1, cu, st)) return rc;
         if (int rc = check_cu(cu, T)) return rc;
@@ -410,6 +413,43 @@ int fold_common(bool kda, int B, const int32_t *m, int Hv, int dk, int dv, const
     a.ring = ring_args(ring); a.ring_base = ring_base; a.q = q; a.out = out; a.eps = eps;
     a.scale = scale;
     return hip_status(la::launch_fold(a, state_dtype, kda, st), fn);
+}
+
+// ---- scratch of kda_prefill_chunked_noalloc --------------------------------
+// A file-scope device array stands in for the caller's workspace.  Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the address comes from hipGetSymbolAddress, once
+// per device with that device current, and is kept per device -- each GPU
+// holds its own copy of the array.
+constexpr size_t kScratchBytes = size_t(128) << 20;  // 128 MiB per GPU
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, or nullptr (after fail()).
+void *scratch_address(const char *fn)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        hip_status(e, fn);
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        fail(LA_ERR_HIP, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+        return nullptr;
+    }
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(LA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                 hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
 }
 
 }  // namespace
@@ -587,6 +627,32 @@ static size_t prefill_ws(int N, int T, int H_qk, int H_v, int d_k, int d_v, int 
     if (N < 0 || T < 0 || H_qk <= 0 || H_v <= 0 || H_v % H_qk || d_k != d_v) return 0;
     if (mode != LA_PREFILL_FP32 && mode != LA_PREFILL_BF16X3) return 0;
     return la::prefill_ws_bytes(N, T, H_qk, H_v, d_k, mode);
+}
+
+int kda_prefill_chunked_noalloc(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
+                                int64_t q_stride, const void *k, int64_t k_stride, const void *v,
+                                int64_t v_stride, int io_dtype, const float *g,
+                                const float *beta, const int32_t *cu_seqlens,
+                                const int32_t *slot_in, const int32_t *slot_out, int num_rows,
+                                void *ssm_pool, int64_t ssm_slot_stride, int state_dtype,
+                                void *out, float eps, float scale, int mode, void *stream)
+{
+    const char *fn = "kda_prefill_chunked_noalloc";
+    const size_t need = prefill_ws(N, T, H_qk, H_v, d_k, d_v, mode);
+    if (need > kScratchBytes)
+        return fail(LA_ERR_WORKSPACE,
+                    "%s: %d tokens x %d value heads need %zu bytes of scratch; this call holds "
+                    "%zu (128 MiB) per GPU -- use kda_prefill_chunked with a workspace",
+                    fn, T, H_v, need, kScratchBytes);
+    void *ws = nullptr;
+    if (need) {
+        ws = scratch_address(fn);
+        if (!ws) return LA_ERR_HIP;
+    }
+    return prefill_common(true, N, T, H_qk, H_v, d_k, d_v, q, q_stride, k, k_stride, v, v_stride,
+                          io_dtype, g, beta, cu_seqlens, slot_in, slot_out, num_rows, ssm_pool,
+                          ssm_slot_stride, state_dtype, out, eps, scale, mode, ws,
+                          need ? kScratchBytes : 0, stream, nullptr, /*may_check=*/false);
 }
 
 size_t kda_prefill_workspace_bytes(int N, int T, int H_qk, int H_v, int d_k, int d_v, int mode)
