@@ -161,6 +161,8 @@ def decode_stack(sh, layers, steps, warmup, seed, dev):
                       device=dev)
     conv = torch.empty((L, sh.P + 1, 3, C), dtype=synth.TORCH_DTYPE[sh.conv], device=dev)
     for l in range(L):
+        if l % 8 == 0:
+            log(f"decode stack: generating layer {l} of {L}")
         ssm[l].view(-1).copy_(synth.normal_torch(seed + l, synth.S_SSM, n_ssm, dev,
                                                  synth.TORCH_DTYPE[sh.state]))
         conv[l].view(-1).copy_(synth.normal_torch(seed + l, synth.S_CONV, n_conv, dev,
@@ -400,6 +402,7 @@ def prefill_bench(dev, reps=20, per_graph=10):
 
     res_modes = {}
     for mode in (0, 1):
+        log(f"prefill: timing mode {mode}")
         run_all(mode)  # every slot a call reads now holds its predecessor's hand-off
         torch.cuda.synchronize()
         t_conv = [time_replays(lambda i=i: [conv(i) for _ in range(per_graph)], per_graph, reps,
@@ -408,6 +411,7 @@ def prefill_bench(dev, reps=20, per_graph=10):
                                 reps, 2)["median_ms_per_launch"] for i in range(4)]
         res_modes[mode] = (t_conv, t_chunk)
     # the conv fused into the prefill's loads (one call per chunk, bf16x3)
+    log("prefill: timing the fused conv")
     t_fused = [time_replays(lambda i=i: [fused(i) for _ in range(per_graph)], per_graph, reps,
                             2)["median_ms_per_launch"] for i in range(4)]
     # primary: the bf16x3 mode (pre-split bf16 operands, fp32 accumulation;
@@ -490,6 +494,7 @@ def gdn_prefill_bench(dev, reps=20, per_graph=10):
     out = torch.empty((sh.T, Hv, D), dtype=torch.bfloat16, device=dev)
     res = {}
     for mode, name in ((1, "bf16x3"), (0, "fp32")):
+        log(f"GDN prefill: timing {name} mode")
         ws = torch.empty(la.gdn_prefill_workspace_bytes(8, sh.T, Hqk, Hv, D, D, mode),
                          dtype=torch.uint8, device=dev)
 
@@ -694,6 +699,11 @@ def main():
                     help="only run a 1 GiB device copy (PMC counter scaling)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the chunked-prefill workloads (for counter profiles)")
+    ap.add_argument("--layers", type=int, default=69,
+                    help="layers of the headline stack (69; fewer only for counter passes, "
+                         "whose per-launch figures do not depend on it)")
+    ap.add_argument("--reps", type=int, default=20,
+                    help="graph replays timed per extra workload (median reported)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU only; --gpus must be 1"}))
@@ -710,11 +720,12 @@ def main():
         return
     la.load_library()
     if args.prefill_only:
-        print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev),
-                          "gdn_prefill_chunked_hqk16_hv32": gdn_prefill_bench(dev)}), flush=True)
+        print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev, args.reps),
+                          "gdn_prefill_chunked_hqk16_hv32": gdn_prefill_bench(dev, args.reps)}),
+              flush=True)
         return
     sh = synth.DecodeShape(B=128, Hqk=96, Hv=96, dk=128, dv=128, P=128)
-    layers = 69
+    layers = args.layers
     log(f"headline: KDA decode, {layers} layers, {args.steps} timed steps after {args.warmup}")
     st = decode_stack(sh, layers, args.steps, args.warmup, 1002, dev)
     nbytes = decode_bytes(sh)
@@ -755,16 +766,14 @@ def main():
     extra = {}
     if not args.no_extra:
         s2 = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
-        extra["kda_decode_single_layer_b64_h12"] = decode_single_layer(s2, max(20, args.steps),
-                                                                        dev)
+        extra["kda_decode_single_layer_b64_h12"] = decode_single_layer(s2, args.reps, dev)
         s4 = synth.DecodeShape(B=256, Hqk=16, Hv=32, dk=128, dv=128, P=256, kda=False, io="fp32",
                                state="fp32", conv="fp32")
-        extra["gdn_decode_48_layers_fp32_b256"] = decode_stack(s4, 48, max(20, args.steps), 2,
-                                                               1003, dev)
+        extra["gdn_decode_48_layers_fp32_b256"] = decode_stack(s4, 48, args.reps, 2, 1003, dev)
         log("prefill")
-        extra["kda_prefill_chunked_h12"] = prefill_bench(dev)
-        extra["gdn_prefill_chunked_hqk16_hv32"] = gdn_prefill_bench(dev)
-        extra["kda_speculative_b64_h12_d8"] = spec_bench(dev)
+        extra["kda_prefill_chunked_h12"] = prefill_bench(dev, args.reps)
+        extra["gdn_prefill_chunked_hqk16_hv32"] = gdn_prefill_bench(dev, args.reps)
+        extra["kda_speculative_b64_h12_d8"] = spec_bench(dev, reps=args.reps)
     if not args.no_cpu:
         log("CPU oracle baselines")
         res["cpu_baseline"] = cpu_decode_rate(sh, layers, 1002, b_sample=8)
