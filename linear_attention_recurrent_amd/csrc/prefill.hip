@@ -600,23 +600,39 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     }
 
     // ---- 3. K Gamma_L / Gamma transposed through LDS and the piece's total
-    //         decay (global, at piece ends): thread (channel c, 16 tokens);
-    //         Q Gamma straight to global in fragment order
+    //         decay (global, at piece ends): thread (token tt = lane, 16
+    //         channels of wave w), so the transposed LDS writes of a wave run
+    //         along the tokens and hit distinct banks; Q Gamma straight to
+    //         global in fragment order
     const int64_t bh = (int64_t)tile * a.Hv + h;
     {
-        const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
-#pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const int tt = tq + i;
-            const int pen_t = pen[tt], f = tfl[tt];
-            const float G = Gc[tt * LDK + c];
-            const float Ge = Gc[pen_t * LDK + c];
-            KhTl[c * LDJ + tt] =
-                Kn[tt * LDK + c] * (KDA ? ((f & TF_LAST) ? exp_acc(Ge - G) : 0.f) : tabE[tt]);
+        const int tt = lane, c0 = 16 * wave;
+        const int pen_t = pen[tt], f = tfl[tt];
+        const bool last = f & TF_LAST, store_ge = tt < nt && tt == pen_t;
+        float kh[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 16; g4 += 4) {
+            const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + c0 + g4);
+            const float4 Ge = *reinterpret_cast<const float4 *>(Gc + pen_t * LDK + c0 + g4);
+            const float4 K = *reinterpret_cast<const float4 *>(Kn + tt * LDK + c0 + g4);
+            if constexpr (KDA) {
+                kh[g4] = last ? K.x * exp_acc(Ge.x - G.x) : 0.f;
+                kh[g4 + 1] = last ? K.y * exp_acc(Ge.y - G.y) : 0.f;
+                kh[g4 + 2] = last ? K.z * exp_acc(Ge.z - G.z) : 0.f;
+                kh[g4 + 3] = last ? K.w * exp_acc(Ge.w - G.w) : 0.f;
+            } else {
+                const float e = tabE[tt];
+                kh[g4] = K.x * e; kh[g4 + 1] = K.y * e; kh[g4 + 2] = K.z * e; kh[g4 + 3] = K.w * e;
+            }
             // the piece's decay of the state entering the tile (none left
             // after a full reset)
-            if (tt < nt && tt == pen_t) ws.Ge[row(tt) * DK + c] = (f & TF_PRESET) ? kGateFloor : Ge;
+            if (store_ge)
+                *reinterpret_cast<float4 *>(ws.Ge + row(tt) * DK + c0 + g4) =
+                    (f & TF_PRESET) ? make_float4(kGateFloor, kGateFloor, kGateFloor, kGateFloor)
+                                    : Ge;
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) KhTl[(c0 + i) * LDJ + tt] = kh[i];
     }
     if constexpr (MODE == PM_F32) {
         for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
