@@ -140,9 +140,31 @@ __device__ __forceinline__ float wave_sum(float x)
            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
 }
 
-// exp via the hardware exp2 (v_exp_f32): relative error a few ulp over the
-// ranges used here (log-decays and conv activations of modest magnitude).
+// exp via the hardware exp2 (v_exp_f32) of the fp32 product x log2(e): the
+// rounding of that product (and of log2(e) itself) adds a relative error of
+// up to about 1.25 |x| 2^-24, so the error grows with |x| (a few ulp for the
+// modest log-decays and conv activations it serves; bounded in
+// tests/test_gpu_device_math.py).
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// exp(x) accurate to about 2 ulp over the whole fp32 range, for the chunked
+// prefill, whose differences of running log-decay sums reach |x| of
+// hundreds.  t = x log2(e) is carried as an unevaluated sum t_hi + t_lo:
+// t_hi = fl(x c_hi) and its exact rounding error from one FMA (the
+// error-free product of Ogita, Rump and Oishi, "Accurate sum and dot
+// product", SIAM J. Sci. Comput. 26, 2005), plus x c_lo for the part of
+// log2(e) beyond fp32 (c_hi + c_lo = log2(e) to about 2^-50).  Then
+// 2^t = 2^t_hi 2^t_lo with 2^t_lo = 1 + t_lo ln 2 to second order, since
+// |t_lo| <= ulp(t_hi).  Bounded against fp64 exp in
+// tests/test_gpu_device_math.py.
+__device__ __forceinline__ float exp_acc(float x)
+{
+    const float kHi = 1.44269502162933349609375f, kLo = 1.925963033500011e-8f;
+    const float t = x * kHi;
+    float e = fmaf(x, kHi, -t);
+    e = fmaf(x, kLo, e);
+    return __builtin_amdgcn_exp2f(t) * fmaf(e, 0.69314718f, 1.0f);
+}
 __device__ __forceinline__ float silu(float y)
 {
     return y * __builtin_amdgcn_rcpf(1.0f + fast_exp(-y));

@@ -91,17 +91,6 @@ constexpr float kExpClamp = 80.f;
 constexpr float kGateFloor = -128.f;  // exp(-128) == 0 in fp32
 enum { PM_F32 = 0, PM_BF16X3 = 1 };
 
-// exp(x) as 2^(x log2 e) with the product carried in two pieces before the
-// hardware exp2: about 2 ulp for the |x| <= 88 used here.
-__device__ __forceinline__ float exp_acc(float x)
-{
-    const float kHi = 1.44269502162933349609375f, kLo = 1.925963033500011e-8f;
-    const float t = x * kHi;
-    float e = fmaf(x, kHi, -t);
-    e = fmaf(x, kLo, e);
-    return __builtin_amdgcn_exp2f(t) * fmaf(e, 0.69314718f, 1.0f);
-}
-
 // ---- NT fragments ---------------------------------------------------------
 // A lane's fragment of one operand row for a K-long contraction holds K/4
 // floats; element idx corresponds to k = frag_k(q, idx).

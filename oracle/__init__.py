@@ -8,8 +8,10 @@ the product path.
 Every function takes numpy arrays holding the exact values of the stored
 tensors (any float dtype; they are converted to fp64 without loss), copies the
 pools it updates, and returns fresh arrays: calls are pure.  The arithmetic is
-in ``oracle.c``; this file only marshals arguments.  Storage dtypes are the
-strings ``"fp32"``, ``"bf16"`` and ``"fp64"`` (no rounding).
+in ``oracle.c``; this file marshals arguments, except for ``track_copy`` and
+``conv_window_scatter``, which are plain row copies (no arithmetic) written
+here with numpy indexing.  Storage dtypes are the strings ``"fp32"``,
+``"bf16"`` and ``"fp64"`` (no rounding).
 """
 from __future__ import annotations
 
@@ -240,7 +242,7 @@ def commit(accepted, slots, ssm_pool, ring, ring_base, *, kda=True, state_dtype=
 
 
 def track_copy(conv_pool, ssm_pool, mask, src, dst):
-    """State tracking ([SGLang-pool] / [mamba-ish] track passage): for every
+    """State tracking (the state-tracking passage of xxmr.cn/news/181459): for every
     entry i with mask[i] (all when mask is None), pool rows dst[i] of both
     pools become copies of rows src[i].  Returns the new (conv, ssm) pools."""
     conv, ssm = np.array(conv_pool, copy=True), np.array(ssm_pool, copy=True)
@@ -252,8 +254,8 @@ def track_copy(conv_pool, ssm_pool, mask, src, dst):
 
 
 def conv_window_scatter(conv_pool, windows, mask, slots, step):
-    """Commit of the conv history after speculative verify ([mamba-ish]
-    "intermediate_conv_window" passage): for every entry b with mask[b] (all
+    """Commit of the conv history after speculative verify (the
+    "intermediate_conv_window" passage of xxmr.cn/news/181459): for every entry b with mask[b] (all
     when mask is None) and 0 <= step[b] < D, pool row slots[b] becomes
     windows[b, step[b]].  Returns the new conv pool."""
     conv = np.array(conv_pool, copy=True)
