@@ -1248,13 +1248,13 @@ __device__ __forceinline__ void split1(float v, bf16_t &hi, bf16_t &lo)
     lo = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
-// PF: operands of the next block prefetched into a second register buffer
-// (for launches with few workgroups).  NSL: 16-row state slices per
-// workgroup; with NSL = 2 every operand fragment loaded serves twice the
-// matrix work, halving the operand traffic per unit of work (for launches with
+// The operands of the next block are prefetched into a second register
+// buffer while the current block runs.  NSL: 16-row state slices per
+// workgroup; with NSL = 4 every operand fragment loaded serves four times the
+// matrix work, cutting the operand traffic per unit of work (for launches with
 // many sequences, where that traffic between L2 and the CUs is the limit).
-template <typename IOT, typename ST, bool PF, int NSL>
-__global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_kernel(PrefillArgs a)
+template <typename IOT, typename ST, int NSL>
+__global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain_x3_kernel(PrefillArgs a)
 {
     constexpr int NR = 16 * NSL;  // state rows of the workgroup
     constexpr int kRowOpsN = 80 + 4 * NSL;  // W 32, Q Gamma 32, P 16, U 4 per slice
@@ -1301,7 +1301,28 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
                 load_run(ops + 80 + 4 * sl, ws.U + bh * kBlkDK + fidx(8 * I + NSL * rs + sl, 0), 1,
                          lane);
         };
-        auto block = [&](int it, const float *cur) {
+        // O of a block stays in registers and is stored under the next
+        // block, ahead of that block's operand loads: the loads are then the
+        // youngest memory operations when the next D waits for them, and that
+        // wait does not cover the stores' completion
+        float oacc[NSL][4];
+        auto store_o = [&](int itp) {
+            const int base = (tb0 + itp) * CB;
+            const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tr = 16 * I + 4 * lq + r;
+                    if (tr >= p0 && tr < p1)
+                        st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + row0 + 16 * sl + li,
+                                a.scale * oacc[sl][r]);
+                }
+        };
+        // nxt: the next block's operands are loaded into it under the O
+        // products, one load between two of them, so their issue overlaps the
+        // matrix work rather than stalling the wave
+        auto block = [&](int it, const float *cur, float *nxt) {
             const int tb = tb0 + it, base = tb * CB;
             const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
             const int b = it & 1;
@@ -1338,6 +1359,8 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
                     make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
             }
             __syncthreads();  // D^T complete
+            if (it > 0) store_o(it - 1);
+            load_ops(min(tb + 1, tb1), nxt);
             // O = scale (Q Gamma S^T + P D) for each slice
 #pragma unroll
             for (int sl = 0; sl < NSL; ++sl) {
@@ -1352,31 +1375,26 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
                     mma3(acc, quad8(cur + 64 + 8 * m), quad8(cur + 64 + 8 * m + 4),
                          lds8(&DH[sr][32 * m + 8 * lq]), lds8(&DL[sr][32 * m + 8 * lq]));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tr = 16 * I + 4 * lq + r;
-                    if (tr >= p0 && tr < p1)
-                        st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + row0 + sr,
-                                a.scale * acc[r]);
+                for (int q = 0; q < 18; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
                 }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[sl][r] = acc[r];
             }
         };
-        if constexpr (PF) {
-            float bufA[kRowOpsN], bufB[kRowOpsN];
-            if (ntiles > 0) load_ops(tb0, bufA);
-            for (int it = 0; it < ntiles; it += 2) {
-                load_ops(min(tb0 + it + 1, tb1), bufB);
-                block(it, bufA);
-                if (it + 1 >= ntiles) break;
-                load_ops(min(tb0 + it + 2, tb1), bufA);
-                block(it + 1, bufB);
-            }
-        } else {
-            float buf[kRowOpsN];
-            for (int it = 0; it < ntiles; ++it) {
-                load_ops(tb0 + it, buf);
-                block(it, buf);
-            }
+        float bufA[kRowOpsN], bufB[kRowOpsN];
+        if (ntiles > 0) load_ops(tb0, bufA);
+        // pairs of blocks, the odd last block peeled: an exit between the two
+        // halves would make the compiler wait for the prefetched operands (and
+        // the stores behind them) at the top of every pair
+        int it = 0;
+        for (; it + 1 < ntiles; it += 2) {
+            block(it, bufA, bufB);
+            block(it + 1, bufB, bufA);
         }
+        if (it < ntiles) block(it, bufA, bufB);
+        if (ntiles > 0) store_o(ntiles - 1);
     } else {
         auto load_ops = [&](int tb, float *ops) {
             const int pend = min(end, tb * CB + CB) - 1;
@@ -1434,23 +1452,19 @@ __global__ void __launch_bounds__(kChainThreads, PF ? 2 : 1) prefill_chain_x3_ke
                     }
             }
         };
-        if constexpr (PF) {
-            float bufA[kColOps], bufB[kColOps];
-            if (ntiles > 0) load_ops(tb0, bufA);
-            for (int it = 0; it < ntiles; it += 2) {
-                load_ops(min(tb0 + it + 1, tb1), bufB);
-                block(it, bufA);
-                if (it + 1 >= ntiles) break;
-                load_ops(min(tb0 + it + 2, tb1), bufA);
-                block(it + 1, bufB);
-            }
-        } else {
-            float buf[kColOps];
-            for (int it = 0; it < ntiles; ++it) {
-                load_ops(tb0 + it, buf);
-                block(it, buf);
-            }
+        float bufA[kColOps], bufB[kColOps];
+        if (ntiles > 0) load_ops(tb0, bufA);
+        // pairs of blocks, the odd last block peeled (an exit between the two
+        // halves would make the compiler wait for the prefetched operands at
+        // the top of every pair)
+        int it = 0;
+        for (; it + 1 < ntiles; it += 2) {
+            load_ops(tb0 + it + 1, bufB);
+            block(it, bufA);
+            load_ops(min(tb0 + it + 2, tb1), bufA);
+            block(it + 1, bufB);
         }
+        if (it < ntiles) block(it, bufA);
     }
     __syncthreads();
     for (int idx = tid; idx < NR * DK; idx += kChainThreads) {
@@ -1491,11 +1505,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     if constexpr (MODE == PM_F32)
         hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), dim3(chain_grid(a, DK / 16)),
                            dim3(kChainThreads), kChainLds, stream, a);
-    else if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: prefetch
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, true, 1>),
+    else if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: 16 state rows each
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, 1>),
                            dim3(chain_grid(a, DK / 16)), dim3(kChainThreads), 0, stream, a);
     else  // many: 64 state rows per workgroup
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, false, 4>),
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, 4>),
                            dim3(chain_grid(a, DK / 64)), dim3(kChainThreads), 0, stream, a);
     return hipGetLastError();
 }
