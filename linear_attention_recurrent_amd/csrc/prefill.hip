@@ -66,6 +66,9 @@
 // the outputs, from cancellation in the contractions, and are not offered.)
 // The result tile D[4 (l/16) + r][l % 16] sits in register r of lane l.
 // The small 16x16 block products of the triangular inverse always use fp32.
+#include <algorithm>
+#include <atomic>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -356,15 +359,81 @@ __device__ __forceinline__ void conv_apply(float *y, const float *xr, const Pref
 // ---------------------------------------------------------------------------
 constexpr int kIntraThreads = 512;
 constexpr int kSeqTab = 512;  // sequences whose cu_seqlens / slot_in kernel 1 stages in LDS
-static_assert(kSeqTab <= kIntraThreads && 2 * kSeqTab <= CB * LDJ,
-              "one table entry per thread, both tables inside N's space");
+static_assert(kSeqTab == kIntraThreads, "one table entry per thread");
 constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
-constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + (5 * CB + 8) * sizeof(int);
+constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + (5 * CB + 8 + 2 * kSeqTab) * sizeof(int);
 // per-token flags of kernel 1 (sub-pieces)
 enum { TF_OPEN = 1,      // no full reset between the piece start and the token
        TF_LAST = 2,      // no full reset after the token up to the piece end
        TF_PRESET = 4,    // the token's piece holds a full reset
        TF_RESET = 8 };   // the token itself resets every key channel
+
+// Kernel 1 runs persistently: a grid of one workgroup per CU walks the
+// (tile, head) items, item = tile * Hv + head.  Without the fused conv, the
+// raw inputs phase 1 reads (thread (token t, 16-channel chunk c0): q, k, the
+// gates and beta) are loaded for the next item while the current one runs,
+// so an item starts on inputs already in registers.
+template <typename IOT, bool KDA> struct IntraIn {
+    static constexpr int QN = sizeof(IOT);  // 16-byte words per 16 q (or k) elements
+    uint4 q[QN], k[QN];
+    float4 g[KDA ? 4 : 1];
+    float bt;
+};
+template <typename IOT, bool KDA>
+__device__ __forceinline__ void intra_issue(IntraIn<IOT, KDA> &r, const PrefillArgs &a, int item,
+                                            int t, int c0)
+{
+    const int tile = item / a.Hv, h = item - tile * a.Hv, kh = h / a.G;
+    const int t0 = tile * CB, nt = min(CB, a.T - t0);
+    const int64_t tok = t0 + min(t, nt - 1);
+    if constexpr (KDA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.g[i] = reinterpret_cast<const float4 *>(a.g + (tok * a.Hv + h) * DK + c0)[i];
+    } else {
+        r.g[0].x = a.g[tok * a.Hv + h];
+    }
+    r.bt = a.beta[tok * a.Hv + h];
+    const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
+    const uint4 *k = reinterpret_cast<const uint4 *>(static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
+#pragma unroll
+    for (int i = 0; i < IntraIn<IOT, KDA>::QN; ++i) r.q[i] = q[i];
+#pragma unroll
+    for (int i = 0; i < IntraIn<IOT, KDA>::QN; ++i) r.k[i] = k[i];
+}
+template <typename IOT>
+__device__ __forceinline__ void unpack16w(const uint4 *w, float *f)
+{
+#pragma unroll
+    for (int i = 0; i < (int)sizeof(IOT); ++i) {
+        const uint32_t u[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(IOT) == 2) {
+                f[8 * i + 2 * j] = bf16_lo(u[j]);
+                f[8 * i + 2 * j + 1] = bf16_hi(u[j]);
+            } else {
+                f[4 * i + j] = __uint_as_float(u[j]);
+            }
+        }
+    }
+}
+template <typename IOT, bool KDA>
+__device__ __forceinline__ void intra_unpack(const IntraIn<IOT, KDA> &r, float *qv, float *kv,
+                                             float *gv, float &bt)
+{
+    unpack16w<IOT>(r.q, qv);
+    unpack16w<IOT>(r.k, kv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 g = r.g[KDA ? i : 0];
+        gv[4 * i] = g.x;
+        gv[4 * i + 1] = KDA ? g.y : g.x;
+        gv[4 * i + 2] = KDA ? g.z : g.x;
+        gv[4 * i + 3] = KDA ? g.w : g.x;
+    }
+    bt = r.bt;
+}
 
 template <typename IOT, bool KDA, int MODE, bool CONV>
 __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArgs a)
@@ -373,8 +442,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     float *Qn = sm;                  // q_hat [64][LDK]; later (beta K Gamma)^T [128][LDJ]
     float *Kn = Qn + kRegion;        // k_hat [64][LDK]; later (beta V)^T [128][LDJ]
     float *Gc = Kn + kRegion;        // cumulative log decay over the tile
-    float *Nm = Gc + kRegion;        // N = Diag(beta) A (strictly lower, masked); earlier the
-                                     // sequence table (step 1), then K Gamma_L / Gamma (step 3)
+    float *Nm = Gc + kRegion;        // N = Diag(beta) A (strictly lower, masked); earlier
+                                     // K Gamma_L / Gamma (step 3)
     float *Tm = Nm + CB * LDJ;       // T = (I + N)^-1; in step 4 also a partial of A
     float *bet = Tm + CB * LDJ;      // beta
     float *qsum = bet + CB;          // [4][128] partial sums of the tile scan
@@ -386,630 +455,681 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     int *ssl = sst + CB;             // fused conv: its history row (-1: zeros)
     int *bigw = ssl + CB;            // [8] KDA: wave w saw a sub-block span above kSpanMax
     int *tfl = bigw + 8;             // TF_* flags per token
+    int *cut = tfl + CB;             // [kSeqTab] cu_seqlens (fewer than kSeqTab sequences)
+    int *sit = cut + kSeqTab;        // [kSeqTab] slot_in
     float *XtK = Qn, *XtV = Kn;      // transposed right-hand sides of phase 6
     float *KhTl = Nm;                // [128][LDJ] staging of K Gamma_L / Gamma, transposed
 
-    const int tile = blockIdx.x, h = blockIdx.y, kh = h / a.G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, lq = lane >> 4;
-    const int t0 = tile * CB;
-    const int nt = min(CB, a.T - t0);
     const Ws ws = ws_layout(a.ws, a.T, a.Hv);
-    auto row = [&](int t) { return ((int64_t)(t0 + t) * a.Hv + h); };
-
-    // ---- 1. loads: thread (token t, 16-channel chunk cq), all issued up front
-    const int t = tid >> 3, cq = tid & 7, c0 = 16 * cq;
-    const bool valid = t < nt;
-    const int64_t tok = t0 + min(t, nt - 1);
-    // With fewer than kSeqTab sequences, cu_seqlens and slot_in go to LDS in
-    // one parallel round (Nm is free until step 3) and each token searches
-    // them there; issued before the data loads, so waiting for them does not
-    // wait for the data (loads complete in issue order).  Larger batches
-    // search cu_seqlens in global memory.
-    int *cut = reinterpret_cast<int *>(Nm), *sit = cut + kSeqTab;
+    const int nitems = (a.T + CB - 1) / CB * a.Hv;
+    // With fewer than kSeqTab sequences, cu_seqlens and slot_in go to LDS
+    // once (one entry per thread; entries past N repeat the last one and are
+    // never read) and tokens search them there.  Larger batches search
+    // cu_seqlens in global memory.
     const bool tab = a.N < kSeqTab;
-    const int cuv = a.cu[min(tid, a.N)], siv = a.slot_in[min(tid, a.N - 1)];
-    __builtin_amdgcn_sched_barrier(0);
-    float qv[16], kv[16], gv[16];
-    if constexpr (KDA) {
-        load16<float>(gv, a.g + (tok * a.Hv + h) * DK + c0);
-    } else {
-        const float g1 = a.g[tok * a.Hv + h];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) gv[e] = g1;
+    {
+        const int i = threadIdx.x;
+        cut[i] = a.cu[min(i, a.N)];
+        sit[i] = a.slot_in[min(i, a.N - 1)];
     }
-    const float bt = a.beta[tok * a.Hv + h];
-    // fused conv: thread (channel cc, 16 tokens tc .. tc + 15); every lane of
-    // a wave shares tc, as conv_apply requires
-    const int cc = tid & (DK - 1), tc = 16 * (tid >> 7);
-    float xq[19], xk[19];
-    if constexpr (CONV) {  // both windows in flight together
-        conv_rows<IOT>(xq, a, t0, tc, kh * DK + cc);
-        conv_rows<IOT>(xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
-    } else {
-        load16<IOT>(qv, static_cast<const IOT *>(a.q) + tok * a.q_stride + kh * DK + c0);
-        load16<IOT>(kv, static_cast<const IOT *>(a.k) + tok * a.k_stride + kh * DK + c0);
-    }
-    // the token's sequence: a search of the LDS table, else of cu_seqlens in
-    // global memory (after the data loads, so its round trips overlap them)
-    cut[tid] = cuv;  // entries past N repeat the last one and are never read
-    sit[tid] = siv;
     __syncthreads();
-    int ps = t, pe = t, s0 = 0, hs = -1;
-    if (valid) {
-        int n, s1, si;
-        if (tab) {
-            int lo = 0, hi = a.N - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (cut[mid] <= t0 + t) lo = mid;
-                else hi = mid - 1;
+    // The sequence of token t of an item (phase 1's mapping): its piece's
+    // start and end in the tile, the sequence's first token, its slot_in row
+    // (-1: none).  Found for the next item at the end of the current one's
+    // step 1.
+    struct Seq { int ps, pe, s0, hs; };
+    auto find_seq_item = [&](int it, int t) {
+        const int t0 = it / a.Hv * CB, nt = min(CB, a.T - t0);
+        Seq r{t, t, 0, -1};
+        if (t < nt) {
+            int n, s0, s1, si;
+            if (tab) {
+                int lo = 0, hi = a.N - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (cut[mid] <= t0 + t) lo = mid;
+                    else hi = mid - 1;
+                }
+                n = lo;
+                s0 = cut[n];
+                s1 = cut[n + 1];
+                si = sit[n];
+                // keeps these LDS reads from being merged with the global ones
+                // below into one generic load, which would wait for every load
+                asm volatile("" : "+v"(s0), "+v"(s1), "+v"(si));
+            } else {
+                n = find_seq_p(a.cu, a.N, t0 + t);
+                s0 = a.cu[n];
+                s1 = a.cu[n + 1];
+                si = a.slot_in[n];
+                // waits for these loads inside this branch, so the join
+                // below does not wait for every memory operation in flight
+                asm volatile("" : "+v"(s0), "+v"(s1), "+v"(si));
             }
-            n = lo;
-            s0 = cut[n];
-            s1 = cut[n + 1];
-            si = sit[n];
-            // keeps these LDS reads from being merged with the global ones
-            // below into one generic load, which would wait for every load
-            asm volatile("" : "+v"(s0), "+v"(s1), "+v"(si));
+            r.ps = max(s0, t0) - t0;
+            r.pe = min(s1, t0 + CB) - 1 - t0;
+            r.s0 = s0;
+            r.hs = (si >= 0 && si < a.num_rows) ? si : -1;
+        }
+        return r;
+    };
+    Seq nseq = find_seq_item(blockIdx.x, threadIdx.x >> 3);
+    // the next item's inputs (without the fused conv), phase 1's mapping
+    IntraIn<IOT, KDA> nx;
+    if constexpr (!CONV) intra_issue(nx, a, blockIdx.x, threadIdx.x >> 3, 16 * (threadIdx.x & 7));
+    // The first item waits for its loads here.  Later items find theirs
+    // complete (see the end of step 1).  Without this wait the loop head
+    // would merge the two cases and wait for every memory operation at each
+    // item, including the previous item's last stores.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+        // an opaque copy of the thread index per item: what derives from it
+        // (lane offsets, LDS addresses) is formed inside the item and not
+        // held live across the whole loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = tid >> 6;
+        const int li = lane & 15, lq = lane >> 4;
+        // phase 1's thread mapping: token t, 16-channel chunk cq
+        const int t = tid >> 3, cq = tid & 7, c0 = 16 * cq;
+        const int tile = item / a.Hv, h = item - tile * a.Hv, kh = h / a.G;
+        const int t0 = tile * CB;
+        const int nt = min(CB, a.T - t0);
+        auto row = [&](int t) { return ((int64_t)(t0 + t) * a.Hv + h); };
+
+        // ---- 1. inputs: thread (token t, 16-channel chunk cq), and the
+        //         token's sequence found under the previous item
+        const bool valid = t < nt;
+        const Seq seq = nseq;
+        const int ps = seq.ps, pe = seq.pe, s0 = seq.s0, hs = seq.hs;
+        float qv[16], kv[16], gv[16], bt;
+        // fused conv: thread (channel cc, 16 tokens tc .. tc + 15); every lane of
+        // a wave shares tc, as conv_apply requires
+        const int cc = tid & (DK - 1), tc = 16 * (tid >> 7);
+        float xq[19], xk[19];
+        if constexpr (CONV) {
+            const int64_t tok = t0 + min(t, nt - 1);
+            if constexpr (KDA) {
+                load16<float>(gv, a.g + (tok * a.Hv + h) * DK + c0);
+            } else {
+                const float g1 = a.g[tok * a.Hv + h];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) gv[e] = g1;
+            }
+            bt = a.beta[tok * a.Hv + h];
+            // both windows in flight together
+            conv_rows<IOT>(xq, a, t0, tc, kh * DK + cc);
+            conv_rows<IOT>(xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
         } else {
-            n = find_seq_p(a.cu, a.N, t0 + t);
-            s0 = a.cu[n];
-            s1 = a.cu[n + 1];
-            si = a.slot_in[n];
+            intra_unpack(nx, qv, kv, gv, bt);
         }
-        ps = max(s0, t0) - t0;
-        pe = min(s1, t0 + CB) - 1 - t0;
-        hs = (si >= 0 && si < a.num_rows) ? si : -1;
-    }
-    if constexpr (CONV) {
-        // conv of q and k into Qn / Kn, then back to the (token, chunk)
-        // mapping for the norms
-        if (cq == 0) {
-            sst[t] = s0;
-            ssl[t] = hs;
+        // this item's LDS writes come after the previous item's last reads
+        __syncthreads();
+        if constexpr (CONV) {
+            // conv of q and k into Qn / Kn, then back to the (token, chunk)
+            // mapping for the norms
+            if (cq == 0) {
+                sst[t] = s0;
+                ssl[t] = hs;
+            }
+            __syncthreads();
+            float y[16];
+            conv_apply(y, xq, a, t0, tc, kh * DK + cc, sst, ssl);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Qn[(tc + i) * LDK + cc] = y[i];
+            conv_apply(y, xk, a, t0, tc, a.Hqk * DK + kh * DK + cc, sst, ssl);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Kn[(tc + i) * LDK + cc] = y[i];
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                const float4 q4 = *reinterpret_cast<const float4 *>(Qn + t * LDK + c0 + e);
+                const float4 k4 = *reinterpret_cast<const float4 *>(Kn + t * LDK + c0 + e);
+                qv[e] = q4.x; qv[e + 1] = q4.y; qv[e + 2] = q4.z; qv[e + 3] = q4.w;
+                kv[e] = k4.x; kv[e + 1] = k4.y; kv[e + 2] = k4.z; kv[e + 3] = k4.w;
+            }
         }
-        __syncthreads();
-        float y[16];
-        conv_apply(y, xq, a, t0, tc, kh * DK + cc, sst, ssl);
+        float sq = 0.f, sk = 0.f, live = 0.f;  // live: channels not reset
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Qn[(tc + i) * LDK + cc] = y[i];
-        conv_apply(y, xk, a, t0, tc, a.Hqk * DK + kh * DK + cc, sst, ssl);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) Kn[(tc + i) * LDK + cc] = y[i];
-        __syncthreads();
+        for (int e = 0; e < 16; ++e) {
+            if (!valid) { qv[e] = 0.f; kv[e] = 0.f; gv[e] = 0.f; }
+            sq = fmaf(qv[e], qv[e], sq);
+            sk = fmaf(kv[e], kv[e], sk);
+            live += gv[e] > kGateFloor ? 1.f : 0.f;
+        }
+        sq = group_sum<8>(sq);
+        sk = group_sum<8>(sk);
+        live = group_sum<8>(live);
+        const float iq = 1.f / sqrtf(sq + a.eps), ik = 1.f / sqrtf(sk + a.eps);
 #pragma unroll
         for (int e = 0; e < 16; e += 4) {
-            const float4 q4 = *reinterpret_cast<const float4 *>(Qn + t * LDK + c0 + e);
-            const float4 k4 = *reinterpret_cast<const float4 *>(Kn + t * LDK + c0 + e);
-            qv[e] = q4.x; qv[e + 1] = q4.y; qv[e + 2] = q4.z; qv[e + 3] = q4.w;
-            kv[e] = k4.x; kv[e + 1] = k4.y; kv[e + 2] = k4.z; kv[e + 3] = k4.w;
+            *reinterpret_cast<float4 *>(Qn + t * LDK + c0 + e) =
+                make_float4(qv[e] * iq, qv[e + 1] * iq, qv[e + 2] * iq, qv[e + 3] * iq);
+            *reinterpret_cast<float4 *>(Kn + t * LDK + c0 + e) =
+                make_float4(kv[e] * ik, kv[e + 1] * ik, kv[e + 2] * ik, kv[e + 3] * ik);
+            *reinterpret_cast<float4 *>(Gc + t * LDK + c0 + e) =
+                make_float4(fmaxf(gv[e], kGateFloor), fmaxf(gv[e + 1], kGateFloor),
+                            fmaxf(gv[e + 2], kGateFloor), fmaxf(gv[e + 3], kGateFloor));
         }
-    }
-    float sq = 0.f, sk = 0.f, live = 0.f;  // live: channels not reset
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        if (!valid) { qv[e] = 0.f; kv[e] = 0.f; gv[e] = 0.f; }
-        sq = fmaf(qv[e], qv[e], sq);
-        sk = fmaf(kv[e], kv[e], sk);
-        live += gv[e] > kGateFloor ? 1.f : 0.f;
-    }
-    sq = group_sum<8>(sq);
-    sk = group_sum<8>(sk);
-    live = group_sum<8>(live);
-    const float iq = 1.f / sqrtf(sq + a.eps), ik = 1.f / sqrtf(sk + a.eps);
-#pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-        *reinterpret_cast<float4 *>(Qn + t * LDK + c0 + e) =
-            make_float4(qv[e] * iq, qv[e + 1] * iq, qv[e + 2] * iq, qv[e + 3] * iq);
-        *reinterpret_cast<float4 *>(Kn + t * LDK + c0 + e) =
-            make_float4(kv[e] * ik, kv[e + 1] * ik, kv[e + 2] * ik, kv[e + 3] * ik);
-        *reinterpret_cast<float4 *>(Gc + t * LDK + c0 + e) =
-            make_float4(fmaxf(gv[e], kGateFloor), fmaxf(gv[e + 1], kGateFloor),
-                        fmaxf(gv[e + 2], kGateFloor), fmaxf(gv[e + 3], kGateFloor));
-    }
-    if (cq == 0) {
-        bet[t] = valid ? bt : 0.f;
-        pst[t] = ps;
-        pen[t] = pe;
-        tfl[t] = TF_OPEN | TF_LAST | (live == 0.f ? TF_RESET : 0);  // final unless a reset
-    }
-    __syncthreads();
-    // sub-pieces: with a full reset in the tile (rm, the same in every wave),
-    // lane t of wave 0 finds the last reset at or before t and the last one
-    // of its piece, then one more barrier publishes them
-    const uint64_t rm = __ballot(tfl[lane] & TF_RESET);
-    if (rm != 0 && wave == 0) {
-        const bool rs = (rm >> lane) & 1;
-        const int ps_l = pst[lane], pe_l = pen[lane];
-        const uint64_t upto = rm & ((2ull << lane) - 1ull), upto_e = rm & ((2ull << pe_l) - 1ull);
-        const int r = upto ? 63 - __builtin_clzll(upto) : -1;       // last reset <= t
-        const int rl = upto_e ? 63 - __builtin_clzll(upto_e) : -1;  // last reset <= piece end
-        pst[lane] = max(ps_l, r);
-        tfl[lane] = (r < ps_l ? TF_OPEN : 0) | (rl <= lane ? TF_LAST : 0) |
-                    (rl >= ps_l ? TF_PRESET : 0) | (rs ? TF_RESET : 0);
-    }
-    if (rm != 0) __syncthreads();
-
-    // ---- 2. cumulative decay over the tile, segmented at piece starts: four
-    //         quarters (the 16-token sub-blocks) of 16 tokens per channel.
-    //         run is the sum inside the quarter since its last piece start;
-    //         a quarter's tokens before its first sub-piece start continue the
-    //         previous quarters' running sum.  -min(run) is the largest decay
-    //         inside the sub-block, the span that bounds the factorised
-    //         diagonal product of step 4.
-    {
-        const int c = tid & (DK - 1), qq = tid >> 7;
-        // wave-uniform bit masks over the tile's tokens: sub-piece starts,
-        // and full resets (those sub-pieces start from zero: the token's own
-        // gate only empties what came before it)
-        const uint64_t sm = __ballot(pst[lane] == lane);
-        const uint32_t smq = (uint32_t)(sm >> (16 * qq)) & 0xFFFFu;
-        const uint32_t rmq = (uint32_t)(rm >> (16 * qq)) & 0xFFFFu;
-        const int first = smq ? __builtin_ctz(smq) : 16;  // first sub-piece start in the quarter
-        float run[16];
-        float acc = 0.f, mn = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float gi = Gc[(16 * qq + i) * LDK + c];
-            acc = ((smq >> i) & 1) ? (((rmq >> i) & 1) ? 0.f : gi) : acc + gi;
-            run[i] = acc;
-            mn = fminf(mn, acc);
+        if (cq == 0) {
+            bet[t] = valid ? bt : 0.f;
+            pst[t] = ps;
+            pen[t] = pe;
+            tfl[t] = TF_OPEN | TF_LAST | (live == 0.f ? TF_RESET : 0);  // final unless a reset
         }
-        qsum[qq * DK + c] = acc;
-        if constexpr (KDA) {
-            const bool big = __ballot(-mn > kSpanMax) != 0;
-            if (lane == 0) bigw[wave] = big;
+        // the next item's sequences and inputs (the last item repeats its
+        // own, without a branch).  They are older than this item's v loads,
+        // so step 6's wait for those completes them too, and the next item
+        // starts without waiting.
+        {
+            const int next = min(item + (int)gridDim.x, nitems - 1);
+            nseq = find_seq_item(next, t);
+            if constexpr (!CONV) intra_issue(nx, a, next, t, c0);
         }
         __syncthreads();
-        // carry into the quarter: the running sum of the sub-piece open at
-        // its start (quarter p restarts iff its last sub-piece began inside
-        // it; quarter 0 always does, at the tile start)
-        float off = 0.f;
-        for (int p = 0; p < qq; ++p)
-            off = ((sm >> (16 * p)) & 0xFFFFu) ? qsum[p * DK + c] : off + qsum[p * DK + c];
+        // sub-pieces: with a full reset in the tile (rm, the same in every wave),
+        // lane t of wave 0 finds the last reset at or before t and the last one
+        // of its piece, then one more barrier publishes them
+        const uint64_t rm = __ballot(tfl[lane] & TF_RESET);
+        if (rm != 0 && wave == 0) {
+            const bool rs = (rm >> lane) & 1;
+            const int ps_l = pst[lane], pe_l = pen[lane];
+            const uint64_t upto = rm & ((2ull << lane) - 1ull), upto_e = rm & ((2ull << pe_l) - 1ull);
+            const int r = upto ? 63 - __builtin_clzll(upto) : -1;       // last reset <= t
+            const int rl = upto_e ? 63 - __builtin_clzll(upto_e) : -1;  // last reset <= piece end
+            pst[lane] = max(ps_l, r);
+            tfl[lane] = (r < ps_l ? TF_OPEN : 0) | (rl <= lane ? TF_LAST : 0) |
+                        (rl >= ps_l ? TF_PRESET : 0) | (rs ? TF_RESET : 0);
+        }
+        if (rm != 0) __syncthreads();
+
+        // ---- 2. cumulative decay over the tile, segmented at piece starts: four
+        //         quarters (the 16-token sub-blocks) of 16 tokens per channel.
+        //         run is the sum inside the quarter since its last piece start;
+        //         a quarter's tokens before its first sub-piece start continue the
+        //         previous quarters' running sum.  -min(run) is the largest decay
+        //         inside the sub-block, the span that bounds the factorised
+        //         diagonal product of step 4.
+        {
+            const int c = tid & (DK - 1), qq = tid >> 7;
+            // wave-uniform bit masks over the tile's tokens: sub-piece starts,
+            // and full resets (those sub-pieces start from zero: the token's own
+            // gate only empties what came before it)
+            const uint64_t sm = __ballot(pst[lane] == lane);
+            const uint32_t smq = (uint32_t)(sm >> (16 * qq)) & 0xFFFFu;
+            const uint32_t rmq = (uint32_t)(rm >> (16 * qq)) & 0xFFFFu;
+            const int first = smq ? __builtin_ctz(smq) : 16;  // first sub-piece start in the quarter
+            float run[16];
+            float acc = 0.f, mn = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            Gc[(16 * qq + i) * LDK + c] = i < first ? run[i] + off : run[i];
-    }
-    __syncthreads();
-    // GDN: one decay per token, so the decay factors of steps 3 and 6 are
-    // per-token scalars, exp(G_end - G_t) and exp(G_t - G_start) over the
-    // token's piece (zero across a reset), formed once here (qsum is free
-    // after step 2)
-    float *tabE = qsum, *tabS = qsum + CB;
-    if constexpr (!KDA) {
-        if (tid < CB) {
-            const float G = Gc[tid * LDK];
-            const int f = tfl[tid];
-            tabE[tid] = (f & TF_LAST) ? exp_acc(Gc[pen[tid] * LDK] - G) : 0.f;
-            tabS[tid] = (f & TF_OPEN) ? exp_acc(G) : 0.f;
+            for (int i = 0; i < 16; ++i) {
+                const float gi = Gc[(16 * qq + i) * LDK + c];
+                acc = ((smq >> i) & 1) ? (((rmq >> i) & 1) ? 0.f : gi) : acc + gi;
+                run[i] = acc;
+                mn = fminf(mn, acc);
+            }
+            qsum[qq * DK + c] = acc;
+            if constexpr (KDA) {
+                const bool big = __ballot(-mn > kSpanMax) != 0;
+                if (lane == 0) bigw[wave] = big;
+            }
+            __syncthreads();
+            // carry into the quarter: the running sum of the sub-piece open at
+            // its start (quarter p restarts iff its last sub-piece began inside
+            // it; quarter 0 always does, at the tile start)
+            float off = 0.f;
+            for (int p = 0; p < qq; ++p)
+                off = ((sm >> (16 * p)) & 0xFFFFu) ? qsum[p * DK + c] : off + qsum[p * DK + c];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                Gc[(16 * qq + i) * LDK + c] = i < first ? run[i] + off : run[i];
         }
         __syncthreads();
-    }
-
-    // ---- 3. K Gamma_L / Gamma transposed through LDS and the piece's total
-    //         decay (global, at piece ends): thread (token tt = lane, 16
-    //         channels of wave w), so the transposed LDS writes of a wave run
-    //         along the tokens and hit distinct banks; Q Gamma straight to
-    //         global in fragment order
-    const int64_t bh = (int64_t)tile * a.Hv + h;
-    {
-        const int tt = lane, c0 = 16 * wave;
-        const int pen_t = pen[tt], f = tfl[tt];
-        const bool last = f & TF_LAST, store_ge = tt < nt && tt == pen_t;
-        float kh[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 16; g4 += 4) {
-            const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + c0 + g4);
-            const float4 Ge = *reinterpret_cast<const float4 *>(Gc + pen_t * LDK + c0 + g4);
-            const float4 K = *reinterpret_cast<const float4 *>(Kn + tt * LDK + c0 + g4);
-            if constexpr (KDA) {
-                kh[g4] = last ? K.x * exp_acc(Ge.x - G.x) : 0.f;
-                kh[g4 + 1] = last ? K.y * exp_acc(Ge.y - G.y) : 0.f;
-                kh[g4 + 2] = last ? K.z * exp_acc(Ge.z - G.z) : 0.f;
-                kh[g4 + 3] = last ? K.w * exp_acc(Ge.w - G.w) : 0.f;
-            } else {
-                const float e = tabE[tt];
-                kh[g4] = K.x * e; kh[g4 + 1] = K.y * e; kh[g4 + 2] = K.z * e; kh[g4 + 3] = K.w * e;
+        // GDN: one decay per token, so the decay factors of steps 3 and 6 are
+        // per-token scalars, exp(G_end - G_t) and exp(G_t - G_start) over the
+        // token's piece (zero across a reset), formed once here (qsum is free
+        // after step 2)
+        float *tabE = qsum, *tabS = qsum + CB;
+        if constexpr (!KDA) {
+            if (tid < CB) {
+                const float G = Gc[tid * LDK];
+                const int f = tfl[tid];
+                tabE[tid] = (f & TF_LAST) ? exp_acc(Gc[pen[tid] * LDK] - G) : 0.f;
+                tabS[tid] = (f & TF_OPEN) ? exp_acc(G) : 0.f;
             }
-            // the piece's decay of the state entering the tile (none left
-            // after a full reset)
-            if (store_ge)
-                *reinterpret_cast<float4 *>(ws.Ge + row(tt) * DK + c0 + g4) =
-                    (f & TF_PRESET) ? make_float4(kGateFloor, kGateFloor, kGateFloor, kGateFloor)
-                                    : Ge;
+            __syncthreads();
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) KhTl[(c0 + i) * LDJ + tt] = kh[i];
-    }
-    if constexpr (MODE == PM_F32) {
-        for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
-            const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
-            const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
-            const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
-            float4 e4;
-            if constexpr (KDA) {
-                const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
-                e4 = (tfl[tt] & TF_OPEN)
-                         ? make_float4(exp_acc(G.x), exp_acc(G.y), exp_acc(G.z), exp_acc(G.w))
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-            } else {
-                const float e = tabS[tt];
-                e4 = make_float4(e, e, e, e);
-            }
-            *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
-                make_float4(qn.x * e4.x, qn.y * e4.y, qn.z * e4.z, qn.w * e4.w);
-        }
-    } else {  // split layout: thread = (row block I, step m, lane), 8 channels
-        for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
-            const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
-            const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
-            const bool open = tfl[tt] & TF_OPEN;
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = Qn[tt * LDK + k0 + e] *
-                       (KDA ? (open ? exp_acc(Gc[tt * LDK + k0 + e]) : 0.f) : tabS[tt]);
-            store_split(ws.Qt + bh * kBlkDK + I * 2048, m, ln, v);
-        }
-    }
-    __syncthreads();
-    if constexpr (MODE == PM_F32) {
-        for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {  // KhT in fragment order
-            const int cg = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
-            const int c = 16 * cg + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
-            *reinterpret_cast<float4 *>(ws.KhT + bh * kBlkDK + 4 * idx) =
-                *reinterpret_cast<const float4 *>(KhTl + c * LDJ + j0);
-        }
-    } else {
-        for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
-            const int cg = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
-            const int c = 16 * cg + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
-            store_split(ws.KhT + bh * kBlkDK + cg * 1024, m, ln, KhTl + c * LDJ + j0);
-        }
-    }
-    __syncthreads();
-    for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
-    // the v loads of step 6 (its thread mapping: channel cc, tokens tc ..
-    // tc + 15) run under steps 4 and 5: the 19-row conv window when the conv
-    // is fused, else the 16 rows of v
-    float xvr[19];
-    if constexpr (CONV) {
-        conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t tk = t0 + min(tc + i, nt - 1);
-            xvr[i] = ld<IOT>(a.v, tk * a.v_stride + h * DK + cc);
-        }
-    }
-    __syncthreads();
 
-    // ---- 4. A and P.  Wave w contracts channel quarter qtr = w & 3 (32
-    //         channels) for the block pairs of two row blocks: even waves
-    //         take row block 3 (J = 0..3) and (0, 0), odd waves row blocks 2
-    //         and 1; that is five pairs each.  A row block's left factors (its k and
-    //         q rows decayed to the block's reference) are formed once for all
-    //         its pairs.  The four quarters' partial sums meet in LDS in a
-    //         fixed order once Q is dead, so the result does not depend on
-    //         which wave finishes first.
-    constexpr int KQ = DK / 4, W = Step<MODE>::W, NS = KQ / Step<MODE>::K;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
-    const int qtr = wv >> 1, grp = wv & 1;  // a quarter's two waves sit on different SIMDs
-    f32x4 pa[5], pp[5];
-    auto rowblock = [&](int I, int nJ, int k0) {
-        const int ti = 16 * I + li;
-        // the row's reference: G_{16I-1} if its piece began before the
-        // sub-block, else 0 (the piece starts inside it)
-        const bool cont = I > 0 && pst[ti] < 16 * I;
-        // sub-block span above kSpanMax: the diagonal pair is formed per element
-        const bool exact_diag =
-            KDA && __builtin_amdgcn_readfirstlane(bigw[2 * I] | bigw[2 * I + 1]);
-        float R[NS][W], fk[NS][W], fq[NS][W], fd[NS][W];
+        // ---- 3. K Gamma_L / Gamma transposed through LDS and the piece's total
+        //         decay (global, at piece ends): thread (token tt = lane, 16
+        //         channels of wave w), so the transposed LDS writes of a wave run
+        //         along the tokens and hit distinct banks; Q Gamma straight to
+        //         global in fragment order
+        const int64_t bh = (int64_t)tile * a.Hv + h;
+        {
+            const int tt = lane, c0 = 16 * wave;
+            const int pen_t = pen[tt], f = tfl[tt];
+            const bool last = f & TF_LAST, store_ge = tt < nt && tt == pen_t;
+            float kh[16];
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
-#pragma unroll
-            for (int e = 0; e < W; ++e) {
-                const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
+            for (int g4 = 0; g4 < 16; g4 += 4) {
+                const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + c0 + g4);
+                const float4 Ge = *reinterpret_cast<const float4 *>(Gc + pen_t * LDK + c0 + g4);
+                const float4 K = *reinterpret_cast<const float4 *>(Kn + tt * LDK + c0 + g4);
                 if constexpr (KDA) {
-                    R[st][e] = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
-                    const float x = Gc[ti * LDK + c] - (cont ? R[st][e] : 0.f);  // <= 0
-                    const float et = exp_acc(fminf(x, kExpClamp));
-                    fk[st][e] = Kn[ti * LDK + c] * et;
-                    fq[st][e] = Qn[ti * LDK + c] * et;
-                    // the diagonal's j-side factor (its column token is this row)
-                    fd[st][e] = Kn[ti * LDK + c] * exp_acc(fminf(-x, kExpClamp));
-                } else {  // GDN: plain k and q rows; the decay is applied per element below
-                    fk[st][e] = Kn[ti * LDK + c];
-                    fq[st][e] = Qn[ti * LDK + c];
-                    fd[st][e] = fk[st][e];
+                    kh[g4] = last ? K.x * exp_acc(Ge.x - G.x) : 0.f;
+                    kh[g4 + 1] = last ? K.y * exp_acc(Ge.y - G.y) : 0.f;
+                    kh[g4 + 2] = last ? K.z * exp_acc(Ge.z - G.z) : 0.f;
+                    kh[g4 + 3] = last ? K.w * exp_acc(Ge.w - G.w) : 0.f;
+                } else {
+                    const float e = tabE[tt];
+                    kh[g4] = K.x * e; kh[g4 + 1] = K.y * e; kh[g4 + 2] = K.z * e; kh[g4 + 3] = K.w * e;
                 }
+                // the piece's decay of the state entering the tile (none left
+                // after a full reset)
+                if (store_ge)
+                    *reinterpret_cast<float4 *>(ws.Ge + row(tt) * DK + c0 + g4) =
+                        (f & TF_PRESET) ? make_float4(kGateFloor, kGateFloor, kGateFloor, kGateFloor)
+                                        : Ge;
             }
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            if (J >= nJ) break;
-            const int tj = 16 * J + li;
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
-            if (J == I && exact_diag) {
-                // exp(G_t - G_j) per element, t = 16I + 4 lq + r, j = tj: the
-                // result tile layout of the matrix-core path; pairs of other
-                // pieces or with j > t are masked later and only kept finite
+            for (int i = 0; i < 16; ++i) KhTl[(c0 + i) * LDJ + tt] = kh[i];
+        }
+        if constexpr (MODE == PM_F32) {
+            for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
+                const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
+                const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
+                const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
+                float4 e4;
+                if constexpr (KDA) {
+                    const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
+                    e4 = (tfl[tt] & TF_OPEN)
+                             ? make_float4(exp_acc(G.x), exp_acc(G.y), exp_acc(G.z), exp_acc(G.w))
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+                } else {
+                    const float e = tabS[tt];
+                    e4 = make_float4(e, e, e, e);
+                }
+                *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
+                    make_float4(qn.x * e4.x, qn.y * e4.y, qn.z * e4.z, qn.w * e4.w);
+            }
+        } else {  // split layout: thread = (row block I, step m, lane), 8 channels
+            for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+                const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
+                const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
+                const bool open = tfl[tt] & TF_OPEN;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = Qn[tt * LDK + k0 + e] *
+                           (KDA ? (open ? exp_acc(Gc[tt * LDK + k0 + e]) : 0.f) : tabS[tt]);
+                store_split(ws.Qt + bh * kBlkDK + I * 2048, m, ln, v);
+            }
+        }
+        __syncthreads();
+        if constexpr (MODE == PM_F32) {
+            for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {  // KhT in fragment order
+                const int cg = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
+                const int c = 16 * cg + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
+                *reinterpret_cast<float4 *>(ws.KhT + bh * kBlkDK + 4 * idx) =
+                    *reinterpret_cast<const float4 *>(KhTl + c * LDJ + j0);
+            }
+        } else {
+            for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+                const int cg = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
+                const int c = 16 * cg + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
+                store_split(ws.KhT + bh * kBlkDK + cg * 1024, m, ln, KhTl + c * LDJ + j0);
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
+        // the v loads of step 6 (its thread mapping: channel cc, tokens tc ..
+        // tc + 15) run under steps 4 and 5: the 19-row conv window when the conv
+        // is fused, else the 16 rows of v
+        float xvr[19];
+        if constexpr (CONV) {
+            conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int64_t tk = t0 + min(tc + i, nt - 1);
+                xvr[i] = ld<IOT>(a.v, tk * a.v_stride + h * DK + cc);
+            }
+        }
+        __syncthreads();
+
+        // ---- 4. A and P.  Wave w contracts channel quarter qtr = w & 3 (32
+        //         channels) for the block pairs of two row blocks: even waves
+        //         take row block 3 (J = 0..3) and (0, 0), odd waves row blocks 2
+        //         and 1; that is five pairs each.  A row block's left factors (its k and
+        //         q rows decayed to the block's reference) are formed once for all
+        //         its pairs.  The four quarters' partial sums meet in LDS in a
+        //         fixed order once Q is dead, so the result does not depend on
+        //         which wave finishes first.
+        constexpr int KQ = DK / 4, W = Step<MODE>::W, NS = KQ / Step<MODE>::K;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
+        const int qtr = wv >> 1, grp = wv & 1;  // a quarter's two waves sit on different SIMDs
+        f32x4 pa[5], pp[5];
+        auto rowblock = [&](int I, int nJ, int k0) {
+            const int ti = 16 * I + li;
+            // the row's reference: G_{16I-1} if its piece began before the
+            // sub-block, else 0 (the piece starts inside it)
+            const bool cont = I > 0 && pst[ti] < 16 * I;
+            // sub-block span above kSpanMax: the diagonal pair is formed per element
+            const bool exact_diag =
+                KDA && __builtin_amdgcn_readfirstlane(bigw[2 * I] | bigw[2 * I + 1]);
+            float R[NS][W], fk[NS][W], fq[NS][W], fd[NS][W];
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+                for (int e = 0; e < W; ++e) {
+                    const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
+                    if constexpr (KDA) {
+                        R[st][e] = I ? Gc[(16 * I - 1) * LDK + c] : 0.f;
+                        const float x = Gc[ti * LDK + c] - (cont ? R[st][e] : 0.f);  // <= 0
+                        const float et = exp_acc(fminf(x, kExpClamp));
+                        fk[st][e] = Kn[ti * LDK + c] * et;
+                        fq[st][e] = Qn[ti * LDK + c] * et;
+                        // the diagonal's j-side factor (its column token is this row)
+                        fd[st][e] = Kn[ti * LDK + c] * exp_acc(fminf(-x, kExpClamp));
+                    } else {  // GDN: plain k and q rows; the decay is applied per element below
+                        fk[st][e] = Kn[ti * LDK + c];
+                        fq[st][e] = Qn[ti * LDK + c];
+                        fd[st][e] = fk[st][e];
+                    }
+                }
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                if (J >= nJ) break;
+                const int tj = 16 * J + li;
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+                if (J == I && exact_diag) {
+                    // exp(G_t - G_j) per element, t = 16I + 4 lq + r, j = tj: the
+                    // result tile layout of the matrix-core path; pairs of other
+                    // pieces or with j > t are masked later and only kept finite
 #pragma unroll 2
-                for (int c = qtr * KQ; c < qtr * KQ + KQ; c += 4) {
-                    const float4 kj = *reinterpret_cast<const float4 *>(Kn + tj * LDK + c);
-                    const float4 gj = *reinterpret_cast<const float4 *>(Gc + tj * LDK + c);
-                    const float kjv[4] = {kj.x, kj.y, kj.z, kj.w}, gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+                    for (int c = qtr * KQ; c < qtr * KQ + KQ; c += 4) {
+                        const float4 kj = *reinterpret_cast<const float4 *>(Kn + tj * LDK + c);
+                        const float4 gj = *reinterpret_cast<const float4 *>(Gc + tj * LDK + c);
+                        const float kjv[4] = {kj.x, kj.y, kj.z, kj.w}, gjv[4] = {gj.x, gj.y, gj.z, gj.w};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tr = 16 * I + 4 * lq + r;
-                        const float4 kt = *reinterpret_cast<const float4 *>(Kn + tr * LDK + c);
-                        const float4 qt = *reinterpret_cast<const float4 *>(Qn + tr * LDK + c);
-                        const float4 gt = *reinterpret_cast<const float4 *>(Gc + tr * LDK + c);
-                        const float ktv[4] = {kt.x, kt.y, kt.z, kt.w};
-                        const float qtv[4] = {qt.x, qt.y, qt.z, qt.w};
-                        const float gtv[4] = {gt.x, gt.y, gt.z, gt.w};
+                        for (int r = 0; r < 4; ++r) {
+                            const int tr = 16 * I + 4 * lq + r;
+                            const float4 kt = *reinterpret_cast<const float4 *>(Kn + tr * LDK + c);
+                            const float4 qt = *reinterpret_cast<const float4 *>(Qn + tr * LDK + c);
+                            const float4 gt = *reinterpret_cast<const float4 *>(Gc + tr * LDK + c);
+                            const float ktv[4] = {kt.x, kt.y, kt.z, kt.w};
+                            const float qtv[4] = {qt.x, qt.y, qt.z, qt.w};
+                            const float gtv[4] = {gt.x, gt.y, gt.z, gt.w};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float kd = kjv[e] * exp_acc(fminf(gtv[e] - gjv[e], 0.f));
-                            accA[r] = fmaf(ktv[e], kd, accA[r]);
-                            accP[r] = fmaf(qtv[e], kd, accP[r]);
+                            for (int e = 0; e < 4; ++e) {
+                                const float kd = kjv[e] * exp_acc(fminf(gtv[e] - gjv[e], 0.f));
+                                accA[r] = fmaf(ktv[e], kd, accA[r]);
+                                accP[r] = fmaf(qtv[e], kd, accP[r]);
+                            }
                         }
                     }
-                }
-            } else {
-#pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    float fj[W];
-#pragma unroll
-                    for (int e = 0; e < W; ++e) {
-                        const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
-                        fj[e] = J == I ? fd[st][e]
-                              : KDA ? Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp))
-                                    : Kn[tj * LDK + c];
-                    }
-                    mma_step<MODE>(accA, fk[st], fj);
-                    mma_step<MODE>(accP, fq[st], fj);
-                }
-            }
-            pa[k0 + J] = accA;
-            pp[k0 + J] = accP;
-        }
-    };
-    if (grp == 0) {
-        rowblock(3, 4, 0);
-        rowblock(0, 1, 4);
-    } else {
-        rowblock(2, 3, 0);
-        rowblock(1, 2, 3);
-    }
-    // the wave's pairs in the order of pa / pp: (3,0..3), (0,0) for group 0;
-    // (2,0..2), (1,0..1) for group 1
-    auto pairI = [&](int k) { return grp ? (k < 3 ? 2 : 1) : (k < 4 ? 3 : 0); };
-    auto pairJ = [&](int k) { return grp ? (k < 3 ? k : k - 3) : (k < 4 ? k : 0); };
-    __syncthreads();
-    float *Ps = Qn;            // P [64][LDJ]; q_hat is no longer read
-    float *Ps2 = Qn + CB * LDJ;  // second half of Q's space: P partial of quarters 2 + 3
-    float *Nm2 = Tm;           // A partial of quarters 2 + 3 (T's lower tiles, rewritten in step 5)
-    // The quarters' partial sums meet in a fixed order, (q0 + q1) + (q2 + q3):
-    // quarters 0 and 2 store theirs, quarters 1 and 3 add theirs in place,
-    // then every thread combines the two halves of its elements.
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        if ((qtr & 1) == st) {
-            float *dA = qtr < 2 ? Nm : Nm2, *dP = qtr < 2 ? Ps : Ps2;
-            float prevA[5][4], prevP[5][4];
-#pragma unroll
-            for (int k = 0; k < 5; ++k)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
-                    prevA[k][r] = st ? dA[at] : 0.f;
-                    prevP[k][r] = st ? dP[at] : 0.f;
-                }
-#pragma unroll
-            for (int k = 0; k < 5; ++k)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
-                    dA[at] = st ? prevA[k][r] + pa[k][r] : pa[k][r];
-                    dP[at] = st ? prevP[k][r] + pp[k][r] : pp[k][r];
-                }
-        }
-        __syncthreads();
-    }
-    // A keeps beta[t] A where j < t in the same piece (else 0), P keeps
-    // j <= t in the same piece (GDN: also the element's decay
-    // exp(G_t - G_j), <= 1 where it is kept); upper tiles of P are zero
-    for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {
-        const int tt = idx / CB, j = idx % CB, at = tt * LDJ + j;
-        if ((j >> 4) > (tt >> 4)) {
-            Ps[at] = 0.f;
-            continue;
-        }
-        float av = Nm[at] + Nm2[at], pv = Ps[at] + Ps2[at];
-        if constexpr (!KDA) {
-            const float e = exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
-            av *= e;
-            pv *= e;
-        }
-        const bool same = j >= pst[tt] && tt < nt;
-        Nm[at] = same && j < tt ? bet[tt] * av : 0.f;
-        Ps[at] = same && j <= tt ? pv : 0.f;
-    }
-    __syncthreads();
-
-    // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
-    //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
-    //         blocks level by level: T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ.
-    if (wave < 4 && lane < 16) {
-        const int I = wave, c = lane;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int j = 0; j < r; ++j) s = fmaf(Nm[(16 * I + r) * LDJ + 16 * I + j], x[j], s);
-            x[r] = r == c ? 1.f : (r < c ? 0.f : -s);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
-    }
-    __syncthreads();
-    if (wave >= 4) {  // P to global in fragment order while waves 0..3 run the levels
-        if constexpr (MODE == PM_F32) {
-            for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
-                const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
-                const int tt = 16 * I + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
-                *reinterpret_cast<float4 *>(ws.P + bh * kBlkCB + 4 * idx) =
-                    *reinterpret_cast<const float4 *>(Ps + tt * LDJ + j0);
-            }
-        } else {
-            for (int idx = tid - 256; idx < kBlkCB / 8; idx += 256) {
-                const int I = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
-                const int tt = 16 * I + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
-                store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
-            }
-        }
-    }
-    float *ws16 = scr + wave * 16 * 17;
-    for (int lev = 1; lev <= 3; ++lev) {
-        const int I = wave, J = wave - lev;
-        if (wave < 4 && J >= 0) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int K = J; K < I; ++K)
-#pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4)
-                    acc = mfma4(Nm[(16 * I + li) * LDJ + 16 * K + k0 + lq],
-                                Tm[(16 * K + k0 + lq) * LDJ + 16 * J + li], acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ws16[(4 * lq + r) * 17 + li] = acc[r];
-            __builtin_amdgcn_wave_barrier();
-            f32x4 t2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 4)
-                t2 = mfma4(Tm[(16 * I + li) * LDJ + 16 * I + k0 + lq], ws16[(k0 + lq) * 17 + li], t2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Tm[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = -t2[r];
-        }
-        __syncthreads();
-    }
-
-    // ---- 6. right-hand sides, transposed: (beta K Gamma)^T and (beta V)^T.
-    //         In bf16x3 mode they and T are stored split (bf16 hi / lo rows),
-    //         so step 7 reads its operands without converting them; T goes
-    //         to N's space, which is dead.
-    if constexpr (MODE != PM_F32) {
-        const int row = tid >> 3, k0 = 8 * (tid & 7);
-        const float4 t0v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0);
-        const float4 t1v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0 + 4);
-        const float tv[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
-        uint4 hi, lo;
-        split8(tv, hi, lo);
-        *reinterpret_cast<uint4 *>(Nm + row * LDJ + k0 / 2) = hi;
-        *reinterpret_cast<uint4 *>(Nm + row * LDJ + 32 + k0 / 2) = lo;
-    }
-    {
-        const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
-        float xk[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int tt = tq + i;
-            if constexpr (KDA) {
-                xk[i] = (tfl[tt] & TF_OPEN) ? bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c])
-                                            : 0.f;
-            } else {
-                xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
-            }
-        }
-        __syncthreads();  // Qn is about to be overwritten
-        if constexpr (MODE == PM_F32) {
-#pragma unroll
-            for (int i = 0; i < 16; i += 4)
-                *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + i) =
-                    make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
-        } else {
-            store_row_split16(XtK + c * LDJ, tq, xk);
-        }
-    }
-    {   // thread (channel c, 16 tokens): rows of (beta V)^T, loads coalesced over c
-        const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
-        float xv[16];
-        if constexpr (CONV) {  // c, tq are cc, tc
-            conv_apply(xv, xvr, a, t0, tq, 2 * a.Hqk * DK + h * DK + c, sst, ssl);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xv[i] *= bet[tq + i];  // bet = 0 past nt
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xv[i] = bet[tq + i] * xvr[i];  // bet = 0 past nt
-        }
-        __syncthreads();  // Kn is free
-        if constexpr (MODE == PM_F32) {
-#pragma unroll
-            for (int i = 0; i < 16; i += 4)
-                *reinterpret_cast<float4 *>(XtV + c * LDJ + tq + i) =
-                    make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
-        } else {
-            store_row_split16(XtV + c * LDJ, tq, xv);
-        }
-    }
-    __syncthreads();
-
-    // ---- 7. U = T (beta V) and W = T (beta K Gamma): wave w owns output
-    //         columns 16w .. 16w + 15 of both, for the four token blocks.
-    //         U leaves in the result layout; W is staged in LDS (the decay
-    //         cumsum is dead) and leaves in fragment order.
-    float *Wst = Gc;  // [64][LDK]
-    {
-        const int C = wave;
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const float *Xt = which ? XtK : XtV;
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (MODE == PM_F32) {
-                    const float *Trow = Tm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
-                    auto fa = [&](int, int j) { return Trow[j]; };
-                    auto fb = [&](int, int j) { return Xrow[j]; };
-                    if (I < 2) mma_gen<MODE, 32>(acc, lq, fa, fb);  // T rows < 32: columns < 32
-                    else mma_gen<MODE, 64>(acc, lq, fa, fb);
-                } else {  // split rows: step m, lane quad lq covers columns 32 m + 8 lq ..
-                    const float *Trow = Nm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
-#pragma unroll
-                    for (int m = 0; m < (I < 2 ? 1 : 2); ++m) {
-                        const int o = 16 * m + 4 * lq;
-                        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(Trow + o);
-                        const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(Trow + 32 + o);
-                        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(Xrow + o);
-                        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(Xrow + 32 + o);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-                    }
-                }
-                if (which == 0) {
-                    *reinterpret_cast<f32x4 *>(ws.U + bh * kBlkDK + fidx(I * 8 + C, lane)) = acc;
                 } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Wst[(16 * I + 4 * lq + r) * LDK + 16 * C + li] = acc[r];
+                    for (int st = 0; st < NS; ++st) {
+                        float fj[W];
+#pragma unroll
+                        for (int e = 0; e < W; ++e) {
+                            const int c = qtr * KQ + frag_k<MODE, KQ>(lq, st * W + e);
+                            fj[e] = J == I ? fd[st][e]
+                                  : KDA ? Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp))
+                                        : Kn[tj * LDK + c];
+                        }
+                        mma_step<MODE>(accA, fk[st], fj);
+                        mma_step<MODE>(accP, fq[st], fj);
+                    }
+                }
+                pa[k0 + J] = accA;
+                pp[k0 + J] = accP;
+            }
+        };
+        if (grp == 0) {
+            rowblock(3, 4, 0);
+            rowblock(0, 1, 4);
+        } else {
+            rowblock(2, 3, 0);
+            rowblock(1, 2, 3);
+        }
+        // the wave's pairs in the order of pa / pp: (3,0..3), (0,0) for group 0;
+        // (2,0..2), (1,0..1) for group 1
+        auto pairI = [&](int k) { return grp ? (k < 3 ? 2 : 1) : (k < 4 ? 3 : 0); };
+        auto pairJ = [&](int k) { return grp ? (k < 3 ? k : k - 3) : (k < 4 ? k : 0); };
+        __syncthreads();
+        float *Ps = Qn;            // P [64][LDJ]; q_hat is no longer read
+        float *Ps2 = Qn + CB * LDJ;  // second half of Q's space: P partial of quarters 2 + 3
+        float *Nm2 = Tm;           // A partial of quarters 2 + 3 (T's lower tiles, rewritten in step 5)
+        // The quarters' partial sums meet in a fixed order, (q0 + q1) + (q2 + q3):
+        // quarters 0 and 2 store theirs, quarters 1 and 3 add theirs in place,
+        // then every thread combines the two halves of its elements.
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            if ((qtr & 1) == st) {
+                float *dA = qtr < 2 ? Nm : Nm2, *dP = qtr < 2 ? Ps : Ps2;
+                float prevA[5][4], prevP[5][4];
+#pragma unroll
+                for (int k = 0; k < 5; ++k)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
+                        prevA[k][r] = st ? dA[at] : 0.f;
+                        prevP[k][r] = st ? dP[at] : 0.f;
+                    }
+#pragma unroll
+                for (int k = 0; k < 5; ++k)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
+                        dA[at] = st ? prevA[k][r] + pa[k][r] : pa[k][r];
+                        dP[at] = st ? prevP[k][r] + pp[k][r] : pp[k][r];
+                    }
+            }
+            __syncthreads();
+        }
+        // A keeps beta[t] A where j < t in the same piece (else 0), P keeps
+        // j <= t in the same piece (GDN: also the element's decay
+        // exp(G_t - G_j), <= 1 where it is kept); upper tiles of P are zero
+        for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {
+            const int tt = idx / CB, j = idx % CB, at = tt * LDJ + j;
+            if ((j >> 4) > (tt >> 4)) {
+                Ps[at] = 0.f;
+                continue;
+            }
+            float av = Nm[at] + Nm2[at], pv = Ps[at] + Ps2[at];
+            if constexpr (!KDA) {
+                const float e = exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
+                av *= e;
+                pv *= e;
+            }
+            const bool same = j >= pst[tt] && tt < nt;
+            Nm[at] = same && j < tt ? bet[tt] * av : 0.f;
+            Ps[at] = same && j <= tt ? pv : 0.f;
+        }
+        __syncthreads();
+
+        // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
+        //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
+        //         blocks level by level: T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ.
+        if (wave < 4 && lane < 16) {
+            const int I = wave, c = lane;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < r; ++j) s = fmaf(Nm[(16 * I + r) * LDJ + 16 * I + j], x[j], s);
+                x[r] = r == c ? 1.f : (r < c ? 0.f : -s);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
+        }
+        __syncthreads();
+        if (wave >= 4) {  // P to global in fragment order while waves 0..3 run the levels
+            if constexpr (MODE == PM_F32) {
+                for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
+                    const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
+                    const int tt = 16 * I + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
+                    *reinterpret_cast<float4 *>(ws.P + bh * kBlkCB + 4 * idx) =
+                        *reinterpret_cast<const float4 *>(Ps + tt * LDJ + j0);
+                }
+            } else {
+                for (int idx = tid - 256; idx < kBlkCB / 8; idx += 256) {
+                    const int I = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
+                    const int tt = 16 * I + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
+                    store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
                 }
             }
         }
-    }
-    __syncthreads();
-    if constexpr (MODE == PM_F32) {
-        for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
-            const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
-            const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
-            *reinterpret_cast<float4 *>(ws.W + bh * kBlkDK + 4 * idx) =
-                *reinterpret_cast<const float4 *>(Wst + tt * LDK + k0);
+        float *ws16 = scr + wave * 16 * 17;
+        for (int lev = 1; lev <= 3; ++lev) {
+            const int I = wave, J = wave - lev;
+            if (wave < 4 && J >= 0) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < I; ++K)
+#pragma unroll
+                    for (int k0 = 0; k0 < 16; k0 += 4)
+                        acc = mfma4(Nm[(16 * I + li) * LDJ + 16 * K + k0 + lq],
+                                    Tm[(16 * K + k0 + lq) * LDJ + 16 * J + li], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ws16[(4 * lq + r) * 17 + li] = acc[r];
+                __builtin_amdgcn_wave_barrier();
+                f32x4 t2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    t2 = mfma4(Tm[(16 * I + li) * LDJ + 16 * I + k0 + lq], ws16[(k0 + lq) * 17 + li], t2);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tm[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = -t2[r];
+            }
+            __syncthreads();
         }
-    } else {
-        for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
-            const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
-            const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
-            store_split(ws.W + bh * kBlkDK + I * 2048, m, ln, Wst + tt * LDK + k0);
+
+        // ---- 6. right-hand sides, transposed: (beta K Gamma)^T and (beta V)^T.
+        //         In bf16x3 mode they and T are stored split (bf16 hi / lo rows),
+        //         so step 7 reads its operands without converting them; T goes
+        //         to N's space, which is dead.
+        if constexpr (MODE != PM_F32) {
+            const int row = tid >> 3, k0 = 8 * (tid & 7);
+            const float4 t0v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0);
+            const float4 t1v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0 + 4);
+            const float tv[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+            uint4 hi, lo;
+            split8(tv, hi, lo);
+            *reinterpret_cast<uint4 *>(Nm + row * LDJ + k0 / 2) = hi;
+            *reinterpret_cast<uint4 *>(Nm + row * LDJ + 32 + k0 / 2) = lo;
+        }
+        {
+            const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
+            float xk[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int tt = tq + i;
+                if constexpr (KDA) {
+                    xk[i] = (tfl[tt] & TF_OPEN) ? bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c])
+                                                : 0.f;
+                } else {
+                    xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
+                }
+            }
+            __syncthreads();  // Qn is about to be overwritten
+            if constexpr (MODE == PM_F32) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 4)
+                    *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + i) =
+                        make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+            } else {
+                store_row_split16(XtK + c * LDJ, tq, xk);
+            }
+        }
+        {   // thread (channel c, 16 tokens): rows of (beta V)^T, loads coalesced over c
+            const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
+            float xv[16];
+            if constexpr (CONV) {  // c, tq are cc, tc
+                conv_apply(xv, xvr, a, t0, tq, 2 * a.Hqk * DK + h * DK + c, sst, ssl);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xv[i] *= bet[tq + i];  // bet = 0 past nt
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xv[i] = bet[tq + i] * xvr[i];  // bet = 0 past nt
+            }
+            __syncthreads();  // Kn is free
+            if constexpr (MODE == PM_F32) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 4)
+                    *reinterpret_cast<float4 *>(XtV + c * LDJ + tq + i) =
+                        make_float4(xv[i], xv[i + 1], xv[i + 2], xv[i + 3]);
+            } else {
+                store_row_split16(XtV + c * LDJ, tq, xv);
+            }
+        }
+        __syncthreads();
+
+        // ---- 7. U = T (beta V) and W = T (beta K Gamma): wave w owns output
+        //         columns 16w .. 16w + 15 of both, for the four token blocks.
+        //         U leaves in the result layout; W is staged in LDS (the decay
+        //         cumsum is dead) and leaves in fragment order.
+        float *Wst = Gc;  // [64][LDK]
+        {
+            const int C = wave;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                const float *Xt = which ? XtK : XtV;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (MODE == PM_F32) {
+                        const float *Trow = Tm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
+                        auto fa = [&](int, int j) { return Trow[j]; };
+                        auto fb = [&](int, int j) { return Xrow[j]; };
+                        if (I < 2) mma_gen<MODE, 32>(acc, lq, fa, fb);  // T rows < 32: columns < 32
+                        else mma_gen<MODE, 64>(acc, lq, fa, fb);
+                    } else {  // split rows: step m, lane quad lq covers columns 32 m + 8 lq ..
+                        const float *Trow = Nm + (16 * I + li) * LDJ, *Xrow = Xt + (16 * C + li) * LDJ;
+#pragma unroll
+                        for (int m = 0; m < (I < 2 ? 1 : 2); ++m) {
+                            const int o = 16 * m + 4 * lq;
+                            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(Trow + o);
+                            const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(Trow + 32 + o);
+                            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(Xrow + o);
+                            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(Xrow + 32 + o);
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+                        }
+                    }
+                    if (which == 0) {
+                        *reinterpret_cast<f32x4 *>(ws.U + bh * kBlkDK + fidx(I * 8 + C, lane)) = acc;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Wst[(16 * I + 4 * lq + r) * LDK + 16 * C + li] = acc[r];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // fixed trip counts, unrolled (the thread index is opaque here, so a
+        // strided loop would not be)
+        static_assert(kBlkDK % (8 * kIntraThreads) == 0, "whole W store rounds");
+        if constexpr (MODE == PM_F32) {
+#pragma unroll
+            for (int r = 0; r < kBlkDK / 4 / kIntraThreads; ++r) {
+                const int idx = tid + r * kIntraThreads;
+                const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
+                const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
+                *reinterpret_cast<float4 *>(ws.W + bh * kBlkDK + 4 * idx) =
+                    *reinterpret_cast<const float4 *>(Wst + tt * LDK + k0);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < kBlkDK / 8 / kIntraThreads; ++r) {
+                const int idx = tid + r * kIntraThreads;
+                const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
+                const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
+                store_split(ws.W + bh * kBlkDK + I * 2048, m, ln, Wst + tt * LDK + k0);
+            }
         }
     }
 }
@@ -1474,6 +1594,22 @@ __global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain
     }
 }
 
+// Compute units of the current device, cached per device: the persistent
+// grid of kernel 1 (one workgroup per CU, its LDS allows no more).
+static int cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <typename IOT, typename ST, int MODE>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
@@ -1489,7 +1625,10 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     }();
     (void)attr_done;
     if (a.T > 0) {
-        const dim3 g1((unsigned)((a.T + CB - 1) / CB), (unsigned)a.Hv);
+        // one workgroup per item with the fused conv; without it, the
+        // persistent grid that loads an item's inputs under the previous one
+        const int64_t nitems = (int64_t)((a.T + CB - 1) / CB) * a.Hv;
+        const dim3 g1((unsigned)(a.conv ? nitems : std::min<int64_t>(nitems, cu_count())));
         const dim3 b1(kIntraThreads);
         if (a.kda && a.conv)
             hipLaunchKernelGGL((prefill_intra_kernel<IOT, true, MODE, true>), g1, b1, kIntraLds, stream, a);
