@@ -913,8 +913,7 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
     // ---- 1. staging: rawk / rawv rows (16-byte loads), gates, betas
     constexpr int VI = V16<IOT>::N, GI = HD / VI, NI = kChunk * 2 * GI, II = (NI + NT - 1) / NT;
     uint4 xr[II];
-    float4 g4[kChunk];
-    float bv = 0.f;
+    float gv[kChunk], bv = 0.f;
 #pragma unroll
     for (int q = 0; q < II; ++q) {
         const int i = min(tid + q * NT, NI - 1), grp = i % GI, which = (i / GI) % 2;
@@ -922,21 +921,30 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
         xr[q] = *reinterpret_cast<const uint4 *>(static_cast<const IOT *>(which ? R.rawv : R.rawk) +
                                                  ring_at(slot, a.Hv, R.L, h, pos_of(t), HD) + grp * VI);
     }
-    // the betas before the gates: wave 0 waits for its first gate load at
-    // the end of the branch below, and its beta load is then already out
     if (tid < kChunk) bv = R.beta[ring_at(slot, a.Hv, R.L, h, pos_of(min(tid, na - 1)), 1)];
-    if (tid < 32) {  // lane l: channels 4 l .. 4 l + 3 of every step
+    if (tid < HD) {  // thread c: channel c of every step
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
             const int pos = pos_of(min(t, na - 1));
-            if constexpr (KDA) {
-                g4[t] = *reinterpret_cast<const float4 *>(R.g + ring_at(slot, a.Hv, R.L, h, pos, HD) + 4 * tid);
-            } else {
-                const float g1 = R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
-                g4[t] = make_float4(g1, g1, g1, g1);
-            }
+            gv[t] = KDA ? R.g[ring_at(slot, a.Hv, R.L, h, pos, HD) + tid] : R.g[ring_at(slot, a.Hv, R.L, h, pos, 1)];
         }
     }
+    // The state, issued right behind the ring records: vector loads return
+    // in order, so the staging below waits for its own data only and the
+    // state streams in under phase 2.  Lane (m, g) of wave w: row 16 w + m,
+    // columns 32 c + 8 g .. 32 c + 8 g + 7 for c < 4.
+    const char *Sb = static_cast<const char *>(a.ssm_pool) +
+                     ((int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD) * sizeof(ST);
+    const char *Srow = Sb + (int64_t)(16 * wave + m) * HD * sizeof(ST);
+    constexpr int LPB = kBf16 ? 1 : 2;   // 16-byte loads per 8-column block
+    uint4 fr[4][LPB];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int l = 0; l < LPB; ++l)
+            fr[c][l] = ld_stream(Srow + (int64_t)(32 * c + 8 * g) * sizeof(ST) + 16 * l);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < II; ++q) {
         const int i = tid + q * NT, grp = i % GI, which = (i / GI) % 2, t = i / (2 * GI);
@@ -950,18 +958,16 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
         }
     }
     if (tid < kChunk) bsh[tid] = bv;
-    if (tid < 32) {
-        float4 G = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < HD) {
+        float G = 0.f;
 #pragma unroll
         for (int t = 0; t < kChunk; ++t) {
             if (t < na) {
-                G.x += fmaxf(g4[t].x, kGFloor); G.y += fmaxf(g4[t].y, kGFloor);
-                G.z += fmaxf(g4[t].z, kGFloor); G.w += fmaxf(g4[t].w, kGFloor);
-                *reinterpret_cast<float4 *>(&gsh[t][4 * tid]) = G;
+                G += fmaxf(gv[t], kGFloor);
+                gsh[t][tid] = G;
             }
         }
-        *reinterpret_cast<float4 *>(&Ee[4 * tid]) =
-            make_float4(fast_exp(G.x), fast_exp(G.y), fast_exp(G.z), fast_exp(G.w));
+        Ee[tid] = fast_exp(G);
     }
     for (int i = tid; i < kChunk * (HD / 4); i += NT) {  // rows past na are zero
         const int t = i / (HD / 4), c = 4 * (i % (HD / 4));
@@ -978,20 +984,7 @@ __global__ void __launch_bounds__(kCommitNT) commit_kernel(CommitArgs a)
     }
     __syncthreads();
 
-    // ---- 2. the state (streams in under this phase); per step wave: the k
-    //      norm, the row of K~ and the row of KD
-    const char *Sb = static_cast<const char *>(a.ssm_pool) +
-                     ((int64_t)slot * a.ssm_stride + (int64_t)h * HD * HD) * sizeof(ST);
-    const char *Srow = Sb + (int64_t)(16 * wave + m) * HD * sizeof(ST);
-    constexpr int LPB = kBf16 ? 1 : 2;   // 16-byte loads per 8-column block
-    uint4 fr[4][LPB];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int l = 0; l < LPB; ++l)
-            fr[c][l] = ld_stream(Srow + (int64_t)(32 * c + 8 * g) * sizeof(ST) + 16 * l);
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- 2. per step wave: the k norm, the row of K~ and the row of KD
     for (int t = wave; t < na; t += NT / 64) {
         const float2 kr = *reinterpret_cast<const float2 *>(&ks[t][2 * lane]);
         const float ik = __builtin_amdgcn_rsqf(wave_sum(fmaf(kr.y, kr.y, kr.x * kr.x)) + a.eps);
