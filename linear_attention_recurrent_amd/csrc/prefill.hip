@@ -830,8 +830,12 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                         const float et = exp_acc(fminf(x, kExpClamp));
                         fk[st][e] = Kn[ti * LDK + c] * et;
                         fq[st][e] = Qn[ti * LDK + c] * et;
-                        // the diagonal's j-side factor (its column token is this row)
-                        fd[st][e] = Kn[ti * LDK + c] * exp_acc(fminf(-x, kExpClamp));
+                        // the diagonal's j-side factor (its column token is
+                        // this row), e^-x as the reciprocal of e^x: it is read
+                        // only when the sub-block's span is at most kSpanMax,
+                        // where x >= -kSpanMax (flagged blocks take the
+                        // per-element path below)
+                        fd[st][e] = Kn[ti * LDK + c] * __builtin_amdgcn_rcpf(et);
                     } else {  // GDN: plain k and q rows; the decay is applied per element below
                         fk[st][e] = Kn[ti * LDK + c];
                         fq[st][e] = Qn[ti * LDK + c];
