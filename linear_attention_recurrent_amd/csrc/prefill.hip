@@ -323,11 +323,16 @@ __device__ __forceinline__ void conv_rows(float *xr, const PrefillArgs &a, int t
     }
 }
 
-__device__ __forceinline__ void conv_apply(float *y, const float *xr, const PrefillArgs &a, int t0,
-                                           int tq, int ch, const int *sst, const int *ssl)
+// The conv weights and bias of channel ch.
+__device__ __forceinline__ void conv_weights(float4 &wc, float &bias, const PrefillArgs &a, int ch)
 {
-    const float4 wc = reinterpret_cast<const float4 *>(a.w)[ch];
-    const float bias = a.bias ? a.bias[ch] : 0.f;
+    wc = reinterpret_cast<const float4 *>(a.w)[ch];
+    bias = a.bias ? a.bias[ch] : 0.f;
+}
+__device__ __forceinline__ void conv_apply(float *y, const float *xr, const PrefillArgs &a, int t0,
+                                           int tq, int ch, const int *sst, const int *ssl,
+                                           float4 wc, float bias)
+{
     const int s_first = wave_uniform(sst[tq]), s_last = wave_uniform(sst[tq + 15]);
     if (s_first == s_last && s_first <= t0 + tq - 3) {
 #pragma unroll
@@ -435,6 +440,37 @@ __device__ __forceinline__ void intra_unpack(const IntraIn<IOT, KDA> &r, float *
     bt = r.bt;
 }
 
+// With the fused conv: the q and k channels' 19-row conv windows of thread
+// (channel cc, tokens tc .. tc + 15), and the gates and beta of thread
+// (token t, 16-channel chunk c0).
+template <typename IOT, bool KDA> struct IntraConvIn {
+    float xq[19], xk[19];
+    float4 wq, wk;  // the two channels' conv weights and biases
+    float bq, bk;
+    float4 g[KDA ? 4 : 1];
+    float bt;
+};
+template <typename IOT, bool KDA>
+__device__ __forceinline__ void intra_issue_conv(IntraConvIn<IOT, KDA> &r, const PrefillArgs &a,
+                                                 int item, int t, int c0, int cc, int tc)
+{
+    const int tile = item / a.Hv, h = item - tile * a.Hv, kh = h / a.G;
+    const int t0 = tile * CB, nt = min(CB, a.T - t0);
+    const int64_t tok = t0 + min(t, nt - 1);
+    if constexpr (KDA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.g[i] = reinterpret_cast<const float4 *>(a.g + (tok * a.Hv + h) * DK + c0)[i];
+    } else {
+        r.g[0].x = a.g[tok * a.Hv + h];
+    }
+    r.bt = a.beta[tok * a.Hv + h];
+    conv_weights(r.wq, r.bq, a, kh * DK + cc);
+    conv_weights(r.wk, r.bk, a, a.Hqk * DK + kh * DK + cc);
+    conv_rows<IOT>(r.xq, a, t0, tc, kh * DK + cc);  // both windows in flight together
+    conv_rows<IOT>(r.xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
+}
+
 template <typename IOT, bool KDA, int MODE, bool CONV>
 __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArgs a)
 {
@@ -514,9 +550,15 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         return r;
     };
     Seq nseq = find_seq_item(blockIdx.x, threadIdx.x >> 3);
-    // the next item's inputs (without the fused conv), phase 1's mapping
+    // the next item's inputs: phase 1's mapping, and with the fused conv the
+    // conv windows in its (channel, 16 tokens) mapping
     IntraIn<IOT, KDA> nx;
-    if constexpr (!CONV) intra_issue(nx, a, blockIdx.x, threadIdx.x >> 3, 16 * (threadIdx.x & 7));
+    IntraConvIn<IOT, KDA> ncx;
+    if constexpr (CONV)
+        intra_issue_conv(ncx, a, blockIdx.x, threadIdx.x >> 3, 16 * (threadIdx.x & 7),
+                         threadIdx.x & (DK - 1), 16 * (threadIdx.x >> 7));
+    else
+        intra_issue(nx, a, blockIdx.x, threadIdx.x >> 3, 16 * (threadIdx.x & 7));
     // The first item waits for its loads here.  Later items find theirs
     // complete (see the end of step 1).  Without this wait the loop head
     // would merge the two cases and wait for every memory operation at each
@@ -548,18 +590,20 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         const int cc = tid & (DK - 1), tc = 16 * (tid >> 7);
         float xq[19], xk[19];
         if constexpr (CONV) {
-            const int64_t tok = t0 + min(t, nt - 1);
-            if constexpr (KDA) {
-                load16<float>(gv, a.g + (tok * a.Hv + h) * DK + c0);
-            } else {
-                const float g1 = a.g[tok * a.Hv + h];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) gv[e] = g1;
+            for (int r = 0; r < 19; ++r) {
+                xq[r] = ncx.xq[r];
+                xk[r] = ncx.xk[r];
             }
-            bt = a.beta[tok * a.Hv + h];
-            // both windows in flight together
-            conv_rows<IOT>(xq, a, t0, tc, kh * DK + cc);
-            conv_rows<IOT>(xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 g = ncx.g[KDA ? i : 0];
+                gv[4 * i] = g.x;
+                gv[4 * i + 1] = KDA ? g.y : g.x;
+                gv[4 * i + 2] = KDA ? g.z : g.x;
+                gv[4 * i + 3] = KDA ? g.w : g.x;
+            }
+            bt = ncx.bt;
         } else {
             intra_unpack(nx, qv, kv, gv, bt);
         }
@@ -574,10 +618,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             }
             __syncthreads();
             float y[16];
-            conv_apply(y, xq, a, t0, tc, kh * DK + cc, sst, ssl);
+            conv_apply(y, xq, a, t0, tc, kh * DK + cc, sst, ssl, ncx.wq, ncx.bq);
 #pragma unroll
             for (int i = 0; i < 16; ++i) Qn[(tc + i) * LDK + cc] = y[i];
-            conv_apply(y, xk, a, t0, tc, a.Hqk * DK + kh * DK + cc, sst, ssl);
+            conv_apply(y, xk, a, t0, tc, a.Hqk * DK + kh * DK + cc, sst, ssl, ncx.wk, ncx.bk);
 #pragma unroll
             for (int i = 0; i < 16; ++i) Kn[(tc + i) * LDK + cc] = y[i];
             __syncthreads();
@@ -624,7 +668,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         {
             const int next = min(item + (int)gridDim.x, nitems - 1);
             nseq = find_seq_item(next, t);
-            if constexpr (!CONV) intra_issue(nx, a, next, t, c0);
+            if constexpr (CONV) intra_issue_conv(ncx, a, next, t, c0, cc, tc);
+            else intra_issue(nx, a, next, t, c0);
         }
         __syncthreads();
         // sub-pieces: with a full reset in the tile (rm, the same in every wave),
@@ -1052,7 +1097,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
             float xv[16];
             if constexpr (CONV) {  // c, tq are cc, tc
-                conv_apply(xv, xvr, a, t0, tq, 2 * a.Hqk * DK + h * DK + c, sst, ssl);
+                float4 wv;
+                float bv;
+                conv_weights(wv, bv, a, 2 * a.Hqk * DK + h * DK + c);
+                conv_apply(xv, xvr, a, t0, tq, 2 * a.Hqk * DK + h * DK + c, sst, ssl, wv, bv);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) xv[i] *= bet[tq + i];  // bet = 0 past nt
             } else {
@@ -1629,10 +1677,9 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     }();
     (void)attr_done;
     if (a.T > 0) {
-        // one workgroup per item with the fused conv; without it, the
-        // persistent grid that loads an item's inputs under the previous one
+        // the persistent grid that loads an item's inputs under the previous one
         const int64_t nitems = (int64_t)((a.T + CB - 1) / CB) * a.Hv;
-        const dim3 g1((unsigned)(a.conv ? nitems : std::min<int64_t>(nitems, cu_count())));
+        const dim3 g1((unsigned)std::min<int64_t>(nitems, cu_count()));
         const dim3 b1(kIntraThreads);
         if (a.kda && a.conv)
             hipLaunchKernelGGL((prefill_intra_kernel<IOT, true, MODE, true>), g1, b1, kIntraLds, stream, a);
