@@ -374,10 +374,11 @@ enum { TF_OPEN = 1,      // no full reset between the piece start and the token
        TF_RESET = 8 };   // the token itself resets every key channel
 
 // Kernel 1 runs persistently: a grid of one workgroup per CU walks the
-// (tile, head) items, item = tile * Hv + head.  Without the fused conv, the
-// raw inputs phase 1 reads (thread (token t, 16-channel chunk c0): q, k, the
-// gates and beta) are loaded for the next item while the current one runs,
-// so an item starts on inputs already in registers.
+// (tile, head) items, item = tile * Hv + head.  The raw inputs phase 1 reads
+// (thread (token t, 16-channel chunk c0): q, k, the gates and beta; with the
+// fused conv the q and k conv windows and weights instead of q and k) are
+// loaded for the next item while the current one runs, so an item starts on
+// inputs already in registers.
 template <typename IOT, bool KDA> struct IntraIn {
     static constexpr int QN = sizeof(IOT);  // 16-byte words per 16 q (or k) elements
     uint4 q[QN], k[QN];
