@@ -550,22 +550,41 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
         return r;
     };
-    Seq nseq = find_seq_item(blockIdx.x, threadIdx.x >> 3);
+    // The items of workgroup w: i0 + k * stride, k < count.  Without the
+    // fused conv a contiguous range, so consecutive items are the heads of
+    // one tile, which share the sequence lookup (and, with GQA, the q/k
+    // rows).  With it every gridDim.x-th item, so the heads of a tile run at
+    // once on different CUs while their conv windows' rows sit in L2 (a
+    // contiguous range was 1.8% slower there).
+    const int G = gridDim.x, w = blockIdx.x;
+    int i0, stride, count;
+    if constexpr (CONV) {
+        i0 = w;
+        stride = G;
+        count = (nitems - w + G - 1) / G;
+    } else {
+        const int per = nitems / G, rem = nitems % G;
+        i0 = w * per + min(w, rem);
+        stride = 1;
+        count = per + (w < rem ? 1 : 0);
+    }
+    const int ilast = i0 + (count - 1) * stride;
+    Seq nseq = find_seq_item(i0, threadIdx.x >> 3);
     // the next item's inputs: phase 1's mapping, and with the fused conv the
     // conv windows in its (channel, 16 tokens) mapping
     IntraIn<IOT, KDA> nx;
     IntraConvIn<IOT, KDA> ncx;
     if constexpr (CONV)
-        intra_issue_conv(ncx, a, blockIdx.x, threadIdx.x >> 3, 16 * (threadIdx.x & 7),
+        intra_issue_conv(ncx, a, i0, threadIdx.x >> 3, 16 * (threadIdx.x & 7),
                          threadIdx.x & (DK - 1), 16 * (threadIdx.x >> 7));
     else
-        intra_issue(nx, a, blockIdx.x, threadIdx.x >> 3, 16 * (threadIdx.x & 7));
+        intra_issue(nx, a, i0, threadIdx.x >> 3, 16 * (threadIdx.x & 7));
     // The first item waits for its loads here.  Later items find theirs
     // complete (see the end of step 1).  Without this wait the loop head
     // would merge the two cases and wait for every memory operation at each
     // item, including the previous item's last stores.
     __builtin_amdgcn_s_waitcnt(0);
-    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    for (int item = i0; item <= ilast; item += stride) {
         // an opaque copy of the thread index per item: what derives from it
         // (lane offsets, LDS addresses) is formed inside the item and not
         // held live across the whole loop
@@ -667,8 +686,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         // so step 6's wait for those completes them too, and the next item
         // starts without waiting.
         {
-            const int next = min(item + (int)gridDim.x, nitems - 1);
-            nseq = find_seq_item(next, t);
+            const int next = min(item + stride, ilast);
+            if (next / a.Hv != tile) nseq = find_seq_item(next, t);
             if constexpr (CONV) intra_issue_conv(ncx, a, next, t, c0, cc, tc);
             else intra_issue(nx, a, next, t, c0);
         }
