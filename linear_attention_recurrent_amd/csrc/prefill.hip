@@ -861,7 +861,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 xvr[i] = ld<IOT>(a.v, tk * a.v_stride + h * DK + cc);
             }
         }
-        __syncthreads();
+        // (no barrier: step 4 reads neither N nor T until the barrier after
+        // its row blocks, which orders the clearing above before its writes)
 
         // ---- 4. A and P.  Wave w contracts channel quarter qtr = w & 3 (32
         //         channels) for the block pairs of two row blocks: even waves
@@ -1053,10 +1054,13 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 }
             }
         }
+        // Column block J of T depends only on its own earlier blocks and on
+        // the diagonal blocks, so wave J (< 3) walks I = J + 1 .. 3 with
+        // wave-local ordering only, and one barrier closes the step.
         float *ws16 = scr + wave * 16 * 17;
-        for (int lev = 1; lev <= 3; ++lev) {
-            const int I = wave, J = wave - lev;
-            if (wave < 4 && J >= 0) {
+        if (wave < 3) {
+            const int J = wave;
+            for (int I = J + 1; I < 4; ++I) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 for (int K = J; K < I; ++K)
 #pragma unroll
@@ -1072,9 +1076,12 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                     t2 = mfma4(Tm[(16 * I + li) * LDJ + 16 * I + k0 + lq], ws16[(k0 + lq) * 17 + li], t2);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Tm[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = -t2[r];
+                // T_IJ is read by the next block of the column, ws16 rewritten
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
             }
-            __syncthreads();
         }
+        __syncthreads();
 
         // ---- 6. right-hand sides, transposed: (beta K Gamma)^T and (beta V)^T.
         //         In bf16x3 mode they and T are stored split (bf16 hi / lo rows),
