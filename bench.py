@@ -699,6 +699,9 @@ def main():
                     help="only run a 1 GiB device copy (PMC counter scaling)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the chunked-prefill workloads (for counter profiles)")
+    ap.add_argument("--single-layer-only", action="store_true",
+                    help="only the single-layer KDA decode, 64 requests x 12 heads (for counter "
+                         "profiles)")
     ap.add_argument("--layers", type=int, default=69,
                     help="layers of the headline stack (69; fewer only for counter passes, "
                          "whose per-launch figures do not depend on it)")
@@ -719,6 +722,11 @@ def main():
         copy_calibration(dev)
         return
     la.load_library()
+    if args.single_layer_only:
+        s2 = synth.DecodeShape(B=64, Hqk=12, Hv=12, dk=128, dv=128, P=80)
+        print(json.dumps({"kda_decode_single_layer_b64_h12": decode_single_layer(s2, args.reps, dev)}),
+              flush=True)
+        return
     if args.prefill_only:
         print(json.dumps({"kda_prefill_chunked_h12": prefill_bench(dev, args.reps),
                           "gdn_prefill_chunked_hqk16_hv32": gdn_prefill_bench(dev, args.reps)}),
