@@ -118,20 +118,42 @@ def test_empty_and_single_token_sequences(dev):
     assert torch.equal(pool[7], before[4])
 
 
-@pytest.mark.parametrize("N", [511, 600])
-def test_sequence_table_edge_and_global_search(N, dev):
+@pytest.mark.parametrize("N,H", [(511, 1), (600, 1), (600, 24)])
+def test_sequence_table_edge_and_global_search(N, H, dev):
     """Kernel 1 stages cu_seqlens and slot_in in LDS for fewer than 512
     sequences (511 fills the table) and searches cu_seqlens in global memory
     beyond (600).  Seeded lengths of 0-3 tokens put dozens of pieces in a
-    tile; every other sequence resumes from a pool slot."""
+    tile; every other sequence resumes from a pool slot.  With 24 heads there
+    are more (tile, head) items than workgroups, so consecutive items of one
+    tile share a lookup, also on the global path."""
     rng = np.random.default_rng(3300 + N)
     lens = [int(x) for x in rng.integers(0, 4, size=N)]
     si = [n + 1 if n % 2 else -1 for n in range(N)]
     so = [N + 1 + n for n in range(N)]
-    sh, inp, pool, si, so = prefill_case(lens, 1, 1, 3300 + N, dev, slot_in=si, slot_out=so,
+    sh, inp, pool, si, so = prefill_case(lens, H, H, 3300 + N, dev, slot_in=si, slot_out=so,
                                          P=2 * N + 1)
-    print(f"[prefill parity] {N} sequences, T={sum(lens)}", flush=True)
-    check(sh, inp, pool, si, so, what=f"{N} sequences", mode=la.LA_PREFILL_BF16X3)
+    print(f"[prefill parity] {N} sequences, {H} heads, T={sum(lens)}", flush=True)
+    check(sh, inp, pool, si, so, what=f"{N} sequences {H} heads", mode=la.LA_PREFILL_BF16X3)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("kda", [True, False], ids=["kda", "gdn"])
+def test_items_across_tiles_with_four_value_heads_per_qk_head(kda, mode, dev):
+    """More (tile, head) items than the persistent grid has workgroups
+    (40 to 46 tiles x 8 value heads), so a workgroup walks more than one item and
+    its range starts and ends inside a tile; the heads of a tile share the
+    sequence lookup, refreshed where the tile changes.  Four value heads
+    share each of the two q/k heads."""
+    rng = np.random.default_rng(3400 + kda)
+    lens = [int(x) for x in rng.integers(1, 300, size=16)]
+    N = len(lens)
+    si = [n + 1 if n % 3 == 0 else -1 for n in range(N)]
+    so = [N + 1 + n for n in range(N)]
+    sh, inp, pool, si, so = prefill_case(lens, 2, 8, 3400 + kda, dev, kda=kda, slot_in=si,
+                                         slot_out=so, P=2 * N + 1)
+    print(f"[prefill parity] kda={kda} mode={mode} {N} sequences, T={sum(lens)}, 2/8 heads",
+          flush=True)
+    check(sh, inp, pool, si, so, what=f"items across tiles kda={kda} {mode}", mode=MODES[mode])
 
 
 @pytest.mark.parametrize("mode", ["fp32", "bf16x3"])

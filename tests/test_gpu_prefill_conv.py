@@ -123,6 +123,21 @@ def test_prefill_conv_with_strong_decay_and_resets(kda, mode, dev):
     check(c, dev, f"gate range kda={kda} mode={mode}", mode)
 
 
+@pytest.mark.parametrize("kda", [True, False], ids=["kda", "gdn"])
+def test_prefill_conv_items_across_tiles_four_value_heads_per_qk_head(kda, dev):
+    """More (tile, head) items than the persistent grid has workgroups (40
+    to 46 tiles x 8 value heads), so workgroups take a second item one grid
+    stride on, in another tile, and fetch its conv window history again.  Four
+    value heads share each of the two q/k heads."""
+    rng = np.random.default_rng(3400 + kda)
+    lens = [int(x) for x in rng.integers(1, 300, size=16)]
+    N = len(lens)
+    si = [n + 1 if n % 3 == 0 else -1 for n in range(N)]
+    so = [N + 1 + n for n in range(N)]
+    c = conv_case(lens, 2, 8, 3210 + kda, dev, kda=kda, slot_in=si, slot_out=so, P=2 * N + 1)
+    check(c, dev, f"items across tiles kda={kda}", "bf16x3")
+
+
 def test_kda_prefill_conv_gqa_matches_oracle(dev):
     c = conv_case([65, 40, 2], 2, 4, 3202, dev, slot_in=[1, -1, 4], slot_out=[2, 3, 4], P=4)
     check(c, dev, "kda gqa", "bf16x3")
