@@ -211,7 +211,9 @@ int shortconv_prefill(int N, int T, int C, const void *x, int io_dtype,
  *   mode: LA_PREFILL_FP32 or LA_PREFILL_BF16X3.
  *   workspace: device scratch of at least kda_prefill_workspace_bytes(...)
  *     bytes, 256-byte aligned; contents need no initialisation.
- * Supported: d_k == d_v == 128; H_v a multiple of H_qk. */
+ * Supported: d_k == d_v == 128; H_v a multiple of H_qk; H_v <= 4096 (larger
+ * values return LA_ERR_UNSUPPORTED: a 64-token block's outputs are addressed
+ * with 32-bit offsets). */
 int kda_prefill_chunked(int N, int T, int H_qk, int H_v, int d_k, int d_v, const void *q,
                         int64_t q_stride, const void *k, int64_t k_stride, const void *v,
                         int64_t v_stride, int io_dtype, const float *g, const float *beta,

@@ -206,6 +206,8 @@ int prefill_common(bool kda, int N, int T, int Hqk, int Hv, int dk, int dv, cons
         return fail(LA_ERR_UNSUPPORTED, "%s: unknown precision mode %d", fn, mode);
     if (dk != 128 || dv != 128)
         return fail(LA_ERR_UNSUPPORTED, "%s: needs d_k == d_v == 128 (got %d, %d)", fn, dk, dv);
+    if (Hv > 4096)  // a block's outputs are addressed with 32-bit byte offsets
+        return fail(LA_ERR_UNSUPPORTED, "%s: H_v = %d exceeds 4096", fn, Hv);
     if (N == 0) return ok();
     // with no tokens the per-token buffers are not read and may be NULL
     if (!cu_seqlens || !slot_in || !slot_out || !ssm_pool ||

@@ -1447,19 +1447,63 @@ __device__ __forceinline__ void split1(float v, bf16_t &hi, bf16_t &lo)
     lo = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
-// The operands of the next block are prefetched into a second register
-// buffer while the current block runs.  NSL: 16-row state slices per
-// workgroup; with NSL = 4 every operand fragment loaded serves four times the
-// matrix work, cutting the operand traffic per unit of work (for launches with
-// many sequences, where that traffic between L2 and the CUs is the limit).
-template <typename IOT, typename ST, int NSL>
-__global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain_x3_kernel(PrefillArgs a)
+// 16-byte stores through a buffer resource.  A lane whose offset is 2^31 or
+// more lies past the resource's range, and the hardware drops its store, so a
+// masked store needs no branch: the stores stay straight-line code, and the
+// waits for loads issued after them count them exactly.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr uint32_t kDropOffset = 0x80000000u;
+template <typename T, int NV>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *v)
 {
-    constexpr int NR = 16 * NSL;  // state rows of the workgroup
-    constexpr int kRowOpsN = 80 + 4 * NSL;  // W 32, Q Gamma 32, P 16, U 4 per slice
-    __shared__ __attribute__((aligned(16))) float Sf[2][NR][LDK];          // fp32 state rows
-    __shared__ __attribute__((aligned(16))) bf16_t SH[2][NR][LDKH], SL[2][NR][LDKH];
-    __shared__ __attribute__((aligned(16))) bf16_t DH[NR][LDJH], DL[NR][LDJH];
+    constexpr int NW = NV * (int)sizeof(T) / 4;  // dwords
+    static_assert(NW % 2 == 0, "whole 8-byte pieces");
+    uint32_t w[NW];
+#pragma unroll
+    for (int e = 0; e < NW; ++e)
+        w[e] = sizeof(T) == 4 ? __float_as_uint(v[e]) : pack_bf16x2(v[2 * e], v[2 * e + 1]);
+#pragma unroll
+    for (int i = 0; i + 4 <= NW; i += 4)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[i], w[i + 1], w[i + 2], w[i + 3]}, r,
+                                               (int)(off + 4 * i), 0, 0);
+    if constexpr (NW % 4 == 2)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w[NW - 2], w[NW - 1]}, r,
+                                              (int)(off + 4 * (NW - 2)), 0, 0);
+}
+
+// NSL: 16-row state slices per workgroup.  With NSL = 4 every operand
+// fragment loaded serves four times the matrix work, cutting the operand
+// traffic per unit of work (for launches with many sequences, where that
+// traffic between L2 and the CUs is the limit).  A block takes two phases,
+// split by one barrier:
+//   1. the row waves form D = U - W S^T and Q Gamma S^T from the same split
+//      state fragments, so each is read from LDS once, and publish D^T;
+//   2. the row waves add P D to the output and stage it in LDS; the column
+//      waves form S Gamma_L + D^T K^ from their fp32 state entries, which
+//      stay in registers for the whole call, and write its split over the
+//      state the row waves finished reading in phase 1.
+// The next block's operands are loaded into a second register buffer under
+// phase 1, after the previous block's outputs leave the staging area as
+// 16-byte stores, so the loads are the youngest memory operations when the
+// next block waits for them.
+template <typename IOT, typename ST, int NSL>
+__global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(PrefillArgs a)
+{
+    constexpr int NR = 16 * NSL;            // state rows of the workgroup
+    constexpr int kRowOpsN = 64 + 4 * NSL;  // W 32, Q Gamma 32, U 4 per slice (P apart)
+    // 16-byte loads a row wave issues per block: P and half of the next W
+    // under phase 1 (kL1, spread over its 24 NSL products), the rest of the
+    // next W, Q Gamma and U under phase 2 (kL2, over its 6 NSL products).  The
+    // CU's memory queue is then fed through the whole block rather than only
+    // while phase 1 runs, and a wave stalls less on a full queue.
+    constexpr int kL1 = 8, kL2 = 12 + NSL;
+    constexpr int LPS1 = (kL1 + NSL - 1) / NSL, MPL1 = 24 / LPS1;
+    constexpr int LPS2 = (kL2 + NSL - 1) / NSL, MPL2 = (6 + LPS2 - 1) / LPS2;
+    constexpr int LDO = NR + 4;             // row stride (floats) of the output staging
+    constexpr int OPL = NR / 4;             // outputs a lane stores per block
+    __shared__ __attribute__((aligned(16))) bf16_t SH[NR][LDKH], SL[NR][LDKH];  // split state
+    __shared__ __attribute__((aligned(16))) bf16_t DH[NR][LDJH], DL[NR][LDJH];  // split D^T
+    __shared__ __attribute__((aligned(16))) float Ost[4][16][LDO];              // O per row wave
 
     int n, h, rs;  // rows NR rs .. NR rs + NR - 1
     if (!chain_ids(a, DK / NR, n, h, rs)) return;
@@ -1478,79 +1522,82 @@ __global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain
         }
         return;
     }
-    for (int idx = tid; idx < NR * DK; idx += kChainThreads) {  // initial state rows
-        const int i = idx / DK, c = idx % DK;
-        float v = 0.f;
-        if (si >= 0)
-            v = ld<ST>(a.ssm_pool, (int64_t)si * a.ssm_stride + ((int64_t)h * DK + row0 + i) * DK + c);
-        Sf[0][i][c] = v;
-        split1(v, SH[0][i][c], SL[0][i][c]);
-    }
-
     const int tb0 = start / CB, tb1 = end > start ? (end - 1) / CB : tb0 - 1;
     const int ntiles = tb1 - tb0 + 1;
+
     if (wave < 4) {
-        auto load_ops = [&](int tb, float *ops) {
+        if (ntiles <= 0) return;  // nothing to output; the column waves hand the state over
+        // W, Q Gamma and U are loaded a block ahead, P (used only after the
+        // barrier) at the start of its own block into a single buffer
+        auto load_w = [&](int tb, float *ops, int g0) {  // W runs g0 .. g0 + 3
+            load_run(ops + 4 * g0, ws.W + ((int64_t)tb * a.Hv + h) * kBlkDK + fidx(8 * I + g0, 0), 4,
+                     lane);
+        };
+        auto load_qu = [&](int tb, float *ops) {
             const int64_t bh = (int64_t)tb * a.Hv + h;
-            load_run(ops, ws.W + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
             load_run(ops + 32, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
-            load_run(ops + 64, ws.P + bh * kBlkCB + fidx(4 * I, 0), 4, lane);
 #pragma unroll
             for (int sl = 0; sl < NSL; ++sl)
-                load_run(ops + 80 + 4 * sl, ws.U + bh * kBlkDK + fidx(8 * I + NSL * rs + sl, 0), 1,
+                load_run(ops + 64 + 4 * sl, ws.U + bh * kBlkDK + fidx(8 * I + NSL * rs + sl, 0), 1,
                          lane);
         };
-        // O of a block stays in registers and is stored under the next
-        // block, ahead of that block's operand loads: the loads are then the
-        // youngest memory operations when the next D waits for them, and that
-        // wait does not cover the stores' completion
-        float oacc[NSL][4];
-        auto store_o = [&](int itp) {
-            const int base = (tb0 + itp) * CB;
+        float pb[16];
+        // The outputs of block itp, staged by this wave: lane = token lane / 4
+        // x a quarter of the workgroup's rows.  Tokens outside the piece, and
+        // every lane when itp < 0, take the dropped offset.
+        auto flush_o = [&](int itp) {
+            const int base = (tb0 + max(itp, 0)) * CB;
             const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
+            const int tok = lane >> 2, ch = lane & 3, tr = 16 * I + tok;
+            float v[OPL];
 #pragma unroll
-            for (int sl = 0; sl < NSL; ++sl)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tr = 16 * I + 4 * lq + r;
-                    if (tr >= p0 && tr < p1)
-                        st<IOT>(a.out, ((int64_t)(base + tr) * a.Hv + h) * DK + row0 + 16 * sl + li,
-                                a.scale * oacc[sl][r]);
-                }
+            for (int e = 0; e < OPL; e += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(&Ost[I][tok][ch * OPL + e]);
+                v[e] = x.x; v[e + 1] = x.y; v[e + 2] = x.z; v[e + 3] = x.w;
+            }
+            const bool keep = itp >= 0 && tr >= p0 && tr < p1;
+            const uint32_t off =
+                keep ? (uint32_t)((tr * a.Hv * DK + ch * OPL) * (int)sizeof(IOT)) : kDropOffset;
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<IOT *>(a.out) + ((int64_t)base * a.Hv + h) * DK + row0, (short)0,
+                p1 * a.Hv * DK * (int)sizeof(IOT), 0x00020000);
+            buf_store<IOT, OPL>(r, off, v);
         };
-        // nxt: the next block's operands are loaded into it under the O
-        // products, one load between two of them, so their issue overlaps the
-        // matrix work rather than stalling the wave
         auto block = [&](int it, const float *cur, float *nxt) {
             const int tb = tb0 + it, base = tb * CB;
             const int p0 = max(start, base) - base, p1 = min(end, base + CB) - base;
-            const int b = it & 1;
-            __syncthreads();  // state rows in place, last D^T consumed
-            // D = U - W S^T for each slice (ops words [8m, 8m+4) hi, [8m+4, 8m+8) lo)
+            __syncthreads();  // split state in place, last D^T consumed
+            flush_o(it - 1);
+            load_run(pb, ws.P + ((int64_t)tb * a.Hv + h) * kBlkCB + fidx(4 * I, 0), 4, lane);
+            load_w(min(tb + 1, tb1), nxt, 0);
+            // phase 1: D = U - W S^T and O = Q Gamma S^T for each slice (ops
+            // words [8m, 8m+4) hi, [8m+4, 8m+8) lo of step m); two D
+            // accumulators (even / odd steps) halve its dependent chain
+            f32x4 oac[NSL];
 #pragma unroll
             for (int sl = 0; sl < NSL; ++sl) {
-                // two accumulators (even / odd 32-deep steps) halve the
-                // dependent matrix-core chain on the block's critical path
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
                 const int sr = 16 * sl + li;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
+                oac[sl] = acc;
 #pragma unroll
-                for (int m = 0; m < 4; m += 2) {
-                    mma3(acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4),
-                         lds8(&SH[b][sr][32 * m + 8 * lq]), lds8(&SL[b][sr][32 * m + 8 * lq]));
-                    mma3(acc1, quad8(cur + 8 * m + 8), quad8(cur + 8 * m + 12),
-                         lds8(&SH[b][sr][32 * m + 32 + 8 * lq]),
-                         lds8(&SL[b][sr][32 * m + 32 + 8 * lq]));
+                for (int m = 0; m < 4; ++m) {
+                    const bf16x8_t sh = lds8(&SH[sr][32 * m + 8 * lq]);
+                    const bf16x8_t sq = lds8(&SL[sr][32 * m + 8 * lq]);
+                    mma3(m & 1 ? acc1 : acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4), sh, sq);
+                    mma3(oac[sl], quad8(cur + 32 + 8 * m), quad8(cur + 32 + 8 * m + 4), sh, sq);
+                }
+#pragma unroll
+                for (int q = 0; q < LPS1; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MPL1, 0);  // products
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one load
                 }
                 acc += acc1;
-                float d[4];
+                bf16_t hi[4], lo[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 16 * I + 4 * lq + r;
-                    d[r] = (tr >= p0 && tr < p1) ? cur[80 + 4 * sl + r] - acc[r] : 0.f;
+                    split1((tr >= p0 && tr < p1) ? cur[64 + 4 * sl + r] - acc[r] : 0.f, hi[r], lo[r]);
                 }
-                bf16_t hi[4], lo[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) split1(d[r], hi[r], lo[r]);
                 const int c0 = 16 * I + 4 * lq;
                 *reinterpret_cast<uint2 *>(&DH[sr][c0]) =
                     make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
@@ -1558,43 +1605,64 @@ __global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain
                     make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
             }
             __syncthreads();  // D^T complete
-            if (it > 0) store_o(it - 1);
-            load_ops(min(tb + 1, tb1), nxt);
-            // O = scale (Q Gamma S^T + P D) for each slice
+            // phase 2: O += P D, scaled into this wave's staging rows
+            load_w(min(tb + 1, tb1), nxt, 4);
+            load_qu(min(tb + 1, tb1), nxt);
 #pragma unroll
             for (int sl = 0; sl < NSL; ++sl) {
                 const int sr = 16 * sl + li;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    mma3(acc, quad8(cur + 32 + 8 * m), quad8(cur + 32 + 8 * m + 4),
-                         lds8(&SH[b][sr][32 * m + 8 * lq]), lds8(&SL[b][sr][32 * m + 8 * lq]));
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    mma3(acc, quad8(cur + 64 + 8 * m), quad8(cur + 64 + 8 * m + 4),
+                    mma3(oac[sl], quad8(pb + 8 * m), quad8(pb + 8 * m + 4),
                          lds8(&DH[sr][32 * m + 8 * lq]), lds8(&DL[sr][32 * m + 8 * lq]));
 #pragma unroll
-                for (int q = 0; q < 18; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+                for (int q = 0; q < LPS2; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, MPL2, 0);  // products
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one load
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) oacc[sl][r] = acc[r];
+                for (int r = 0; r < 4; ++r) Ost[I][4 * lq + r][16 * sl + li] = a.scale * oac[sl][r];
             }
         };
         float bufA[kRowOpsN], bufB[kRowOpsN];
-        if (ntiles > 0) load_ops(tb0, bufA);
+        load_w(tb0, bufA, 0);
+        load_w(tb0, bufA, 4);
+        load_qu(tb0, bufA);
         // pairs of blocks, the odd last block peeled: an exit between the two
-        // halves would make the compiler wait for the prefetched operands (and
-        // the stores behind them) at the top of every pair
+        // halves would make the compiler wait for the prefetched operands at
+        // the top of every pair
         int it = 0;
         for (; it + 1 < ntiles; it += 2) {
             block(it, bufA, bufB);
             block(it + 1, bufB, bufA);
         }
         if (it < ntiles) block(it, bufA, bufB);
-        if (ntiles > 0) store_o(ntiles - 1);
+        flush_o(ntiles - 1);
     } else {
+        // this lane's fp32 state entries S[16 sl + 4 lq + r][32 I + 16 q + li]
+        // (workgroup rows), held in registers from the first block to the last
+        // (all loads issued before the first use)
+        float sreg[NSL][2][4];
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * sl + 4 * lq + r, c = 32 * I + 16 * q + li;
+                    sreg[sl][q][r] =
+                        ld<ST>(a.ssm_pool, (int64_t)max(si, 0) * a.ssm_stride + ((int64_t)h * DK + row0 + row) * DK + c);
+                }
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * sl + 4 * lq + r, c = 32 * I + 16 * q + li;
+                    if (si < 0) sreg[sl][q][r] = 0.f;  // a fresh sequence starts from zero
+                    split1(sreg[sl][q][r], SH[row][c], SL[row][c]);
+                }
         auto load_ops = [&](int tb, float *ops) {
             const int pend = min(end, tb * CB + CB) - 1;
 #pragma unroll
@@ -1606,18 +1674,10 @@ __global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain
                 ops[32 + q] = ws.Ge[((int64_t)pend * a.Hv + h) * DK + c];
             }
         };
-        auto block = [&](int it, const float *cur) {
-            const int b = it & 1;
+        auto block = [&](int it, const float *cur, float *nxt) {
             __syncthreads();
-            float sc[NSL][2][4];  // this lane's old state entries, read while D is formed
-#pragma unroll
-            for (int sl = 0; sl < NSL; ++sl)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sc[sl][q][r] = Sf[b][16 * sl + 4 * lq + r][32 * I + 16 * q + li];
-            __syncthreads();  // D^T complete
+            load_ops(min(tb0 + it + 1, tb1), nxt);  // under phase 1, where these waves wait
+            __syncthreads();  // D^T complete; the row waves are done with the state
             // new state columns: S Gamma_L + D^T K^.  The products of both
             // 16-column halves are formed before either is written back, so
             // their matrix-core chains overlap.
@@ -1645,31 +1705,35 @@ __global__ void __launch_bounds__(kChainThreads, NSL == 1 ? 2 : 1) prefill_chain
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = 16 * sl + 4 * lq + r;
-                        const float v = fmaf(sc[sl][q][r], gm, acc[q][sl][r]);
-                        Sf[b ^ 1][row][c] = v;
-                        split1(v, SH[b ^ 1][row][c], SL[b ^ 1][row][c]);
+                        const float v = fmaf(sreg[sl][q][r], gm, acc[q][sl][r]);
+                        sreg[sl][q][r] = v;
+                        split1(v, SH[row][c], SL[row][c]);
                     }
             }
         };
         float bufA[kColOps], bufB[kColOps];
-        if (ntiles > 0) load_ops(tb0, bufA);
-        // pairs of blocks, the odd last block peeled (an exit between the two
-        // halves would make the compiler wait for the prefetched operands at
-        // the top of every pair)
-        int it = 0;
-        for (; it + 1 < ntiles; it += 2) {
-            load_ops(tb0 + it + 1, bufB);
-            block(it, bufA);
-            load_ops(min(tb0 + it + 2, tb1), bufA);
-            block(it + 1, bufB);
+        if (ntiles > 0) {
+            load_ops(tb0, bufA);
+            // pairs of blocks, the odd last block peeled (an exit between the two
+            // halves would make the compiler wait for the prefetched operands at
+            // the top of every pair)
+            int it = 0;
+            for (; it + 1 < ntiles; it += 2) {
+                block(it, bufA, bufB);
+                block(it + 1, bufB, bufA);
+            }
+            if (it < ntiles) block(it, bufA, bufB);
         }
-        if (it < ntiles) block(it, bufA);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < NR * DK; idx += kChainThreads) {
-        const int i = idx / DK, c = idx % DK;
-        st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + row0 + i) * DK + c,
-               Sf[ntiles & 1][i][c]);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * sl + 4 * lq + r, c = 32 * I + 16 * q + li;
+                    st<ST>(a.ssm_pool, (int64_t)so * a.ssm_stride + ((int64_t)h * DK + row0 + row) * DK + c,
+                           sreg[sl][q][r]);
+                }
     }
 }
 

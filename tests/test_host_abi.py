@@ -133,6 +133,11 @@ def test_prefill_validation(lib):
     bad[25] = 2                                           # unknown mode
     assert lib.kda_prefill_chunked(*bad) == -2
     bad = list(args)
+    bad[2], bad[3] = 1, 4097                              # H_v beyond the 32-bit output offsets
+    bad[11] = 4097 * d
+    assert lib.kda_prefill_chunked(*bad) == -2
+    assert b"4096" in lib.la_last_error()
+    bad = list(args)
     bad[0] = 0                                            # no sequences: no-op
     assert lib.kda_prefill_chunked(*bad) == 0
 
