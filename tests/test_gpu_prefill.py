@@ -14,7 +14,7 @@ import torch
 import oracle
 from linear_attention_recurrent_amd import binding as la
 from linear_attention_recurrent_amd import synth
-from parity_util import assert_close_seqs, assert_close_units, f64
+from parity_util import assert_close_seqs, assert_close_units, elem_tol, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -69,10 +69,14 @@ def check(sh, inp, pool, si, so, heads=None, what="", mode=la.LA_PREFILL_FP32):
     p = f64(pool)
     if heads is not None:
         o, p = o[:, heads], p[:, heads]
-    # outputs per (token, head); states per (slot, head)
-    # both precision modes are held to the bar of the tensor's storage dtype
-    assert_close_seqs(o, o_ref, inp["cu_seqlens"].cpu().numpy(), sh.io, f"{what} outputs")
-    assert_close_units(p[so], p_ref[so], 2, sh.state, f"{what} final states")
+    # outputs per (sequence, head); states per (slot, head).  Both precision
+    # modes are held to the bar of the tensor's storage dtype, the split
+    # products of bf16x3 mode to the derived element bar for fp32 tensors
+    split = mode == la.LA_PREFILL_BF16X3
+    assert_close_seqs(o, o_ref, inp["cu_seqlens"].cpu().numpy(), sh.io, f"{what} outputs",
+                      etol=elem_tol(sh.io, split))
+    assert_close_units(p[so], p_ref[so], 2, sh.state, f"{what} final states",
+                       etol=elem_tol(sh.state, split))
     untouched = np.setdiff1d(np.arange(pool.shape[0]), so)
     assert np.array_equal(f64(pool)[untouched], f64(before)[untouched])
     return out
@@ -136,24 +140,28 @@ def test_sequence_table_edge_and_global_search(N, H, dev):
     check(sh, inp, pool, si, so, what=f"{N} sequences {H} heads", mode=la.LA_PREFILL_BF16X3)
 
 
+@pytest.mark.parametrize("io,state", [("bf16", "fp32"), ("fp32", "bf16"), ("bf16", "bf16")])
 @pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("kda", [True, False], ids=["kda", "gdn"])
-def test_items_across_tiles_with_four_value_heads_per_qk_head(kda, mode, dev):
+def test_items_across_tiles_with_four_value_heads_per_qk_head(kda, mode, io, state, dev):
     """More (tile, head) items than the persistent grid has workgroups
     (40 to 46 tiles x 8 value heads), so a workgroup walks more than one item and
     its range starts and ends inside a tile; the heads of a tile share the
     sequence lookup, refreshed where the tile changes.  Four value heads
-    share each of the two q/k heads."""
+    share each of the two q/k heads.  The 128 (sequence, head) pairs take
+    the chain's 64-row form in bf16x3 mode, here with every dtype pairing of
+    its state load, split and store."""
     rng = np.random.default_rng(3400 + kda)
     lens = [int(x) for x in rng.integers(1, 300, size=16)]
     N = len(lens)
     si = [n + 1 if n % 3 == 0 else -1 for n in range(N)]
     so = [N + 1 + n for n in range(N)]
-    sh, inp, pool, si, so = prefill_case(lens, 2, 8, 3400 + kda, dev, kda=kda, slot_in=si,
-                                         slot_out=so, P=2 * N + 1)
-    print(f"[prefill parity] kda={kda} mode={mode} {N} sequences, T={sum(lens)}, 2/8 heads",
-          flush=True)
-    check(sh, inp, pool, si, so, what=f"items across tiles kda={kda} {mode}", mode=MODES[mode])
+    sh, inp, pool, si, so = prefill_case(lens, 2, 8, 3400 + kda, dev, kda=kda, io=io, state=state,
+                                         slot_in=si, slot_out=so, P=2 * N + 1)
+    print(f"[prefill parity] kda={kda} mode={mode} io={io} state={state} {N} sequences, "
+          f"T={sum(lens)}, 2/8 heads", flush=True)
+    check(sh, inp, pool, si, so, what=f"items across tiles kda={kda} {mode} {io}/{state}",
+          mode=MODES[mode])
 
 
 @pytest.mark.parametrize("mode", ["fp32", "bf16x3"])

@@ -18,7 +18,7 @@ import torch
 import oracle
 from linear_attention_recurrent_amd import binding as la
 from linear_attention_recurrent_amd import synth
-from parity_util import assert_close_seqs, assert_close_units, f64
+from parity_util import assert_close_seqs, assert_close_units, elem_tol, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -74,8 +74,11 @@ def check(c, dev, what, mode):
     out = run_fused(c, dev, mode=MODES[mode])
     torch.cuda.synchronize()
     sh, so = c["sh"], c["so"]
-    assert_close_seqs(f64(out), o_ref, c["cu"].cpu().numpy(), sh.io, f"{what} outputs")
-    assert_close_units(f64(c["spool"])[so], spool_ref[so], 2, sh.state, f"{what} final states")
+    split = MODES[mode] == la.LA_PREFILL_BF16X3  # split products: the derived element bar
+    assert_close_seqs(f64(out), o_ref, c["cu"].cpu().numpy(), sh.io, f"{what} outputs",
+                      etol=elem_tol(sh.io, split))
+    assert_close_units(f64(c["spool"])[so], spool_ref[so], 2, sh.state, f"{what} final states",
+                       etol=elem_tol(sh.state, split))
     assert np.array_equal(f64(c["cpool"]), cpool_ref), f"{what}: conv pool must match bit for bit"
     untouched = np.setdiff1d(np.arange(c["spool"].shape[0]), so)
     assert torch.equal(c["spool"][untouched], sbefore[untouched])
