@@ -1473,8 +1473,8 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 // NSL: 16-row state slices per workgroup.  With NSL = 4 every operand
 // fragment loaded serves four times the matrix work, cutting the operand
-// traffic per unit of work (for launches with many sequences, where that
-// traffic between L2 and the CUs is the limit).  A block takes two phases,
+// bytes per unit of work (for launches with many sequences, where the bytes
+// a CU can keep in flight bound the block rate).  A block takes two phases,
 // split by one barrier:
 //   1. the row waves form D = U - W S^T and Q Gamma S^T from the same split
 //      state fragments, so each is read from LDS once, and publish D^T;
@@ -1482,10 +1482,11 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 //      waves form S Gamma_L + D^T K^ from their fp32 state entries, which
 //      stay in registers for the whole call, and write its split over the
 //      state the row waves finished reading in phase 1.
-// The next block's operands are loaded into a second register buffer under
-// phase 1, after the previous block's outputs leave the staging area as
-// 16-byte stores, so the loads are the youngest memory operations when the
-// next block waits for them.
+// The previous block's outputs leave the staging area as 16-byte stores at
+// the start of a block, ahead of its loads: the next block's W, Q Gamma and U
+// (into a second register buffer) and this block's P, spread over both
+// phases, so the loads are the youngest memory operations when a block
+// waits for them.
 template <typename IOT, typename ST, int NSL>
 __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(PrefillArgs a)
 {
