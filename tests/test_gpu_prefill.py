@@ -483,14 +483,18 @@ def test_shortconv_prefill_then_decode_continues_history(dev):
     assert torch.equal(pool[1], pool[2])
 
 
-def test_graph_replay_matches_eager(dev):
+@pytest.mark.parametrize("lens", [[40, 100, 7], [23 + 9 * n for n in range(30)]],
+                         ids=["3seq", "30seq"])
+def test_graph_replay_matches_eager(lens, dev):
     """Chunked prefill (bf16x3) captured in a HIP graph and replayed several
     times, each replay continuing the states in place, with eager work and
     synchronisations between replays: bit-identical to eager calls at every
-    replay."""
-    lens = [40, 100, 7]
-    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3400, dev, slot_in=[1, 2, 3],
-                                         slot_out=[1, 2, 3], P=4)
+    replay.  Thirty sequences x 2 heads take the chain's 64-row form (its
+    masked buffer stores and register-held state)."""
+    N = len(lens)
+    slots = list(range(1, N + 1))
+    sh, inp, pool, si, so = prefill_case(lens, 2, 2, 3400, dev, slot_in=slots, slot_out=slots,
+                                         P=N + 1)
     si_t, so_t = torch.from_numpy(si).to(dev), torch.from_numpy(so).to(dev)
     pool_b = pool.clone()
     mode = la.LA_PREFILL_BF16X3
