@@ -671,9 +671,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 make_float4(qv[e] * iq, qv[e + 1] * iq, qv[e + 2] * iq, qv[e + 3] * iq);
             *reinterpret_cast<float4 *>(Kn + t * LDK + c0 + e) =
                 make_float4(kv[e] * ik, kv[e + 1] * ik, kv[e + 2] * ik, kv[e + 3] * ik);
-            *reinterpret_cast<float4 *>(Gc + t * LDK + c0 + e) =
-                make_float4(fmaxf(gv[e], kGateFloor), fmaxf(gv[e + 1], kGateFloor),
-                            fmaxf(gv[e + 2], kGateFloor), fmaxf(gv[e + 3], kGateFloor));
+            if (KDA || c0 == 0)  // GDN: one decay per token, kept in channel 0
+                *reinterpret_cast<float4 *>(Gc + t * LDK + c0 + e) =
+                    make_float4(fmaxf(gv[e], kGateFloor), fmaxf(gv[e + 1], kGateFloor),
+                                fmaxf(gv[e + 2], kGateFloor), fmaxf(gv[e + 3], kGateFloor));
         }
         if (cq == 0) {
             bet[t] = valid ? bt : 0.f;
@@ -724,16 +725,19 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             const uint32_t smq = (uint32_t)(sm >> (16 * qq)) & 0xFFFFu;
             const uint32_t rmq = (uint32_t)(rm >> (16 * qq)) & 0xFFFFu;
             const int first = smq ? __builtin_ctz(smq) : 16;  // first sub-piece start in the quarter
+            const bool chan = KDA || c == 0;  // GDN: channel 0 only
             float run[16];
             float acc = 0.f, mn = 0.f;
+            if (chan) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float gi = Gc[(16 * qq + i) * LDK + c];
-                acc = ((smq >> i) & 1) ? (((rmq >> i) & 1) ? 0.f : gi) : acc + gi;
-                run[i] = acc;
-                mn = fminf(mn, acc);
+                for (int i = 0; i < 16; ++i) {
+                    const float gi = Gc[(16 * qq + i) * LDK + c];
+                    acc = ((smq >> i) & 1) ? (((rmq >> i) & 1) ? 0.f : gi) : acc + gi;
+                    run[i] = acc;
+                    mn = fminf(mn, acc);
+                }
+                qsum[qq * DK + c] = acc;
             }
-            qsum[qq * DK + c] = acc;
             if constexpr (KDA) {
                 const bool big = __ballot(-mn > kSpanMax) != 0;
                 if (lane == 0) bigw[wave] = big;
@@ -742,12 +746,14 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             // carry into the quarter: the running sum of the sub-piece open at
             // its start (quarter p restarts iff its last sub-piece began inside
             // it; quarter 0 always does, at the tile start)
-            float off = 0.f;
-            for (int p = 0; p < qq; ++p)
-                off = ((sm >> (16 * p)) & 0xFFFFu) ? qsum[p * DK + c] : off + qsum[p * DK + c];
+            if (chan) {
+                float off = 0.f;
+                for (int p = 0; p < qq; ++p)
+                    off = ((sm >> (16 * p)) & 0xFFFFu) ? qsum[p * DK + c] : off + qsum[p * DK + c];
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                Gc[(16 * qq + i) * LDK + c] = i < first ? run[i] + off : run[i];
+                for (int i = 0; i < 16; ++i)
+                    Gc[(16 * qq + i) * LDK + c] = i < first ? run[i] + off : run[i];
+            }
         }
         __syncthreads();
         // GDN: one decay per token, so the decay factors of steps 3 and 6 are
@@ -779,7 +785,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
             for (int g4 = 0; g4 < 16; g4 += 4) {
                 const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + c0 + g4);
-                const float4 Ge = *reinterpret_cast<const float4 *>(Gc + pen_t * LDK + c0 + g4);
+                // GDN keeps its decay in channel 0 only
+                const float4 Ge = KDA ? *reinterpret_cast<const float4 *>(Gc + pen_t * LDK + c0 + g4)
+                                      : make_float4(Gc[pen_t * LDK], Gc[pen_t * LDK], Gc[pen_t * LDK],
+                                                    Gc[pen_t * LDK]);
                 const float4 K = *reinterpret_cast<const float4 *>(Kn + tt * LDK + c0 + g4);
                 if constexpr (KDA) {
                     kh[g4] = last ? K.x * exp_acc(Ge.x - G.x) : 0.f;
