@@ -92,6 +92,10 @@ constexpr int kRegion = 128 * LDJ > CB * LDK ? 128 * LDJ : CB * LDK;  // one [64
 constexpr float kSpanMax = 64.f;
 constexpr float kExpClamp = 80.f;
 constexpr float kGateFloor = -128.f;  // exp(-128) == 0 in fp32
+// exp(x) where on, else 0: the exponential is taken unconditionally (a masked
+// lane's argument is replaced by one whose exponential is 0 in fp32), so the
+// masked products of steps 3 and 6 compile to straight-line code.
+__device__ __forceinline__ float exp_if(bool on, float x) { return exp_acc(on ? x : -200.f); }
 enum { PM_F32 = 0, PM_BF16X3 = 1 };
 
 // ---- NT fragments ---------------------------------------------------------
@@ -127,12 +131,17 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(const float *f)
     for (int e = 0; e < 8; ++e) v[e] = f[e];
     return __builtin_convertvector(v, bf16x8_t);
 }
+// The lo part: each hi word is read back as a float from its packed dword (the
+// low word by a shift, the high word by a mask) rather than converted again.
 __device__ __forceinline__ bf16x8_t lo_bf16x8(const float *f, bf16x8_t hi)
 {
-    const f32x8 back = __builtin_convertvector(hi, f32x8);
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, hi);
     f32x8 v;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = f[e] - back[e];
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = f[2 * i] - __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = f[2 * i + 1] - __uint_as_float(w[i] & 0xFFFF0000u);
+    }
     return __builtin_convertvector(v, bf16x8_t);
 }
 
@@ -791,23 +800,39 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                                                     Gc[pen_t * LDK]);
                 const float4 K = *reinterpret_cast<const float4 *>(Kn + tt * LDK + c0 + g4);
                 if constexpr (KDA) {
-                    kh[g4] = last ? K.x * exp_acc(Ge.x - G.x) : 0.f;
-                    kh[g4 + 1] = last ? K.y * exp_acc(Ge.y - G.y) : 0.f;
-                    kh[g4 + 2] = last ? K.z * exp_acc(Ge.z - G.z) : 0.f;
-                    kh[g4 + 3] = last ? K.w * exp_acc(Ge.w - G.w) : 0.f;
+                    // G_e <= G_t wherever the token is its piece's last (sums of
+                    // gates <= 0 only fall), so the min changes nothing there and
+                    // keeps the other lanes finite.  The exponentials are pinned
+                    // as computed on every lane, so the masked products stay
+                    // straight-line code.
+                    const float e0 = exp_acc(fminf(Ge.x - G.x, 0.f)), e1 = exp_acc(fminf(Ge.y - G.y, 0.f));
+                    const float e2 = exp_acc(fminf(Ge.z - G.z, 0.f)), e3 = exp_acc(fminf(Ge.w - G.w, 0.f));
+                    asm volatile("" ::"v"(e0), "v"(e1), "v"(e2), "v"(e3));
+                    kh[g4] = last ? K.x * e0 : 0.f;
+                    kh[g4 + 1] = last ? K.y * e1 : 0.f;
+                    kh[g4 + 2] = last ? K.z * e2 : 0.f;
+                    kh[g4 + 3] = last ? K.w * e3 : 0.f;
                 } else {
                     const float e = tabE[tt];
                     kh[g4] = K.x * e; kh[g4 + 1] = K.y * e; kh[g4 + 2] = K.z * e; kh[g4 + 3] = K.w * e;
                 }
-                // the piece's decay of the state entering the tile (none left
-                // after a full reset)
-                if (store_ge)
-                    *reinterpret_cast<float4 *>(ws.Ge + row(tt) * DK + c0 + g4) =
-                        (f & TF_PRESET) ? make_float4(kGateFloor, kGateFloor, kGateFloor, kGateFloor)
-                                        : Ge;
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) KhTl[(c0 + i) * LDJ + tt] = kh[i];
+            // the piece's decay of the state entering the tile (none left
+            // after a full reset), stored by the piece's last token in one
+            // branch after the straight-line products above
+            if (store_ge) {
+#pragma unroll
+                for (int g4 = 0; g4 < 16; g4 += 4) {
+                    const float4 Ge = KDA ? *reinterpret_cast<const float4 *>(Gc + pen_t * LDK + c0 + g4)
+                                          : make_float4(Gc[pen_t * LDK], Gc[pen_t * LDK], Gc[pen_t * LDK],
+                                                        Gc[pen_t * LDK]);
+                    *reinterpret_cast<float4 *>(ws.Ge + row(tt) * DK + c0 + g4) =
+                        (f & TF_PRESET) ? make_float4(kGateFloor, kGateFloor, kGateFloor, kGateFloor)
+                                        : Ge;
+                }
+            }
         }
         if constexpr (MODE == PM_F32) {
             for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
@@ -817,9 +842,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 float4 e4;
                 if constexpr (KDA) {
                     const float4 G = *reinterpret_cast<const float4 *>(Gc + tt * LDK + k0);
-                    e4 = (tfl[tt] & TF_OPEN)
-                             ? make_float4(exp_acc(G.x), exp_acc(G.y), exp_acc(G.z), exp_acc(G.w))
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const bool open = tfl[tt] & TF_OPEN;
+                    e4 = make_float4(exp_if(open, G.x), exp_if(open, G.y), exp_if(open, G.z),
+                                     exp_if(open, G.w));
                 } else {
                     const float e = tabS[tt];
                     e4 = make_float4(e, e, e, e);
@@ -836,7 +861,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     v[e] = Qn[tt * LDK + k0 + e] *
-                           (KDA ? (open ? exp_acc(Gc[tt * LDK + k0 + e]) : 0.f) : tabS[tt]);
+                           (KDA ? exp_if(open, Gc[tt * LDK + k0 + e]) : tabS[tt]);
                 store_split(ws.Qt + bh * kBlkDK + I * 2048, m, ln, v);
             }
         }
@@ -1113,8 +1138,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             for (int i = 0; i < 16; ++i) {
                 const int tt = tq + i;
                 if constexpr (KDA) {
-                    xk[i] = (tfl[tt] & TF_OPEN) ? bet[tt] * Kn[tt * LDK + c] * exp_acc(Gc[tt * LDK + c])
-                                                : 0.f;
+                    const bool open = tfl[tt] & TF_OPEN;
+                    const float x = bet[tt] * Kn[tt * LDK + c] * exp_if(open, Gc[tt * LDK + c]);
+                    xk[i] = open ? x : 0.f;
                 } else {
                     xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
                 }
