@@ -1058,21 +1058,23 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
         //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
         //         blocks level by level: T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ.
-        if (wave < 4 && lane < 16) {
-            const int I = wave, c = lane;
-            float x[16];
+        //         Meanwhile waves 4..7 store P and then form step 6's
+        //         (beta K Gamma)^T in Q's space, which P's store frees.
+        if (wave < 4) {
+            if (lane < 16) {
+                const int I = wave, c = lane;
+                float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < r; ++j) s = fmaf(Nm[(16 * I + r) * LDJ + 16 * I + j], x[j], s);
-                x[r] = r == c ? 1.f : (r < c ? 0.f : -s);
+                    for (int j = 0; j < r; ++j) s = fmaf(Nm[(16 * I + r) * LDJ + 16 * I + j], x[j], s);
+                    x[r] = r == c ? 1.f : (r < c ? 0.f : -s);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
-        }
-        __syncthreads();
-        if (wave >= 4) {  // P to global in fragment order while waves 0..3 run the levels
+        } else {  // P to global in fragment order
             if constexpr (MODE == PM_F32) {
                 for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
                     const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
@@ -1085,6 +1087,35 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                     const int I = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
                     const int tt = 16 * I + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
                     store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
+                }
+            }
+        }
+        __syncthreads();  // diagonal blocks of T done; P is read out
+        if (wave >= 4) {
+            // (beta K Gamma)^T: thread (channel c, tokens tq .. tq + 31), rows
+            // of the transposed right-hand side written to Q's space
+            const int u = tid - 256, c = u & (DK - 1), tq = 32 * (u >> 7);
+#pragma unroll
+            for (int hf = 0; hf < 32; hf += 16) {
+                float xk[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int tt = tq + hf + i;
+                    if constexpr (KDA) {
+                        const bool open = tfl[tt] & TF_OPEN;
+                        const float x = bet[tt] * Kn[tt * LDK + c] * exp_if(open, Gc[tt * LDK + c]);
+                        xk[i] = open ? x : 0.f;
+                    } else {
+                        xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
+                    }
+                }
+                if constexpr (MODE == PM_F32) {
+#pragma unroll
+                    for (int i = 0; i < 16; i += 4)
+                        *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + hf + i) =
+                            make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+                } else {
+                    store_row_split16(XtK + c * LDJ, tq + hf, xk);
                 }
             }
         }
@@ -1117,10 +1148,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
         __syncthreads();
 
-        // ---- 6. right-hand sides, transposed: (beta K Gamma)^T and (beta V)^T.
-        //         In bf16x3 mode they and T are stored split (bf16 hi / lo rows),
-        //         so step 7 reads its operands without converting them; T goes
-        //         to N's space, which is dead.
+        // ---- 6. right-hand sides, transposed: (beta V)^T here, (beta K Gamma)^T
+        //         formed under step 5.  In bf16x3 mode they and T are stored
+        //         split (bf16 hi / lo rows), so step 7 reads its operands without
+        //         converting them; T goes to N's space, which is dead.
         if constexpr (MODE != PM_F32) {
             const int row = tid >> 3, k0 = 8 * (tid & 7);
             const float4 t0v = *reinterpret_cast<const float4 *>(Tm + row * LDJ + k0);
@@ -1130,30 +1161,6 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             split8(tv, hi, lo);
             *reinterpret_cast<uint4 *>(Nm + row * LDJ + k0 / 2) = hi;
             *reinterpret_cast<uint4 *>(Nm + row * LDJ + 32 + k0 / 2) = lo;
-        }
-        {
-            const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
-            float xk[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int tt = tq + i;
-                if constexpr (KDA) {
-                    const bool open = tfl[tt] & TF_OPEN;
-                    const float x = bet[tt] * Kn[tt * LDK + c] * exp_if(open, Gc[tt * LDK + c]);
-                    xk[i] = open ? x : 0.f;
-                } else {
-                    xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
-                }
-            }
-            __syncthreads();  // Qn is about to be overwritten
-            if constexpr (MODE == PM_F32) {
-#pragma unroll
-                for (int i = 0; i < 16; i += 4)
-                    *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + i) =
-                        make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
-            } else {
-                store_row_split16(XtK + c * LDJ, tq, xk);
-            }
         }
         {   // thread (channel c, 16 tokens): rows of (beta V)^T, loads coalesced over c
             const int c = tid & (DK - 1), tq = 16 * (tid >> 7);
@@ -1169,7 +1176,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
                 for (int i = 0; i < 16; ++i) xv[i] = bet[tq + i] * xvr[i];  // bet = 0 past nt
             }
-            __syncthreads();  // Kn is free
+            // K's space is free: its last reads formed (beta K Gamma)^T under step 5
             if constexpr (MODE == PM_F32) {
 #pragma unroll
                 for (int i = 0; i < 16; i += 4)
@@ -1481,6 +1488,18 @@ __device__ __forceinline__ void split1(float v, bf16_t &hi, bf16_t &lo)
     hi = f32_to_bf16(v);
     lo = f32_to_bf16(v - bf16_to_f32(hi));
 }
+// The same for two values at once: one packed conversion per part, the hi
+// values read back from the packed dword (equal to split1 of each value).
+__device__ __forceinline__ void split2(float v0, float v1, bf16_t &h0, bf16_t &h1, bf16_t &l0,
+                                       bf16_t &l1)
+{
+    const uint32_t h = pack_bf16x2(v0, v1);
+    const uint32_t l = pack_bf16x2(v0 - __uint_as_float(h << 16), v1 - __uint_as_float(h & 0xFFFF0000u));
+    h0 = (bf16_t)(h & 0xFFFFu);
+    h1 = (bf16_t)(h >> 16);
+    l0 = (bf16_t)(l & 0xFFFFu);
+    l1 = (bf16_t)(l >> 16);
+}
 
 // 16-byte stores through a buffer resource.  A lane whose offset is 2^31 or
 // more lies past the resource's range, and the hardware drops its store, so a
@@ -1628,17 +1647,21 @@ __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(Pref
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // one load
                 }
                 acc += acc1;
-                bf16_t hi[4], lo[4];
+                float d[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 16 * I + 4 * lq + r;
-                    split1((tr >= p0 && tr < p1) ? cur[64 + 4 * sl + r] - acc[r] : 0.f, hi[r], lo[r]);
+                    d[r] = (tr >= p0 && tr < p1) ? cur[64 + 4 * sl + r] - acc[r] : 0.f;
                 }
+                // hi and lo words of the four tokens, two per packed conversion
+                const uint32_t h01 = pack_bf16x2(d[0], d[1]), h23 = pack_bf16x2(d[2], d[3]);
+                const uint32_t l01 = pack_bf16x2(d[0] - __uint_as_float(h01 << 16),
+                                                 d[1] - __uint_as_float(h01 & 0xFFFF0000u));
+                const uint32_t l23 = pack_bf16x2(d[2] - __uint_as_float(h23 << 16),
+                                                 d[3] - __uint_as_float(h23 & 0xFFFF0000u));
                 const int c0 = 16 * I + 4 * lq;
-                *reinterpret_cast<uint2 *>(&DH[sr][c0]) =
-                    make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
-                *reinterpret_cast<uint2 *>(&DL[sr][c0]) =
-                    make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+                *reinterpret_cast<uint2 *>(&DH[sr][c0]) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2 *>(&DL[sr][c0]) = make_uint2(l01, l23);
             }
             __syncthreads();  // D^T complete
             // phase 2: O += P D, scaled into this wave's staging rows
@@ -1694,10 +1717,11 @@ __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(Pref
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 0; r < 4; r += 2) {
                     const int row = 16 * sl + 4 * lq + r, c = 32 * I + 16 * q + li;
-                    if (si < 0) sreg[sl][q][r] = 0.f;  // a fresh sequence starts from zero
-                    split1(sreg[sl][q][r], SH[row][c], SL[row][c]);
+                    if (si < 0) sreg[sl][q][r] = sreg[sl][q][r + 1] = 0.f;  // a fresh sequence starts from zero
+                    split2(sreg[sl][q][r], sreg[sl][q][r + 1], SH[row][c], SH[row + 1][c], SL[row][c],
+                           SL[row + 1][c]);
                 }
         auto load_ops = [&](int tb, float *ops) {
             const int pend = min(end, tb * CB + CB) - 1;
@@ -1739,11 +1763,13 @@ __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(Pref
 #pragma unroll
                 for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
+                    for (int r = 0; r < 4; r += 2) {
                         const int row = 16 * sl + 4 * lq + r;
-                        const float v = fmaf(sreg[sl][q][r], gm, acc[q][sl][r]);
-                        sreg[sl][q][r] = v;
-                        split1(v, SH[row][c], SL[row][c]);
+                        const float v0 = fmaf(sreg[sl][q][r], gm, acc[q][sl][r]);
+                        const float v1 = fmaf(sreg[sl][q][r + 1], gm, acc[q][sl][r + 1]);
+                        sreg[sl][q][r] = v0;
+                        sreg[sl][q][r + 1] = v1;
+                        split2(v0, v1, SH[row][c], SH[row + 1][c], SL[row][c], SL[row + 1][c]);
                     }
             }
         };
