@@ -177,7 +177,7 @@ __global__ void __launch_bounds__((DecodeCfg<D, ST>::NT)) decode_kernel(DecodeAr
     // state stream -- these launches run one workgroup per CU in many rounds,
     // where that wait is exposed.
     constexpr bool kSplit = GT == 1;
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];
 
     const int b = blockIdx.x / a.Hqk, kh = blockIdx.x % a.Hqk;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

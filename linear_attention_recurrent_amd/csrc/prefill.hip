@@ -484,7 +484,7 @@ __device__ __forceinline__ void intra_issue_conv(IntraConvIn<IOT, KDA> &r, const
 template <typename IOT, bool KDA, int MODE, bool CONV>
 __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArgs a)
 {
-    extern __shared__ float sm[];
+    extern __shared__ __attribute__((aligned(16))) float sm[];
     float *Qn = sm;                  // q_hat [64][LDK]; later (beta K Gamma)^T [128][LDJ]
     float *Kn = Qn + kRegion;        // k_hat [64][LDK]; later (beta V)^T [128][LDJ]
     float *Gc = Kn + kRegion;        // cumulative log decay over the tile
@@ -1299,7 +1299,7 @@ constexpr int kRowOps = 84, kColOps = 34;
 template <typename IOT, typename ST, int MODE>
 __global__ void __launch_bounds__(kChainThreads) prefill_chain_kernel(PrefillArgs a)
 {
-    extern __shared__ float sm[];
+    extern __shared__ __attribute__((aligned(16))) float sm[];
     float *Sbuf = sm;                 // two state slices [16 rows][LDK]
     float *Dt = sm + 2 * 16 * LDK;    // D^T of the tile [16 rows][LDJ] (tile-local tokens)
 
