@@ -1092,9 +1092,13 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
         __syncthreads();  // diagonal blocks of T done; P is read out
         if (wave >= 4) {
-            // (beta K Gamma)^T: thread (channel c, tokens tq .. tq + 31), rows
-            // of the transposed right-hand side written to Q's space
-            const int u = tid - 256, c = u & (DK - 1), tq = 32 * (u >> 7);
+            // (beta K Gamma)^T: thread (row rho, tokens tq .. tq + 31) of the
+            // transposed right-hand side, written to Q's space.  In bf16x3 mode
+            // row rho holds channel pi(rho), bits 2 and 3 of the index swapped
+            // (pi is its own inverse): the row order in which step 7's
+            // transposed W product reads it without bank conflicts.
+            const int u = tid - 256, rho = u & (DK - 1), tq = 32 * (u >> 7);
+            const int c = MODE == PM_F32 ? rho : (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 #pragma unroll
             for (int hf = 0; hf < 32; hf += 16) {
                 float xk[16];
@@ -1112,10 +1116,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 if constexpr (MODE == PM_F32) {
 #pragma unroll
                     for (int i = 0; i < 16; i += 4)
-                        *reinterpret_cast<float4 *>(XtK + c * LDJ + tq + hf + i) =
+                        *reinterpret_cast<float4 *>(XtK + rho * LDJ + tq + hf + i) =
                             make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
                 } else {
-                    store_row_split16(XtK + c * LDJ, tq + hf, xk);
+                    store_row_split16(XtK + rho * LDJ, tq + hf, xk);
                 }
             }
         }
@@ -1188,15 +1192,20 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
         __syncthreads();
 
-        // ---- 7. U = T (beta V) and W = T (beta K Gamma): wave w owns output
-        //         columns 16w .. 16w + 15 of both, for the four token blocks.
-        //         U leaves in the result layout; W is staged in LDS (the decay
-        //         cumsum is dead) and leaves in fragment order.
+        // ---- 7. U = T (beta V) and W = T (beta K Gamma).  U: wave w owns
+        //         output columns 16w .. 16w + 15 for the four token blocks and
+        //         leaves them in the result layout.  W, fp32 mode: the same, staged
+        //         in LDS (the decay cumsum is dead) and stored in fragment order.
+        //         W, bf16x3 mode: wave w takes the 32-channel step s = w & 3 of
+        //         token blocks w >> 2 and 3 - (w >> 2) and forms W^T tiles whose
+        //         rows are channels 32 s + 8 (i >> 2) + 4 h + (i & 3), h = 0, 1: each
+        //         lane then holds the 8 consecutive channels of one token that W's
+        //         fragment order wants, and stores them split from registers.
         float *Wst = Gc;  // [64][LDK]
         {
             const int C = wave;
 #pragma unroll
-            for (int which = 0; which < 2; ++which) {
+            for (int which = 0; which < (MODE == PM_F32 ? 2 : 1); ++which) {
                 const float *Xt = which ? XtK : XtV;
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
@@ -1230,11 +1239,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 }
             }
         }
-        __syncthreads();
-        // fixed trip counts, unrolled (the thread index is opaque here, so a
-        // strided loop would not be)
-        static_assert(kBlkDK % (8 * kIntraThreads) == 0, "whole W store rounds");
         if constexpr (MODE == PM_F32) {
+            __syncthreads();
+            // fixed trip counts, unrolled (the thread index is opaque here, so a
+            // strided loop would not be)
 #pragma unroll
             for (int r = 0; r < kBlkDK / 4 / kIntraThreads; ++r) {
                 const int idx = tid + r * kIntraThreads;
@@ -1244,12 +1252,35 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                     *reinterpret_cast<const float4 *>(Wst + tt * LDK + k0);
             }
         } else {
+            const int st = wv & 3;
 #pragma unroll
-            for (int r = 0; r < kBlkDK / 8 / kIntraThreads; ++r) {
-                const int idx = tid + r * kIntraThreads;
-                const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
-                const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
-                store_split(ws.W + bh * kBlkDK + I * 2048, m, ln, Wst + tt * LDK + k0);
+            for (int k = 0; k < 2; ++k) {
+                const int I = k ? 3 - (wv >> 2) : wv >> 2;
+                const float *Trow = Nm + (16 * I + li) * LDJ;
+                float v[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    // channel 32 st + 8 (li >> 2) + 4 hh + (li & 3) sits in row pi of it
+                    const float *Xrow = XtK + (32 * st + 16 * (li >> 3) + 8 * hh + (li & 7)) * LDJ;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        if (m == 1 && I < 2) break;  // T rows < 32: columns < 32
+                        const int o = 16 * m + 4 * lq;
+                        const bf16x8_t xh = *reinterpret_cast<const bf16x8_t *>(Xrow + o);
+                        const bf16x8_t xl = *reinterpret_cast<const bf16x8_t *>(Xrow + 32 + o);
+                        const bf16x8_t th = *reinterpret_cast<const bf16x8_t *>(Trow + o);
+                        const bf16x8_t tl = *reinterpret_cast<const bf16x8_t *>(Trow + 32 + o);
+                        // the three products in the order U's take them: lo(T) hi(X),
+                        // hi(T) lo(X), hi(T) hi(X)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, tl, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, th, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, th, acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[4 * hh + r] = acc[r];
+                }
+                store_split(ws.W + bh * kBlkDK + I * 2048, st, lane, v);
             }
         }
     }
