@@ -196,6 +196,24 @@ __device__ __forceinline__ void mma_step(f32x4 &acc, const float *a, const float
     }
 }
 
+// The transposed tile of the same step: acc += B_step A_step^T, with the three
+// bf16x3 products taken in mma_step's order (lo(a) hi(b), hi(a) lo(b),
+// hi(a) hi(b)).  Lane (i, q) then holds row i of A's tile against columns
+// 4q .. 4q + 3 of B's.
+template <int MODE>
+__device__ __forceinline__ void mma_step_t(f32x4 &acc, const float *a, const float *b)
+{
+    if constexpr (MODE == PM_F32) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(b[0], a[0], acc, 0, 0, 0);
+    } else {
+        const bf16x8_t ah = to_bf16x8(a), bh = to_bf16x8(b);
+        const bf16x8_t al = lo_bf16x8(a, ah), bl = lo_bf16x8(b, bh);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, al, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, ah, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, ah, acc, 0, 0, 0);
+    }
+}
+
 // acc += A B^T over K.  fa(idx, k) / fb(idx, k) return this lane's operand
 // element for fragment index idx, which covers contraction index
 // k = frag_k(q, idx): a register fragment ignores k, an LDS row ignores idx.
@@ -903,9 +921,12 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         //         take row block 3 (J = 0..3) and (0, 0), odd waves row blocks 2
         //         and 1; that is five pairs each.  A row block's left factors (its k and
         //         q rows decayed to the block's reference) are formed once for all
-        //         its pairs.  The four quarters' partial sums meet in LDS in a
-        //         fixed order once Q is dead, so the result does not depend on
-        //         which wave finishes first.
+        //         its pairs.  Each pair is formed as the transposed tile, so lane
+        //         (i, q) holds row 16I + i against columns 16J + 4q .. 16J + 4q + 3
+        //         and every LDS access of the combining below is 16 bytes.  The
+        //         four quarters' partial sums meet in LDS in a fixed order once Q
+        //         is dead, so the result does not depend on which wave finishes
+        //         first.
         constexpr int KQ = DK / 4, W = Step<MODE>::W, NS = KQ / Step<MODE>::K;
         const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform
         const int qtr = wv >> 1, grp = wv & 1;  // a quarter's two waves sit on different SIMDs
@@ -948,23 +969,24 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 const int tj = 16 * J + li;
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
                 if (J == I && exact_diag) {
-                    // exp(G_t - G_j) per element, t = 16I + 4 lq + r, j = tj: the
-                    // result tile layout of the matrix-core path; pairs of other
-                    // pieces or with j > t are masked later and only kept finite
+                    // exp(G_t - G_j) per element, t = ti, j = 16J + 4 lq + r: the
+                    // transposed tile layout of the matrix-core path; pairs of
+                    // other pieces or with j > t are masked later and only kept
+                    // finite
 #pragma unroll 2
                     for (int c = qtr * KQ; c < qtr * KQ + KQ; c += 4) {
-                        const float4 kj = *reinterpret_cast<const float4 *>(Kn + tj * LDK + c);
-                        const float4 gj = *reinterpret_cast<const float4 *>(Gc + tj * LDK + c);
-                        const float kjv[4] = {kj.x, kj.y, kj.z, kj.w}, gjv[4] = {gj.x, gj.y, gj.z, gj.w};
+                        const float4 kt = *reinterpret_cast<const float4 *>(Kn + ti * LDK + c);
+                        const float4 qt = *reinterpret_cast<const float4 *>(Qn + ti * LDK + c);
+                        const float4 gt = *reinterpret_cast<const float4 *>(Gc + ti * LDK + c);
+                        const float ktv[4] = {kt.x, kt.y, kt.z, kt.w};
+                        const float qtv[4] = {qt.x, qt.y, qt.z, qt.w};
+                        const float gtv[4] = {gt.x, gt.y, gt.z, gt.w};
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const int tr = 16 * I + 4 * lq + r;
-                            const float4 kt = *reinterpret_cast<const float4 *>(Kn + tr * LDK + c);
-                            const float4 qt = *reinterpret_cast<const float4 *>(Qn + tr * LDK + c);
-                            const float4 gt = *reinterpret_cast<const float4 *>(Gc + tr * LDK + c);
-                            const float ktv[4] = {kt.x, kt.y, kt.z, kt.w};
-                            const float qtv[4] = {qt.x, qt.y, qt.z, qt.w};
-                            const float gtv[4] = {gt.x, gt.y, gt.z, gt.w};
+                            const int jr = 16 * J + 4 * lq + r;
+                            const float4 kj = *reinterpret_cast<const float4 *>(Kn + jr * LDK + c);
+                            const float4 gj = *reinterpret_cast<const float4 *>(Gc + jr * LDK + c);
+                            const float kjv[4] = {kj.x, kj.y, kj.z, kj.w}, gjv[4] = {gj.x, gj.y, gj.z, gj.w};
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const float kd = kjv[e] * exp_acc(fminf(gtv[e] - gjv[e], 0.f));
@@ -984,8 +1006,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                                   : KDA ? Kn[tj * LDK + c] * exp_acc(fminf(R[st][e] - Gc[tj * LDK + c], kExpClamp))
                                         : Kn[tj * LDK + c];
                         }
-                        mma_step<MODE>(accA, fk[st], fj);
-                        mma_step<MODE>(accP, fq[st], fj);
+                        mma_step_t<MODE>(accA, fk[st], fj);
+                        mma_step_t<MODE>(accP, fq[st], fj);
                     }
                 }
                 pa[k0 + J] = accA;
@@ -1014,44 +1036,52 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         for (int st = 0; st < 2; ++st) {
             if ((qtr & 1) == st) {
                 float *dA = qtr < 2 ? Nm : Nm2, *dP = qtr < 2 ? Ps : Ps2;
-                float prevA[5][4], prevP[5][4];
+                f32x4 prevA[5], prevP[5];
 #pragma unroll
-                for (int k = 0; k < 5; ++k)
+                for (int k = 0; k < 5; ++k) {
+                    const int at = (16 * pairI(k) + li) * LDJ + 16 * pairJ(k) + 4 * lq;
+                    prevA[k] = st ? *reinterpret_cast<const f32x4 *>(dA + at) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    prevP[k] = st ? *reinterpret_cast<const f32x4 *>(dP + at) : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
-                        prevA[k][r] = st ? dA[at] : 0.f;
-                        prevP[k][r] = st ? dP[at] : 0.f;
-                    }
-#pragma unroll
-                for (int k = 0; k < 5; ++k)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int at = (16 * pairI(k) + 4 * lq + r) * LDJ + 16 * pairJ(k) + li;
-                        dA[at] = st ? prevA[k][r] + pa[k][r] : pa[k][r];
-                        dP[at] = st ? prevP[k][r] + pp[k][r] : pp[k][r];
-                    }
+                for (int k = 0; k < 5; ++k) {
+                    const int at = (16 * pairI(k) + li) * LDJ + 16 * pairJ(k) + 4 * lq;
+                    *reinterpret_cast<f32x4 *>(dA + at) = st ? prevA[k] + pa[k] : pa[k];
+                    *reinterpret_cast<f32x4 *>(dP + at) = st ? prevP[k] + pp[k] : pp[k];
+                }
             }
             __syncthreads();
         }
         // A keeps beta[t] A where j < t in the same piece (else 0), P keeps
         // j <= t in the same piece (GDN: also the element's decay
-        // exp(G_t - G_j), <= 1 where it is kept); upper tiles of P are zero
-        for (int idx = tid; idx < CB * CB; idx += kIntraThreads) {
-            const int tt = idx / CB, j = idx % CB, at = tt * LDJ + j;
-            if ((j >> 4) > (tt >> 4)) {
-                Ps[at] = 0.f;
-                continue;
+        // exp(G_t - G_j), <= 1 where it is kept); upper tiles are zero.  Thread
+        // (row tt, columns j0 .. j0 + 3), straight-line: the upper tiles' sums
+        // (zeros in A, stale rows in P) are read and then discarded by the masks.
+        static_assert(CB * CB / 4 % kIntraThreads == 0, "whole mask rounds");
+#pragma unroll
+        for (int rr = 0; rr < CB * CB / 4 / kIntraThreads; ++rr) {
+            const int idx = tid + rr * kIntraThreads;
+            const int tt = idx >> 4, j0 = 4 * (idx & 15), at = tt * LDJ + j0;
+            const f32x4 av = *reinterpret_cast<const f32x4 *>(Nm + at) + *reinterpret_cast<const f32x4 *>(Nm2 + at);
+            const f32x4 pv = *reinterpret_cast<const f32x4 *>(Ps + at) + *reinterpret_cast<const f32x4 *>(Ps2 + at);
+            const int p0 = pst[tt];
+            const float bt = bet[tt];
+            f32x4 na, np;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + q;
+                float a1 = av[q], p1 = pv[q];
+                if constexpr (!KDA) {
+                    const float e = exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
+                    a1 *= e;
+                    p1 *= e;
+                }
+                const bool same = j >= p0 && tt < nt;
+                na[q] = same && j < tt ? bt * a1 : 0.f;
+                np[q] = same && j <= tt ? p1 : 0.f;
             }
-            float av = Nm[at] + Nm2[at], pv = Ps[at] + Ps2[at];
-            if constexpr (!KDA) {
-                const float e = exp_acc(fminf(Gc[tt * LDK] - Gc[j * LDK], 0.f));
-                av *= e;
-                pv *= e;
-            }
-            const bool same = j >= pst[tt] && tt < nt;
-            Nm[at] = same && j < tt ? bet[tt] * av : 0.f;
-            Ps[at] = same && j <= tt ? pv : 0.f;
+            *reinterpret_cast<f32x4 *>(Nm + at) = na;
+            *reinterpret_cast<f32x4 *>(Ps + at) = np;
         }
         __syncthreads();
 
