@@ -899,7 +899,14 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             }
         }
         __syncthreads();
-        for (int i = tid; i < 2 * CB * LDJ; i += kIntraThreads) Nm[i] = 0.f;  // Nm and Tm
+        // T's six upper tiles are cleared here and stay zero through steps 4 and
+        // 5, which write only its lower tiles; every element of N is written by
+        // step 4's mask pass
+        if (tid < 6 * 64) {
+            const int u = tid >> 6, r = (tid >> 2) & 15, q = tid & 3;  // tile (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+            const int I = u < 3 ? 0 : (u < 5 ? 1 : 2), J = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+            *reinterpret_cast<float4 *>(Tm + (16 * I + r) * LDJ + 16 * J + 4 * q) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         // the v loads of step 6 (its thread mapping: channel cc, tokens tc ..
         // tc + 15) run under steps 4 and 5: the 19-row conv window when the conv
         // is fused, else the 16 rows of v
@@ -1088,8 +1095,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
         //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
         //         blocks level by level: T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ.
-        //         Meanwhile waves 4..7 store P and then form step 6's
-        //         (beta K Gamma)^T in Q's space, which P's store frees.
+        //         Meanwhile waves 4..7 store P and form step 6's (beta K Gamma)^T:
+        //         its first half before the barrier that ends the diagonal solve,
+        //         all of it written to Q's space after that barrier, once P's
+        //         store has freed it.
         if (wave < 4) {
             if (lane < 16) {
                 const int I = wave, c = lane;
@@ -1104,7 +1113,39 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
             }
-        } else {  // P to global in fragment order
+        }
+        // step 6's (beta K Gamma)^T, formed by waves 4..7: thread (row rho,
+        // tokens xt .. xt + 31) of the transposed right-hand side, written to Q's
+        // space.  In bf16x3 mode row rho holds channel pi(rho), bits 2 and 3 of
+        // the index swapped (pi is its own inverse): the row order in which step
+        // 7's transposed W product reads it without bank conflicts.
+        const int xu = tid - 256, rho = xu & (DK - 1), xt = 32 * (xu >> 7);
+        const int xc = MODE == PM_F32 ? rho : (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+        auto form_xk = [&](int t1, float *xk) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int tt = t1 + i;
+                if constexpr (KDA) {
+                    const bool open = tfl[tt] & TF_OPEN;
+                    const float x = bet[tt] * Kn[tt * LDK + xc] * exp_if(open, Gc[tt * LDK + xc]);
+                    xk[i] = open ? x : 0.f;
+                } else {
+                    xk[i] = bet[tt] * Kn[tt * LDK + xc] * tabS[tt];
+                }
+            }
+        };
+        auto write_xk = [&](int t1, const float *xk) {
+            if constexpr (MODE == PM_F32) {
+#pragma unroll
+                for (int i = 0; i < 16; i += 4)
+                    *reinterpret_cast<float4 *>(XtK + rho * LDJ + t1 + i) =
+                        make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
+            } else {
+                store_row_split16(XtK + rho * LDJ, t1, xk);
+            }
+        };
+        float xk0[16];
+        if (wave >= 4) {  // P to global in fragment order
             if constexpr (MODE == PM_F32) {
                 for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
                     const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
@@ -1119,39 +1160,14 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                     store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
                 }
             }
+            form_xk(xt, xk0);  // the first half under the diagonal solve
         }
         __syncthreads();  // diagonal blocks of T done; P is read out
         if (wave >= 4) {
-            // (beta K Gamma)^T: thread (row rho, tokens tq .. tq + 31) of the
-            // transposed right-hand side, written to Q's space.  In bf16x3 mode
-            // row rho holds channel pi(rho), bits 2 and 3 of the index swapped
-            // (pi is its own inverse): the row order in which step 7's
-            // transposed W product reads it without bank conflicts.
-            const int u = tid - 256, rho = u & (DK - 1), tq = 32 * (u >> 7);
-            const int c = MODE == PM_F32 ? rho : (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
-#pragma unroll
-            for (int hf = 0; hf < 32; hf += 16) {
-                float xk[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int tt = tq + hf + i;
-                    if constexpr (KDA) {
-                        const bool open = tfl[tt] & TF_OPEN;
-                        const float x = bet[tt] * Kn[tt * LDK + c] * exp_if(open, Gc[tt * LDK + c]);
-                        xk[i] = open ? x : 0.f;
-                    } else {
-                        xk[i] = bet[tt] * Kn[tt * LDK + c] * tabS[tt];
-                    }
-                }
-                if constexpr (MODE == PM_F32) {
-#pragma unroll
-                    for (int i = 0; i < 16; i += 4)
-                        *reinterpret_cast<float4 *>(XtK + rho * LDJ + tq + hf + i) =
-                            make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
-                } else {
-                    store_row_split16(XtK + rho * LDJ, tq + hf, xk);
-                }
-            }
+            write_xk(xt, xk0);
+            float xk1[16];
+            form_xk(xt + 16, xk1);
+            write_xk(xt + 16, xk1);
         }
         // Column block J of T depends only on its own earlier blocks and on
         // the diagonal blocks, so wave J (< 3) walks I = J + 1 .. 3 with
