@@ -68,6 +68,7 @@
 // The small 16x16 block products of the triangular inverse always use fp32.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "la_device.h"
 #include "la_internal.h"
@@ -392,7 +393,7 @@ __device__ __forceinline__ void conv_apply(float *y, const float *xr, const Pref
 constexpr int kIntraThreads = 512;
 constexpr int kSeqTab = 512;  // sequences whose cu_seqlens / slot_in kernel 1 stages in LDS
 static_assert(kSeqTab == kIntraThreads, "one table entry per thread");
-constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK + 8 * 16 * 17;
+constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK;
 constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + (5 * CB + 8 + 2 * kSeqTab) * sizeof(int);
 // per-token flags of kernel 1 (sub-pieces)
 enum { TF_OPEN = 1,      // no full reset between the piece start and the token
@@ -511,8 +512,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     float *Tm = Nm + CB * LDJ;       // T = (I + N)^-1; in step 4 also a partial of A
     float *bet = Tm + CB * LDJ;      // beta
     float *qsum = bet + CB;          // [4][128] partial sums of the tile scan
-    float *scr = qsum + 4 * DK;      // per-wave 16x17 scratch
-    int *pst = reinterpret_cast<int *>(scr + 8 * 16 * 17);  // piece start, then sub-piece
+    int *pst = reinterpret_cast<int *>(qsum + 4 * DK);  // piece start, then sub-piece
                                                               // start (tile-local)
     int *pen = pst + CB;                                      // piece end (inclusive)
     int *sst = pen + CB;             // fused conv: the token's sequence start (global)
@@ -1095,10 +1095,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         // ---- 5. T = (I + N)^-1: diagonal 16x16 blocks by forward substitution
         //         (waves 0..3, lane c < 16 holds column c), then the off-diagonal
         //         blocks level by level: T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ.
-        //         Meanwhile waves 4..7 store P and form step 6's (beta K Gamma)^T:
-        //         its first half before the barrier that ends the diagonal solve,
-        //         all of it written to Q's space after that barrier, once P's
-        //         store has freed it.
+        //         Meanwhile waves 4..7 store P and form step 6's (beta K Gamma)^T
+        //         before the barrier that ends the diagonal solve, and write it to
+        //         Q's space after that barrier, once P's store has freed it.
         if (wave < 4) {
             if (lane < 16) {
                 const int I = wave, c = lane;
@@ -1114,37 +1113,37 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 for (int r = 0; r < 16; ++r) Tm[(16 * I + r) * LDJ + 16 * I + c] = x[r];
             }
         }
-        // step 6's (beta K Gamma)^T, formed by waves 4..7: thread (row rho,
-        // tokens xt .. xt + 31) of the transposed right-hand side, written to Q's
-        // space.  In bf16x3 mode row rho holds channel pi(rho), bits 2 and 3 of
-        // the index swapped (pi is its own inverse): the row order in which step
-        // 7's transposed W product reads it without bank conflicts.
-        const int xu = tid - 256, rho = xu & (DK - 1), xt = 32 * (xu >> 7);
-        const int xc = MODE == PM_F32 ? rho : (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
-        auto form_xk = [&](int t1, float *xk) {
+        // step 6's (beta K Gamma)^T, formed by waves 4..7 before the barrier that
+        // ends the diagonal solve and written to Q's space after it: thread
+        // (rows 4 rq .. 4 rq + 3, tokens 8 tg .. 8 tg + 7).  In bf16x3 mode row
+        // rho holds channel pi(rho), bits 2 and 3 of the index swapped (pi is its
+        // own inverse): the row order in which step 7's transposed W product
+        // reads it without bank conflicts.  pi keeps bits 0 and 1, so a thread's
+        // four rows are four consecutive channels, read 16 bytes at a time.
+        const int xu = tid - 256, rq = xu & 31, tg = xu >> 5;
+        const int xc = MODE == PM_F32 ? 4 * rq : (4 * rq & ~12) | ((4 * rq & 4) << 1) | ((4 * rq & 8) >> 1);
+        float bk[8][4];  // [token][row]
+        auto form_bk = [&](int i) {
+            const int tt = 8 * tg + i;
+            const float4 K4 = *reinterpret_cast<const float4 *>(Kn + tt * LDK + xc);
+            const float kv[4] = {K4.x, K4.y, K4.z, K4.w};
+            if constexpr (KDA) {
+                const float4 G4 = *reinterpret_cast<const float4 *>(Gc + tt * LDK + xc);
+                const float gv[4] = {G4.x, G4.y, G4.z, G4.w};
+                const bool open = tfl[tt] & TF_OPEN;
+                const float b = bet[tt];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int tt = t1 + i;
-                if constexpr (KDA) {
-                    const bool open = tfl[tt] & TF_OPEN;
-                    const float x = bet[tt] * Kn[tt * LDK + xc] * exp_if(open, Gc[tt * LDK + xc]);
-                    xk[i] = open ? x : 0.f;
-                } else {
-                    xk[i] = bet[tt] * Kn[tt * LDK + xc] * tabS[tt];
+                for (int r = 0; r < 4; ++r) {
+                    const float x = b * kv[r] * exp_if(open, gv[r]);
+                    bk[i][r] = open ? x : 0.f;
                 }
-            }
-        };
-        auto write_xk = [&](int t1, const float *xk) {
-            if constexpr (MODE == PM_F32) {
-#pragma unroll
-                for (int i = 0; i < 16; i += 4)
-                    *reinterpret_cast<float4 *>(XtK + rho * LDJ + t1 + i) =
-                        make_float4(xk[i], xk[i + 1], xk[i + 2], xk[i + 3]);
             } else {
-                store_row_split16(XtK + rho * LDJ, t1, xk);
+                const float b = bet[tt], e = tabS[tt];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bk[i][r] = b * kv[r] * e;
             }
         };
-        float xk0[16];
+        constexpr int kPre = CONV && KDA ? 4 : 8;
         if (wave >= 4) {  // P to global in fragment order
             if constexpr (MODE == PM_F32) {
                 for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
@@ -1160,42 +1159,63 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                     store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
                 }
             }
-            form_xk(xt, xk0);  // the first half under the diagonal solve
+            // (beta K Gamma)^T under the diagonal solve (with the fused conv's
+            // windows live, half of it, to stay within the registers)
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) form_bk(i);
         }
         __syncthreads();  // diagonal blocks of T done; P is read out
         if (wave >= 4) {
-            write_xk(xt, xk0);
-            float xk1[16];
-            form_xk(xt + 16, xk1);
-            write_xk(xt + 16, xk1);
-        }
-        // Column block J of T depends only on its own earlier blocks and on
-        // the diagonal blocks, so wave J (< 3) walks I = J + 1 .. 3 with
-        // wave-local ordering only, and one barrier closes the step.
-        float *ws16 = scr + wave * 16 * 17;
-        if (wave < 3) {
-            const int J = wave;
-            for (int I = J + 1; I < 4; ++I) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < I; ++K)
 #pragma unroll
-                    for (int k0 = 0; k0 < 16; k0 += 4)
-                        acc = mfma4(Nm[(16 * I + li) * LDJ + 16 * K + k0 + lq],
-                                    Tm[(16 * K + k0 + lq) * LDJ + 16 * J + li], acc);
+            for (int i = kPre; i < 8; ++i) form_bk(i);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ws16[(4 * lq + r) * 17 + li] = acc[r];
-                __builtin_amdgcn_wave_barrier();
-                f32x4 t2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4)
-                    t2 = mfma4(Tm[(16 * I + li) * LDJ + 16 * I + k0 + lq], ws16[(k0 + lq) * 17 + li], t2);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Tm[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = -t2[r];
-                // T_IJ is read by the next block of the column, ws16 rewritten
-                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-                __builtin_amdgcn_wave_barrier();
+            for (int r = 0; r < 4; ++r) {
+                float *row = XtK + (4 * rq + r) * LDJ;
+                const float v[8] = {bk[0][r], bk[1][r], bk[2][r], bk[3][r], bk[4][r], bk[5][r], bk[6][r], bk[7][r]};
+                if constexpr (MODE == PM_F32) {
+                    *reinterpret_cast<float4 *>(row + 8 * tg) = make_float4(v[0], v[1], v[2], v[3]);
+                    *reinterpret_cast<float4 *>(row + 8 * tg + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                } else {  // split row: hi words 0..31, lo words 32..63 for tokens 0..63
+                    uint4 hi, lo;
+                    split8(v, hi, lo);
+                    *reinterpret_cast<uint4 *>(row + 4 * tg) = hi;
+                    *reinterpret_cast<uint4 *>(row + 32 + 4 * tg) = lo;
+                }
             }
         }
+        // Column block J of T depends only on its own earlier blocks and on
+        // the diagonal blocks, so wave J (< 3) walks I = J + 1 .. 3 alone, and
+        // one barrier closes the step.  Its products take the contraction index
+        // of step s in lane quad q as k = 4q + s: lane (i, q) then supplies row i
+        // of the left factor (one 16-byte read of N or T_II) and holds, in its
+        // result registers, exactly the right factor of the next product (X for
+        // T_II X, and T_IJ for the later X's), so the chain stays in registers.
+        auto levels = [&](auto Jc) {
+            constexpr int J = decltype(Jc)::value;
+            f32x4 Tc[4];  // Tc[K][s] = T_KJ[4 lq + s][li]
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Tc[J][s] = Tm[(16 * J + 4 * lq + s) * LDJ + 16 * J + li];
+#pragma unroll
+            for (int I = J + 1; I < 4; ++I) {
+                f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int K = J; K < I; ++K) {
+                    const f32x4 n4 = *reinterpret_cast<const f32x4 *>(Nm + (16 * I + li) * LDJ + 16 * K + 4 * lq);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) X = mfma4(n4[s], Tc[K][s], X);
+                }
+                const f32x4 t4 = *reinterpret_cast<const f32x4 *>(Tm + (16 * I + li) * LDJ + 16 * I + 4 * lq);
+                f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) Y = mfma4(t4[s], X[s], Y);
+                Tc[I] = -Y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tm[(16 * I + 4 * lq + r) * LDJ + 16 * J + li] = -Y[r];
+            }
+        };
+        if (wv == 0) levels(std::integral_constant<int, 0>{});
+        else if (wv == 1) levels(std::integral_constant<int, 1>{});
+        else if (wv == 2) levels(std::integral_constant<int, 2>{});
         __syncthreads();
 
         // ---- 6. right-hand sides, transposed: (beta V)^T here, (beta K Gamma)^T
