@@ -691,7 +691,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         sq = group_sum<8>(sq);
         sk = group_sum<8>(sk);
         live = group_sum<8>(live);
-        const float iq = 1.f / sqrtf(sq + a.eps), ik = 1.f / sqrtf(sk + a.eps);
+        const float iq = __builtin_amdgcn_rsqf(sq + a.eps), ik = __builtin_amdgcn_rsqf(sk + a.eps);
 #pragma unroll
         for (int e = 0; e < 16; e += 4) {
             *reinterpret_cast<float4 *>(Qn + t * LDK + c0 + e) =
