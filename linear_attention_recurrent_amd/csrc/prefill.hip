@@ -526,6 +526,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
 
     const Ws ws = ws_layout(a.ws, a.T, a.Hv);
     const int nitems = (a.T + CB - 1) / CB * a.Hv;
+    // the store rounds of steps 3 and 5 run unrolled, so their loads and
+    // exponentials overlap; with the fused conv's windows live that spills,
+    // so there they stay loops
+    constexpr int kStoreUnroll = CONV ? 1 : 4;
     // With fewer than kSeqTab sequences, cu_seqlens and slot_in go to LDS
     // once (one entry per thread; entries past N repeat the last one and are
     // never read) and tokens search them there.  Larger batches search
@@ -853,7 +857,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
             }
         }
         if constexpr (MODE == PM_F32) {
-            for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {
+#pragma unroll kStoreUnroll
+            for (int rr = 0; rr < kBlkDK / 4 / kIntraThreads; ++rr) {
+                const int idx = tid + rr * kIntraThreads;
                 const int I = idx >> 9, g = (idx >> 6) & 7, ln = idx & 63;
                 const int tt = 16 * I + (ln & 15), k0 = frag_off4<MODE, DK>(ln >> 4, g);
                 const float4 qn = *reinterpret_cast<const float4 *>(Qn + tt * LDK + k0);
@@ -871,7 +877,9 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                     make_float4(qn.x * e4.x, qn.y * e4.y, qn.z * e4.z, qn.w * e4.w);
             }
         } else {  // split layout: thread = (row block I, step m, lane), 8 channels
-            for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+#pragma unroll kStoreUnroll
+            for (int rr = 0; rr < kBlkDK / 8 / kIntraThreads; ++rr) {
+                const int idx = tid + rr * kIntraThreads;
                 const int I = idx >> 8, m = (idx >> 6) & 3, ln = idx & 63;
                 const int tt = 16 * I + (ln & 15), k0 = 32 * m + 8 * (ln >> 4);
                 const bool open = tfl[tt] & TF_OPEN;
@@ -885,14 +893,18 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
         __syncthreads();
         if constexpr (MODE == PM_F32) {
-            for (int idx = tid; idx < kBlkDK / 4; idx += kIntraThreads) {  // KhT in fragment order
+#pragma unroll kStoreUnroll
+            for (int rr = 0; rr < kBlkDK / 4 / kIntraThreads; ++rr) {  // KhT in fragment order
+                const int idx = tid + rr * kIntraThreads;
                 const int cg = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
                 const int c = 16 * cg + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
                 *reinterpret_cast<float4 *>(ws.KhT + bh * kBlkDK + 4 * idx) =
                     *reinterpret_cast<const float4 *>(KhTl + c * LDJ + j0);
             }
         } else {
-            for (int idx = tid; idx < kBlkDK / 8; idx += kIntraThreads) {
+#pragma unroll kStoreUnroll
+            for (int rr = 0; rr < kBlkDK / 8 / kIntraThreads; ++rr) {
+                const int idx = tid + rr * kIntraThreads;
                 const int cg = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
                 const int c = 16 * cg + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
                 store_split(ws.KhT + bh * kBlkDK + cg * 1024, m, ln, KhTl + c * LDJ + j0);
@@ -1146,14 +1158,18 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         constexpr int kPre = CONV && KDA ? 4 : 8;
         if (wave >= 4) {  // P to global in fragment order
             if constexpr (MODE == PM_F32) {
-                for (int idx = tid - 256; idx < kBlkCB / 4; idx += 256) {
+#pragma unroll kStoreUnroll
+                for (int rr = 0; rr < kBlkCB / 4 / 256; ++rr) {
+                    const int idx = tid - 256 + rr * 256;
                     const int I = idx >> 8, g = (idx >> 6) & 3, ln = idx & 63;
                     const int tt = 16 * I + (ln & 15), j0 = frag_off4<MODE, CB>(ln >> 4, g);
                     *reinterpret_cast<float4 *>(ws.P + bh * kBlkCB + 4 * idx) =
                         *reinterpret_cast<const float4 *>(Ps + tt * LDJ + j0);
                 }
             } else {
-                for (int idx = tid - 256; idx < kBlkCB / 8; idx += 256) {
+#pragma unroll kStoreUnroll
+                for (int rr = 0; rr < kBlkCB / 8 / 256; ++rr) {
+                    const int idx = tid - 256 + rr * 256;
                     const int I = idx >> 7, m = (idx >> 6) & 1, ln = idx & 63;
                     const int tt = 16 * I + (ln & 15), j0 = 32 * m + 8 * (ln >> 4);
                     store_split(ws.P + bh * kBlkCB + I * 1024, m, ln, Ps + tt * LDJ + j0);
