@@ -340,14 +340,26 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 template <typename IOT>
 __device__ __forceinline__ void conv_rows(float *xr, const PrefillArgs &a, int t0, int tq, int ch)
 {
-    // opaque copy of the window start: without it the 19 row offsets are
-    // shared between calls and held live across the kernel's phases
-    int tb = t0 + tq - 3;
-    asm volatile("" : "+v"(tb));
+    // The window's rows t0 + tq - 3 .. t0 + tq + 15 (tq is the same in every
+    // lane of a wave) through a buffer resource over its rows inside [0, T):
+    // a row's address is one 32-bit add, and rows outside read as 0.
+    // conv_apply never uses those: they lie before the sequence's first token
+    // or past the input's end (tokens whose outputs are dropped).  A row
+    // before the resource's first one has a negative offset, which as an
+    // unsigned offset lies past the range.
+    const int tb = __builtin_amdgcn_readfirstlane(t0 + tq - 3), b0 = max(tb, 0);
+    const int rs = a.C * (int)sizeof(IOT);  // bytes between rows
+    const int nrows = max(min(tb + 19, a.T) - b0, 0);
+    const __amdgpu_buffer_rsrc_t xr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<IOT *>(static_cast<const IOT *>(a.x)) + (int64_t)b0 * a.C, (short)0, nrows * rs,
+        0x00020000);
+    const int vo = ch * (int)sizeof(IOT) + (tb - b0) * rs;
 #pragma unroll
     for (int r = 0; r < 19; ++r) {
-        const int64_t pos = max(min((int64_t)tb + r, (int64_t)a.T - 1), (int64_t)0);
-        xr[r] = ld<IOT>(a.x, pos * a.C + ch);
+        if constexpr (sizeof(IOT) == 2)
+            xr[r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr_rsrc, vo + r * rs, 0, 0) << 16);
+        else
+            xr[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr_rsrc, vo + r * rs, 0, 0));
     }
 }
 
@@ -926,10 +938,22 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         if constexpr (CONV) {
             conv_rows<IOT>(xvr, a, t0, tc, 2 * a.Hqk * DK + h * DK + cc);
         } else {
+            // through a buffer resource over the wave's rows tc .. nt - 1 of the
+            // tile (tc is the same in every lane of a wave): a row's address is
+            // one 32-bit add, and rows past the tile's end read as 0 (their
+            // beta is 0 too)
+            const int tw = __builtin_amdgcn_readfirstlane(tc);
+            const int vs = (int)(a.v_stride * (int64_t)sizeof(IOT));  // bytes between rows
+            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<IOT *>(static_cast<const IOT *>(a.v)) + ((int64_t)(t0 + tw) * a.v_stride + h * DK),
+                (short)0, max(nt - tw, 0) * vs, 0x00020000);
+            const int vo = cc * (int)sizeof(IOT);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int64_t tk = t0 + min(tc + i, nt - 1);
-                xvr[i] = ld<IOT>(a.v, tk * a.v_stride + h * DK + cc);
+                if constexpr (sizeof(IOT) == 2)
+                    xvr[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(vr, vo + i * vs, 0, 0) << 16);
+                else
+                    xvr[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, vo + i * vs, 0, 0));
             }
         }
         // (no barrier: step 4 reads neither N nor T until the barrier after
