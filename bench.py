@@ -90,11 +90,13 @@ def source_hash(*names) -> str:
 
 
 DECODE_SOURCES = ("decode_kernel.h", "la_device.h")
+PREFILL_SOURCES = ("prefill.hip", "la_device.h")
 
 
-def measured_traffic(tag: str, src_hash: str):
-    """HBM bytes per launch from profiles/<tag>.traffic.txt, or None when that
-    summary is absent or was taken for a different kernel source."""
+def measured_traffic(tag: str, src_hash: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes (per launch, or the `key` given) from profiles/<tag>.traffic.txt,
+    or None when that summary is absent or was taken for a different kernel
+    source."""
     path = os.path.join(PROFILES, f"{tag}.traffic.txt")
     if not os.path.exists(path):
         return None
@@ -103,9 +105,9 @@ def measured_traffic(tag: str, src_hash: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != src_hash or "hbm_bytes_per_launch" not in kv:
+    if kv.get("source_hash") != src_hash or key not in kv:
         return None
-    return float(kv["hbm_bytes_per_launch"])
+    return float(kv[key])
 
 
 def events():
@@ -427,6 +429,13 @@ def prefill_bench(dev, reps=20, per_graph=10):
     tf_issued = flops / (chunk_ms * 1e-3) / 1e12
     conv_bytes = sum(2 * cl[0].numel() * 2 for cl in calls)  # x read + y written, bf16
     conv_gbs = conv_bytes / (sum(t_conv) * 1e-3) / 1e9
+    # HBM view: the algorithmic bytes (q, k, v, g, beta read and the outputs
+    # written once per token-head, each sequence's state read and written
+    # once per call) against the kernels' measured traffic
+    alg_bytes = T_all * H * (3 * D * 2 + D * 4 + 4 + D * 2) + 11 * H * D * D * 4 * 2
+    traffic = measured_traffic("prefill_kda_h12_13600x3chunks_8x4096", source_hash(*PREFILL_SOURCES),
+                               "hbm_bytes_per_call_set")
+    hbm_gbs = traffic / (chunk_ms * 1e-3) / 1e9 if traffic else None
     f_conv, f_chunk = res_modes[0]
     f_w1 = sum(f_conv[:3]) + sum(f_chunk[:3])
     f_w2 = f_conv[3] + f_chunk[3]
@@ -449,7 +458,15 @@ def prefill_bench(dev, reps=20, per_graph=10):
                              "algorithmic flops (164 kFLOP per token-head) / time; issued "
                              "flops count the three bf16 products of every split step; the "
                              "chain over 213 dependent blocks of the 13,600-token sequence "
-                             "bounds W1"},
+                             "bounds W1",
+                     "hbm_view": {"bound": "hbm", "algorithmic_bytes": alg_bytes, "traffic": traffic,
+                                  "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": hbm_gbs / HBM_PEAK_GBS if hbm_gbs else None,
+                                  "traffic_over_algorithmic": traffic / alg_bytes if traffic else None,
+                                  "note": "measured HBM bytes of kernel 1 and the chain over the four "
+                                          "calls (rocprofv3 FETCH_SIZE / WRITE_SIZE) per chunked time; "
+                                          "the excess over the algorithmic bytes is the workspace "
+                                          "kernel 1 writes and the chain reads back"}},
         "conv_roofline": {"bound": "hbm", "achieved": conv_gbs, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": conv_gbs / HBM_PEAK_GBS},
         "fp32_mode": {
