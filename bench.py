@@ -318,12 +318,13 @@ def spec_bench(dev, D=8, L=16, reps=20):
 
 # --------------------------------------------------------------- prefill ----
 
-def prefill_mfma_flops(seqlens, Hv, mode=0) -> float:
+def prefill_mfma_flops(seqlens, Hv, mode=0, raw_q=False) -> float:
     """Matrix-core flops the two prefill kernels issue for one packed call,
     following their loop structure.  mode 0 (fp32): v_mfma_f32_16x16x4f32,
     2,048 flops each; mode 1 (bf16x3): three v_mfma_f32_16x16x32_bf16 per
     32-deep step, 16,384 flops each (the T-inverse level products stay fp32
-    in both modes)."""
+    in both modes).  raw_q (GDN, bf16 inputs, mode 1): the chain forms Q S^T
+    from the q rows themselves, two products per step instead of three."""
     T = int(sum(seqlens))
     tiles = -(-T // 64)
     if mode == 0:
@@ -332,7 +333,7 @@ def prefill_mfma_flops(seqlens, Hv, mode=0) -> float:
         per_chain_tile = (4 * 80 + 4 * 32) * 2048.0       # row waves D + O; column waves
     else:
         intra = tiles * Hv * ((240 + 288) * 16384.0 + 64 * 2048.0)
-        per_chain_tile = (4 * 30 + 4 * 12) * 16384.0
+        per_chain_tile = (4 * (26 if raw_q else 30) + 4 * 12) * 16384.0
     chain_tiles = 0
     cu = np.concatenate([[0], np.cumsum(seqlens)])
     for n in range(len(seqlens)):
@@ -524,7 +525,7 @@ def gdn_prefill_bench(dev, reps=20, per_graph=10):
         torch.cuda.synchronize()
         ms = time_replays(lambda: [call() for _ in range(per_graph)], per_graph, reps,
                           2)["median_ms_per_launch"]
-        flops = prefill_mfma_flops(sh.seqlens, Hv, mode)
+        flops = prefill_mfma_flops(sh.seqlens, Hv, mode, raw_q=mode == 1 and sh.io == "bf16")
         alg = PREFILL_ALG_FLOPS_PER_TOKEN_HEAD * sh.T * Hv
         peak = MFMA_BF16_PEAK_TFS if mode else MFMA_FP32_PEAK_TFS
         tf = alg / (ms * 1e-3) / 1e12

@@ -405,7 +405,7 @@ __device__ __forceinline__ void conv_apply(float *y, const float *xr, const Pref
 constexpr int kIntraThreads = 512;
 constexpr int kSeqTab = 512;  // sequences whose cu_seqlens / slot_in kernel 1 stages in LDS
 static_assert(kSeqTab == kIntraThreads, "one table entry per thread");
-constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + CB + 4 * DK;
+constexpr size_t kIntraLdsFloats = 3 * kRegion + 2 * CB * LDJ + 2 * CB + 4 * DK;
 constexpr size_t kIntraLds = kIntraLdsFloats * sizeof(float) + (5 * CB + 8 + 2 * kSeqTab) * sizeof(int);
 // per-token flags of kernel 1 (sub-pieces)
 enum { TF_OPEN = 1,      // no full reset between the piece start and the token
@@ -512,6 +512,15 @@ __device__ __forceinline__ void intra_issue_conv(IntraConvIn<IOT, KDA> &r, const
     conv_rows<IOT>(r.xk, a, t0, tc, a.Hqk * DK + kh * DK + cc);
 }
 
+// GDN with bf16 inputs in bf16x3 mode: the decayed queries are a per-token
+// scale of the q rows, which are exact bf16 matrix-core operands, so kernel 1
+// stores only that scale and the chain reads the q rows (shared by the value
+// heads of a q/k head) instead of a split copy of Q Gamma.
+template <typename IOT, bool KDA, int MODE, bool CONV> constexpr bool raw_q_chain()
+{
+    return !KDA && !CONV && MODE == PM_BF16X3 && std::is_same<IOT, bf16_t>::value;
+}
+
 template <typename IOT, bool KDA, int MODE, bool CONV>
 __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArgs a)
 {
@@ -524,7 +533,8 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     float *Tm = Nm + CB * LDJ;       // T = (I + N)^-1; in step 4 also a partial of A
     float *bet = Tm + CB * LDJ;      // beta
     float *qsum = bet + CB;          // [4][128] partial sums of the tile scan
-    int *pst = reinterpret_cast<int *>(qsum + 4 * DK);  // piece start, then sub-piece
+    float *inq = qsum + 4 * DK;      // 1 / |q_t| (0 past the input's end)
+    int *pst = reinterpret_cast<int *>(inq + CB);       // piece start, then sub-piece
                                                               // start (tile-local)
     int *pen = pst + CB;                                      // piece end (inclusive)
     int *sst = pen + CB;             // fused conv: the token's sequence start (global)
@@ -542,6 +552,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
     // exponentials overlap; with the fused conv's windows live that spills,
     // so there they stay loops
     constexpr int kStoreUnroll = CONV ? 1 : 4;
+    constexpr bool kRawQ = raw_q_chain<IOT, KDA, MODE, CONV>();
     // With fewer than kSeqTab sequences, cu_seqlens and slot_in go to LDS
     // once (one entry per thread; entries past N repeat the last one and are
     // never read) and tokens search them there.  Larger batches search
@@ -721,6 +732,7 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
         }
         if (cq == 0) {
             bet[t] = valid ? bt : 0.f;
+            inq[t] = valid ? iq : 0.f;
             pst[t] = ps;
             pen[t] = pe;
             tfl[t] = TF_OPEN | TF_LAST | (live == 0.f ? TF_RESET : 0);  // final unless a reset
@@ -888,6 +900,10 @@ __global__ void __launch_bounds__(kIntraThreads) prefill_intra_kernel(PrefillArg
                 *reinterpret_cast<float4 *>(ws.Qt + bh * kBlkDK + 4 * idx) =
                     make_float4(qn.x * e4.x, qn.y * e4.y, qn.z * e4.z, qn.w * e4.w);
             }
+        } else if constexpr (kRawQ) {
+            // GDN, bf16 inputs: Q Gamma = Diag(s) Q with s_t = exp(G_t - G_start) / |q_t|,
+            // so the chain reads the q rows themselves (exact bf16 operands) and s
+            if (tid < CB) ws.Qt[bh * kBlkDK + tid] = inq[tid] * tabS[tid];
         } else {  // split layout: thread = (row block I, step m, lane), 8 channels
 #pragma unroll kStoreUnroll
             for (int rr = 0; rr < kBlkDK / 8 / kIntraThreads; ++rr) {
@@ -1677,8 +1693,10 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off
 // the start of a block, ahead of its loads: the next block's W, Q Gamma and U
 // (into a second register buffer) and this block's P, spread over both
 // phases, so the loads are the youngest memory operations when a block
-// waits for them.
-template <typename IOT, typename ST, int NSL>
+// waits for them.  RAWQ (raw_q_chain): the row waves read the block's q rows
+// and the per-token scale s instead of Q Gamma, form Q S^T from two products
+// (the q rows exact in bf16, the state split) and scale its rows by s.
+template <typename IOT, typename ST, int NSL, bool RAWQ>
 __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(PrefillArgs a)
 {
     constexpr int NR = 16 * NSL;            // state rows of the workgroup
@@ -1688,8 +1706,8 @@ __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(Pref
     // next W, Q Gamma and U under phase 2 (kL2, over its 6 NSL products).  The
     // CU's memory queue is then fed through the whole block rather than only
     // while phase 1 runs, and a wave stalls less on a full queue.
-    constexpr int kL1 = 8, kL2 = 12 + NSL;
-    constexpr int LPS1 = (kL1 + NSL - 1) / NSL, MPL1 = 24 / LPS1;
+    constexpr int kL1 = 8, kL2 = (RAWQ ? 9 : 12) + NSL;
+    constexpr int LPS1 = (kL1 + NSL - 1) / NSL, MPL1 = (RAWQ ? 20 : 24) / LPS1;
     constexpr int LPS2 = (kL2 + NSL - 1) / NSL, MPL2 = (6 + LPS2 - 1) / LPS2;
     constexpr int LDO = NR + 4;             // row stride (floats) of the output staging
     constexpr int OPL = NR / 4;             // outputs a lane stores per block
@@ -1727,7 +1745,26 @@ __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(Pref
         };
         auto load_qu = [&](int tb, float *ops) {
             const int64_t bh = (int64_t)tb * a.Hv + h;
-            load_run(ops + 32, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            if constexpr (RAWQ) {
+                // ops [32, 48): the q row fragments of steps 0..3 (bf16 bits);
+                // [48, 52): s of the lane's four result tokens.  Rows past the
+                // input's end repeat its last row (their s is 0).
+                const int tok = min(tb * CB + 16 * I + li, a.T - 1);
+                const uint4 *qr = reinterpret_cast<const uint4 *>(
+                    static_cast<const IOT *>(a.q) + (int64_t)tok * a.q_stride + (h / a.G) * DK + 8 * lq);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint4 w = qr[4 * m];
+                    ops[32 + 4 * m] = __uint_as_float(w.x);
+                    ops[33 + 4 * m] = __uint_as_float(w.y);
+                    ops[34 + 4 * m] = __uint_as_float(w.z);
+                    ops[35 + 4 * m] = __uint_as_float(w.w);
+                }
+                const float4 s4 = *reinterpret_cast<const float4 *>(ws.Qt + bh * kBlkDK + 16 * I + 4 * lq);
+                ops[48] = s4.x; ops[49] = s4.y; ops[50] = s4.z; ops[51] = s4.w;
+            } else {
+                load_run(ops + 32, ws.Qt + bh * kBlkDK + fidx(8 * I, 0), 8, lane);
+            }
 #pragma unroll
             for (int sl = 0; sl < NSL; ++sl)
                 load_run(ops + 64 + 4 * sl, ws.U + bh * kBlkDK + fidx(8 * I + NSL * rs + sl, 0), 1,
@@ -1776,7 +1813,17 @@ __global__ void __launch_bounds__(kChainThreads, 1) prefill_chain_x3_kernel(Pref
                     const bf16x8_t sh = lds8(&SH[sr][32 * m + 8 * lq]);
                     const bf16x8_t sq = lds8(&SL[sr][32 * m + 8 * lq]);
                     mma3(m & 1 ? acc1 : acc, quad8(cur + 8 * m), quad8(cur + 8 * m + 4), sh, sq);
-                    mma3(oac[sl], quad8(cur + 32 + 8 * m), quad8(cur + 32 + 8 * m + 4), sh, sq);
+                    if constexpr (RAWQ) {  // q exact in bf16: no lo part
+                        const bf16x8_t qm = quad8(cur + 32 + 4 * m);
+                        oac[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm, sq, oac[sl], 0, 0, 0);
+                        oac[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm, sh, oac[sl], 0, 0, 0);
+                    } else {
+                        mma3(oac[sl], quad8(cur + 32 + 8 * m), quad8(cur + 32 + 8 * m + 4), sh, sq);
+                    }
+                }
+                if constexpr (RAWQ) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) oac[sl][r] *= cur[48 + r];
                 }
 #pragma unroll
                 for (int q = 0; q < LPS1; ++q) {
@@ -1952,6 +1999,17 @@ static int cu_count()
     return n;
 }
 
+template <typename IOT, typename ST, bool RAWQ>
+static void launch_chain_x3(const PrefillArgs &a, hipStream_t stream)
+{
+    if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: 16 state rows each
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, 1, RAWQ>),
+                           dim3(chain_grid(a, DK / 16)), dim3(kChainThreads), 0, stream, a);
+    else  // many: 64 state rows per workgroup
+        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, 4, RAWQ>),
+                           dim3(chain_grid(a, DK / 64)), dim3(kChainThreads), 0, stream, a);
+}
+
 template <typename IOT, typename ST, int MODE>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
 {
@@ -1985,12 +2043,14 @@ static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream)
     if constexpr (MODE == PM_F32)
         hipLaunchKernelGGL((prefill_chain_kernel<IOT, ST, MODE>), dim3(chain_grid(a, DK / 16)),
                            dim3(kChainThreads), kChainLds, stream, a);
-    else if ((int64_t)a.N * a.Hv * (DK / 16) <= 384)  // few workgroups: 16 state rows each
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, 1>),
-                           dim3(chain_grid(a, DK / 16)), dim3(kChainThreads), 0, stream, a);
-    else  // many: 64 state rows per workgroup
-        hipLaunchKernelGGL((prefill_chain_x3_kernel<IOT, ST, 4>),
-                           dim3(chain_grid(a, DK / 64)), dim3(kChainThreads), 0, stream, a);
+    else if constexpr (std::is_same<IOT, bf16_t>::value) {
+        if (!a.kda && !a.conv)  // kernel 1 stored s, not Q Gamma (raw_q_chain)
+            launch_chain_x3<IOT, ST, true>(a, stream);
+        else
+            launch_chain_x3<IOT, ST, false>(a, stream);
+    } else {
+        launch_chain_x3<IOT, ST, false>(a, stream);
+    }
     return hipGetLastError();
 }
 
