@@ -376,6 +376,41 @@ def test_sampled_kda_prefill_long_sequence_in_scheduler_chunks(mode, dev):
 
 
 @pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
+def test_sampled_gdn_prefill_long_sequence_in_scheduler_chunks(mode, dev):
+    """GDN prefill with 16 q/k heads shared by 32 value heads, bf16 I/O, fp32
+    state: one 13,600-token sequence in 6,144 / 6,144 / 1,312-token scheduler
+    chunks through pool slots (one sequence: the chain's 16-row form; in
+    bf16x3 mode it reads the q rows and kernel 1's per-token scale).  Value
+    heads 4 and 5 (both reading q/k head 2) and 30 are checked against the
+    oracle."""
+    Hqk, Hv = 16, 32
+    sh = synth.PrefillShape(seqlens=(13600,), Hqk=Hqk, Hv=Hv, dk=D, dv=D, kda=False)
+    inp = synth.prefill_inputs(sh, 1009, dev)
+    pool = torch.zeros((4, Hv, D, D), dtype=torch.float32, device=dev)
+    heads = [4, 5, 30]
+    o_ref, p_ref = run_oracle(sh, inp, pool, np.array([-1], np.int32), np.array([1], np.int32),
+                              heads)
+    print(f"[prefill parity] gdn 16/32 heads 13600 tokens in 3 chunks mode={mode}", flush=True)
+    cuts = [0, 6144, 12288, 13600]
+    outs = []
+    for c in range(3):
+        a, b = cuts[c], cuts[c + 1]
+        sub = {x: inp[x][a:b].contiguous() for x in ("q", "k", "v", "g", "beta")}
+        sub["cu_seqlens"] = torch.tensor([0, b - a], dtype=torch.int32, device=dev)
+        csh = synth.PrefillShape(seqlens=(b - a,), Hqk=Hqk, Hv=Hv, dk=D, dv=D, kda=False)
+        slot_in = np.array([-1 if c == 0 else c], np.int32)
+        outs.append(run_gpu(csh, sub, pool, slot_in, np.array([c + 1], np.int32),
+                            mode=MODES[mode]))
+    torch.cuda.synchronize()
+    split = mode == "bf16x3"
+    out = f64(torch.cat(outs))[:, heads]
+    assert_close_seqs(out, o_ref, [0, 13600], "bf16", "gdn 13600-token outputs (sampled heads)",
+                      etol=elem_tol("bf16", split))
+    assert_close_units(f64(pool[3])[heads], p_ref[1], 1, "fp32", "gdn end state (sampled heads)",
+                       etol=elem_tol("fp32", split))
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16x3"])
 def test_sampled_kda_prefill_eight_packed_sequences(mode, dev):
     """Eight 4,096-token sequences packed into one varlen call (H=12), fresh
     states to eight distinct slots; heads 3 and 11 checked."""
